@@ -1,0 +1,143 @@
+"""Paged decode attention in float64, by the definition.
+
+One query token per sequence attends over that sequence's keys, which sit in
+fixed-size pages found through the block table [metrale: paged decode
+launchers' doc comments]. Query head h reads kv head h / (Hq/Hkv), consecutive
+q heads sharing one kv head (R16) [AstrAI log: q_head/kv_head divisibility
+check]. The logit is the q.k dot product multiplied by the softmax scale after
+the dot [AstrAI log: numerics bullets]. With a sliding window W > 0 the
+sequence attends to its last W keys, the current one included (R17); W = 0
+means no window. An empty key range gives a zero output (R19).
+
+The split-KV form [metrale: paged_decode_attn_splitk_nvfp4 and
+paged_decode_attn_reduce_fp8: per split a partial output plus the softmax
+state (m, l), then a combine into the output; AstrAI log: split-KV decode with
+one shared combine]: the pages of the attended range are cut into chunks of
+``c`` pages, c = ceil(P / S) for a page bound P that the launch knows (R20);
+split i takes chunk i. Each split keeps o_i = sum p v / l_i (normalized),
+m_i = its largest scaled logit, l_i = sum exp(s - m_i); an empty split has
+m = -inf, l = 0, o = 0. The combine weighs split i by l_i * exp(m_i - M), M
+the largest m_i of a non-empty split, and divides by max(sum of weights,
+1e-20) [AstrAI log: divide-by-zero guard].
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+from .cache import CacheGeometry, read_kv_rows
+from .formats import bf16_to_f64
+
+
+def window_start(seq_len: int, sliding_window: int) -> int:
+    """First attended position: L - W when a window W > 0 is shorter than L."""
+    if sliding_window > 0 and seq_len > sliding_window:
+        return seq_len - sliding_window
+    return 0
+
+
+def attention_rows(q: np.ndarray, K: np.ndarray, V: np.ndarray, scale: float) -> np.ndarray:
+    """Softmax attention of q [Hq, D] over K, V [n, Hkv, D], float64."""
+    Hq, D = q.shape
+    n, Hkv, _ = K.shape
+    G = Hq // Hkv
+    out = np.zeros((Hq, D), dtype=np.float64)
+    if n == 0:
+        return out
+    for h in range(Hq):
+        g = h // G
+        s = (K[:, g, :] @ q[h]) * float(scale)
+        p = np.exp(s - s.max())
+        out[h] = (p @ V[:, g, :]) / p.sum()
+    return out
+
+
+def _q_rows(q_bits, b, Hq, D, q_stride):
+    flat = np.asarray(q_bits, dtype=np.uint16).reshape(-1)
+    idx = b * q_stride + np.arange(Hq)[:, None] * D + np.arange(D)[None, :]
+    return bf16_to_f64(flat[idx])
+
+
+def _seq_kv(geom, k_cache, v_cache, block_tables, b, lo, L, k_scale, v_scale):
+    j = np.arange(lo, L, dtype=np.int64)
+    bs = geom.block_size
+    pages = np.asarray(block_tables)[b, j // bs].astype(np.int64)
+    offs = j % bs
+    K = read_kv_rows(geom, k_cache, pages, offs, k_scale)
+    V = read_kv_rows(geom, v_cache, pages, offs, v_scale)
+    return K, V
+
+
+def paged_decode_attention(geom: CacheGeometry, q_bits, k_cache, v_cache, block_tables,
+                           seq_lens, num_q_heads, scale, q_stride=None,
+                           sliding_window=0, k_scale=1.0, v_scale=1.0, seqs=None) -> np.ndarray:
+    """Exact output [len(seqs), Hq, D] (float64) of paged decode attention:
+    gather the attended pages into contiguous K/V, dequantize, softmax."""
+    D = geom.head_dim
+    Hq = num_q_heads
+    q_stride = Hq * D if q_stride is None else q_stride
+    seq_lens = np.asarray(seq_lens).reshape(-1)
+    seqs = range(len(seq_lens)) if seqs is None else seqs
+    out = []
+    for b in seqs:
+        L = int(seq_lens[b])
+        lo = window_start(L, sliding_window)
+        K, V = _seq_kv(geom, k_cache, v_cache, block_tables, b, lo, L, k_scale, v_scale)
+        out.append(attention_rows(_q_rows(q_bits, b, Hq, D, q_stride), K, V, scale))
+    return np.stack(out) if out else np.zeros((0, Hq, D))
+
+
+def split_page_bound(max_blocks_per_seq: int, block_size: int, sliding_window: int) -> int:
+    """Most pages one sequence's attended range can touch: the block-table
+    width, or, with a window of W keys, (W + block_size - 2) // block_size + 1
+    when that is smaller (W keys starting mid-page)."""
+    bound = max_blocks_per_seq
+    if sliding_window > 0:
+        bound = min(bound, (sliding_window + block_size - 2) // block_size + 1)
+    return max(1, bound)
+
+
+def split_partials(geom: CacheGeometry, q_bits, k_cache, v_cache, block_tables, seq_lens,
+                   num_q_heads, scale, num_splits, max_blocks_per_seq, q_stride=None,
+                   sliding_window=0, k_scale=1.0, v_scale=1.0):
+    """Per-split partials: o [B, Hq, S, D] (normalized), m [B, Hq, S], l [B, Hq, S]."""
+    D, bs = geom.head_dim, geom.block_size
+    Hq = num_q_heads
+    q_stride = Hq * D if q_stride is None else q_stride
+    seq_lens = np.asarray(seq_lens).reshape(-1)
+    B, S = len(seq_lens), int(num_splits)
+    c = math.ceil(split_page_bound(max_blocks_per_seq, bs, sliding_window) / S)
+    o = np.zeros((B, Hq, S, D))
+    m = np.full((B, Hq, S), -np.inf)
+    l = np.zeros((B, Hq, S))
+    for b in range(B):
+        L = int(seq_lens[b])
+        lo = window_start(L, sliding_window)
+        p0, pend = lo // bs, (L + bs - 1) // bs
+        q = _q_rows(q_bits, b, Hq, D, q_stride)
+        G = Hq // geom.num_kv_heads
+        for i in range(S):
+            t0 = max(lo, (p0 + i * c) * bs)
+            t1 = min(L, min(p0 + (i + 1) * c, pend) * bs)
+            if t1 <= t0:
+                continue
+            K, V = _seq_kv(geom, k_cache, v_cache, block_tables, b, t0, t1, k_scale, v_scale)
+            for h in range(Hq):
+                s = (K[:, h // G, :] @ q[h]) * float(scale)
+                m[b, h, i] = s.max()
+                p = np.exp(s - m[b, h, i])
+                l[b, h, i] = p.sum()
+                o[b, h, i] = (p @ V[:, h // G, :]) / l[b, h, i]
+    return o, m, l
+
+
+def combine_partials(o: np.ndarray, m: np.ndarray, l: np.ndarray) -> np.ndarray:
+    """Merge split partials [B, Hq, S, ...] into the output [B, Hq, D]."""
+    live = l > 0
+    M = np.where(live, m, -np.inf).max(axis=-1, initial=-np.inf)
+    safe_M = np.where(np.isfinite(M), M, 0.0)
+    w = np.where(live, l * np.exp(np.where(live, m, 0.0) - safe_M[..., None]), 0.0)
+    num = (w[..., None] * o).sum(axis=-2)
+    den = np.maximum(w.sum(axis=-1), 1e-20)
+    return num / den[..., None]
