@@ -1,0 +1,217 @@
+/*
+ * pkd.h - C ABI of the paged KV decode library (MI355X / gfx950).
+ *
+ * Paged decode attention over a block-table KV cache: one query token per
+ * sequence, grouped-query heads, split-KV partials that carry the softmax
+ * state (max, sum), a combine pass into BF16, and BF16 / FP8-E4M3 / NVFP4
+ * caches filled through a slot mapping. The calls and their argument order
+ * follow the launchers of the metrale API page
+ * "metrale_model_layers/layers/ops/prefill_attn_b.rs" (the GPU-backend and
+ * kernel-handle arguments dropped, the stream passed as a hipStream_t).
+ *
+ * Conventions for every call
+ *  - Buffers are device pointers owned by the caller. The library never
+ *    allocates, frees or synchronizes; every call only enqueues kernels on
+ *    `stream` (0 = the null stream) and returns. No call reads device data
+ *    back to the host, so a sequence of calls can be captured in a HIP graph.
+ *  - BF16 data is passed as its 16-bit patterns (uint16_t). Counts are
+ *    uint32_t, byte sizes uint64_t, indices int32_t (page ids, sequence
+ *    lengths, slots), scales float.
+ *  - Return value: PKD_OK (0), or a negative status, in which case nothing
+ *    was enqueued (except PKD_ERR_LAUNCH, reported after a launch failed).
+ *    Only host-side arguments are validated; values that live in device
+ *    memory (sequence lengths, block-table entries, slots) are the caller's
+ *    contract as stated on each call.
+ *  - A call with no work (num_tokens, num_seqs or n_elems equal to 0) is a
+ *    valid no-op and may pass null buffers.
+ *  - Supported shapes: head_dim in {64, 128, 256, 512}; block_size in
+ *    {16, 32, 64, 128, 256}; num_q_heads a multiple of num_kv_heads (any
+ *    group size); 1 <= num_splits <= PKD_MAX_SPLITS.
+ *  - Alignment: every buffer is 16-byte aligned; element strides (q_stride,
+ *    key_stride, value_stride) are multiples of 8 elements; byte strides and
+ *    section sizes of the FP8 / NVFP4 caches are multiples of 16.
+ *
+ * Cache layouts (K and V are two separate pools with the same layout):
+ *  - BF16:  [num_pages][block_size][num_kv_heads][head_dim] elements; page p
+ *           starts at element p * block_size * num_kv_heads * head_dim (the
+ *           order stated for the BF16 split-K launcher on the metrale page).
+ *  - FP8:   the same index order, one E4M3FN byte per element, page p starts
+ *           at byte p * cache_stride.
+ *  - NVFP4: page p starts at byte p * block_stride_bytes. Its first
+ *           data_section_bytes hold E2M1 codes, the E4M3FN scales follow
+ *           (reshape_and_cache_nvfp4 on the metrale page). Element d of
+ *           (offset o, kv head h) is a nibble of byte (o*Hkv + h)*D/2 + d/2,
+ *           the low nibble holding the even element; its group scale is byte
+ *           data_section_bytes + (o*Hkv + h)*D/16 + d/16.
+ *  A slot s names page s / block_size, offset s % block_size.
+ */
+#ifndef PKD_H
+#define PKD_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PKD_OK 0
+#define PKD_ERR_INVALID_ARG (-1) /* null buffer with work to do, bad count, stride or alignment */
+#define PKD_ERR_UNSUPPORTED (-2) /* head_dim / block_size / num_splits outside the supported set */
+#define PKD_ERR_LAUNCH (-3)      /* the HIP runtime reported an error after the launch */
+
+#define PKD_MAX_SPLITS 4096u
+
+#if defined(__GNUC__)
+#define PKD_API __attribute__((visibility("default")))
+#else
+#define PKD_API
+#endif
+
+/* ---------------------------------------------------------------- cache writes
+ * Write each token's K and V rows into the paged cache at its slot_mapping
+ * slot; one workgroup per token (reshape_and_cache_nvfp4 on the metrale page).
+ *   key, value    BF16 [num_tokens] rows; token t, kv head h starts at element
+ *                 t*key_stride + h*head_dim (resp. value_stride).
+ *   k_cache, v_cache  the pools described above.
+ *   slot_mapping  int32 [num_tokens]. A negative slot skips the token. Valid
+ *                 slots must lie inside the pools and be distinct (two tokens
+ *                 writing one slot race). Bytes of slots not written, padding
+ *                 between sections and after a page's scales keep their value.
+ * Encoding (exact, bit for bit the same as the CPU oracle):
+ *   FP8:   code = E4M3FN(x / scale): IEEE float32 division, round to nearest
+ *          with ties to the even code, |y| >= 448 saturates to +-448, NaN ->
+ *          0x7F, the sign of y kept (a negative value that rounds to zero is
+ *          0x80); scale == 0 writes code 0.
+ *   NVFP4: per group of 16 consecutive elements of a row: amax = max |x|;
+ *          scale code = E4M3FN(amax / 6) with the same rounding; S its value;
+ *          S == 0 -> all 16 codes 0; else code_i = E2M1(x_i / S) (float32
+ *          division, ties to the even code, |y| >= 6 saturates, sign kept).
+ *          Non-finite inputs are outside the contract.
+ */
+PKD_API int reshape_and_cache_bf16(const uint16_t* key, const uint16_t* value,
+                                   uint16_t* k_cache, uint16_t* v_cache,
+                                   const int32_t* slot_mapping, uint32_t num_tokens,
+                                   uint32_t num_kv_heads, uint32_t head_dim,
+                                   uint32_t block_size, uint32_t key_stride,
+                                   uint32_t value_stride, hipStream_t stream);
+
+/* cache_stride: bytes between consecutive pages, >= block_size*num_kv_heads*head_dim. */
+PKD_API int reshape_and_cache_fp8(const uint16_t* key, const uint16_t* value,
+                                  uint8_t* k_cache, uint8_t* v_cache,
+                                  const int32_t* slot_mapping, uint32_t num_tokens,
+                                  uint32_t num_kv_heads, uint32_t head_dim,
+                                  uint32_t block_size, uint32_t key_stride,
+                                  uint32_t value_stride, float k_scale, float v_scale,
+                                  uint64_t cache_stride, hipStream_t stream);
+
+/* data_section_bytes >= block_size*num_kv_heads*head_dim/2;
+ * block_stride_bytes >= data_section_bytes + block_size*num_kv_heads*head_dim/16. */
+PKD_API int reshape_and_cache_nvfp4(const uint16_t* key, const uint16_t* value,
+                                    uint8_t* k_cache, uint8_t* v_cache,
+                                    const int32_t* slot_mapping, uint32_t num_tokens,
+                                    uint32_t num_kv_heads, uint32_t head_dim,
+                                    uint32_t block_size, uint32_t key_stride,
+                                    uint32_t value_stride, uint64_t block_stride_bytes,
+                                    uint64_t data_section_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------- FP8 calibration
+ * *out_max = max(*out_max, max_i |data[i]|) over n_elems BF16 values, folded in
+ * with an atomic max (bf16_absmax on the metrale page). NaN inputs are
+ * ignored. *out_max must hold a non-negative float on entry: the caller zeroes
+ * it before a new tensor. The FP8 scale of a tensor is then absmax / 448. */
+PKD_API int bf16_absmax(const uint16_t* data, float* out_max, uint64_t n_elems,
+                        hipStream_t stream);
+
+/* ---------------------------------------------------------------- split-K decode
+ * Paged decode attention, split-KV pass (paged_decode_attn_splitk_* on the
+ * metrale page). For sequence b and q head h:
+ *   kv head g = h / (num_q_heads / num_kv_heads);
+ *   L = seq_lens[b]; lo = (sliding_window > 0 && L > sliding_window)
+ *                         ? L - sliding_window : 0;
+ *   keys j in [lo, L), row j at page block_tables[b*max_blocks_per_seq + j/bs],
+ *   offset j % bs; logit s_j = (q . k_j) * scale (the scale applied after the
+ *   dot); output = softmax(s) . V.
+ * Split partition: the pages [lo/bs, ceil(L/bs)) are cut into chunks of
+ *   c = ceil(P / num_splits) pages, P = max_blocks_per_seq, or with a window
+ *   W > 0 the smaller of that and (W + bs - 2)/bs + 1; split i takes chunk i.
+ * Workspace: float32 [num_seqs][num_q_heads][num_splits][head_dim + 2]; split i
+ *   of (b, h) stores o (head_dim values, the split's softmax-normalized
+ *   output), m (its largest logit) and l (sum of exp(s_j - m)); an empty split
+ *   stores o = 0, m = -inf, l = 0. Size: paged_decode_workspace_bytes().
+ *   q:            BF16; row of (b, h) at element b*q_stride + h*head_dim,
+ *                 q_stride >= num_q_heads*head_dim.
+ *   block_tables: int32 [num_seqs][max_blocks_per_seq]; the entries of the
+ *                 first ceil(L/bs) columns of row b must be valid pages.
+ *   seq_lens:     int32 [num_seqs], 0 <= L <= max_blocks_per_seq*block_size.
+ *   scale:        softmax scale (1/sqrt(head_dim) typically), used as given.
+ *   sliding_window: 0 = attend to every key.
+ * Follow with paged_decode_attn_reduce() on the same stream. */
+PKD_API int paged_decode_attn_splitk_bf16(const uint16_t* q, const uint16_t* k_cache,
+                                          const uint16_t* v_cache, float* workspace,
+                                          const int32_t* block_tables, const int32_t* seq_lens,
+                                          uint32_t max_blocks_per_seq, uint32_t num_q_heads,
+                                          uint32_t num_kv_heads, uint32_t head_dim,
+                                          uint32_t block_size, float scale, uint32_t num_splits,
+                                          uint32_t q_stride, uint32_t num_seqs,
+                                          uint32_t sliding_window, hipStream_t stream);
+
+/* FP8-E4M3FN cache: k_j = code * k_scale, v_j = code * v_scale; cache_stride
+ * as for reshape_and_cache_fp8. */
+PKD_API int paged_decode_attn_splitk_fp8(const uint16_t* q, const uint8_t* k_cache,
+                                         const uint8_t* v_cache, float* workspace,
+                                         const int32_t* block_tables, const int32_t* seq_lens,
+                                         uint32_t max_blocks_per_seq, uint32_t num_q_heads,
+                                         uint32_t num_kv_heads, uint32_t head_dim,
+                                         uint32_t block_size, float scale, uint32_t num_splits,
+                                         float k_scale, float v_scale, uint32_t q_stride,
+                                         uint64_t cache_stride, uint32_t num_seqs,
+                                         uint32_t sliding_window, hipStream_t stream);
+
+/* NVFP4 cache: element = E2M1 value * E4M3 group scale. The sliding_window
+ * argument is an extension of the metrale NVFP4 launcher (0 = off). */
+PKD_API int paged_decode_attn_splitk_nvfp4(const uint16_t* q, const uint8_t* k_cache,
+                                           const uint8_t* v_cache, float* workspace,
+                                           const int32_t* block_tables, const int32_t* seq_lens,
+                                           uint32_t max_blocks_per_seq, uint32_t num_q_heads,
+                                           uint32_t num_kv_heads, uint32_t head_dim,
+                                           uint32_t block_size, float scale, uint32_t num_splits,
+                                           uint32_t q_stride, uint64_t block_stride_bytes,
+                                           uint64_t data_section_bytes, uint32_t num_seqs,
+                                           uint32_t sliding_window, hipStream_t stream);
+
+/* ---------------------------------------------------------------- combine
+ * Merge the split partials of every (b, h) into output BF16
+ * [num_seqs][num_q_heads][head_dim] (contiguous), one combine for every cache
+ * type (paged_decode_attn_reduce_fp8 on the metrale page): M = max m_i over
+ * splits with l_i > 0; w_i = l_i * exp(m_i - M); out = sum w_i o_i /
+ * max(sum w_i, 1e-20), rounded to BF16 (nearest even). A sequence with
+ * seq_lens[b] == 0 gets zeros. Deterministic: a fixed summation order. */
+PKD_API int paged_decode_attn_reduce(const float* workspace, uint16_t* output,
+                                     const int32_t* seq_lens, uint32_t num_q_heads,
+                                     uint32_t head_dim, uint32_t num_splits, uint32_t num_seqs,
+                                     hipStream_t stream);
+
+/* ---------------------------------------------------------------- host helpers
+ * Bytes of the split-K workspace: num_seqs*num_q_heads*num_splits*(head_dim+2)*4. */
+PKD_API size_t paged_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads,
+                                            uint32_t head_dim, uint32_t num_splits);
+
+/* A split count that gives every compute unit several waves: the sequences'
+ * (kv head, 16-q-head chunk) work items times the split count aims at 8 waves
+ * per CU, with at least 4 pages per split where the sequences are long
+ * enough. Pure host arithmetic; num_cus = the device's compute-unit count. */
+PKD_API uint32_t paged_decode_num_splits(uint32_t num_seqs, uint32_t num_q_heads,
+                                         uint32_t num_kv_heads, uint32_t max_blocks_per_seq,
+                                         uint32_t block_size, uint32_t sliding_window,
+                                         uint32_t num_cus);
+
+/* Static description of a status code. */
+PKD_API const char* pkd_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKD_H */

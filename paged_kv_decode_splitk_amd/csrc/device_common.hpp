@@ -1,0 +1,98 @@
+// Device-side helpers for gfx950: vector types, BF16 / E4M3FN / E2M1 codecs.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <cstdint>
+
+namespace pkd {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// float -> BF16 bits, round to nearest even (the gfx950 pack instruction).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float x) {
+  __bf16 b = (__bf16)x;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// Two floats -> packed BF16 pair (low half = a), round to nearest even.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return uint32_t(f32_to_bf16_bits(a)) | (uint32_t(f32_to_bf16_bits(b)) << 16);
+}
+
+// E4M3FN encode of an already divided value y, bit for bit the rounding the
+// cache format uses: nearest, ties to even code, saturate at 448, NaN -> 0x7F,
+// sign of y kept. Written from the format's definition (exponent bias 7,
+// subnormal step 2^-9).
+__device__ __forceinline__ uint32_t e4m3_from_f32(float y) {
+  const uint32_t u = __float_as_uint(y);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7Fu;  // NaN
+  const float a = __uint_as_float(u & 0x7FFFFFFFu);
+  if (a >= 448.0f) return sign | 0x7Eu;
+  if (a < 0.015625f) {                    // below 2^-6: multiples of 2^-9
+    const float q = __builtin_rintf(a * 512.0f);   // exact scaling; ties to even
+    return sign | uint32_t(q);            // q in [0, 8]; 8 is the code of 2^-6
+  }
+  const uint32_t ua = __float_as_uint(a);
+  int e = int(ua >> 23) - 127;            // -6 .. 8
+  uint32_t mant = (ua >> 20) & 7u;
+  const uint32_t rem = ua & 0xFFFFFu;
+  if (rem > 0x80000u || (rem == 0x80000u && (mant & 1u))) {
+    ++mant;
+    if (mant == 8u) { mant = 0; ++e; }
+  }
+  return sign | (uint32_t(e + 7) << 3) | mant;
+}
+
+// E4M3FN code -> float, exact; 0x7F / 0xFF -> NaN.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t c) {
+  const uint32_t s = (c & 0x80u) << 24;
+  const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  if (e == 15u && m == 7u) return __uint_as_float(0x7FC00000u | s);
+  float mag;
+  if (e == 0) mag = float(m) * 0.001953125f;                       // m * 2^-9
+  else mag = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return __uint_as_float(__float_as_uint(mag) | s);
+}
+
+// E2M1 code of y: nearest of {0, .5, 1, 1.5, 2, 3, 4, 6}, ties to the even
+// code, saturating at 6, sign bit from y.
+__device__ __forceinline__ uint32_t e2m1_from_f32(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 28) & 0x8u;
+  const float a = __builtin_fabsf(y);
+  uint32_t c;
+  if (a <= 0.25f) c = 0;
+  else if (a < 0.75f) c = 1;
+  else if (a <= 1.25f) c = 2;
+  else if (a < 1.75f) c = 3;
+  else if (a <= 2.5f) c = 4;
+  else if (a < 3.5f) c = 5;
+  else if (a <= 5.0f) c = 6;
+  else c = 7;                               // also NaN / inf (outside the contract)
+  return sign | c;
+}
+
+// wave64 reductions (full wave).
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+
+}  // namespace pkd

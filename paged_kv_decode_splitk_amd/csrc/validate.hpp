@@ -1,0 +1,123 @@
+// Host-side argument checks and launch arithmetic shared by the entry points.
+// Plain C++ (no HIP), so the checks can be built and exercised without a GPU.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+namespace pkd {
+
+constexpr int kOk = 0;
+constexpr int kInvalid = -1;
+constexpr int kUnsupported = -2;
+constexpr int kLaunch = -3;
+constexpr uint32_t kMaxSplits = 4096;
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+inline bool supported_head_dim(uint32_t d) { return d == 64 || d == 128 || d == 256 || d == 512; }
+
+inline bool supported_block_size(uint32_t bs) {
+  return bs == 16 || bs == 32 || bs == 64 || bs == 128 || bs == 256;
+}
+
+// Shape checks common to the three cache writes.
+inline int check_cache_write(const void* key, const void* value, const void* kc, const void* vc,
+                             const void* slots, uint32_t num_kv_heads, uint32_t head_dim,
+                             uint32_t block_size, uint32_t key_stride, uint32_t value_stride) {
+  if (num_kv_heads == 0) return kInvalid;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return kUnsupported;
+  const uint64_t row = uint64_t(num_kv_heads) * head_dim;
+  if (key_stride < row || value_stride < row) return kInvalid;
+  if ((key_stride % 8) || (value_stride % 8)) return kInvalid;
+  if (!key || !value || !kc || !vc || !slots) return kInvalid;
+  if (!aligned16(key) || !aligned16(value) || !aligned16(kc) || !aligned16(vc)) return kInvalid;
+  return kOk;
+}
+
+inline int check_fp8_stride(uint32_t num_kv_heads, uint32_t head_dim, uint32_t block_size,
+                            uint64_t cache_stride) {
+  const uint64_t page = uint64_t(block_size) * num_kv_heads * head_dim;
+  if (cache_stride < page || (cache_stride % 16)) return kInvalid;
+  return kOk;
+}
+
+inline int check_nvfp4_sections(uint32_t num_kv_heads, uint32_t head_dim, uint32_t block_size,
+                                uint64_t block_stride_bytes, uint64_t data_section_bytes) {
+  const uint64_t elems = uint64_t(block_size) * num_kv_heads * head_dim;
+  if (data_section_bytes < elems / 2 || (data_section_bytes % 16)) return kInvalid;
+  if (block_stride_bytes < data_section_bytes + elems / 16 || (block_stride_bytes % 16))
+    return kInvalid;
+  return kOk;
+}
+
+// Checks common to the three split-K decode calls.
+inline int check_decode(const void* q, const void* kc, const void* vc, const void* ws,
+                        const void* bt, const void* lens, uint32_t max_blocks_per_seq,
+                        uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
+                        uint32_t block_size, uint32_t num_splits, uint32_t q_stride) {
+  if (num_kv_heads == 0 || num_q_heads == 0 || num_q_heads % num_kv_heads) return kInvalid;
+  if (max_blocks_per_seq == 0) return kInvalid;
+  if (!supported_head_dim(head_dim) || !supported_block_size(block_size)) return kUnsupported;
+  if (num_splits == 0 || num_splits > kMaxSplits) return kUnsupported;
+  if (q_stride < uint64_t(num_q_heads) * head_dim || (q_stride % 8)) return kInvalid;
+  if (!q || !kc || !vc || !ws || !bt || !lens) return kInvalid;
+  if (!aligned16(q) || !aligned16(kc) || !aligned16(vc) || !aligned16(ws)) return kInvalid;
+  return kOk;
+}
+
+inline int check_reduce(const void* ws, const void* out, const void* lens, uint32_t num_q_heads,
+                        uint32_t head_dim, uint32_t num_splits) {
+  if (num_q_heads == 0) return kInvalid;
+  if (!supported_head_dim(head_dim)) return kUnsupported;
+  if (num_splits == 0 || num_splits > kMaxSplits) return kUnsupported;
+  if (!ws || !out || !lens) return kInvalid;
+  if (!aligned16(ws) || !aligned16(out)) return kInvalid;
+  return kOk;
+}
+
+// Most pages one sequence's attended key range can touch.
+inline uint32_t split_page_bound(uint32_t max_blocks_per_seq, uint32_t block_size,
+                                 uint32_t sliding_window) {
+  uint32_t bound = max_blocks_per_seq;
+  if (sliding_window > 0) {
+    const uint64_t w = (uint64_t(sliding_window) + block_size - 2) / block_size + 1;
+    if (w < bound) bound = uint32_t(w);
+  }
+  return bound ? bound : 1;
+}
+
+inline uint32_t pages_per_split(uint32_t max_blocks_per_seq, uint32_t block_size,
+                                uint32_t sliding_window, uint32_t num_splits) {
+  const uint32_t p = split_page_bound(max_blocks_per_seq, block_size, sliding_window);
+  return (p + num_splits - 1) / num_splits;
+}
+
+inline uint32_t head_chunks(uint32_t group) { return (group + 15) / 16; }
+
+inline size_t workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads, uint32_t head_dim,
+                              uint32_t num_splits) {
+  return size_t(num_seqs) * num_q_heads * num_splits * (size_t(head_dim) + 2) * sizeof(float);
+}
+
+// Split-count heuristic: aim at ~8 waves per CU in total, never fewer than
+// 4 pages per split unless the page bound itself is smaller.
+inline uint32_t num_splits_heuristic(uint32_t num_seqs, uint32_t num_q_heads,
+                                     uint32_t num_kv_heads, uint32_t max_blocks_per_seq,
+                                     uint32_t block_size, uint32_t sliding_window,
+                                     uint32_t num_cus) {
+  if (num_seqs == 0 || num_kv_heads == 0 || num_q_heads < num_kv_heads || block_size == 0)
+    return 1;
+  const uint64_t units =
+      uint64_t(num_seqs) * num_kv_heads * head_chunks(num_q_heads / num_kv_heads);
+  const uint64_t target = uint64_t(num_cus ? num_cus : 256) * 8;
+  uint64_t s = (target + units - 1) / units;
+  const uint32_t bound = split_page_bound(max_blocks_per_seq, block_size, sliding_window);
+  const uint64_t cap = bound >= 4 ? bound / 4 : 1;
+  if (s > cap) s = cap;
+  if (s < 1) s = 1;
+  if (s > kMaxSplits) s = kMaxSplits;
+  return uint32_t(s);
+}
+
+}  // namespace pkd

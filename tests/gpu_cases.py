@@ -1,0 +1,161 @@
+"""Helpers for the GPU parity tests: device pools written through the
+library, oracle pools written by the oracle from the same seeded inputs, and
+the comparison rule. Nothing here computes attention or encodes values."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import paged_kv_decode_splitk_amd as pkd
+
+POISON = {"bf16": 0x7FC0, "fp8": 0x7F, "nvfp4": 0x7F}    # NaN patterns
+ATOL = 1e-2
+RTOL = 1e-2
+
+
+def dev():
+    return torch.device("cuda:0")
+
+
+def u16_to_dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint16).view(np.int16)).to(dev())
+
+
+def i32_to_dev(a: np.ndarray) -> torch.Tensor:
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev())
+
+
+def pool_to_np(t: torch.Tensor, fmt: str) -> np.ndarray:
+    a = t.cpu().numpy()
+    return a.view(np.uint16) if fmt == "bf16" else a.view(np.uint8)
+
+
+def geometry(w, fmt=None, cache_stride=0, block_stride_bytes=0, data_section_bytes=0):
+    fmt = fmt or w.kv_dtype
+    return oracle.CacheGeometry(fmt, w.num_pages, w.block_size, w.num_kv_heads, w.head_dim,
+                                cache_stride=cache_stride, block_stride_bytes=block_stride_bytes,
+                                data_section_bytes=data_section_bytes)
+
+
+def alloc_pool(geom, fill) -> torch.Tensor:
+    n = geom.num_pages * geom.page_units()
+    if geom.fmt == "bf16":
+        return torch.full((n,), np.int16(np.uint16(fill).view(np.int16)), dtype=torch.int16,
+                          device=dev())
+    return torch.full((n,), int(fill), dtype=torch.uint8, device=dev())
+
+
+def gpu_absmax(bits: np.ndarray) -> float:
+    out = torch.zeros(1, dtype=torch.float32, device=dev())
+    x = u16_to_dev(bits.reshape(-1))
+    pkd.bf16_absmax(x, out)
+    torch.cuda.synchronize()
+    return float(out.item())
+
+
+class DeviceKV:
+    """K/V pools on the GPU, filled by the library's cache write."""
+
+    def __init__(self, w, geom, k_scale=1.0, v_scale=1.0, fill=None, tokens=None):
+        self.w, self.geom = w, geom
+        self.k_scale, self.v_scale = float(k_scale), float(v_scale)
+        fill = POISON[geom.fmt] if fill is None else fill
+        self.k = alloc_pool(geom, fill)
+        self.v = alloc_pool(geom, fill)
+        sel = slice(None) if tokens is None else tokens
+        key = u16_to_dev(w.k_bits[sel].reshape(-1, w.num_kv_heads * w.head_dim))
+        val = u16_to_dev(w.v_bits[sel].reshape(-1, w.num_kv_heads * w.head_dim))
+        slots = i32_to_dev(w.slot_mapping[sel])
+        Hkv, D, bs = w.num_kv_heads, w.head_dim, w.block_size
+        if geom.fmt == "bf16":
+            pkd.reshape_and_cache_bf16(key, val, self.k, self.v, slots, Hkv, D, bs)
+        elif geom.fmt == "fp8":
+            pkd.reshape_and_cache_fp8(key, val, self.k, self.v, slots, Hkv, D, bs, k_scale,
+                                      v_scale, cache_stride=geom.fp8_stride())
+        else:
+            stride, data = geom.nvfp4_sections()
+            pkd.reshape_and_cache_nvfp4(key, val, self.k, self.v, slots, Hkv, D, bs,
+                                        block_stride_bytes=stride, data_section_bytes=data)
+        del key, val, slots
+
+    def decode(self, num_splits, q_bits=None, sliding_window=None, q_stride=None, seq_lens=None,
+               return_ws=False):
+        w, g = self.w, self.geom
+        B, Hq, Hkv, D, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+        q_bits = w.q_bits if q_bits is None else q_bits
+        q_stride = Hq * D if q_stride is None else q_stride
+        window = w.sliding_window if sliding_window is None else sliding_window
+        lens_np = w.seq_lens if seq_lens is None else seq_lens
+        q = u16_to_dev(q_bits.reshape(-1))
+        bt = i32_to_dev(w.block_tables)
+        lens = i32_to_dev(lens_np)
+        ws = torch.empty(pkd.paged_decode_workspace_bytes(B, Hq, D, num_splits) // 4,
+                         dtype=torch.float32, device=dev())
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev())
+        common = (q, self.k, self.v, ws, bt, lens, w.max_blocks_per_seq, Hq, Hkv, D, bs,
+                  float(w.scale), num_splits)
+        if g.fmt == "bf16":
+            pkd.paged_decode_attn_splitk_bf16(*common, q_stride, B, window)
+        elif g.fmt == "fp8":
+            pkd.paged_decode_attn_splitk_fp8(*common, self.k_scale, self.v_scale, q_stride,
+                                             g.fp8_stride(), B, window)
+        else:
+            stride, data = g.nvfp4_sections()
+            pkd.paged_decode_attn_splitk_nvfp4(*common, q_stride, stride, data, B, window)
+        pkd.paged_decode_attn_reduce(ws, out, lens, Hq, D, num_splits, B)
+        torch.cuda.synchronize()
+        res = out.float().cpu().numpy().astype(np.float64)
+        if return_ws:
+            return res, ws.cpu().numpy().reshape(B, Hq, num_splits, D + 2)
+        return res
+
+
+def oracle_pools(w, geom, k_scale=1.0, v_scale=1.0, seqs=None, fill=None):
+    """Oracle pools written by the oracle's cache write (all tokens, or only
+    the tokens of the sequences in ``seqs``)."""
+    fill = POISON[geom.fmt] if fill is None else fill
+    kc, vc = oracle.new_cache(geom, fill), oracle.new_cache(geom, fill)
+    if seqs is None:
+        tok = np.arange(w.num_tokens)
+    else:
+        tok = np.nonzero(np.isin(w.token_seq, np.asarray(seqs)))[0]
+    oracle.reshape_and_cache(geom, w.k_bits[tok], w.v_bits[tok], kc, vc, w.slot_mapping[tok],
+                             k_scale=k_scale, v_scale=v_scale)
+    return kc, vc
+
+
+def oracle_decode(w, geom, kc, vc, k_scale=1.0, v_scale=1.0, seqs=None, q_bits=None,
+                  sliding_window=None, q_stride=None, seq_lens=None):
+    return oracle.paged_decode_attention(
+        geom, w.q_bits if q_bits is None else q_bits, kc, vc, w.block_tables,
+        w.seq_lens if seq_lens is None else seq_lens, w.num_q_heads, w.scale, q_stride=q_stride,
+        sliding_window=w.sliding_window if sliding_window is None else sliding_window,
+        k_scale=k_scale, v_scale=v_scale, seqs=seqs)
+
+
+def assert_close(got, ref, what=""):
+    err = np.abs(got - ref)
+    bad = ~(err <= ATOL + RTOL * np.abs(ref))
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside atol=rtol=1e-2; "
+                             f"max err {np.nanmax(err):.3e}; first {idx.tolist()}")
+    return float(err.max()) if err.size else 0.0
+
+
+def fp8_scales(w):
+    """Per-tensor FP8 scales from the GPU absmax (K, then V) and from the
+    oracle's absmax; they must agree bit for bit."""
+    k_gpu = gpu_absmax(w.k_bits)
+    v_gpu = gpu_absmax(w.v_bits)
+    k_ref = np.float32(0.0)
+    v_ref = np.float32(0.0)
+    flat_k = w.k_bits.reshape(-1)
+    flat_v = w.v_bits.reshape(-1)
+    step = 1 << 24
+    for i in range(0, flat_k.size, step):
+        k_ref = oracle.bf16_absmax(flat_k[i:i + step], k_ref)
+        v_ref = oracle.bf16_absmax(flat_v[i:i + step], v_ref)
+    assert np.float32(k_gpu) == k_ref and np.float32(v_gpu) == v_ref
+    return np.float32(k_ref) / np.float32(448.0), np.float32(v_ref) / np.float32(448.0)

@@ -1,0 +1,132 @@
+"""The C ABI library on the CPU (no GPU calls): it loads, exports exactly the
+symbols include/pkd.h declares, its host helpers compute what the header
+states, and argument validation returns the documented status codes before
+anything is launched."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import paged_kv_decode_splitk_amd as pkd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pkd.h")
+
+
+def _header_symbols():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"PKD_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(pkd.LIB_PATH):
+        pytest.skip("libpkd.so not built")
+    return pkd.lib()
+
+
+def test_header_and_binding_agree():
+    assert _header_symbols() == list(pkd.EXPORTED_SYMBOLS)
+
+
+def test_library_exports_exactly_the_header_symbols(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", pkd.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    text_syms = sorted(line.split()[-1] for line in out.splitlines()
+                       if len(line.split()) == 3 and line.split()[1] in ("T", "t"))
+    assert text_syms == _header_symbols()
+
+
+def test_workspace_bytes(lib):
+    assert pkd.paged_decode_workspace_bytes(32, 32, 128, 8) == 32 * 32 * 8 * 130 * 4
+    assert pkd.paged_decode_workspace_bytes(1, 1, 64, 1) == 66 * 4
+    assert pkd.paged_decode_workspace_bytes(0, 32, 128, 8) == 0
+
+
+def test_num_splits_heuristic(lib):
+    ns = pkd.paged_decode_num_splits
+    # B=1, 8 kv heads, 32K keys: 8 units -> 2048 waves wanted, 2048 pages / 4 = 512 cap
+    assert ns(1, 32, 8, 2048, 16, 0, 256) == 256
+    # B=32: 256 units -> 8 splits
+    assert ns(32, 32, 8, 256, 16, 0, 256) == 8
+    # tiny sequences are capped by their page bound (at least 4 pages per split)
+    assert ns(2, 4, 2, 4, 16, 0, 256) == 1
+    # a window bounds the pages: W=4096 -> 257 pages -> at most 64 splits
+    assert ns(1, 16, 8, 512, 16, 4096, 256) == 64
+    # more than 16 q heads per kv head counts head chunks as separate units
+    assert ns(1, 64, 1, 4096, 16, 0, 256) == 512
+    for args in [(0, 8, 8, 10, 16, 0, 256), (3, 8, 8, 1, 16, 0, 0)]:
+        assert ns(*args) >= 1
+
+
+def test_status_strings(lib):
+    assert pkd.pkd_status_string(0) == "ok"
+    assert pkd.pkd_status_string(-1) == "invalid argument"
+    assert pkd.pkd_status_string(-2) == "unsupported shape"
+    assert pkd.pkd_status_string(-3) == "kernel launch failed"
+    assert pkd.pkd_status_string(7) == "unknown status"
+
+
+A16 = 0x10000          # a 16-byte aligned, never dereferenced address
+
+
+def _decode(lib, **kw):
+    args = dict(q=A16, kc=A16, vc=A16, ws=A16, bt=A16, lens=A16, maxb=4, Hq=4, Hkv=2, D=64,
+                bs=16, scale=0.125, S=1, q_stride=256, B=2, W=0)
+    args.update(kw)
+    a = args
+    return lib.paged_decode_attn_splitk_bf16(a["q"], a["kc"], a["vc"], a["ws"], a["bt"], a["lens"],
+                                             a["maxb"], a["Hq"], a["Hkv"], a["D"], a["bs"],
+                                             a["scale"], a["S"], a["q_stride"], a["B"], a["W"],
+                                             None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), -1),
+    (dict(ws=None), -1),
+    (dict(q=A16 + 2), -1),              # misaligned
+    (dict(Hq=5), -1),                   # not a multiple of the kv heads
+    (dict(Hkv=0), -1),
+    (dict(maxb=0), -1),
+    (dict(q_stride=200), -1),           # shorter than Hq * D
+    (dict(q_stride=260), -1),           # not a multiple of 8
+    (dict(D=96), -2),
+    (dict(D=1024), -2),
+    (dict(bs=8), -2),
+    (dict(bs=48), -2),
+    (dict(S=0), -2),
+    (dict(S=4097), -2),
+])
+def test_decode_validation(lib, kw, status):
+    assert _decode(lib, **kw) == status
+
+
+def test_zero_work_calls_are_noops(lib):
+    assert _decode(lib, B=0, q=None, ws=None) == 0
+    assert lib.reshape_and_cache_bf16(None, None, None, None, None, 0, 2, 64, 16, 128, 128, None) == 0
+    assert lib.bf16_absmax(None, None, 0, None) == 0
+    assert lib.paged_decode_attn_reduce(None, None, None, 4, 64, 1, 0, None) == 0
+
+
+def test_fp8_nvfp4_specific_validation(lib):
+    f8 = lib.paged_decode_attn_splitk_fp8
+    ok = (A16, A16, A16, A16, A16, A16, 4, 4, 2, 64, 16, 0.125, 1, 1.0, 1.0, 256)
+    assert f8(*ok, 16 * 2 * 64 - 16, 2, 0, None) == -1     # cache stride shorter than a page
+    assert f8(*ok, 16 * 2 * 64 + 8, 2, 0, None) == -1      # not a multiple of 16
+    n4 = lib.paged_decode_attn_splitk_nvfp4
+    ok4 = (A16, A16, A16, A16, A16, A16, 4, 4, 2, 64, 16, 0.125, 1, 256)
+    data = 16 * 2 * 64 // 2
+    assert n4(*ok4, data + 128, data - 16, 2, 0, None) == -1   # data section too small
+    assert n4(*ok4, data + 64, data, 2, 0, None) == -1         # no room for the scales
+    assert n4(*ok4, data + 128 + 8, data, 2, 0, None) == -1    # stride not a multiple of 16
+    w = lib.reshape_and_cache_nvfp4
+    assert w(A16, A16, A16, A16, A16, 3, 2, 64, 16, 128, 128, data + 64, data, None) == -1
+    wf = lib.reshape_and_cache_fp8
+    assert wf(A16, A16, A16, A16, A16, 3, 2, 64, 16, 120, 128, 1.0, 1.0, 2048, None) == -1
+    assert wf(A16, A16, A16, A16, A16, 3, 2, 64, 16, 132, 128, 1.0, 1.0, 2048, None) == -1
+    assert lib.bf16_absmax(A16 + 2, A16, 10, None) == -1
+    assert lib.paged_decode_attn_reduce(A16, A16, A16, 4, 96, 1, 2, None) == -2
+    assert lib.paged_decode_attn_reduce(A16, A16, None, 4, 64, 1, 2, None) == -1

@@ -1,0 +1,285 @@
+"""GPU parity: the HIP library, called through the C ABI, against the CPU
+oracle on the same seeded inputs.
+
+Cache writes and the absmax must match bit for bit; attention outputs must lie
+within atol = rtol = 1e-2 of the float64 oracle (the tolerance of the AstrAI
+paged and contiguous decode tests, restated in the problem statement).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import paged_kv_decode_splitk_amd as pkd
+import workloads
+from gpu_cases import (DeviceKV, POISON, assert_close, dev, fp8_scales, geometry, gpu_absmax,
+                       i32_to_dev, oracle_decode, oracle_pools, pool_to_np, u16_to_dev)
+
+pytestmark = pytest.mark.gpu
+
+
+def _num_cus():
+    return torch.cuda.get_device_properties(0).multi_processor_count
+
+
+def _fp8_small_scales(w):
+    k = oracle.bf16_absmax(w.k_bits) / np.float32(448.0)
+    v = oracle.bf16_absmax(w.v_bits) / np.float32(448.0)
+    return np.float32(k), np.float32(v)
+
+
+# ------------------------------------------------------------------ cache writes
+
+@pytest.mark.parametrize("fmt,pad", [("bf16", 0), ("fp8", 0), ("fp8", 48), ("nvfp4", 0),
+                                     ("nvfp4", 32)])
+def test_cache_write_bit_exact(fmt, pad):
+    w = workloads.make_workload("tiny", lens=(17, 40, 5, 64), num_q_heads=8, num_kv_heads=2,
+                                head_dim=128, kv_dtype=fmt, sigma=1.5, seed=11)
+    w.slot_mapping[[3, 20]] = -1                    # skipped tokens
+    if fmt == "fp8":
+        geom = geometry(w, cache_stride=16 * 2 * 128 + pad)
+        ks, vs = _fp8_small_scales(w)
+    elif fmt == "nvfp4":
+        data = 16 * 2 * 128 // 2 + pad
+        geom = geometry(w, data_section_bytes=data, block_stride_bytes=data + 16 * 2 * 8 + pad)
+        ks = vs = 1.0
+    else:
+        geom = geometry(w)
+        ks = vs = 1.0
+    d = DeviceKV(w, geom, ks, vs)
+    kc, vc = oracle_pools(w, geom, ks, vs)
+    torch.cuda.synchronize()
+    assert np.array_equal(pool_to_np(d.k, fmt), kc)
+    assert np.array_equal(pool_to_np(d.v, fmt), vc)
+
+
+@pytest.mark.parametrize("scale", [1.0, 0.37, 1.0 / 448.0, 3.0e-3, 0.0])
+def test_fp8_encoder_exhaustive_over_bf16(scale):
+    """Every BF16 pattern (NaN and inf included) through the FP8 cache write."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    D, Hkv, bs = 256, 1, 16
+    T = bits.size // D
+    key = bits.reshape(T, Hkv, D)
+    val = key[::-1].copy()
+    slots = np.arange(T, dtype=np.int32)[::-1].copy()
+    geom = oracle.CacheGeometry("fp8", (T + bs - 1) // bs, bs, Hkv, D)
+    kc, vc = oracle.new_cache(geom, 0), oracle.new_cache(geom, 0)
+    oracle.reshape_and_cache(geom, key, val, kc, vc, slots, k_scale=scale, v_scale=scale)
+    kd = torch.zeros(kc.size, dtype=torch.uint8, device=dev())
+    vd = torch.zeros_like(kd)
+    pkd.reshape_and_cache_fp8(u16_to_dev(key), u16_to_dev(val), kd, vd, i32_to_dev(slots), Hkv, D,
+                              bs, scale, scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(kd.cpu().numpy(), kc)
+    assert np.array_equal(vd.cpu().numpy(), vc)
+
+
+def test_nvfp4_encoder_ties_and_ranges():
+    """Groups at exact E2M1 ties, saturating scales and a wide magnitude range."""
+    rng = np.random.default_rng(5)
+    G = 4096
+    S = oracle.e4m3_decode(rng.integers(0x08, 0x70, G).astype(np.uint8))
+    ties = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 0.0, 0.5, 1.0, 3.0, 4.0, 0.1, 2.2,
+                     5.9])
+    x = (S[:, None] * rng.permutation(np.tile(ties, (G, 1)).T).T
+         * np.where(rng.random((G, 16)) < 0.5, -1.0, 1.0))
+    x[: G // 4] *= rng.uniform(0.5, 1.5, (G // 4, 1))          # off-grid groups
+    x[G // 4: G // 2] = rng.standard_normal((G // 4, 16)) * np.exp(rng.uniform(-8, 8, (G // 4, 1)))
+    bits = workloads.bf16_bits_from_f32(x.astype(np.float32))
+    D, Hkv, bs = 512, 1, 16
+    T = bits.size // D
+    key = bits.reshape(T, Hkv, D)
+    slots = rng.permutation(T).astype(np.int32)
+    geom = oracle.CacheGeometry("nvfp4", (T + bs - 1) // bs, bs, Hkv, D)
+    kc, vc = oracle.new_cache(geom, 0xAB), oracle.new_cache(geom, 0xAB)
+    oracle.reshape_and_cache(geom, key, key, kc, vc, slots)
+    kd = torch.full((kc.size,), 0xAB, dtype=torch.uint8, device=dev())
+    vd = kd.clone()
+    pkd.reshape_and_cache_nvfp4(u16_to_dev(key), u16_to_dev(key), kd, vd, i32_to_dev(slots), Hkv, D,
+                                bs)
+    torch.cuda.synchronize()
+    assert np.array_equal(kd.cpu().numpy(), kc)
+
+
+@pytest.mark.parametrize("n", [1, 7, 8, 1000, 65536 + 3, 3_000_001])
+def test_absmax_bit_exact(n):
+    rng = np.random.default_rng(n)
+    x = workloads.bf16_bits_from_f32((rng.standard_normal(n) * 3).astype(np.float32))
+    if n > 10:
+        x[rng.integers(0, n, 5)] = 0x7FC0           # NaN is ignored
+        x[n - 1] = workloads.bf16_bits_from_f32(np.array([-1000.0], np.float32))[0]  # in the tail
+    assert np.float32(gpu_absmax(x)) == oracle.bf16_absmax(x)
+
+
+def test_absmax_folds_into_existing_value():
+    x = workloads.bf16_bits_from_f32(np.array([1.0, -2.0, 3.0, 0.5] * 64, np.float32))
+    out = torch.tensor([10.0], dtype=torch.float32, device=dev())
+    pkd.bf16_absmax(u16_to_dev(x), out)
+    torch.cuda.synchronize()
+    assert float(out.item()) == 10.0
+
+
+# ------------------------------------------------------------------ decode, small cases
+
+@pytest.mark.parametrize("S", [1, 3])
+def test_tiny_decode_and_partials(S):
+    w = workloads.make_workload("tiny")
+    geom = geometry(w)
+    d = DeviceKV(w, geom)
+    kc, vc = oracle_pools(w, geom)
+    got, ws = d.decode(S, return_ws=True)
+    ref = oracle_decode(w, geom, kc, vc)
+    assert_close(got, ref, f"tiny S={S}")
+    o, m, l = oracle.split_partials(geom, w.q_bits, kc, vc, w.block_tables, w.seq_lens,
+                                    w.num_q_heads, w.scale, S, w.max_blocks_per_seq)
+    live = l > 0
+    assert np.array_equal(ws[..., -1] > 0, live)
+    assert np.allclose(ws[..., -2][live], m[live], atol=1e-5, rtol=1e-5)
+    assert np.allclose(ws[..., -1][live], l[live], atol=1e-3, rtol=1e-2)
+    assert np.allclose(ws[..., :-2][live], o[live], atol=1e-2, rtol=1e-2)
+    assert np.all(np.isneginf(ws[..., -2][~live])) and np.all(ws[..., :-2][~live] == 0)
+
+
+CASES = [
+    # fmt, lens, Hq, Hkv, D, bs, window, S
+    ("bf16", (1, 15, 16, 17, 100, 300), 8, 2, 128, 16, 0, 1),
+    ("bf16", (1, 15, 16, 17, 100, 300), 8, 2, 128, 16, 0, 4),
+    ("bf16", (33, 257, 1000), 32, 8, 128, 16, 0, 7),
+    ("bf16", (5, 77, 130), 4, 4, 64, 32, 0, 2),
+    ("bf16", (64, 200), 16, 1, 256, 64, 0, 3),
+    ("bf16", (50, 180), 8, 1, 512, 16, 0, 2),
+    ("bf16", (90, 400), 40, 2, 128, 16, 0, 3),          # 20 q heads per kv head: two chunks
+    ("bf16", (90, 400, 17), 6, 2, 64, 16, 37, 3),       # sliding window, mid-page start
+    ("bf16", (90, 400, 17), 6, 2, 64, 128, 100, 2),
+    ("fp8", (1, 17, 300, 1000), 16, 8, 256, 16, 0, 3),
+    ("fp8", (1, 17, 300, 1000), 16, 8, 256, 16, 129, 5),
+    ("fp8", (40, 333), 4, 2, 64, 32, 0, 2),
+    ("fp8", (40, 333), 8, 1, 128, 16, 60, 2),
+    ("fp8", (40, 100), 16, 2, 512, 16, 0, 2),
+    ("nvfp4", (1, 17, 300, 1000), 16, 2, 512, 16, 0, 3),
+    ("nvfp4", (1, 17, 300, 700), 16, 2, 512, 16, 200, 4),
+    ("nvfp4", (40, 333), 8, 2, 128, 16, 0, 2),
+    ("nvfp4", (40, 333), 8, 2, 64, 32, 0, 2),
+    ("nvfp4", (40, 200), 4, 2, 256, 64, 0, 2),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[f"{c[0]}-D{c[4]}-G{c[2]//c[3]}-bs{c[5]}-W{c[6]}-S{c[7]}"
+                                             for c in CASES])
+def test_decode_matches_oracle(case):
+    fmt, lens, Hq, Hkv, D, bs, window, S = case
+    w = workloads.make_workload("tiny", lens=lens, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                                block_size=bs, sliding_window=window, kv_dtype=fmt, seed=D + S)
+    geom = geometry(w)
+    ks, vs = _fp8_small_scales(w) if fmt == "fp8" else (1.0, 1.0)
+    d = DeviceKV(w, geom, ks, vs)
+    kc, vc = oracle_pools(w, geom, ks, vs)
+    torch.cuda.synchronize()
+    assert np.array_equal(pool_to_np(d.k, fmt), kc)          # both sides read the same bytes
+    got = d.decode(S)
+    ref = oracle_decode(w, geom, kc, vc, ks, vs)
+    assert_close(got, ref, str(case))
+
+
+def test_empty_and_single_key_sequences():
+    w = workloads.make_workload("tiny", lens=(0, 1, 0, 1), num_q_heads=8, num_kv_heads=2,
+                                head_dim=128, seed=3)
+    geom = geometry(w)
+    d = DeviceKV(w, geom)
+    for S in (1, 2, 5):
+        got = d.decode(S)
+        assert np.all(got[[0, 2]] == 0)
+        # one key: softmax weight exactly 1, the output is its V row, bit for bit
+        V = oracle.bf16_to_f64(w.v_bits)                     # tokens: seq 1, seq 3
+        for i, b in enumerate((1, 3)):
+            for h in range(8):
+                assert np.array_equal(got[b, h], V[i, h // 4])
+
+
+def test_zero_query_gives_mean_of_values():
+    w = workloads.make_workload("tiny", lens=(37, 200), num_q_heads=4, num_kv_heads=2,
+                                head_dim=64, seed=4)
+    q0 = np.zeros_like(w.q_bits)
+    geom = geometry(w)
+    d = DeviceKV(w, geom)
+    got = d.decode(3, q_bits=q0)
+    kc, vc = oracle_pools(w, geom)
+    ref = oracle_decode(w, geom, kc, vc, q_bits=q0)
+    assert_close(got, ref, "q = 0")
+
+
+def test_q_stride_and_split_invariance():
+    w = workloads.make_workload("tiny", lens=(100, 513, 40), num_q_heads=16, num_kv_heads=4,
+                                head_dim=128, seed=6)
+    geom = geometry(w)
+    d = DeviceKV(w, geom)
+    stride = 16 * 128 + 64
+    qp = np.full((3, stride), 0x7FC0, np.uint16)              # NaN padding must not be read
+    qp[:, :16 * 128] = w.q_bits.reshape(3, -1)
+    kc, vc = oracle_pools(w, geom)
+    ref = oracle_decode(w, geom, kc, vc)
+    outs = [d.decode(S, q_bits=qp, q_stride=stride) for S in (1, 2, 9, 33, 200)]
+    for o in outs:
+        assert_close(o, ref, "q_stride / splits")
+
+
+def test_deterministic():
+    w = workloads.make_workload("tiny", lens=(100, 513, 40), num_q_heads=16, num_kv_heads=4,
+                                head_dim=128, seed=7)
+    d = DeviceKV(w, geometry(w))
+    a = d.decode(5)
+    b = d.decode(5)
+    assert np.array_equal(a, b)
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def _full_size(name, sample):
+    w = workloads.make_workload(name)
+    fmt = w.kv_dtype
+    print(f"[{name}] B={w.num_seqs} T={w.num_tokens} fmt={fmt}", flush=True)
+    geom = geometry(w)
+    if fmt == "fp8":
+        ks, vs = fp8_scales(w)
+    else:
+        ks = vs = 1.0
+    d = DeviceKV(w, geom, ks, vs)
+    S = pkd.paged_decode_num_splits(w.num_seqs, w.num_q_heads, w.num_kv_heads,
+                                    w.max_blocks_per_seq, w.block_size, w.sliding_window,
+                                    _num_cus())
+    got = d.decode(S)
+    seqs = sample(w)
+    kc, vc = oracle_pools(w, geom, ks, vs, seqs=seqs)
+    # the pages of the sampled sequences hold the same bytes on both sides
+    units = geom.page_units()
+    kd = pool_to_np(d.k, fmt).reshape(w.num_pages, units)
+    ko = kc.reshape(w.num_pages, units)
+    vd = pool_to_np(d.v, fmt).reshape(w.num_pages, units)
+    vo = vc.reshape(w.num_pages, units)
+    for b in seqs:
+        n = (int(w.seq_lens[b]) + w.block_size - 1) // w.block_size
+        pages = w.block_tables[b, :n]
+        full = pages[: int(w.seq_lens[b]) // w.block_size]      # completely written pages
+        assert np.array_equal(kd[full], ko[full]) and np.array_equal(vd[full], vo[full])
+    ref = oracle_decode(w, geom, kc, vc, ks, vs, seqs=seqs)
+    err = assert_close(got[seqs], ref, name)
+    print(f"[{name}] num_splits={S} sampled seqs={list(seqs)} max_abs_err={err:.3e}", flush=True)
+    del d
+    torch.cuda.empty_cache()
+
+
+def _spread(w, k=4):
+    order = np.argsort(w.seq_lens)
+    pick = {int(order[0]), int(order[-1])}
+    pick.update(int(i) for i in np.linspace(0, w.num_seqs - 1, k).astype(int))
+    return sorted(pick)
+
+
+@pytest.mark.parametrize("name", ["llama8b", "fp8", "nvfp4"])
+def test_full_size_batched(name):
+    _full_size(name, _spread)
+
+
+@pytest.mark.parametrize("name", ["b1_1k", "b1_4k", "b1_8k", "b1_16k", "b1_32k"])
+def test_full_size_b1_long_context(name):
+    _full_size(name, lambda w: [0])

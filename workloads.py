@@ -113,16 +113,29 @@ def make_workload(
     extra_pages: int = 8,
     identity_pages: bool = False,
     with_kv: bool = True,
+    num_q_heads: Optional[int] = None,
+    num_kv_heads: Optional[int] = None,
+    head_dim: Optional[int] = None,
+    block_size: Optional[int] = None,
+    sliding_window: Optional[int] = None,
+    sigma: Optional[float] = None,
 ) -> DecodeWorkload:
     """Draw a workload. ``num_seqs`` keeps the first sequence lengths of the
     full draw and draws everything else at that smaller size (a sample of the
     same distribution, not a slice of the full run's values); ``lens``
     overrides the lengths; ``identity_pages`` lays the pool out in order
-    instead of shuffling it; ``with_kv=False`` skips K/V."""
+    instead of shuffling it; ``with_kv=False`` skips K/V. The shape
+    arguments override the named workload's heads, head_dim, block size,
+    window and K/V standard deviation."""
     spec = _SPECS[name]
-    (dt, B, Hq, Hkv, D, bs, lens_spec, window, sigma, seed0, splits) = spec
-    if kv_dtype is not None:
-        dt = kv_dtype
+    (dt, B, Hq, Hkv, D, bs, lens_spec, window, sig, seed0, splits) = spec
+    dt = kv_dtype or dt
+    Hq = num_q_heads or Hq
+    Hkv = num_kv_heads or Hkv
+    D = head_dim or D
+    bs = block_size or bs
+    window = window if sliding_window is None else sliding_window
+    sigma = sig if sigma is None else sigma
     rng = np.random.default_rng(seed0 if seed is None else seed)
 
     if lens is not None:
@@ -137,7 +150,7 @@ def make_workload(
         B = num_seqs
 
     pages_per_seq = (seq_lens + bs - 1) // bs
-    if name == "tiny" and lens is None and num_seqs is None:
+    if name == "tiny" and lens is None and num_seqs is None and block_size is None:
         # 8 physical pages laid out as a 2 x 4 table; entries past a
         # sequence's last page are valid page ids that are never read.
         max_blocks = 4
@@ -146,7 +159,7 @@ def make_workload(
         block_tables = perm.reshape(B, max_blocks).astype(np.int32)
     else:
         max_blocks = int(max(1, pages_per_seq.max(initial=1)))
-        if lens_spec[0] == "uniform" and lens is None:
+        if lens_spec[0] == "uniform" and lens is None and block_size is None:
             max_blocks = int((lens_spec[2] + bs - 1) // bs)
         used = int(pages_per_seq.sum())
         num_pages = used + extra_pages
