@@ -1,0 +1,371 @@
+"""Benchmark of one paged decode step on one MI355X.
+
+A step is the whole decode path for one attention layer over one batch:
+write the new token's K/V through slot_mapping (reshape_and_cache), run the
+split-KV pass and the combine. Inputs are seeded synthetic tensors already
+resident in HBM. Steps rotate over several layers' KV pools whose total size
+is several times the 256 MB Infinity Cache, so every step reads its KV from
+HBM, as the layers of a model do. The timed loop replays a HIP graph of one
+step per layer.
+
+Prints ONE JSON line: KV-read GB/s and us/step on the Llama-3-8B-shaped batch
+(B=32), the B=1 32K-context figures beside it, the roofline of the split-KV
+kernel (live HIP-event timing), and the float64 CPU oracle timed on the host.
+
+  python bench.py [--steps K] [--warmup W] [--workload NAME] [--extra NAME ...]
+  python bench.py --copy-calibration      # plain copy of known size (for rocprof counters)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KV-read HBM GB/s (% of peak) + us/decode step, B=32 and B=1@32K ctx"
+PEAK_HBM_GBS = 8000.0
+MALL_BYTES = 256 << 20
+DESCRIPTIONS = {
+    "llama8b": "Llama-3-8B-shaped BF16 decode: B=32, 32 q / 8 kv heads, head_dim 128, block 16, "
+               "seq_lens U[512, 4096], shuffled page pool",
+    "b1_32k": "B=1 BF16 decode at 32K context: 32 q / 8 kv heads, head_dim 128, block 16",
+    "b1_16k": "B=1 BF16 decode at 16K context: 32 q / 8 kv heads, head_dim 128, block 16",
+    "b1_8k": "B=1 BF16 decode at 8K context: 32 q / 8 kv heads, head_dim 128, block 16",
+    "b1_4k": "B=1 BF16 decode at 4K context: 32 q / 8 kv heads, head_dim 128, block 16",
+    "b1_1k": "B=1 BF16 decode at 1K context: 32 q / 8 kv heads, head_dim 128, block 16",
+    "fp8": "FP8-E4M3 KV decode: B=64, 16 q / 8 kv heads, head_dim 256, block 16, "
+           "seq_lens U[1K, 8K], sliding window 4096",
+    "nvfp4": "NVFP4 KV decode: B=16, 16 q / 2 kv heads, head_dim 512, block 16, "
+             "seq_lens U[2K, 16K]",
+}
+
+
+def kv_bytes_per_token(w) -> int:
+    """Algorithmic K+V bytes one attended token costs (all kv heads)."""
+    D, Hkv = w.head_dim, w.num_kv_heads
+    if w.kv_dtype == "bf16":
+        return 2 * Hkv * D * 2
+    if w.kv_dtype == "fp8":
+        return 2 * Hkv * D
+    return 2 * Hkv * (D // 2 + D // 16)
+
+
+def attended_tokens(w) -> int:
+    L = w.seq_lens.astype(np.int64)
+    if w.sliding_window > 0:
+        return int(np.minimum(L, w.sliding_window).sum())
+    return int(L.sum())
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "paged_kv_decode_splitk_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+class Layers:
+    """NL layers' K/V pools of one workload, written by the library's cache write."""
+
+    def __init__(self, w, num_layers=None, dev="cuda:0"):
+        import torch
+        import paged_kv_decode_splitk_amd as pkd
+        self.w, self.dev = w, torch.device(dev)
+        B, Hq, Hkv, D, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+        fmt = w.kv_dtype
+        if fmt == "bf16":
+            self.page_units = bs * Hkv * D
+            pool_dtype = torch.int16
+            page_bytes = self.page_units * 2
+        elif fmt == "fp8":
+            self.page_units = bs * Hkv * D
+            pool_dtype = torch.uint8
+            page_bytes = self.page_units
+        else:
+            self.block_stride, self.data_section = pkd.nvfp4_default_sections(Hkv, D, bs)
+            self.page_units = self.block_stride
+            pool_dtype = torch.uint8
+            page_bytes = self.page_units
+        pool_bytes = 2 * w.num_pages * page_bytes
+        if num_layers is None:
+            num_layers = max(2, int(np.ceil(4 * MALL_BYTES / pool_bytes)))
+        self.num_layers = num_layers
+        self.pool_bytes = pool_bytes
+
+        def u16(a):
+            return torch.from_numpy(np.ascontiguousarray(a, np.uint16).view(np.int16)).to(self.dev)
+
+        key = u16(w.k_bits.reshape(w.num_tokens, -1))
+        val = u16(w.v_bits.reshape(w.num_tokens, -1))
+        slots = torch.from_numpy(w.slot_mapping).to(self.dev)
+        self.k_scale = self.v_scale = 1.0
+        if fmt == "fp8":          # calibration: absmax of K, then V, scale = absmax / 448
+            amax = torch.zeros(2, dtype=torch.float32, device=self.dev)
+            pkd.bf16_absmax(key, amax[0:1])
+            pkd.bf16_absmax(val, amax[1:2])
+            a = amax.cpu().numpy()
+            self.k_scale = float(np.float32(a[0]) / np.float32(448.0))
+            self.v_scale = float(np.float32(a[1]) / np.float32(448.0))
+        self.k, self.v = [], []
+        for _ in range(num_layers):
+            kp = torch.zeros(w.num_pages * self.page_units, dtype=pool_dtype, device=self.dev)
+            vp = torch.zeros_like(kp)
+            self._write(key, val, kp, vp, slots)
+            self.k.append(kp)
+            self.v.append(vp)
+        last = w.last_token_index()
+        live = last >= 0
+        self.new_key = key[torch.from_numpy(last[live]).to(self.dev)].contiguous()
+        self.new_val = val[torch.from_numpy(last[live]).to(self.dev)].contiguous()
+        self.new_slots = slots[torch.from_numpy(last[live]).to(self.dev)].contiguous()
+        del key, val, slots
+        self.q = u16(w.q_bits.reshape(-1))
+        self.bt = torch.from_numpy(w.block_tables).to(self.dev)
+        self.lens = torch.from_numpy(w.seq_lens).to(self.dev)
+        cus = torch.cuda.get_device_properties(self.dev).multi_processor_count
+        self.num_splits = pkd.paged_decode_num_splits(B, Hq, Hkv, w.max_blocks_per_seq, bs,
+                                                      w.sliding_window, cus)
+        self.ws = torch.empty(pkd.paged_decode_workspace_bytes(B, Hq, D, self.num_splits) // 4,
+                              dtype=torch.float32, device=self.dev)
+        self.out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=self.dev)
+        torch.cuda.synchronize()
+
+    def _write(self, key, val, kp, vp, slots):
+        import paged_kv_decode_splitk_amd as pkd
+        w = self.w
+        args = (key, val, kp, vp, slots, w.num_kv_heads, w.head_dim, w.block_size)
+        if w.kv_dtype == "bf16":
+            pkd.reshape_and_cache_bf16(*args)
+        elif w.kv_dtype == "fp8":
+            pkd.reshape_and_cache_fp8(*args, self.k_scale, self.v_scale)
+        else:
+            pkd.reshape_and_cache_nvfp4(*args, self.block_stride, self.data_section)
+
+    def splitk(self, layer):
+        import paged_kv_decode_splitk_amd as pkd
+        w = self.w
+        common = (self.q, self.k[layer], self.v[layer], self.ws, self.bt, self.lens,
+                  w.max_blocks_per_seq, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size,
+                  float(w.scale), self.num_splits)
+        qs = w.num_q_heads * w.head_dim
+        if w.kv_dtype == "bf16":
+            pkd.paged_decode_attn_splitk_bf16(*common, qs, w.num_seqs, w.sliding_window)
+        elif w.kv_dtype == "fp8":
+            pkd.paged_decode_attn_splitk_fp8(*common, self.k_scale, self.v_scale, qs,
+                                             self.page_units, w.num_seqs, w.sliding_window)
+        else:
+            pkd.paged_decode_attn_splitk_nvfp4(*common, qs, self.block_stride, self.data_section,
+                                               w.num_seqs, w.sliding_window)
+
+    def step(self, layer):
+        import paged_kv_decode_splitk_amd as pkd
+        w = self.w
+        self._write(self.new_key, self.new_val, self.k[layer], self.v[layer], self.new_slots)
+        self.splitk(layer)
+        pkd.paged_decode_attn_reduce(self.ws, self.out, self.lens, w.num_q_heads, w.head_dim,
+                                     self.num_splits, w.num_seqs)
+
+
+def time_workload(name, steps, warmup, kernel_reps=200):
+    import torch
+    import workloads
+    w = workloads.make_workload(name)
+    lay = Layers(w)
+    NL = lay.num_layers
+    # warm up eagerly (also loads the code objects), then capture one step per layer
+    for i in range(max(1, warmup)):
+        lay.step(i % NL)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for layer in range(NL):
+            lay.step(layer)
+    reps = max(1, -(-steps // NL))
+    steps_run = reps * NL
+    for _ in range(max(1, warmup // NL)):
+        graph.replay()
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record()
+    for _ in range(reps):
+        graph.replay()
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / steps_run
+
+    # split-KV kernel alone: HIP events around each launch on the launching stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(kernel_reps)]
+    for i, (a, b) in enumerate(evs):
+        a.record()
+        lay.splitk(i % NL)
+        b.record()
+    torch.cuda.synchronize()
+    k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+
+    kv_bytes = attended_tokens(w) * kv_bytes_per_token(w)
+    res = dict(
+        workload=name, description=DESCRIPTIONS.get(name, name), kv_dtype=w.kv_dtype,
+        num_seqs=w.num_seqs, num_splits=lay.num_splits, layers_rotated=NL,
+        kv_pool_bytes_per_layer=lay.pool_bytes, attended_tokens=attended_tokens(w),
+        kv_bytes_per_step=kv_bytes, steps=steps_run, ms_per_step=ms_step,
+        us_per_step=ms_step * 1e3, kv_gbs=kv_bytes / (ms_step * 1e-3) / 1e9,
+        wall_s=wall, splitk_us=k_ms * 1e3, splitk_gbs=kv_bytes / (k_ms * 1e-3) / 1e9,
+    )
+    res["pct_of_peak"] = 100.0 * res["kv_gbs"] / PEAK_HBM_GBS
+    del lay, graph
+    torch.cuda.empty_cache()
+    return res, w
+
+
+def traffic_record(name):
+    """HBM bytes per split-KV launch from committed rocprof counter runs, if the
+    kernel sources still match the ones that were profiled."""
+    path = os.path.join(ROOT, "profiles", f"traffic_splitk_{name}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_hash") != source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(w, budget_s=12.0, max_reps=50):
+    """The float64 oracle on the host: repeated decode steps of the same
+    workload (gather + dequantize + attention of every sequence) until the
+    time budget is spent; the caches are written once before timing."""
+    import oracle
+    from threadpoolctl import threadpool_info
+    geom = oracle.CacheGeometry(w.kv_dtype, w.num_pages, w.block_size, w.num_kv_heads,
+                                w.head_dim)
+    kc, vc = oracle.new_cache(geom, 0), oracle.new_cache(geom, 0)
+    oracle.reshape_and_cache(geom, w.k_bits, w.v_bits, kc, vc, w.slot_mapping)
+    kv_bytes = attended_tokens(w) * kv_bytes_per_token(w)
+    per_seq = []
+    total_t, total_bytes, reps = 0.0, 0, 0
+    lens = w.seq_lens.astype(np.int64)
+    while total_t < budget_s and reps < max_reps:
+        for b in range(w.num_seqs):
+            t0 = time.perf_counter()
+            oracle.paged_decode_attention(geom, w.q_bits, kc, vc, w.block_tables, w.seq_lens,
+                                          w.num_q_heads, w.scale, sliding_window=w.sliding_window,
+                                          seqs=[b])
+            dt = time.perf_counter() - t0
+            total_t += dt
+            L = lens[b] if w.sliding_window <= 0 else min(lens[b], w.sliding_window)
+            total_bytes += int(L) * kv_bytes_per_token(w)
+            if total_t >= budget_s:
+                break
+        reps += 1
+    blas = [p.get("num_threads", 1) for p in threadpool_info()]
+    threads = max(blas) if blas else 1
+    return dict(value=total_bytes / total_t / 1e9, unit="GB/s", cores=int(threads),
+                kind="oracle",
+                sample=(f"{w.name}: float64 NumPy oracle decode (page gather, dequant, softmax "
+                        f"attention) of the workload's sequences, {total_bytes / kv_bytes:.2f} "
+                        f"steps' worth of KV in {total_t:.1f} s; cache write untimed; "
+                        f"{len(os.sched_getaffinity(0))} host cores visible, BLAS threads "
+                        f"{threads}"),
+                s_per_step=total_t * kv_bytes / total_bytes)
+
+
+def copy_calibration(nbytes=1 << 30, reps=5):
+    """A plain device copy of known size, for scaling the rocprof byte counters."""
+    import torch
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda:0")
+    b = torch.empty_like(a)
+    for _ in range(reps):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": nbytes, "reps": reps}))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--workload", default="llama8b")
+    ap.add_argument("--extra", nargs="*", default=["b1_32k"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: the paged decode path runs on a single MI355X "
+              "and has no multi-GPU mode; run it with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if args.copy_calibration:
+        copy_calibration()
+        return
+    print(f"bench: {args.workload} steps={args.steps} warmup={args.warmup}", file=sys.stderr,
+          flush=True)
+    main_res, w = time_workload(args.workload, args.steps, args.warmup)
+    print(f"bench: {args.workload} {main_res['us_per_step']:.2f} us/step "
+          f"{main_res['kv_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+    extras = {}
+    for name in args.extra:
+        r, _ = time_workload(name, args.steps, args.warmup)
+        extras[name] = {k: r[k] for k in ("us_per_step", "kv_gbs", "pct_of_peak", "splitk_us",
+                                          "splitk_gbs", "num_splits", "kv_bytes_per_step",
+                                          "layers_rotated")}
+        print(f"bench: {name} {r['us_per_step']:.2f} us/step {r['kv_gbs']:.0f} GB/s",
+              file=sys.stderr, flush=True)
+
+    achieved = main_res["splitk_gbs"]
+    traffic = traffic_record(args.workload)
+    roofline = dict(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s",
+                    frac=achieved / PEAK_HBM_GBS, traffic=traffic,
+                    kernel=f"paged_decode_attn_splitk_{main_res['kv_dtype']}",
+                    algorithmic_bytes_per_launch=main_res["kv_bytes_per_step"],
+                    avg_launch_us=main_res["splitk_us"])
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, budget_s=args.cpu_budget)
+    line = {
+        "metric": METRIC,
+        "value": main_res["kv_gbs"],
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": main_res["steps"],
+        "warmup": args.warmup,
+        "ms_per_step": main_res["ms_per_step"],
+        "us_per_step": main_res["us_per_step"],
+        "pct_of_peak": main_res["pct_of_peak"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": main_res["kv_dtype"],
+        "data": "synthetic (seeded N(0,1) q/k/v, shuffled page pool)",
+        "config": {
+            "workload": main_res["description"],
+            "num_splits": main_res["num_splits"],
+            "layers_rotated": main_res["layers_rotated"],
+            "kv_bytes_per_step": main_res["kv_bytes_per_step"],
+            "step": "reshape_and_cache of the new token + split-KV pass + combine, "
+                    "HIP-graph replay",
+        },
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+    }
+    for name, r in extras.items():
+        line[name] = r
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

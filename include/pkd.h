@@ -198,10 +198,11 @@ PKD_API int paged_decode_attn_reduce(const float* workspace, uint16_t* output,
 PKD_API size_t paged_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads,
                                             uint32_t head_dim, uint32_t num_splits);
 
-/* A split count that gives every compute unit several waves: the sequences'
- * (kv head, 16-q-head chunk) work items times the split count aims at 8 waves
- * per CU, with at least 4 pages per split where the sequences are long
- * enough. Pure host arithmetic; num_cus = the device's compute-unit count. */
+/* A split count for the split-K calls: splits of about 16 pages, or fewer
+ * pages (down to 2) when the batch's (sequence, kv head, 16-q-head chunk)
+ * work items would otherwise give fewer than ~4 waves per compute unit. The
+ * page bound is max_blocks_per_seq (or the window's). Pure host arithmetic;
+ * num_cus = the device's compute-unit count. */
 PKD_API uint32_t paged_decode_num_splits(uint32_t num_seqs, uint32_t num_q_heads,
                                          uint32_t num_kv_heads, uint32_t max_blocks_per_seq,
                                          uint32_t block_size, uint32_t sliding_window,

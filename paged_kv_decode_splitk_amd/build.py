@@ -30,6 +30,7 @@ def hipcc_command(out=LIB_PATH):
         "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
         "-I", os.path.join(ROOT, "include"),
+        *os.environ.get("PKD_EXTRA_HIPCC_FLAGS", "").split(),
         "-o", out, *sources(),
     ]
 

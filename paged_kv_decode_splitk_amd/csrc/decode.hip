@@ -65,8 +65,12 @@ struct Traits {
   static constexpr int NLOAD = D / (4 * E);                 // loads per tile per lane
   static constexpr int MPER = E / 8;                        // bf16x8 fragments per load
   static constexpr int NFRAG = D / 32;                      // QK MFMAs per tile
-  static constexpr int RS = D + 8;                          // LDS row stride (elements)
+  static constexpr int RS = D + 16;                         // LDS row stride (elements)
   static constexpr int ROW_BYTES = D * kElemBits / 8;       // bytes of one (token, head) row
+  // tiles in flight per wave: about 128 VGPRs of raw K+V bytes, 1 to 4 tiles
+  static constexpr int kTileRegs = 2 * NLOAD * (kLoadBytes / 4 + (FMT == kNvfp4 ? 1 : 0));
+  static constexpr int kRing = 128 / kTileRegs;
+  static constexpr int NBUF = kRing < 1 ? 1 : (kRing > 4 ? 4 : kRing);
 };
 
 // Raw bytes of one lane's share of a K or V tile.
@@ -76,39 +80,56 @@ struct RawTile {
   uint32_t s[Traits<FMT, D>::NLOAD];     // NVFP4 group-scale bytes
 };
 
+// Loads one lane's share of a K or V tile with buffer instructions. The
+// descriptor covers one page; live == false gives it zero records, so the
+// loads return zeros without touching memory (phantom tiles past the end of a
+// split keep the loop's load count uniform).
 template <int FMT, int D>
 __device__ __forceinline__ void load_tile(RawTile<FMT, D>& t, const uint8_t* pool,
-                                          const DecodeArgs& a, uint32_t phys, uint32_t off,
-                                          uint32_t kvh, int g) {
+                                          const DecodeArgs& a, uint32_t phys, bool live,
+                                          uint32_t off, uint32_t kvh, int g) {
   using T = Traits<FMT, D>;
-  const uint64_t page = uint64_t(phys) * a.page_bytes;
-  const uint64_t rowidx = uint64_t(off) * a.num_kv_heads + kvh;   // (offset, head) row
-  const uint8_t* row = pool + page + rowidx * T::ROW_BYTES;
+  const uint8_t* page = pool + uint64_t(phys) * a.page_bytes;
+  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(page), 0, live ? int(a.page_bytes) : 0, 0x00020000);
+  const uint32_t rowidx = off * a.num_kv_heads + kvh;               // (offset, head) row
 #pragma unroll
   for (int r = 0; r < T::NLOAD; ++r) {
     const int e0 = r * 4 * T::E + g * T::E;                        // first element
-    const uint8_t* p = row + (e0 * T::kElemBits) / 8;
+    const int voff = int(rowidx * T::ROW_BYTES + (e0 * T::kElemBits) / 8);
     if constexpr (T::kLoadBytes == 16) {
-      t.d[r] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+      t.d[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, 0, 2));
     } else {
-      const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+      const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rsrc, voff, 0, 2));
       t.d[r][0] = v[0];
       t.d[r][1] = v[1];
     }
     if constexpr (FMT == kNvfp4) {
-      const uint8_t* sp = pool + page + a.data_section + rowidx * (D / 16) + e0 / 16;
-      if constexpr (T::E == 32) t.s[r] = *reinterpret_cast<const uint16_t*>(sp);
-      else t.s[r] = *sp;
+      const int soff = int(a.data_section) + int(rowidx * (D / 16) + e0 / 16);
+      if constexpr (T::E == 32) t.s[r] = __builtin_amdgcn_raw_buffer_load_b16(rsrc, soff, 0, 2);
+      else t.s[r] = __builtin_amdgcn_raw_buffer_load_b8(rsrc, soff, 0, 2);
     }
   }
 }
 
-__device__ __forceinline__ float e2m1_value(uint32_t c) {
-  // magnitudes 0, .5, 1, 1.5, 2, 3, 4, 6 from the exponent / mantissa bits
-  const uint32_t e = (c >> 1) & 3u, m = c & 1u;
-  uint32_t bits = e ? (((e + 126u) << 23) | (m << 22)) : (m ? 0x3F000000u : 0u);
-  bits |= (c & 8u) << 28;
-  return __uint_as_float(bits);
+// Two FP8-E4M3FN codes (bytes `hi` selects 0/1 or 2/3 of w) -> packed BF16 pair.
+// gfx950 converts E4M3FN exactly; every value fits BF16.
+template <bool HI>
+__device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
+  const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
+  return pack_bf16x2(f[0], f[1]);
+}
+
+// Two E2M1 codes (byte `sel` of w) times scale S -> packed BF16 pair (exact).
+__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w, int sel, float S) {
+  f32x2 f;
+  switch (sel) {
+    case 0: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); break;
+    case 1: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); break;
+    case 2: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); break;
+    default: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); break;
+  }
+  return pack_bf16x2(f[0] * S, f[1] * S);
 }
 
 // Fragment f (8 consecutive elements) of a lane's load r, as BF16.
@@ -121,32 +142,34 @@ __device__ __forceinline__ bf16x8 dequant_frag(const RawTile<FMT, D>& t, int r, 
 #pragma unroll
     for (int w = 0; w < 2; ++w) {
       const uint32_t word = t.d[r][2 * f + w];
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float lo = e4m3_to_f32((word >> (16 * h)) & 0xFFu);
-        const float hi = e4m3_to_f32((word >> (16 * h + 8)) & 0xFFu);
-        out[2 * w + h] = pack_bf16x2(lo, hi);      // exact: codes fit BF16
-      }
+      out[2 * w] = fp8x2_to_bf16x2<false>(word);
+      out[2 * w + 1] = fp8x2_to_bf16x2<true>(word);
     }
     return __builtin_bit_cast(bf16x8, out);
   } else {
     // 8 codes = one 32-bit word; group scale = byte f/2 of the lane's scales
     const uint32_t word = t.d[r][f];
-    const float S = e4m3_to_f32((t.s[r] >> (8 * (f >> 1))) & 0xFFu);
+    const float S = (f >> 1) ? __builtin_amdgcn_cvt_f32_fp8(t.s[r], 1)
+                             : __builtin_amdgcn_cvt_f32_fp8(t.s[r], 0);
     u32x4 out;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float lo = e2m1_value((word >> (8 * i)) & 0xFu) * S;
-      const float hi = e2m1_value((word >> (8 * i + 4)) & 0xFu) * S;
-      out[i] = pack_bf16x2(lo, hi);                // exact: <= 6 significant bits
-    }
+    for (int i = 0; i < 4; ++i) out[i] = fp4x2_to_bf16x2(word, i, S);
     return __builtin_bit_cast(bf16x8, out);
   }
+}
+
+// Orders this wave's LDS accesses around the V transpose for the compiler; a
+// wave's LDS operations execute in issue order, so no wait is needed.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 template <int FMT, int D>
 __global__ __launch_bounds__(64) void splitk_kernel(DecodeArgs a) {
   using T = Traits<FMT, D>;
+  constexpr int NBUF = T::NBUF;
   const int lane = threadIdx.x;
   const int g = lane >> 4;          // lane group: k-run for loads, token quad for outputs
   const int n = lane & 15;          // head column / token row / dim column
@@ -180,6 +203,11 @@ __global__ __launch_bounds__(64) void splitk_kernel(DecodeArgs a) {
     return;
   }
 
+  const uint32_t tpp = bs / 16;                              // tiles per page
+  const uint32_t t0 = max(pa * tpp, lo / 16);
+  const uint32_t t1 = min(pb * tpp, (L + 15) / 16);
+  const int32_t* bt = a.block_tables + uint64_t(b) * a.max_blocks;
+
   // q as the B operand of the QK MFMAs: column n = head, k-run of group g.
   bf16x8 qf[T::NFRAG];
   {
@@ -195,22 +223,10 @@ __global__ __launch_bounds__(64) void splitk_kernel(DecodeArgs a) {
   }
 
   __shared__ __attribute__((aligned(16))) uint16_t vlds[16 * T::RS];
-
-  const uint32_t tpp = bs / 16;                              // tiles per page
-  const uint32_t t0 = max(pa * tpp, lo / 16);
-  const uint32_t t1 = min(pb * tpp, (L + 15) / 16);
-  const int32_t* bt = a.block_tables + uint64_t(b) * a.max_blocks;
-
-  // block-table entries of the split, 64 at a time, one per lane
-  uint32_t bt_base = pa;
-  int32_t bt_reg = (pa + lane < pb) ? bt[pa + lane] : 0;
-  auto phys_of = [&](uint32_t page) -> uint32_t {
-    if (page >= bt_base + 64) {
-      bt_base = page;
-      bt_reg = (page + lane < pb) ? bt[page + lane] : 0;
-    }
-    return uint32_t(__builtin_amdgcn_readlane(bt_reg, int(page - bt_base)));
-  };
+  // transposed-read address of this lane: row 4g + n/4, column 4*(n%4) (+16 per M tile)
+  typedef __attribute__((address_space(3))) uint16_t lds_u16;
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  lds_u16* const tr_base = (lds_u16*)(vlds) + (4 * g + (n >> 2)) * T::RS + 4 * (n & 3);
 
   f32x4 acc[D / 16];
 #pragma unroll
@@ -218,86 +234,104 @@ __global__ __launch_bounds__(64) void splitk_kernel(DecodeArgs a) {
   float m_run = -__builtin_inff();
   float l_run = 0.0f;
 
-  RawTile<FMT, D> kn, vn;
-  {
-    const uint32_t page = t0 / tpp, off = (t0 % tpp) * 16 + n;
-    const uint32_t phys = phys_of(page);
-    load_tile<FMT, D>(kn, a.k_cache, a, phys, off, kvh, g);
-    load_tile<FMT, D>(vn, a.v_cache, a, phys, off, kvh, g);
-  }
+  RawTile<FMT, D> kb[NBUF], vb[NBUF];
 
-  for (uint32_t t = t0; t < t1; ++t) {
-    RawTile<FMT, D> kt = kn, vt = vn;
-    if (t + 1 < t1) {
-      const uint32_t page = (t + 1) / tpp, off = ((t + 1) % tpp) * 16 + n;
-      const uint32_t phys = phys_of(page);
-      load_tile<FMT, D>(kn, a.k_cache, a, phys, off, kvh, g);
-      load_tile<FMT, D>(vn, a.v_cache, a, phys, off, kvh, g);
-    }
-    const uint32_t tok0 = t * 16;
-
-    // ---- S = K Q^T
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  // Pages in chunks of 64 (one block-table entry per lane); within a chunk the
+  // NBUF-deep register ring keeps NBUF tiles of K and V in flight.
+  for (uint32_t cp = pa; cp < pb; cp += 64) {
+    const uint32_t cpe = min(cp + 64, pb);
+    const int32_t bt_reg = (cp + lane < cpe) ? bt[cp + lane] : 0;
+    const uint32_t ct0 = max(cp * tpp, t0);
+    const uint32_t ct1 = min(cpe * tpp, t1);
+    auto issue = [&](RawTile<FMT, D>& dst, const uint8_t* pool, uint32_t t) {
+      const bool live = t < ct1;
+      const uint32_t page = min(t / tpp, cpe - 1);
+      const uint32_t phys = uint32_t(__builtin_amdgcn_readlane(bt_reg, int(page - cp)));
+      load_tile<FMT, D>(dst, pool, a, phys, live, (t % tpp) * 16 + n, kvh, g);
+    };
 #pragma unroll
-    for (int c = 0; c < T::NFRAG; ++c) {
-      const bf16x8 kf = dequant_frag<FMT, D>(kt, c / T::MPER, c % T::MPER);
-      s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c], s, 0, 0, 0);
+    for (int s = 0; s < NBUF; ++s) {
+      issue(kb[s], a.k_cache, ct0 + s);
+      issue(vb[s], a.v_cache, ct0 + s);
     }
 
-    // ---- online softmax (lane: head n, tokens tok0 + 4g + j)
-    float sv[4];
-    float mx = -__builtin_inff();
+    for (uint32_t tb = ct0; tb < ct1; tb += NBUF) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t tok = tok0 + 4 * g + j;
-      sv[j] = (tok >= lo && tok < L) ? s[j] * a.logit_scale : -__builtin_inff();
-      mx = fmaxf(mx, sv[j]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-    const float m_new = fmaxf(m_run, mx);                   // finite: the tile holds a key
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
-    uint32_t pbits[4];
-    float psum = 0.0f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float p = __builtin_amdgcn_exp2f(sv[j] - m_new);
-      pbits[j] = f32_to_bf16_bits(p);
-      psum += __uint_as_float(pbits[j] << 16);
-    }
-    l_run = l_run * alpha + psum;
-    s16x4 pf;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) pf[j] = short(pbits[j]);
+      for (int s = 0; s < NBUF; ++s) {
+        const uint32_t t = tb + s;                 // t >= ct1: phantom tile, all keys masked
+        const uint32_t tok0 = t * 16;
+        const uint32_t klo = lo, khi = t < ct1 ? L : 0u;
 
-    // ---- V tile -> LDS rows (token n of the tile), masked tokens as zeros
-    {
-      const uint32_t tok = tok0 + n;
-      const bool ok = tok >= lo && tok < L;
-      uint16_t* dst = vlds + n * T::RS;
+        // ---- S = K Q^T, then the slot's K registers take the tile NBUF ahead
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < T::NLOAD; ++r) {
-#pragma unroll
-        for (int f = 0; f < T::MPER; ++f) {
-          u32x4 v = __builtin_bit_cast(u32x4, dequant_frag<FMT, D>(vt, r, f));
-          if (!ok) v = u32x4{0u, 0u, 0u, 0u};
-          *reinterpret_cast<u32x4*>(dst + r * 4 * T::E + g * T::E + 8 * f) = v;
+        for (int c = 0; c < T::NFRAG; ++c) {
+          const bf16x8 kf = dequant_frag<FMT, D>(kb[s], c / T::MPER, c % T::MPER);
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c], sc, 0, 0, 0);
         }
+        // the refill reuses the slot's registers only if it stays after their last use
+        __builtin_amdgcn_sched_barrier(0);
+        issue(kb[s], a.k_cache, t + NBUF);
+
+        // ---- V tile -> LDS rows (token n of the tile), masked tokens as zeros
+        {
+          const uint32_t tok = tok0 + n;
+          const bool ok = tok >= klo && tok < khi;
+          uint16_t* dst = vlds + n * T::RS;
+#pragma unroll
+          for (int r = 0; r < T::NLOAD; ++r) {
+#pragma unroll
+            for (int f = 0; f < T::MPER; ++f) {
+              u32x4 v = __builtin_bit_cast(u32x4, dequant_frag<FMT, D>(vb[s], r, f));
+              if (!ok) v = u32x4{0u, 0u, 0u, 0u};
+              *reinterpret_cast<u32x4*>(dst + r * 4 * T::E + g * T::E + 8 * f) = v;
+            }
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        issue(vb[s], a.v_cache, t + NBUF);
+
+        // ---- online softmax (lane: head n, tokens tok0 + 4g + j)
+        float sv[4];
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t tok = tok0 + 4 * g + j;
+          sv[j] = (tok >= klo && tok < khi) ? sc[j] * a.logit_scale : -__builtin_inff();
+          mx = fmaxf(mx, sv[j]);
+        }
+        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+        // finite: the first tile of a split holds a key, phantom tiles come after it
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        uint32_t pbits[4];
+        float psum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p = __builtin_amdgcn_exp2f(sv[j] - m_new);
+          pbits[j] = f32_to_bf16_bits(p);
+          psum += __uint_as_float(pbits[j] << 16);
+        }
+        l_run = l_run * alpha + psum;
+        s16x4 pf;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pf[j] = short(pbits[j]);
+
+        wave_lds_fence();
+        // ---- O^T += V^T P  (A: V^T rows = dims of M tile mt, k = tokens 4g..4g+3)
+#pragma unroll
+        for (int mt = 0; mt < D / 16; ++mt) {
+          const bf16x4 vt =
+              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tr_base + mt * 16));
+          f32x4 c = acc[mt] * alpha;
+          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vt), pf,
+                                                              c, 0, 0, 0);
+        }
+        wave_lds_fence();
       }
     }
-    __syncthreads();
-
-    // ---- O^T += V^T P  (A: V^T rows = dims, k = tokens 4g..4g+3)
-#pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt) {
-      s16x4 vf;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) vf[j] = short(vlds[(4 * g + j) * T::RS + mt * 16 + n]);
-      f32x4 c = acc[mt] * alpha;
-      acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(vf, pf, c, 0, 0, 0);
-    }
-    __syncthreads();
   }
 
   // ---- partial state out: o = acc / l, m in natural-log units
@@ -319,34 +353,331 @@ __global__ __launch_bounds__(64) void splitk_kernel(DecodeArgs a) {
   }
 }
 
-// Combine: one wavefront per (sequence, q head).
+// ---------------------------------------------------------------------------
+// BF16 cache: K and V tiles stream into an LDS ring with direct-to-LDS buffer
+// loads (gfx950 16-byte LDS DMA). Each load instruction moves whole rows:
+// lane l of instruction i fetches row i*RPI + l/CPR of the tile, and the
+// 16-byte chunk (l % CPR) ^ row of it, so the tile lands in LDS row-major
+// with the chunks of row r XOR-permuted by r. Reading K as the MFMA A
+// operand (16 rows, one chunk each) then hits 16 different bank groups, and
+// V is read transposed with ds_read_b64_tr_b16. No VGPRs hold data in
+// flight, so the ring depth is set by LDS alone; the waits on the DMA are
+// explicit (the compiler does not track LDS-DMA writes).
 template <int D>
-__global__ __launch_bounds__(64) void reduce_kernel(const float* ws, uint16_t* out,
-                                                    const int32_t* seq_lens, uint32_t num_q_heads,
-                                                    uint32_t num_splits) {
-  extern __shared__ float wsh[];                    // num_splits weights
+struct LdsTraits {
+  static constexpr int RB = 2 * D;              // bytes of one (token, head) row
+  static constexpr int CPR = D / 8;             // 16-byte chunks per row
+  static constexpr int RPI = 64 / CPR;          // rows per load instruction (1..8)
+  static constexpr int NI = 16 / RPI;           // load instructions per 16-token tile
+  static constexpr int TILE = 16 * RB;          // bytes of one K or V tile
+#ifndef PKD_LDS_NBUF128
+#define PKD_LDS_NBUF128 1
+#endif
+  static constexpr int NBUF = D <= 64 ? 4 : (D == 128 ? PKD_LDS_NBUF128 : (D == 256 ? 2 : 1));
+  static constexpr int SLOT = 2 * TILE;         // K tile + V tile
+  static constexpr int WAIT = (2 * NBUF - 1) * NI;   // DMA loads allowed in flight at a read
+};
+
+// s_waitcnt that waits for vmcnt <= N only (expcnt / lgkmcnt left at their maximum).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+#ifndef PKD_HEAD_FASTEST
+#define PKD_HEAD_FASTEST 1
+#endif
+template <int D>
+__global__ __launch_bounds__(64) void splitk_bf16_lds(DecodeArgs a) {
+  using T = LdsTraits<D>;
+  constexpr int NBUF = T::NBUF;
   const int lane = threadIdx.x;
+  const int g = lane >> 4;
+  const int n = lane & 15;
+
+  // Workgroup order: the kv heads of one (sequence, split) are adjacent, so the
+  // heads of a page, which share one contiguous block of the pool, are read
+  // at about the same time.
+  uint32_t wg = blockIdx.x;
+#if PKD_HEAD_FASTEST
+  const uint32_t kvh = wg % a.num_kv_heads;
+  wg /= a.num_kv_heads;
+  const uint32_t hc = wg % a.head_chunks;
+  wg /= a.head_chunks;
+  const uint32_t split = wg % a.num_splits;
+  const uint32_t b = wg / a.num_splits;
+#else
+  const uint32_t split = wg % a.num_splits;
+  wg /= a.num_splits;
+  const uint32_t hc = wg % a.head_chunks;
+  wg /= a.head_chunks;
+  const uint32_t kvh = wg % a.num_kv_heads;
+  const uint32_t b = wg / a.num_kv_heads;
+#endif
+
+  // Without a window the split's first page is known before its length: the
+  // block-table entries are fetched speculatively, alongside the length.
+  const int32_t* bt = a.block_tables + uint64_t(b) * a.max_blocks;
+  const uint32_t spec_page = split * a.pages_per_split;
+  int32_t bt_spec = 0;
+  if (a.window == 0) bt_spec = bt[min(spec_page + lane, a.max_blocks - 1)];
+
+  const int32_t Ls = a.seq_lens[b];
+  const uint32_t L = Ls > 0 ? uint32_t(Ls) : 0u;
+  const uint32_t lo = (a.window > 0 && L > a.window) ? L - a.window : 0u;
+  const uint32_t bs = a.block_size;
+  const uint32_t p0 = lo / bs, pend = (L + bs - 1) / bs;
+  const uint32_t pa = p0 + spec_page;
+  const uint32_t pb = min(pa + a.pages_per_split, pend);
+
+  const uint32_t head_in_group = hc * 16 + n;
+  const bool head_ok = head_in_group < a.group;
+  const uint32_t qh = kvh * a.group + head_in_group;
+  float* wrow = a.ws + ((uint64_t(b) * a.num_q_heads + qh) * a.num_splits + split) * (D + 2);
+
+  if (pa >= pb) {                                           // empty split
+    if (head_ok) {
+      for (int d = g; d < D + 2; d += 4)
+        wrow[d] = d == D ? -__builtin_inff() : 0.0f;
+    }
+    return;
+  }
+
+  const uint32_t tpp = bs / 16;
+  const uint32_t t0 = max(pa * tpp, lo / 16);
+  const uint32_t t1 = min(pb * tpp, (L + 15) / 16);
+
+  // q as the B operand of the QK MFMAs: column n = head, dims 32c + 8g .. +8;
+  // issued ahead of the tile loads, which only ever wait for later loads.
+  bf16x8 qf[D / 32];
+  {
+    const uint16_t* qrow = a.q + uint64_t(b) * a.q_stride + uint64_t(qh) * D;
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (head_ok) v = *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * g);
+      qf[c] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF * T::SLOT];
+  typedef __attribute__((address_space(3))) uint8_t lds_u8;
+  typedef __attribute__((address_space(3))) void lds_void;
+  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  lds_u8* const ring3 = (lds_u8*)(ring);
+
+  // this lane's row and chunk within each load instruction
+  const int ld_row = lane / T::CPR;                  // + i * RPI
+  const int ld_pos = lane % T::CPR;
+
+  f32x4 acc[D / 16];
+#pragma unroll
+  for (int mt = 0; mt < D / 16; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_run = -__builtin_inff();
+  float l_run = 0.0f;
+  // Segments of up to 64 pages: the block-table entries of a segment sit in
+  // one VGPR (entry per lane); the DMA ring restarts at every segment.
+  for (uint32_t cp = pa; cp < pb; cp += 64) {
+    const uint32_t cpe = min(cp + 64, pb);
+    const int32_t bt_reg = (a.window == 0 && cp == pa) ? bt_spec
+                                                       : ((cp + lane < cpe) ? bt[cp + lane] : 0);
+    const uint32_t ct0 = max(cp * tpp, t0);
+    const uint32_t ct1 = min(cpe * tpp, t1);
+
+    auto issue = [&](int s, int kv, uint32_t t) {
+      const bool live = t < ct1;
+      const uint32_t page = min(t / tpp, cpe - 1);
+      const uint32_t phys = uint32_t(__builtin_amdgcn_readlane(bt_reg, int(page - cp)));
+      const uint8_t* pool = kv ? a.v_cache : a.k_cache;
+      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(pool + uint64_t(phys) * a.page_bytes), 0,
+          live ? int(a.page_bytes) : 0, 0x00020000);
+      const uint32_t off0 = (t % tpp) * 16;
+#pragma unroll
+      for (int i = 0; i < T::NI; ++i) {
+        const int row = i * T::RPI + ld_row;
+        const int chunk = ld_pos ^ (row % T::CPR);
+        const int voff = int(((off0 + row) * a.num_kv_heads + kvh) * T::RB + chunk * 16);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (lds_void*)(ring3 + s * T::SLOT + kv * T::TILE + i * 1024), 16, voff, 0, 0, 2);
+      }
+    };
+
+#pragma unroll
+    for (int s = 0; s < NBUF; ++s) {
+      issue(s, 0, ct0 + s);
+      issue(s, 1, ct0 + s);
+    }
+
+    for (uint32_t tb = ct0; tb < ct1; tb += NBUF) {
+#pragma unroll
+      for (int s = 0; s < NBUF; ++s) {
+        const uint32_t t = tb + s;               // t >= ct1: phantom tile, all keys masked
+        const uint32_t tok0 = t * 16;
+        const uint32_t khi = t < ct1 ? L : 0u;
+        lds_u8* const kt = ring3 + s * T::SLOT;
+        lds_u8* const vt = kt + T::TILE;
+
+        // ---- S = K Q^T from the LDS tile (row n, chunk 4c+g swizzled by n)
+        wait_vmcnt<T::WAIT>();
+        wave_lds_fence();
+        __builtin_amdgcn_sched_barrier(0);
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < D / 32; ++c) {
+          const int chunk = (4 * c + g) ^ (n % T::CPR);
+          const u32x4 kv = *(lds_u32x4*)(kt + n * T::RB + chunk * 16);
+          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qf[c], sc,
+                                                       0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        issue(s, 0, t + NBUF);
+
+        // ---- online softmax (lane: head n, tokens tok0 + 4g + j)
+        float sv[4];
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t tok = tok0 + 4 * g + j;
+          sv[j] = (tok >= lo && tok < khi) ? sc[j] * a.logit_scale : -__builtin_inff();
+          mx = fmaxf(mx, sv[j]);
+        }
+        mx = max_over_rows(mx);
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        // the accumulator is rescaled only when some head's running max moved
+        const bool rescale = __builtin_amdgcn_ballot_w64(m_new != m_run) != 0;
+        m_run = m_new;
+        uint32_t pbits[4];
+        float psum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p = __builtin_amdgcn_exp2f(sv[j] - m_new);
+          pbits[j] = f32_to_bf16_bits(p);
+          psum += __uint_as_float(pbits[j] << 16);
+        }
+        l_run = l_run * alpha + psum;
+        s16x4 pf;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pf[j] = short(pbits[j]);
+
+        // ---- V tile: wait, zero the rows of masked tokens (partial tiles only)
+        wait_vmcnt<T::WAIT>();
+        wave_lds_fence();
+        __builtin_amdgcn_sched_barrier(0);
+        if (tok0 < lo || tok0 + 16 > khi) {
+#pragma unroll
+          for (int i = 0; i < T::NI; ++i) {
+            const uint32_t tok = tok0 + i * T::RPI + ld_row;
+            if (tok < lo || tok >= khi)
+              *(lds_u32x4*)(vt + i * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+          }
+          wave_lds_fence();
+        }
+        // ---- O^T += V^T P: lane supplies V[4g + n/4][16mt + 4(n%4) .. +4]. The
+        // transposed reads are issued as inline asm: the compiler would otherwise
+        // wait for every pending LDS-DMA load before each of them.
+        {
+          const int vtok = 4 * g + (n >> 2);
+          const uint32_t vrow = uint32_t(uintptr_t(vt)) + vtok * T::RB + (n & 1) * 8;
+          u32x2 vv[D / 16];
+#pragma unroll
+          for (int q4 = 0; q4 < D / 64; ++q4) {
+            uint32_t ad[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int mt = 4 * q4 + u;
+              ad[u] = vrow + (((2 * mt + ((n & 3) >> 1)) ^ (vtok % T::CPR)) * 16);
+            }
+            // four transposed reads and their wait in one statement: the outputs
+            // exist only after the wait, so no consumer can be scheduled earlier
+            asm volatile(
+                "ds_read_b64_tr_b16 %0, %4\n\t"
+                "ds_read_b64_tr_b16 %1, %5\n\t"
+                "ds_read_b64_tr_b16 %2, %6\n\t"
+                "ds_read_b64_tr_b16 %3, %7\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(vv[4 * q4]), "=&v"(vv[4 * q4 + 1]), "=&v"(vv[4 * q4 + 2]), "=&v"(vv[4 * q4 + 3])
+                : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+                : "memory");
+          }
+          if (rescale) {
+#pragma unroll
+            for (int mt = 0; mt < D / 16; ++mt) acc[mt] *= alpha;
+          }
+#pragma unroll
+          for (int mt = 0; mt < D / 16; ++mt)
+            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vv[mt]),
+                                                                pf, acc[mt], 0, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        issue(s, 1, t + NBUF);
+      }
+    }
+    wait_vmcnt<0>();                               // the ring restarts with the next segment
+    wave_lds_fence();
+  }
+
+  const float l_tot = sum_over_rows(l_run);
+  if (head_ok) {
+    const float inv = a.out_scale / l_tot;
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) {
+      f32x2 lo2 = {acc[mt][0] * inv, acc[mt][1] * inv};
+      f32x2 hi2 = {acc[mt][2] * inv, acc[mt][3] * inv};
+      *reinterpret_cast<f32x2*>(wrow + mt * 16 + 4 * g) = lo2;
+      *reinterpret_cast<f32x2*>(wrow + mt * 16 + 4 * g + 2) = hi2;
+    }
+    if (g == 0) {
+      wrow[D] = m_run * kLn2;
+      wrow[D + 1] = l_tot;
+    }
+  }
+}
+
+// Combine: one 256-lane workgroup per (sequence, q head). The weights of all
+// splits go to LDS first; then lane t accumulates the float2 column t % (D/2)
+// over the splits i = t / (D/2) (mod KS), and the KS partial sums are added in
+// a fixed order (deterministic).
+template <int D>
+__global__ __launch_bounds__(256) void reduce_kernel(const float* ws, uint16_t* out,
+                                                     const int32_t* seq_lens,
+                                                     uint32_t num_q_heads, uint32_t num_splits) {
+  constexpr int COLS = D / 2;                 // float2 columns of one split row
+  constexpr int KS = 256 / COLS;              // split lanes
+  extern __shared__ float wsh[];              // num_splits weights
+  __shared__ float red[4];
+  __shared__ f32x2 part[KS][COLS];
+  const int tid = threadIdx.x;
   const uint32_t bh = blockIdx.x;
   const uint32_t b = bh / num_q_heads;
   uint16_t* o = out + uint64_t(bh) * D;
   const float* base = ws + uint64_t(bh) * num_splits * (D + 2);
-  constexpr int PER = D / 64;
 
-  float M = -__builtin_inff();
-  if (seq_lens[b] > 0) {
-    for (uint32_t i = lane; i < num_splits; i += 64) {
-      const float l = base[uint64_t(i) * (D + 2) + D + 1];
-      if (l > 0.0f) M = fmaxf(M, base[uint64_t(i) * (D + 2) + D]);
-    }
-    M = wave_max(M);
+  if (seq_lens[b] <= 0) {                     // empty sequence: zeros
+    if (tid < D) o[tid] = 0;
+    if (tid + 256 < D) o[tid + 256] = 0;
+    return;
   }
-  if (M == -__builtin_inff()) {                     // empty sequence: zeros
-#pragma unroll
-    for (int k = 0; k < PER; ++k) o[k * 64 + lane] = 0;
+  float M = -__builtin_inff();
+  for (uint32_t i = tid; i < num_splits; i += 256) {
+    const float l = base[uint64_t(i) * (D + 2) + D + 1];
+    if (l > 0.0f) M = fmaxf(M, base[uint64_t(i) * (D + 2) + D]);
+  }
+  M = wave_max(M);
+  if ((tid & 63) == 0) red[tid >> 6] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  __syncthreads();
+  if (M == -__builtin_inff()) {               // no split holds a key
+    if (tid < D) o[tid] = 0;
+    if (tid + 256 < D) o[tid + 256] = 0;
     return;
   }
   float wsum = 0.0f;
-  for (uint32_t i = lane; i < num_splits; i += 64) {
+  for (uint32_t i = tid; i < num_splits; i += 256) {
     const float l = base[uint64_t(i) * (D + 2) + D + 1];
     const float m = base[uint64_t(i) * (D + 2) + D];
     const float w = l > 0.0f ? l * __builtin_amdgcn_exp2f((m - M) * kLog2e) : 0.0f;
@@ -354,20 +685,41 @@ __global__ __launch_bounds__(64) void reduce_kernel(const float* ws, uint16_t* o
     wsum += w;
   }
   wsum = wave_sum(wsum);
+  if ((tid & 63) == 0) red[tid >> 6] = wsum;
   __syncthreads();
-  float accv[PER];
+  wsum = (red[0] + red[1]) + (red[2] + red[3]);
+
+  const int col = tid % COLS, ks = tid / COLS;
+  f32x2 acc = {0.0f, 0.0f};
+  uint32_t i = ks;
+  for (; i + 3 * KS < num_splits; i += 4 * KS) {
+    f32x2 v[4];
 #pragma unroll
-  for (int k = 0; k < PER; ++k) accv[k] = 0.0f;
-  for (uint32_t i = 0; i < num_splits; ++i) {
-    const float w = wsh[i];
-    if (w == 0.0f) continue;
-    const float* oi = base + uint64_t(i) * (D + 2);
+    for (int u = 0; u < 4; ++u)
+      v[u] = *reinterpret_cast<const f32x2*>(base + uint64_t(i + u * KS) * (D + 2) + 2 * col);
 #pragma unroll
-    for (int k = 0; k < PER; ++k) accv[k] = fmaf(w, oi[k * 64 + lane], accv[k]);
+    for (int u = 0; u < 4; ++u) {
+      const float w = wsh[i + u * KS];
+      acc[0] = fmaf(w, v[u][0], acc[0]);
+      acc[1] = fmaf(w, v[u][1], acc[1]);
+    }
   }
-  const float inv = 1.0f / fmaxf(wsum, 1e-20f);
+  for (; i < num_splits; i += KS) {
+    const f32x2 v = *reinterpret_cast<const f32x2*>(base + uint64_t(i) * (D + 2) + 2 * col);
+    const float w = wsh[i];
+    acc[0] = fmaf(w, v[0], acc[0]);
+    acc[1] = fmaf(w, v[1], acc[1]);
+  }
+  part[ks][col] = acc;
+  __syncthreads();
+  if (tid < COLS) {
+    f32x2 sum = part[0][tid];
 #pragma unroll
-  for (int k = 0; k < PER; ++k) o[k * 64 + lane] = f32_to_bf16_bits(accv[k] * inv);
+    for (int k = 1; k < KS; ++k) sum += part[k][tid];
+    const float inv = 1.0f / fmaxf(wsum, 1e-20f);
+    const uint32_t packed = pack_bf16x2(sum[0] * inv, sum[1] * inv);
+    *reinterpret_cast<uint32_t*>(o + 2 * tid) = packed;
+  }
 }
 
 static int launch_status() {
@@ -381,6 +733,16 @@ static int launch_splitk(const DecodeArgs& a, uint32_t num_seqs, uint32_t head_d
   const uint64_t grid = uint64_t(num_seqs) * a.num_kv_heads * a.head_chunks * a.num_splits;
   if (grid > 0x7FFFFFFFull) return kUnsupported;
   const dim3 gd = dim3(uint32_t(grid)), bd = dim3(64);
+  if (FMT == kBf16) {
+    switch (head_dim) {
+      case 64: hipLaunchKernelGGL(splitk_bf16_lds<64>, gd, bd, 0, stream, a); break;
+      case 128: hipLaunchKernelGGL(splitk_bf16_lds<128>, gd, bd, 0, stream, a); break;
+      case 256: hipLaunchKernelGGL(splitk_bf16_lds<256>, gd, bd, 0, stream, a); break;
+      case 512: hipLaunchKernelGGL(splitk_bf16_lds<512>, gd, bd, 0, stream, a); break;
+      default: return kUnsupported;
+    }
+    return launch_status();
+  }
   switch (head_dim) {
     case 64: hipLaunchKernelGGL((splitk_kernel<FMT, 64>), gd, bd, 0, stream, a); break;
     case 128: hipLaunchKernelGGL((splitk_kernel<FMT, 128>), gd, bd, 0, stream, a); break;
@@ -495,7 +857,7 @@ extern "C" PKD_API int paged_decode_attn_reduce(const float* workspace, uint16_t
   const uint64_t grid = uint64_t(num_seqs) * num_q_heads;
   if (grid > 0x7FFFFFFFull) return kUnsupported;
   const size_t lds = size_t(num_splits) * sizeof(float);
-  const dim3 gd = dim3(uint32_t(grid)), bd = dim3(64);
+  const dim3 gd = dim3(uint32_t(grid)), bd = dim3(256);
   switch (head_dim) {
     case 64: hipLaunchKernelGGL(reduce_kernel<64>, gd, bd, lds, stream, workspace, output, seq_lens, num_q_heads, num_splits); break;
     case 128: hipLaunchKernelGGL(reduce_kernel<128>, gd, bd, lds, stream, workspace, output, seq_lens, num_q_heads, num_splits); break;

@@ -7,6 +7,7 @@
 namespace pkd {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -81,6 +82,21 @@ __device__ __forceinline__ uint32_t e2m1_from_f32(float y) {
   else if (a <= 5.0f) c = 6;
   else c = 7;                               // also NaN / inf (outside the contract)
   return sign | c;
+}
+
+// Max / sum over the four 16-lane rows of a wave (lanes n, n+16, n+32, n+48),
+// with the gfx950 row-swap permutes (VALU only, no LDS round trip).
+__device__ __forceinline__ float max_over_rows(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r2[0]), __uint_as_float(r2[1]));
+}
+__device__ __forceinline__ float sum_over_rows(float x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+  const auto r2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
 }
 
 // wave64 reductions (full wave).

@@ -100,8 +100,11 @@ inline size_t workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads, uint32_t 
   return size_t(num_seqs) * num_q_heads * num_splits * (size_t(head_dim) + 2) * sizeof(float);
 }
 
-// Split-count heuristic: aim at ~8 waves per CU in total, never fewer than
-// 4 pages per split unless the page bound itself is smaller.
+// Split-count heuristic: splits of about 16 pages (256 keys at block size 16)
+// keep every wave's stream long enough to amortize its start; smaller splits
+// (down to 2 pages) are used when the whole batch would otherwise give fewer
+// than ~4 waves per CU. The page bound is the block-table width (or the
+// window), since the sequence lengths live on the device.
 inline uint32_t num_splits_heuristic(uint32_t num_seqs, uint32_t num_q_heads,
                                      uint32_t num_kv_heads, uint32_t max_blocks_per_seq,
                                      uint32_t block_size, uint32_t sliding_window,
@@ -110,11 +113,12 @@ inline uint32_t num_splits_heuristic(uint32_t num_seqs, uint32_t num_q_heads,
     return 1;
   const uint64_t units =
       uint64_t(num_seqs) * num_kv_heads * head_chunks(num_q_heads / num_kv_heads);
-  const uint64_t target = uint64_t(num_cus ? num_cus : 256) * 8;
-  uint64_t s = (target + units - 1) / units;
   const uint32_t bound = split_page_bound(max_blocks_per_seq, block_size, sliding_window);
-  const uint64_t cap = bound >= 4 ? bound / 4 : 1;
-  if (s > cap) s = cap;
+  const uint64_t target_waves = uint64_t(num_cus ? num_cus : 256) * 4;
+  uint64_t c = (uint64_t(bound) * units + target_waves - 1) / target_waves;
+  if (c > 16) c = 16;
+  if (c < 2) c = 2;
+  uint64_t s = (bound + c - 1) / c;
   if (s < 1) s = 1;
   if (s > kMaxSplits) s = kMaxSplits;
   return uint32_t(s);
