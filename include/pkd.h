@@ -133,13 +133,17 @@ PKD_API int bf16_absmax(const uint16_t* data, float* out_max, uint64_t n_elems,
  *   keys j in [lo, L), row j at page block_tables[b*max_blocks_per_seq + j/bs],
  *   offset j % bs; logit s_j = (q . k_j) * scale (the scale applied after the
  *   dot); output = softmax(s) . V.
- * Split partition: the pages [lo/bs, ceil(L/bs)) are cut into chunks of
- *   c = ceil(P / num_splits) pages, P = max_blocks_per_seq, or with a window
- *   W > 0 the smaller of that and (W + bs - 2)/bs + 1; split i takes chunk i.
- * Workspace: float32 [num_seqs][num_q_heads][num_splits][head_dim + 2]; split i
- *   of (b, h) stores o (head_dim values, the split's softmax-normalized
- *   output), m (its largest logit) and l (sum of exp(s_j - m)); an empty split
- *   stores o = 0, m = -inf, l = 0. Size: paged_decode_workspace_bytes().
+ * Splits: the keys of every (b, h) are divided into at most num_splits
+ *   pieces, each a contiguous key range; how the launch's work is divided
+ *   among waves is internal (the BF16 path balances equal key counts across
+ *   the waves it launches, whatever the batch's length mix).
+ * Workspace: float32 [num_seqs][num_q_heads][num_splits][head_dim + 2]; slot i
+ *   of (b, h) holds a piece's o (head_dim values, its softmax-normalized
+ *   output), m (its largest logit) and l (sum of exp(s_j - m)). A slot that
+ *   holds no keys has l = 0 (m = -inf); a slot with l < 0 is an end marker:
+ *   it and every later slot of (b, h) hold no keys, whatever they contain.
+ *   The o of a slot without keys is unspecified. Size:
+ *   paged_decode_workspace_bytes(). Any contents on entry are fine.
  *   q:            BF16; row of (b, h) at element b*q_stride + h*head_dim,
  *                 q_stride >= num_q_heads*head_dim.
  *   block_tables: int32 [num_seqs][max_blocks_per_seq]; the entries of the
@@ -184,10 +188,12 @@ PKD_API int paged_decode_attn_splitk_nvfp4(const uint16_t* q, const uint8_t* k_c
 /* ---------------------------------------------------------------- combine
  * Merge the split partials of every (b, h) into output BF16
  * [num_seqs][num_q_heads][head_dim] (contiguous), one combine for every cache
- * type (paged_decode_attn_reduce_fp8 on the metrale page): M = max m_i over
- * splits with l_i > 0; w_i = l_i * exp(m_i - M); out = sum w_i o_i /
- * max(sum w_i, 1e-20), rounded to BF16 (nearest even). A sequence with
- * seq_lens[b] == 0 gets zeros. Deterministic: a fixed summation order. */
+ * type (paged_decode_attn_reduce_fp8 on the metrale page): over the slots
+ * before the first end marker that have l_i > 0, M = max m_i;
+ * w_i = l_i * exp(m_i - M); out = sum w_i o_i / max(sum w_i, 1e-20), rounded
+ * to BF16 (nearest even). A
+ * sequence with seq_lens[b] == 0 gets zeros. Deterministic: a fixed
+ * summation order. */
 PKD_API int paged_decode_attn_reduce(const float* workspace, uint16_t* output,
                                      const int32_t* seq_lens, uint32_t num_q_heads,
                                      uint32_t head_dim, uint32_t num_splits, uint32_t num_seqs,
@@ -198,11 +204,13 @@ PKD_API int paged_decode_attn_reduce(const float* workspace, uint16_t* output,
 PKD_API size_t paged_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads,
                                             uint32_t head_dim, uint32_t num_splits);
 
-/* A split count for the split-K calls: splits of about 16 pages, or fewer
- * pages (down to 2) when the batch's (sequence, kv head, 16-q-head chunk)
- * work items would otherwise give fewer than ~4 waves per compute unit. The
- * page bound is max_blocks_per_seq (or the window's). Pure host arithmetic;
- * num_cus = the device's compute-unit count. */
+/* A split count for the split-K calls: 1 + 4 * (4 * num_cus) / rows, rows =
+ * num_seqs * num_kv_heads * ceil(group / 16), capped at the row's tile bound
+ * (16-key tiles within max_blocks_per_seq pages, or the window) and at
+ * PKD_MAX_SPLITS. The BF16 pass launches about four waves per CU and spreads
+ * the batch's tiles evenly over them, so this count only needs to exceed the
+ * pieces a row is cut into; the FP8 / NVFP4 passes give each row num_splits
+ * equal page chunks. Pure host arithmetic; num_cus = compute-unit count. */
 PKD_API uint32_t paged_decode_num_splits(uint32_t num_seqs, uint32_t num_q_heads,
                                          uint32_t num_kv_heads, uint32_t max_blocks_per_seq,
                                          uint32_t block_size, uint32_t sliding_window,

@@ -53,6 +53,8 @@ struct DecodeArgs {
   uint64_t page_bytes;     // bytes per page of one pool
   uint64_t data_section;   // NVFP4: byte offset of the scales within a page
   uint32_t window;
+  uint32_t num_seqs;
+  uint32_t chunk_min;      // stream partition: least tiles per wave (S - 1 pieces per row at most)
 };
 
 template <int FMT, int D>
@@ -385,68 +387,100 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-#ifndef PKD_HEAD_FASTEST
-#define PKD_HEAD_FASTEST 1
-#endif
+// Balanced ("stream") partition of one launch's work. A row is a (sequence,
+// kv head, chunk of up to 16 q heads) triple; row (b, k) has n_b tiles, the
+// 16-key tiles overlapping the sequence's attended keys. The rows are laid end
+// to end, sequence-major, into one index space of T tiles; wave w of the P
+// launched waves takes tiles [w*c, (w+1)*c) with c = max(ceil(T/P), c_min) and
+// c_min = ceil(n_bound / (S - 1)) for the host's bound n_bound on n_b. A wave
+// thus covers one or more row pieces, each a contiguous key range; the piece
+// of row r starting at flat tile f goes to workspace slot
+// floor(f/c) - floor(start(r)/c) <= S - 1. The wave that ends a row marks the
+// row's later slots empty. With S == 1, wave w takes row w whole. Every wave
+// gets the same number of tiles whatever the length mix of the batch.
+
+__device__ __forceinline__ uint32_t row_tiles(uint32_t L, uint32_t window) {
+  if (L == 0) return 0;
+  const uint32_t lo = (window > 0 && L > window) ? L - window : 0u;
+  return (L + 15) / 16 - lo / 16;
+}
+
+// inclusive prefix sum over the 64 lanes
+__device__ __forceinline__ uint32_t wave_scan(uint32_t x) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  return x;
+}
+
+struct RowLoc {
+  uint32_t b, kh, n, start;     // sequence, kv-head/chunk index, tiles, flat start of the row
+};
+
+// Total tiles T of the launch (all rows of all sequences).
+__device__ __forceinline__ uint32_t total_tiles(const DecodeArgs& a, uint32_t rows_per_seq) {
+  uint32_t tot = 0;
+  for (uint32_t b0 = 0; b0 < a.num_seqs; b0 += 64) {
+    const uint32_t bb = b0 + threadIdx.x;
+    const int32_t Ls = bb < a.num_seqs ? a.seq_lens[bb] : 0;
+    const uint32_t t = row_tiles(Ls > 0 ? uint32_t(Ls) : 0u, a.window) * rows_per_seq;
+    tot += __shfl(wave_scan(t), 63, 64);
+  }
+  return tot;
+}
+
+// The row holding flat tile `pos` (pos < T).
+__device__ __forceinline__ RowLoc find_row(const DecodeArgs& a, uint32_t pos,
+                                           uint32_t rows_per_seq) {
+  uint32_t base = 0;
+  for (uint32_t b0 = 0; b0 < a.num_seqs; b0 += 64) {
+    const uint32_t bb = b0 + threadIdx.x;
+    const int32_t Ls = bb < a.num_seqs ? a.seq_lens[bb] : 0;
+    const uint32_t n = row_tiles(Ls > 0 ? uint32_t(Ls) : 0u, a.window);
+    const uint32_t incl = wave_scan(n * rows_per_seq);
+    const uint64_t hit = __builtin_amdgcn_ballot_w64(base + incl > pos);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      const uint32_t nl = __shfl(n, l, 64);
+      const uint32_t excl = __shfl(incl - n * rows_per_seq, l, 64);
+      const uint32_t kh = (pos - base - excl) / nl;
+      return RowLoc{b0 + l, kh, nl, base + excl + kh * nl};
+    }
+    base += __shfl(incl, 63, 64);
+  }
+  return RowLoc{a.num_seqs, 0, 0, base};
+}
+
 template <int D>
-__global__ __launch_bounds__(64) void splitk_bf16_lds(DecodeArgs a) {
+struct StreamLds {
+  __attribute__((aligned(1024))) uint8_t ring[LdsTraits<D>::NBUF * LdsTraits<D>::SLOT];
+};
+
+// One row piece: tiles [tau0, tau1) of row (b, kh), partial state to `slot`.
+template <int D>
+__device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<D>& sh, uint32_t b,
+                                          uint32_t kh, uint32_t tau0, uint32_t tau1,
+                                          uint32_t slot, bool last, uint32_t L) {
   using T = LdsTraits<D>;
   constexpr int NBUF = T::NBUF;
   const int lane = threadIdx.x;
   const int g = lane >> 4;
   const int n = lane & 15;
+  const uint32_t kvh = kh / a.head_chunks, hc = kh % a.head_chunks;
 
-  // Workgroup order: the kv heads of one (sequence, split) are adjacent, so the
-  // heads of a page, which share one contiguous block of the pool, are read
-  // at about the same time.
-  uint32_t wg = blockIdx.x;
-#if PKD_HEAD_FASTEST
-  const uint32_t kvh = wg % a.num_kv_heads;
-  wg /= a.num_kv_heads;
-  const uint32_t hc = wg % a.head_chunks;
-  wg /= a.head_chunks;
-  const uint32_t split = wg % a.num_splits;
-  const uint32_t b = wg / a.num_splits;
-#else
-  const uint32_t split = wg % a.num_splits;
-  wg /= a.num_splits;
-  const uint32_t hc = wg % a.head_chunks;
-  wg /= a.head_chunks;
-  const uint32_t kvh = wg % a.num_kv_heads;
-  const uint32_t b = wg / a.num_kv_heads;
-#endif
-
-  // Without a window the split's first page is known before its length: the
-  // block-table entries are fetched speculatively, alongside the length.
-  const int32_t* bt = a.block_tables + uint64_t(b) * a.max_blocks;
-  const uint32_t spec_page = split * a.pages_per_split;
-  int32_t bt_spec = 0;
-  if (a.window == 0) bt_spec = bt[min(spec_page + lane, a.max_blocks - 1)];
-
-  const int32_t Ls = a.seq_lens[b];
-  const uint32_t L = Ls > 0 ? uint32_t(Ls) : 0u;
   const uint32_t lo = (a.window > 0 && L > a.window) ? L - a.window : 0u;
-  const uint32_t bs = a.block_size;
-  const uint32_t p0 = lo / bs, pend = (L + bs - 1) / bs;
-  const uint32_t pa = p0 + spec_page;
-  const uint32_t pb = min(pa + a.pages_per_split, pend);
+  const uint32_t tpp = a.block_size / 16;
+  const uint32_t t0 = lo / 16 + tau0, t1 = lo / 16 + tau1;   // tiles of the sequence
+  const uint32_t pa = t0 / tpp, pb = (t1 + tpp - 1) / tpp;
 
   const uint32_t head_in_group = hc * 16 + n;
   const bool head_ok = head_in_group < a.group;
   const uint32_t qh = kvh * a.group + head_in_group;
-  float* wrow = a.ws + ((uint64_t(b) * a.num_q_heads + qh) * a.num_splits + split) * (D + 2);
-
-  if (pa >= pb) {                                           // empty split
-    if (head_ok) {
-      for (int d = g; d < D + 2; d += 4)
-        wrow[d] = d == D ? -__builtin_inff() : 0.0f;
-    }
-    return;
-  }
-
-  const uint32_t tpp = bs / 16;
-  const uint32_t t0 = max(pa * tpp, lo / 16);
-  const uint32_t t1 = min(pb * tpp, (L + 15) / 16);
+  float* const wbase = a.ws + (uint64_t(b) * a.num_q_heads + qh) * a.num_splits * (D + 2);
+  const int32_t* bt = a.block_tables + uint64_t(b) * a.max_blocks;
 
   // q as the B operand of the QK MFMAs: column n = head, dims 32c + 8g .. +8;
   // issued ahead of the tile loads, which only ever wait for later loads.
@@ -461,14 +495,10 @@ __global__ __launch_bounds__(64) void splitk_bf16_lds(DecodeArgs a) {
     }
   }
 
-  __shared__ __attribute__((aligned(1024))) uint8_t ring[NBUF * T::SLOT];
   typedef __attribute__((address_space(3))) uint8_t lds_u8;
   typedef __attribute__((address_space(3))) void lds_void;
-  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
   typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
-  lds_u8* const ring3 = (lds_u8*)(ring);
-
-  // this lane's row and chunk within each load instruction
+  lds_u8* const ring3 = (lds_u8*)(sh.ring);
   const int ld_row = lane / T::CPR;                  // + i * RPI
   const int ld_pos = lane % T::CPR;
 
@@ -477,12 +507,12 @@ __global__ __launch_bounds__(64) void splitk_bf16_lds(DecodeArgs a) {
   for (int mt = 0; mt < D / 16; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -__builtin_inff();
   float l_run = 0.0f;
+
   // Segments of up to 64 pages: the block-table entries of a segment sit in
   // one VGPR (entry per lane); the DMA ring restarts at every segment.
   for (uint32_t cp = pa; cp < pb; cp += 64) {
     const uint32_t cpe = min(cp + 64, pb);
-    const int32_t bt_reg = (a.window == 0 && cp == pa) ? bt_spec
-                                                       : ((cp + lane < cpe) ? bt[cp + lane] : 0);
+    const int32_t bt_reg = (cp + lane < cpe) ? bt[cp + lane] : 0;
     const uint32_t ct0 = max(cp * tpp, t0);
     const uint32_t ct1 = min(cpe * tpp, t1);
 
@@ -622,6 +652,7 @@ __global__ __launch_bounds__(64) void splitk_bf16_lds(DecodeArgs a) {
 
   const float l_tot = sum_over_rows(l_run);
   if (head_ok) {
+    float* wrow = wbase + uint64_t(slot) * (D + 2);
     const float inv = a.out_scale / l_tot;
 #pragma unroll
     for (int mt = 0; mt < D / 16; ++mt) {
@@ -634,20 +665,84 @@ __global__ __launch_bounds__(64) void splitk_bf16_lds(DecodeArgs a) {
       wrow[D] = m_run * kLn2;
       wrow[D + 1] = l_tot;
     }
+    // the row ends in this piece: an end marker (l = -1) in the next slot
+    // tells the combine to ignore that slot and all later ones
+    if (last && g == 0 && slot + 1 < a.num_splits) {
+      float* e = wbase + uint64_t(slot + 1) * (D + 2);
+      e[D] = -__builtin_inff();
+      e[D + 1] = -1.0f;
+    }
   }
 }
 
-// Combine: one 256-lane workgroup per (sequence, q head). The weights of all
-// splits go to LDS first; then lane t accumulates the float2 column t % (D/2)
-// over the splits i = t / (D/2) (mod KS), and the KS partial sums are added in
-// a fixed order (deterministic).
+template <int D>
+__global__ __launch_bounds__(64) void splitk_bf16_stream(DecodeArgs a) {
+  __shared__ StreamLds<D> sh;
+  const uint32_t R = a.num_kv_heads * a.head_chunks;          // rows per sequence
+  if (a.num_splits == 1) {                                    // one wave per row
+    const uint32_t b = blockIdx.x / R, kh = blockIdx.x % R;
+    const int32_t Ls = a.seq_lens[b];
+    const uint32_t L = Ls > 0 ? uint32_t(Ls) : 0u;
+    const uint32_t n = row_tiles(L, a.window);
+    if (n) run_piece<D>(a, sh, b, kh, 0, n, 0, true, L);
+    return;
+  }
+  const uint32_t P = gridDim.x;
+  if (a.num_seqs <= 64) {
+    // one length per lane, loaded once: the tile counts, their prefix sums and
+    // every row lookup come from these registers
+    const uint32_t lane = threadIdx.x;
+    const int32_t Ls = lane < a.num_seqs ? a.seq_lens[lane] : 0;
+    const uint32_t L_l = Ls > 0 ? uint32_t(Ls) : 0u;
+    const uint32_t n_l = row_tiles(L_l, a.window);
+    const uint32_t incl = wave_scan(n_l * R);
+    const uint32_t T = __shfl(incl, 63, 64);
+    const uint32_t c = max((T + P - 1) / P, a.chunk_min);
+    uint32_t pos = blockIdx.x * c;
+    const uint32_t end = min(pos + c, T);
+    while (pos < end) {
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(incl > pos);
+      const int l = __builtin_ctzll(hit);
+      const uint32_t n = __shfl(n_l, l, 64);
+      const uint32_t excl = __shfl(incl, l, 64) - n * R;
+      const uint32_t L = __shfl(L_l, l, 64);
+      const uint32_t kh = (pos - excl) / n;
+      const uint32_t start = excl + kh * n;
+      const uint32_t tau1 = min(n, end - start);
+      run_piece<D>(a, sh, uint32_t(l), kh, pos - start, tau1, pos / c - start / c,
+                   start + n <= end, L);
+      pos = start + tau1;
+    }
+    return;
+  }
+  const uint32_t T = total_tiles(a, R);
+  const uint32_t c = max((T + P - 1) / P, a.chunk_min);
+  uint32_t pos = blockIdx.x * c;
+  const uint32_t end = min(pos + c, T);
+  while (pos < end) {
+    const RowLoc r = find_row(a, pos, R);
+    const uint32_t tau0 = pos - r.start;
+    const uint32_t tau1 = min(r.n, end - r.start);
+    const uint32_t slot = pos / c - r.start / c;
+    const int32_t Ls = a.seq_lens[r.b];
+    run_piece<D>(a, sh, r.b, r.kh, tau0, tau1, slot, r.start + r.n <= end,
+                 Ls > 0 ? uint32_t(Ls) : 0u);
+    pos = r.start + tau1;
+  }
+}
+
+// Combine: one 256-lane workgroup per (sequence, q head). The (m, l) of all
+// slots are read once into LDS and turned into weights; then lane t
+// accumulates the float2 column t % (D/2) over the slots i = t / (D/2)
+// (mod KS), eight loads in flight, skipping groups of unused slots, and the
+// KS partial sums are added in a fixed order (deterministic).
 template <int D>
 __global__ __launch_bounds__(256) void reduce_kernel(const float* ws, uint16_t* out,
                                                      const int32_t* seq_lens,
                                                      uint32_t num_q_heads, uint32_t num_splits) {
   constexpr int COLS = D / 2;                 // float2 columns of one split row
   constexpr int KS = 256 / COLS;              // split lanes
-  extern __shared__ float wsh[];              // num_splits weights
+  extern __shared__ float wsh[];              // num_splits weights (m first, then weights)
   __shared__ float red[4];
   __shared__ f32x2 part[KS][COLS];
   const int tid = threadIdx.x;
@@ -661,26 +756,38 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* ws, uint16_t* 
     if (tid + 256 < D) o[tid + 256] = 0;
     return;
   }
-  float M = -__builtin_inff();
+  // slot i counts if l_i > 0 and no earlier slot holds an end marker (l < 0)
+  uint32_t stop = num_splits;
   for (uint32_t i = tid; i < num_splits; i += 256) {
-    const float l = base[uint64_t(i) * (D + 2) + D + 1];
-    if (l > 0.0f) M = fmaxf(M, base[uint64_t(i) * (D + 2) + D]);
+    const f32x2 ml = *reinterpret_cast<const f32x2*>(base + uint64_t(i) * (D + 2) + D);
+    wsh[i] = ml[1];
+    wsh[num_splits + i] = ml[0];
+    if (ml[1] < 0.0f) stop = min(stop, i);
   }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) stop = min(stop, uint32_t(__shfl_xor(int(stop), o, 64)));
+  __shared__ uint32_t stops[4];
+  if ((tid & 63) == 0) stops[tid >> 6] = stop;
+  __syncthreads();
+  stop = min(min(stops[0], stops[1]), min(stops[2], stops[3]));
+  float M = -__builtin_inff();
+  for (uint32_t i = tid; i < stop; i += 256)
+    if (wsh[i] > 0.0f) M = fmaxf(M, wsh[num_splits + i]);
   M = wave_max(M);
   if ((tid & 63) == 0) red[tid >> 6] = M;
   __syncthreads();
   M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   __syncthreads();
-  if (M == -__builtin_inff()) {               // no split holds a key
+  if (M == -__builtin_inff()) {               // no slot holds a key
     if (tid < D) o[tid] = 0;
     if (tid + 256 < D) o[tid + 256] = 0;
     return;
   }
   float wsum = 0.0f;
   for (uint32_t i = tid; i < num_splits; i += 256) {
-    const float l = base[uint64_t(i) * (D + 2) + D + 1];
-    const float m = base[uint64_t(i) * (D + 2) + D];
-    const float w = l > 0.0f ? l * __builtin_amdgcn_exp2f((m - M) * kLog2e) : 0.0f;
+    const float l = wsh[i];
+    const float w = (i < stop && l > 0.0f)
+                        ? l * __builtin_amdgcn_exp2f((wsh[num_splits + i] - M) * kLog2e) : 0.0f;
     wsh[i] = w;
     wsum += w;
   }
@@ -691,24 +798,29 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* ws, uint16_t* 
 
   const int col = tid % COLS, ks = tid / COLS;
   f32x2 acc = {0.0f, 0.0f};
-  uint32_t i = ks;
-  for (; i + 3 * KS < num_splits; i += 4 * KS) {
-    f32x2 v[4];
+  for (uint32_t i0 = 0; i0 < stop; i0 += 8 * KS) {
+    float w[8];
+    bool any = false;
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      v[u] = *reinterpret_cast<const f32x2*>(base + uint64_t(i + u * KS) * (D + 2) + 2 * col);
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float w = wsh[i + u * KS];
-      acc[0] = fmaf(w, v[u][0], acc[0]);
-      acc[1] = fmaf(w, v[u][1], acc[1]);
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t i = i0 + u * KS + ks;
+      w[u] = i < num_splits ? wsh[i] : 0.0f;
+      any |= w[u] != 0.0f;
     }
-  }
-  for (; i < num_splits; i += KS) {
-    const f32x2 v = *reinterpret_cast<const f32x2*>(base + uint64_t(i) * (D + 2) + 2 * col);
-    const float w = wsh[i];
-    acc[0] = fmaf(w, v[0], acc[0]);
-    acc[1] = fmaf(w, v[1], acc[1]);
+    if (!any) continue;                         // eight unused slots: nothing to read
+    f32x2 v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t i = min(i0 + u * KS + ks, num_splits - 1);
+      v[u] = *reinterpret_cast<const f32x2*>(base + uint64_t(i) * (D + 2) + 2 * col);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      if (w[u] != 0.0f) {                       // unused slots may hold anything
+        acc[0] = fmaf(w[u], v[u][0], acc[0]);
+        acc[1] = fmaf(w[u], v[u][1], acc[1]);
+      }
+    }
   }
   part[ks][col] = acc;
   __syncthreads();
@@ -727,18 +839,59 @@ static int launch_status() {
   return e == hipSuccess ? kOk : kLaunch;
 }
 
+// Waves the stream kernel launches on the current device: all resident at
+// once (at most the occupancy), cached per device and head_dim.
+static uint64_t stream_capacity(uint32_t head_dim) {
+  static uint64_t cache[64][4];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  const int di = head_dim == 64 ? 0 : head_dim == 128 ? 1 : head_dim == 256 ? 2 : 3;
+  if (cache[dev][di]) return cache[dev][di];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  hipError_t e = hipErrorInvalidValue;
+  switch (head_dim) {
+    case 64: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, splitk_bf16_stream<64>, 64, 0); break;
+    case 128: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, splitk_bf16_stream<128>, 64, 0); break;
+    case 256: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, splitk_bf16_stream<256>, 64, 0); break;
+    case 512: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, splitk_bf16_stream<512>, 64, 0); break;
+  }
+  if (e != hipSuccess || per_cu <= 0 || cus <= 0) return 0;
+#ifndef PKD_STREAM_WAVES_PER_CU
+#define PKD_STREAM_WAVES_PER_CU 4
+#endif
+  // four long waves per CU stream better than more, shorter ones; the count is
+  // a multiple of the CU count so that every CU gets the same work
+  if (per_cu > PKD_STREAM_WAVES_PER_CU) per_cu = PKD_STREAM_WAVES_PER_CU;
+  cache[dev][di] = uint64_t(per_cu) * uint64_t(cus);
+  return cache[dev][di];
+}
+
 template <int FMT>
-static int launch_splitk(const DecodeArgs& a, uint32_t num_seqs, uint32_t head_dim,
+static int launch_splitk(DecodeArgs a, uint32_t num_seqs, uint32_t head_dim,
                          hipStream_t stream) {
+  a.num_seqs = num_seqs;
   const uint64_t grid = uint64_t(num_seqs) * a.num_kv_heads * a.head_chunks * a.num_splits;
   if (grid > 0x7FFFFFFFull) return kUnsupported;
   const dim3 gd = dim3(uint32_t(grid)), bd = dim3(64);
   if (FMT == kBf16) {
+    const uint32_t rows = num_seqs * a.num_kv_heads * a.head_chunks;
+    uint32_t tile_bound = a.max_blocks * (a.block_size / 16);
+    if (a.window > 0) tile_bound = min(tile_bound, (a.window + 14) / 16 + 1);
+    a.chunk_min = a.num_splits > 1 ? (tile_bound + a.num_splits - 2) / (a.num_splits - 1) : 1;
+    uint64_t waves = rows;
+    if (a.num_splits > 1) {
+      waves = uint64_t(rows) * a.num_splits;
+      const uint64_t cap = stream_capacity(head_dim);
+      if (cap && waves > cap) waves = cap;
+    }
+    const dim3 sgd = dim3(uint32_t(waves));
     switch (head_dim) {
-      case 64: hipLaunchKernelGGL(splitk_bf16_lds<64>, gd, bd, 0, stream, a); break;
-      case 128: hipLaunchKernelGGL(splitk_bf16_lds<128>, gd, bd, 0, stream, a); break;
-      case 256: hipLaunchKernelGGL(splitk_bf16_lds<256>, gd, bd, 0, stream, a); break;
-      case 512: hipLaunchKernelGGL(splitk_bf16_lds<512>, gd, bd, 0, stream, a); break;
+      case 64: hipLaunchKernelGGL(splitk_bf16_stream<64>, sgd, bd, 0, stream, a); break;
+      case 128: hipLaunchKernelGGL(splitk_bf16_stream<128>, sgd, bd, 0, stream, a); break;
+      case 256: hipLaunchKernelGGL(splitk_bf16_stream<256>, sgd, bd, 0, stream, a); break;
+      case 512: hipLaunchKernelGGL(splitk_bf16_stream<512>, sgd, bd, 0, stream, a); break;
       default: return kUnsupported;
     }
     return launch_status();
@@ -779,6 +932,8 @@ static DecodeArgs make_args(const uint16_t* q, const void* kc, const void* vc, f
   a.page_bytes = page_bytes;
   a.data_section = data_section;
   a.window = window;
+  a.num_seqs = 0;
+  a.chunk_min = 1;
   return a;
 }
 
@@ -856,7 +1011,7 @@ extern "C" PKD_API int paged_decode_attn_reduce(const float* workspace, uint16_t
   if (st) return st;
   const uint64_t grid = uint64_t(num_seqs) * num_q_heads;
   if (grid > 0x7FFFFFFFull) return kUnsupported;
-  const size_t lds = size_t(num_splits) * sizeof(float);
+  const size_t lds = 2 * size_t(num_splits) * sizeof(float);
   const dim3 gd = dim3(uint32_t(grid)), bd = dim3(256);
   switch (head_dim) {
     case 64: hipLaunchKernelGGL(reduce_kernel<64>, gd, bd, lds, stream, workspace, output, seq_lens, num_q_heads, num_splits); break;

@@ -100,26 +100,27 @@ inline size_t workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads, uint32_t 
   return size_t(num_seqs) * num_q_heads * num_splits * (size_t(head_dim) + 2) * sizeof(float);
 }
 
-// Split-count heuristic: splits of about 16 pages (256 keys at block size 16)
-// keep every wave's stream long enough to amortize its start; smaller splits
-// (down to 2 pages) are used when the whole batch would otherwise give fewer
-// than ~4 waves per CU. The page bound is the block-table width (or the
-// window), since the sequence lengths live on the device.
+// Split-count heuristic. The BF16 split-K pass launches about 4 waves per CU
+// and balances the batch's tiles evenly over them; num_splits only bounds how
+// many pieces one (sequence, kv head) row may be cut into. It is chosen so
+// that this bound does not force pieces longer than an even share, with room
+// for batches whose sequences are shorter than the block-table width (4x).
+// The FP8 / NVFP4 passes cut each row into num_splits chunks of the page
+// bound, so the same count also gives them several waves per CU.
 inline uint32_t num_splits_heuristic(uint32_t num_seqs, uint32_t num_q_heads,
                                      uint32_t num_kv_heads, uint32_t max_blocks_per_seq,
                                      uint32_t block_size, uint32_t sliding_window,
                                      uint32_t num_cus) {
   if (num_seqs == 0 || num_kv_heads == 0 || num_q_heads < num_kv_heads || block_size == 0)
     return 1;
-  const uint64_t units =
+  const uint64_t rows =
       uint64_t(num_seqs) * num_kv_heads * head_chunks(num_q_heads / num_kv_heads);
+  const uint64_t waves = uint64_t(num_cus ? num_cus : 256) * 4;
   const uint32_t bound = split_page_bound(max_blocks_per_seq, block_size, sliding_window);
-  const uint64_t target_waves = uint64_t(num_cus ? num_cus : 256) * 4;
-  uint64_t c = (uint64_t(bound) * units + target_waves - 1) / target_waves;
-  if (c > 16) c = 16;
-  if (c < 2) c = 2;
-  uint64_t s = (bound + c - 1) / c;
-  if (s < 1) s = 1;
+  const uint64_t tiles = uint64_t(bound) * (block_size / 16);
+  uint64_t s = 1 + (4 * waves + rows - 1) / rows;
+  if (s > tiles) s = tiles;                    // a piece holds at least one tile
+  if (s < 2) s = tiles >= 2 ? 2 : 1;
   if (s > kMaxSplits) s = kMaxSplits;
   return uint32_t(s);
 }

@@ -80,7 +80,7 @@ class DeviceKV:
         del key, val, slots
 
     def decode(self, num_splits, q_bits=None, sliding_window=None, q_stride=None, seq_lens=None,
-               return_ws=False):
+               return_ws=False, ws_fill=None):
         w, g = self.w, self.geom
         B, Hq, Hkv, D, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
         q_bits = w.q_bits if q_bits is None else q_bits
@@ -92,6 +92,8 @@ class DeviceKV:
         lens = i32_to_dev(lens_np)
         ws = torch.empty(pkd.paged_decode_workspace_bytes(B, Hq, D, num_splits) // 4,
                          dtype=torch.float32, device=dev())
+        if ws_fill is not None:
+            ws.fill_(ws_fill)
         out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev())
         common = (q, self.k, self.v, ws, bt, lens, w.max_blocks_per_seq, Hq, Hkv, D, bs,
                   float(w.scale), num_splits)

@@ -48,19 +48,17 @@ def test_workspace_bytes(lib):
 
 def test_num_splits_heuristic(lib):
     ns = pkd.paged_decode_num_splits
-    # about 16 pages per split when the batch is large enough
-    assert ns(1, 32, 8, 2048, 16, 0, 256) == 128         # B=1, 32K keys
-    assert ns(32, 32, 8, 256, 16, 0, 256) == 16          # B=32, up to 4K keys
-    # small batches use smaller splits (down to 2 pages) to reach ~4 waves per CU
-    assert ns(1, 32, 8, 64, 16, 0, 256) == 32            # B=1, 1K keys: 2 pages per split
-    assert ns(2, 4, 2, 4, 16, 0, 256) == 2
-    # a window bounds the pages: W=4096 -> 257 pages
-    assert ns(64, 16, 8, 512, 16, 4096, 256) == 17
-    assert ns(1, 16, 8, 512, 16, 4096, 256) == 86        # 3 pages per split
-    # more than 16 q heads per kv head count as separate work items
-    assert ns(1, 64, 1, 4096, 16, 0, 256) == 256
-    for args in [(0, 8, 8, 10, 16, 0, 256), (3, 8, 8, 1, 16, 0, 0)]:
-        assert ns(*args) >= 1
+    # 1 + 4 * (4 waves per CU * CUs) / rows, at most one piece per 16-key tile
+    assert ns(1, 32, 8, 2048, 16, 0, 256) == 513          # B=1, 32K keys: 8 rows
+    assert ns(32, 32, 8, 256, 16, 0, 256) == 17           # B=32: 256 rows
+    assert ns(1, 32, 8, 64, 16, 0, 256) == 64             # B=1, 1K keys: capped by 64 tiles
+    assert ns(2, 4, 2, 4, 16, 0, 256) == 4
+    assert ns(64, 16, 8, 512, 16, 4096, 256) == 9         # 512 rows
+    assert ns(1, 16, 8, 512, 16, 4096, 256) == 257        # window: 257 tiles at most
+    assert ns(1, 64, 1, 4096, 16, 0, 256) == 1025         # 4 rows (16-q-head chunks)
+    assert ns(4096, 8, 8, 10, 16, 0, 256) == 2
+    assert ns(3, 8, 8, 1, 16, 0, 0) == 1                  # a single tile per row
+    assert ns(0, 8, 8, 10, 16, 0, 256) == 1
 
 
 def test_status_strings(lib):
