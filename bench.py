@@ -175,7 +175,7 @@ class Layers:
                                      self.num_splits, w.num_seqs)
 
 
-def time_workload(name, steps, warmup, kernel_reps=200):
+def time_workload(name, steps, warmup, kernel_reps=100):
     import torch
     import workloads
     w = workloads.make_workload(name)
@@ -204,15 +204,22 @@ def time_workload(name, steps, warmup, kernel_reps=200):
     wall = time.perf_counter() - t0
     ms_step = start.elapsed_time(end) / steps_run
 
-    # split-KV kernel alone: HIP events around each launch on the launching stream
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(kernel_reps)]
-    for i, (a, b) in enumerate(evs):
-        a.record()
-        lay.splitk(i % NL)
-        b.record()
+    # split-KV kernel alone: a graph of back-to-back launches (rotating layers)
+    # between two HIP events on the stream it runs on
+    kgraph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(kgraph):
+        for i in range(kernel_reps):
+            lay.splitk(i % NL)
+    kgraph.replay()
     torch.cuda.synchronize()
-    k_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    ka, kb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ka.record()
+    for _ in range(3):
+        kgraph.replay()
+    kb.record()
+    torch.cuda.synchronize()
+    k_ms = ka.elapsed_time(kb) / (3 * kernel_reps)
+    del kgraph
 
     kv_bytes = attended_tokens(w) * kv_bytes_per_token(w)
     res = dict(
@@ -230,15 +237,23 @@ def time_workload(name, steps, warmup, kernel_reps=200):
 
 
 def traffic_record(name):
-    """HBM bytes per split-KV launch from committed rocprof counter runs, if the
-    kernel sources still match the ones that were profiled."""
-    path = os.path.join(ROOT, "profiles", f"traffic_splitk_{name}.json")
+    """HBM bytes per split-K launch from the committed rocprofv3 counter
+    summary (profiles/traffic_splitk_<workload>.txt), used only while the
+    kernel sources still hash to what was profiled."""
+    path = os.path.join(ROOT, "profiles", f"traffic_splitk_{name}.txt")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path))
+    rec = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
     if rec.get("source_hash") != source_hash():
         return None
-    return rec.get("bytes_per_launch")
+    try:
+        return float(rec["bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def cpu_baseline(w, budget_s=12.0, max_reps=50):

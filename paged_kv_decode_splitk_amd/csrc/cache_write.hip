@@ -105,6 +105,25 @@ template <int FMT>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(WriteArgs a) {
   const uint32_t t = blockIdx.x;
   const int32_t slot = a.slots[t];
+  if constexpr (FMT == kBf16) {
+    // rows of up to 256 x 16 bytes: the source loads go out together with the
+    // slot load instead of waiting for it
+    const uint32_t row = a.num_kv_heads * a.head_dim;
+    if (row <= 256 * 8) {
+      const uint32_t c = threadIdx.x;
+      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
+      if (c < row / 8) {
+        kv = *reinterpret_cast<const u32x4*>(a.key + uint64_t(t) * a.key_stride + c * 8);
+        vv = *reinterpret_cast<const u32x4*>(a.value + uint64_t(t) * a.value_stride + c * 8);
+      }
+      if (slot < 0 || c >= row / 8) return;
+      const uint64_t dst = (uint64_t(uint32_t(slot) / a.block_size) * a.block_size +
+                            uint32_t(slot) % a.block_size) * row + c * 8;
+      *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.k_cache) + dst) = kv;
+      *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.v_cache) + dst) = vv;
+      return;
+    }
+  }
   if (slot < 0) return;
   const uint32_t page = uint32_t(slot) / a.block_size;
   const uint32_t off = uint32_t(slot) % a.block_size;

@@ -731,19 +731,22 @@ __global__ __launch_bounds__(64) void splitk_bf16_stream(DecodeArgs a) {
   }
 }
 
-// Combine: one 256-lane workgroup per (sequence, q head). The (m, l) of all
-// slots are read once into LDS and turned into weights; then lane t
+// Combine: one workgroup of NT lanes per (sequence, q head); NT = 1024 when
+// there are many slots. The (m, l) of all slots are read once into LDS (with
+// the sequence length alongside) and turned into weights; then lane t
 // accumulates the float2 column t % (D/2) over the slots i = t / (D/2)
-// (mod KS), eight loads in flight, skipping groups of unused slots, and the
-// KS partial sums are added in a fixed order (deterministic).
-template <int D>
-__global__ __launch_bounds__(256) void reduce_kernel(const float* ws, uint16_t* out,
-                                                     const int32_t* seq_lens,
-                                                     uint32_t num_q_heads, uint32_t num_splits) {
+// (mod KS), eight loads in flight, slots without keys not read, and the KS
+// partial sums are added in a fixed order (deterministic).
+template <int D, int NT>
+__global__ __launch_bounds__(NT) void reduce_kernel(const float* ws, uint16_t* out,
+                                                    const int32_t* seq_lens,
+                                                    uint32_t num_q_heads, uint32_t num_splits) {
   constexpr int COLS = D / 2;                 // float2 columns of one split row
-  constexpr int KS = 256 / COLS;              // split lanes
-  extern __shared__ float wsh[];              // num_splits weights (m first, then weights)
-  __shared__ float red[4];
+  constexpr int KS = NT / COLS;               // split lanes
+  constexpr int NW = NT / 64;                 // waves
+  extern __shared__ float wsh[];              // l (then weights) and m of every slot
+  __shared__ float red[NW];
+  __shared__ uint32_t stops[NW];
   __shared__ f32x2 part[KS][COLS];
   const int tid = threadIdx.x;
   const uint32_t bh = blockIdx.x;
@@ -751,40 +754,38 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* ws, uint16_t* 
   uint16_t* o = out + uint64_t(bh) * D;
   const float* base = ws + uint64_t(bh) * num_splits * (D + 2);
 
-  if (seq_lens[b] <= 0) {                     // empty sequence: zeros
-    if (tid < D) o[tid] = 0;
-    if (tid + 256 < D) o[tid + 256] = 0;
-    return;
-  }
   // slot i counts if l_i > 0 and no earlier slot holds an end marker (l < 0)
+  const int32_t L = seq_lens[b];
   uint32_t stop = num_splits;
-  for (uint32_t i = tid; i < num_splits; i += 256) {
+  for (uint32_t i = tid; i < num_splits; i += NT) {
     const f32x2 ml = *reinterpret_cast<const f32x2*>(base + uint64_t(i) * (D + 2) + D);
     wsh[i] = ml[1];
     wsh[num_splits + i] = ml[0];
     if (ml[1] < 0.0f) stop = min(stop, i);
   }
+  if (L <= 0) stop = 0;                       // empty sequence: zeros
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) stop = min(stop, uint32_t(__shfl_xor(int(stop), o, 64)));
-  __shared__ uint32_t stops[4];
+  for (int of = 32; of >= 1; of >>= 1) stop = min(stop, uint32_t(__shfl_xor(int(stop), of, 64)));
   if ((tid & 63) == 0) stops[tid >> 6] = stop;
   __syncthreads();
-  stop = min(min(stops[0], stops[1]), min(stops[2], stops[3]));
+#pragma unroll
+  for (int k = 0; k < NW; ++k) stop = min(stop, stops[k]);
   float M = -__builtin_inff();
-  for (uint32_t i = tid; i < stop; i += 256)
+  for (uint32_t i = tid; i < stop; i += NT)
     if (wsh[i] > 0.0f) M = fmaxf(M, wsh[num_splits + i]);
   M = wave_max(M);
   if ((tid & 63) == 0) red[tid >> 6] = M;
   __syncthreads();
-  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  M = red[0];
+#pragma unroll
+  for (int k = 1; k < NW; ++k) M = fmaxf(M, red[k]);
   __syncthreads();
   if (M == -__builtin_inff()) {               // no slot holds a key
-    if (tid < D) o[tid] = 0;
-    if (tid + 256 < D) o[tid + 256] = 0;
+    for (int d = tid; d < D; d += NT) o[d] = 0;
     return;
   }
   float wsum = 0.0f;
-  for (uint32_t i = tid; i < num_splits; i += 256) {
+  for (uint32_t i = tid; i < num_splits; i += NT) {
     const float l = wsh[i];
     const float w = (i < stop && l > 0.0f)
                         ? l * __builtin_amdgcn_exp2f((wsh[num_splits + i] - M) * kLog2e) : 0.0f;
@@ -794,32 +795,29 @@ __global__ __launch_bounds__(256) void reduce_kernel(const float* ws, uint16_t* 
   wsum = wave_sum(wsum);
   if ((tid & 63) == 0) red[tid >> 6] = wsum;
   __syncthreads();
-  wsum = (red[0] + red[1]) + (red[2] + red[3]);
+  wsum = 0.0f;
+#pragma unroll
+  for (int k = 0; k < NW; ++k) wsum += red[k];
 
   const int col = tid % COLS, ks = tid / COLS;
   f32x2 acc = {0.0f, 0.0f};
-  for (uint32_t i0 = 0; i0 < stop; i0 += 8 * KS) {
+  for (uint32_t i0 = ks; i0 < stop; i0 += 8 * KS) {
+    // eight slots per round; a slot without keys is not read (the weight is
+    // the same for every lane of a wave when D >= 128)
     float w[8];
-    bool any = false;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const uint32_t i = i0 + u * KS + ks;
-      w[u] = i < num_splits ? wsh[i] : 0.0f;
-      any |= w[u] != 0.0f;
-    }
-    if (!any) continue;                         // eight unused slots: nothing to read
     f32x2 v[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const uint32_t i = min(i0 + u * KS + ks, num_splits - 1);
-      v[u] = *reinterpret_cast<const f32x2*>(base + uint64_t(i) * (D + 2) + 2 * col);
+      const uint32_t i = i0 + u * KS;
+      w[u] = i < stop ? wsh[i] : 0.0f;
+      v[u] = f32x2{0.0f, 0.0f};
+      if (w[u] != 0.0f)
+        v[u] = *reinterpret_cast<const f32x2*>(base + uint64_t(i) * (D + 2) + 2 * col);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      if (w[u] != 0.0f) {                       // unused slots may hold anything
-        acc[0] = fmaf(w[u], v[u][0], acc[0]);
-        acc[1] = fmaf(w[u], v[u][1], acc[1]);
-      }
+      acc[0] = fmaf(w[u], v[u][0], acc[0]);
+      acc[1] = fmaf(w[u], v[u][1], acc[1]);
     }
   }
   part[ks][col] = acc;
@@ -1012,14 +1010,19 @@ extern "C" PKD_API int paged_decode_attn_reduce(const float* workspace, uint16_t
   const uint64_t grid = uint64_t(num_seqs) * num_q_heads;
   if (grid > 0x7FFFFFFFull) return kUnsupported;
   const size_t lds = 2 * size_t(num_splits) * sizeof(float);
-  const dim3 gd = dim3(uint32_t(grid)), bd = dim3(256);
+  const bool wide = num_splits >= 64;          // many slots: more lanes per (b, h)
+  const dim3 gd = dim3(uint32_t(grid)), bd = dim3(wide ? 1024 : 256);
+#define PKD_REDUCE(DD) \
+  if (wide) hipLaunchKernelGGL((reduce_kernel<DD, 1024>), gd, bd, lds, stream, workspace, output, seq_lens, num_q_heads, num_splits); \
+  else hipLaunchKernelGGL((reduce_kernel<DD, 256>), gd, bd, lds, stream, workspace, output, seq_lens, num_q_heads, num_splits);
   switch (head_dim) {
-    case 64: hipLaunchKernelGGL(reduce_kernel<64>, gd, bd, lds, stream, workspace, output, seq_lens, num_q_heads, num_splits); break;
-    case 128: hipLaunchKernelGGL(reduce_kernel<128>, gd, bd, lds, stream, workspace, output, seq_lens, num_q_heads, num_splits); break;
-    case 256: hipLaunchKernelGGL(reduce_kernel<256>, gd, bd, lds, stream, workspace, output, seq_lens, num_q_heads, num_splits); break;
-    case 512: hipLaunchKernelGGL(reduce_kernel<512>, gd, bd, lds, stream, workspace, output, seq_lens, num_q_heads, num_splits); break;
+    case 64: PKD_REDUCE(64) break;
+    case 128: PKD_REDUCE(128) break;
+    case 256: PKD_REDUCE(256) break;
+    case 512: PKD_REDUCE(512) break;
     default: return kUnsupported;
   }
+#undef PKD_REDUCE
   return launch_status();
 }
 
