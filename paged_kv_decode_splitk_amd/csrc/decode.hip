@@ -8,22 +8,23 @@
 // softmax state (m, l) to a float32 workspace [head_dim values, m, l]; one
 // combine merges them into BF16 with a 1e-20 guard on the denominator.
 //
-// Work unit: one wavefront per (sequence, kv head, chunk of up to 16 q heads
-// of that kv head's group, split). All q heads sharing a kv head are served by
-// the one pass over its pages, so each K/V byte leaves HBM once per step.
+// Work unit: one wavefront per piece of a (sequence, kv head, chunk of up to
+// 16 q heads of that kv head's group) row. All q heads sharing a kv head are
+// served by the one pass over its pages, so each K/V byte leaves HBM once per
+// step.
 //
 // Per 16-token tile (a page holds block_size/16 tiles):
-//  * K tile -> MFMA A operand straight from 16-byte global loads: lane l owns
-//    token l%16 and a contiguous run of E elements of its row per load
-//    (lane group g = l/16 takes the g-th run of every 4E-element stripe).
-//    FP8 / NVFP4 codes are dequantized to BF16 in registers (exact).
+//  * K and V tiles stream from HBM into an LDS ring with direct-to-LDS buffer
+//    loads, one block-table lookup per tile.
 //  * S = K . Q^T on v_mfma_f32_16x16x32_bf16 (M = tokens, N = q heads, K =
-//    head_dim; q heads beyond the group are zero columns).
+//    head_dim; q heads beyond the group are zero columns). FP8 / NVFP4 K codes
+//    are dequantized to BF16 in registers on their way from LDS to the MFMA
+//    (exact: every E4M3 value and every E2M1 x E4M3 product is a BF16 value).
 //  * Online softmax in fp32 on the MFMA output layout (lane l: head l%16,
 //    tokens 4g..4g+3), exp2 with log2(e) folded into the logit scale.
-//  * V tile -> BF16 rows in LDS (masked tokens written as zeros), read back
-//    transposed as the A operand of v_mfma_f32_16x16x16_bf16 computing
-//    O^T[dim][head] += V^T . P, P rounded to BF16 in registers.
+//  * O^T[dim][head] += V^T . P on v_mfma_f32_16x16x16_bf16, V^T read from
+//    LDS with transposed reads, P rounded to BF16 in registers. A quantized V
+//    tile is first dequantized into a BF16 copy in LDS.
 #include "../../include/pkd.h"
 #include "device_common.hpp"
 #include "validate.hpp"
@@ -48,81 +49,31 @@ struct DecodeArgs {
   float logit_scale;       // scale * log2(e) (* k_scale for FP8)
   float out_scale;         // v_scale for FP8, 1 otherwise
   uint32_t num_splits;
-  uint32_t pages_per_split;
   uint32_t q_stride;
   uint64_t page_bytes;     // bytes per page of one pool
   uint64_t data_section;   // NVFP4: byte offset of the scales within a page
   uint32_t window;
   uint32_t num_seqs;
-  uint32_t chunk_min;      // stream partition: least tiles per wave (S - 1 pieces per row at most)
+  uint32_t chunk_min;      // least tiles per wave (at most S pieces per row)
 };
 
-template <int FMT, int D>
-struct Traits {
-  // elements of one row a lane loads per instruction (at most 16 bytes)
-  static constexpr int kElemBits = FMT == kBf16 ? 16 : (FMT == kFp8 ? 8 : 4);
-  static constexpr int kE0 = 128 / kElemBits;               // 16 bytes worth
-  static constexpr int E = kE0 < D / 4 ? kE0 : D / 4;
-  static constexpr int kLoadBytes = E * kElemBits / 8;      // 16 or 8
-  static constexpr int NLOAD = D / (4 * E);                 // loads per tile per lane
-  static constexpr int MPER = E / 8;                        // bf16x8 fragments per load
-  static constexpr int NFRAG = D / 32;                      // QK MFMAs per tile
-  static constexpr int RS = D + 16;                         // LDS row stride (elements)
-  static constexpr int ROW_BYTES = D * kElemBits / 8;       // bytes of one (token, head) row
-  // tiles in flight per wave: about 128 VGPRs of raw K+V bytes, 1 to 4 tiles
-  static constexpr int kTileRegs = 2 * NLOAD * (kLoadBytes / 4 + (FMT == kNvfp4 ? 1 : 0));
-  static constexpr int kRing = 128 / kTileRegs;
-  static constexpr int NBUF = kRing < 1 ? 1 : (kRing > 4 ? 4 : kRing);
-};
-
-// Raw bytes of one lane's share of a K or V tile.
-template <int FMT, int D>
-struct RawTile {
-  u32x4 d[Traits<FMT, D>::NLOAD];
-  uint32_t s[Traits<FMT, D>::NLOAD];     // NVFP4 group-scale bytes
-};
-
-// Loads one lane's share of a K or V tile with buffer instructions. The
-// descriptor covers one page; live == false gives it zero records, so the
-// loads return zeros without touching memory (phantom tiles past the end of a
-// split keep the loop's load count uniform).
-template <int FMT, int D>
-__device__ __forceinline__ void load_tile(RawTile<FMT, D>& t, const uint8_t* pool,
-                                          const DecodeArgs& a, uint32_t phys, bool live,
-                                          uint32_t off, uint32_t kvh, int g) {
-  using T = Traits<FMT, D>;
-  const uint8_t* page = pool + uint64_t(phys) * a.page_bytes;
-  const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(page), 0, live ? int(a.page_bytes) : 0, 0x00020000);
-  const uint32_t rowidx = off * a.num_kv_heads + kvh;               // (offset, head) row
-#pragma unroll
-  for (int r = 0; r < T::NLOAD; ++r) {
-    const int e0 = r * 4 * T::E + g * T::E;                        // first element
-    const int voff = int(rowidx * T::ROW_BYTES + (e0 * T::kElemBits) / 8);
-    if constexpr (T::kLoadBytes == 16) {
-      t.d[r] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, voff, 0, 2));
-    } else {
-      const u32x2 v = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rsrc, voff, 0, 2));
-      t.d[r][0] = v[0];
-      t.d[r][1] = v[1];
-    }
-    if constexpr (FMT == kNvfp4) {
-      const int soff = int(a.data_section) + int(rowidx * (D / 16) + e0 / 16);
-      if constexpr (T::E == 32) t.s[r] = __builtin_amdgcn_raw_buffer_load_b16(rsrc, soff, 0, 2);
-      else t.s[r] = __builtin_amdgcn_raw_buffer_load_b8(rsrc, soff, 0, 2);
-    }
-  }
-}
-
-// Two FP8-E4M3FN codes (bytes `hi` selects 0/1 or 2/3 of w) -> packed BF16 pair.
-// gfx950 converts E4M3FN exactly; every value fits BF16.
+// Two FP8-E4M3FN codes (bytes 0/1 or 2/3 of w) -> packed BF16 pair (exact;
+// the gfx950 convert decodes E4M3FN, 0x7F / 0xFF giving NaN).
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
   const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
   return pack_bf16x2(f[0], f[1]);
 }
 
-// Two E2M1 codes (byte `sel` of w) times scale S -> packed BF16 pair (exact).
+// Eight FP8 codes (little-endian in w) -> eight BF16 values.
+__device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
+  return u32x4{fp8x2_to_bf16x2<false>(w0), fp8x2_to_bf16x2<true>(w0),
+               fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1)};
+}
+
+// Two E2M1 codes (byte `sel` of w, low nibble first) times the group scale S
+// -> packed BF16 pair. The fp4 convert takes only the exponent of its scale
+// operand, so it runs at scale 1 and S is applied by a multiply (exact).
 __device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w, int sel, float S) {
   f32x2 f;
   switch (sel) {
@@ -134,250 +85,59 @@ __device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w, int sel, float S
   return pack_bf16x2(f[0] * S, f[1] * S);
 }
 
-// Fragment f (8 consecutive elements) of a lane's load r, as BF16.
-template <int FMT, int D>
-__device__ __forceinline__ bf16x8 dequant_frag(const RawTile<FMT, D>& t, int r, int f) {
-  if constexpr (FMT == kBf16) {
-    return __builtin_bit_cast(bf16x8, t.d[r]);
-  } else if constexpr (FMT == kFp8) {
-    u32x4 out;
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      const uint32_t word = t.d[r][2 * f + w];
-      out[2 * w] = fp8x2_to_bf16x2<false>(word);
-      out[2 * w + 1] = fp8x2_to_bf16x2<true>(word);
-    }
-    return __builtin_bit_cast(bf16x8, out);
-  } else {
-    // 8 codes = one 32-bit word; group scale = byte f/2 of the lane's scales
-    const uint32_t word = t.d[r][f];
-    const float S = (f >> 1) ? __builtin_amdgcn_cvt_f32_fp8(t.s[r], 1)
-                             : __builtin_amdgcn_cvt_f32_fp8(t.s[r], 0);
-    u32x4 out;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) out[i] = fp4x2_to_bf16x2(word, i, S);
-    return __builtin_bit_cast(bf16x8, out);
-  }
+// Eight E2M1 codes (one 32-bit word) of one scale group -> eight BF16 values.
+__device__ __forceinline__ u32x4 fp4x8_to_bf16x8(uint32_t w, float S) {
+  return u32x4{fp4x2_to_bf16x2(w, 0, S), fp4x2_to_bf16x2(w, 1, S), fp4x2_to_bf16x2(w, 2, S),
+               fp4x2_to_bf16x2(w, 3, S)};
 }
 
-// Orders this wave's LDS accesses around the V transpose for the compiler; a
-// wave's LDS operations execute in issue order, so no wait is needed.
+// Orders this wave's LDS accesses for the compiler; a wave's LDS operations
+// execute in issue order, so no wait is needed.
 __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int FMT, int D>
-__global__ __launch_bounds__(64) void splitk_kernel(DecodeArgs a) {
-  using T = Traits<FMT, D>;
-  constexpr int NBUF = T::NBUF;
-  const int lane = threadIdx.x;
-  const int g = lane >> 4;          // lane group: k-run for loads, token quad for outputs
-  const int n = lane & 15;          // head column / token row / dim column
-
-  uint32_t wg = blockIdx.x;
-  const uint32_t split = wg % a.num_splits;
-  wg /= a.num_splits;
-  const uint32_t hc = wg % a.head_chunks;
-  wg /= a.head_chunks;
-  const uint32_t kvh = wg % a.num_kv_heads;
-  const uint32_t b = wg / a.num_kv_heads;
-
-  const int32_t Ls = a.seq_lens[b];
-  const uint32_t L = Ls > 0 ? uint32_t(Ls) : 0u;
-  const uint32_t lo = (a.window > 0 && L > a.window) ? L - a.window : 0u;
-  const uint32_t bs = a.block_size;
-  const uint32_t p0 = lo / bs, pend = (L + bs - 1) / bs;
-  const uint32_t pa = p0 + split * a.pages_per_split;
-  const uint32_t pb = min(pa + a.pages_per_split, pend);
-
-  const uint32_t head_in_group = hc * 16 + n;
-  const bool head_ok = head_in_group < a.group;
-  const uint32_t qh = kvh * a.group + head_in_group;        // q head of this lane's column
-  float* wrow = a.ws + ((uint64_t(b) * a.num_q_heads + qh) * a.num_splits + split) * (D + 2);
-
-  if (pa >= pb) {                                           // empty split
-    if (head_ok) {
-      for (int d = g; d < D + 2; d += 4)
-        wrow[d] = d == D ? -__builtin_inff() : 0.0f;
-    }
-    return;
-  }
-
-  const uint32_t tpp = bs / 16;                              // tiles per page
-  const uint32_t t0 = max(pa * tpp, lo / 16);
-  const uint32_t t1 = min(pb * tpp, (L + 15) / 16);
-  const int32_t* bt = a.block_tables + uint64_t(b) * a.max_blocks;
-
-  // q as the B operand of the QK MFMAs: column n = head, k-run of group g.
-  bf16x8 qf[T::NFRAG];
-  {
-    const uint16_t* qrow = a.q + uint64_t(b) * a.q_stride + uint64_t(qh) * D;
-#pragma unroll
-    for (int c = 0; c < T::NFRAG; ++c) {
-      const int r = c / T::MPER, f = c % T::MPER;
-      const int e0 = r * 4 * T::E + g * T::E + 8 * f;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (head_ok) v = *reinterpret_cast<const u32x4*>(qrow + e0);
-      qf[c] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-
-  __shared__ __attribute__((aligned(16))) uint16_t vlds[16 * T::RS];
-  // transposed-read address of this lane: row 4g + n/4, column 4*(n%4) (+16 per M tile)
-  typedef __attribute__((address_space(3))) uint16_t lds_u16;
-  typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-  lds_u16* const tr_base = (lds_u16*)(vlds) + (4 * g + (n >> 2)) * T::RS + 4 * (n & 3);
-
-  f32x4 acc[D / 16];
-#pragma unroll
-  for (int mt = 0; mt < D / 16; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -__builtin_inff();
-  float l_run = 0.0f;
-
-  RawTile<FMT, D> kb[NBUF], vb[NBUF];
-
-  // Pages in chunks of 64 (one block-table entry per lane); within a chunk the
-  // NBUF-deep register ring keeps NBUF tiles of K and V in flight.
-  for (uint32_t cp = pa; cp < pb; cp += 64) {
-    const uint32_t cpe = min(cp + 64, pb);
-    const int32_t bt_reg = (cp + lane < cpe) ? bt[cp + lane] : 0;
-    const uint32_t ct0 = max(cp * tpp, t0);
-    const uint32_t ct1 = min(cpe * tpp, t1);
-    auto issue = [&](RawTile<FMT, D>& dst, const uint8_t* pool, uint32_t t) {
-      const bool live = t < ct1;
-      const uint32_t page = min(t / tpp, cpe - 1);
-      const uint32_t phys = uint32_t(__builtin_amdgcn_readlane(bt_reg, int(page - cp)));
-      load_tile<FMT, D>(dst, pool, a, phys, live, (t % tpp) * 16 + n, kvh, g);
-    };
-#pragma unroll
-    for (int s = 0; s < NBUF; ++s) {
-      issue(kb[s], a.k_cache, ct0 + s);
-      issue(vb[s], a.v_cache, ct0 + s);
-    }
-
-    for (uint32_t tb = ct0; tb < ct1; tb += NBUF) {
-#pragma unroll
-      for (int s = 0; s < NBUF; ++s) {
-        const uint32_t t = tb + s;                 // t >= ct1: phantom tile, all keys masked
-        const uint32_t tok0 = t * 16;
-        const uint32_t klo = lo, khi = t < ct1 ? L : 0u;
-
-        // ---- S = K Q^T, then the slot's K registers take the tile NBUF ahead
-        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int c = 0; c < T::NFRAG; ++c) {
-          const bf16x8 kf = dequant_frag<FMT, D>(kb[s], c / T::MPER, c % T::MPER);
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[c], sc, 0, 0, 0);
-        }
-        // the refill reuses the slot's registers only if it stays after their last use
-        __builtin_amdgcn_sched_barrier(0);
-        issue(kb[s], a.k_cache, t + NBUF);
-
-        // ---- V tile -> LDS rows (token n of the tile), masked tokens as zeros
-        {
-          const uint32_t tok = tok0 + n;
-          const bool ok = tok >= klo && tok < khi;
-          uint16_t* dst = vlds + n * T::RS;
-#pragma unroll
-          for (int r = 0; r < T::NLOAD; ++r) {
-#pragma unroll
-            for (int f = 0; f < T::MPER; ++f) {
-              u32x4 v = __builtin_bit_cast(u32x4, dequant_frag<FMT, D>(vb[s], r, f));
-              if (!ok) v = u32x4{0u, 0u, 0u, 0u};
-              *reinterpret_cast<u32x4*>(dst + r * 4 * T::E + g * T::E + 8 * f) = v;
-            }
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        issue(vb[s], a.v_cache, t + NBUF);
-
-        // ---- online softmax (lane: head n, tokens tok0 + 4g + j)
-        float sv[4];
-        float mx = -__builtin_inff();
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t tok = tok0 + 4 * g + j;
-          sv[j] = (tok >= klo && tok < khi) ? sc[j] * a.logit_scale : -__builtin_inff();
-          mx = fmaxf(mx, sv[j]);
-        }
-        mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
-        mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-        // finite: the first tile of a split holds a key, phantom tiles come after it
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        m_run = m_new;
-        uint32_t pbits[4];
-        float psum = 0.0f;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p = __builtin_amdgcn_exp2f(sv[j] - m_new);
-          pbits[j] = f32_to_bf16_bits(p);
-          psum += __uint_as_float(pbits[j] << 16);
-        }
-        l_run = l_run * alpha + psum;
-        s16x4 pf;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pf[j] = short(pbits[j]);
-
-        wave_lds_fence();
-        // ---- O^T += V^T P  (A: V^T rows = dims of M tile mt, k = tokens 4g..4g+3)
-#pragma unroll
-        for (int mt = 0; mt < D / 16; ++mt) {
-          const bf16x4 vt =
-              __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(tr_base + mt * 16));
-          f32x4 c = acc[mt] * alpha;
-          acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vt), pf,
-                                                              c, 0, 0, 0);
-        }
-        wave_lds_fence();
-      }
-    }
-  }
-
-  // ---- partial state out: o = acc / l, m in natural-log units
-  float l_tot = l_run + __shfl_xor(l_run, 16, 64);
-  l_tot += __shfl_xor(l_tot, 32, 64);
-  if (head_ok) {
-    const float inv = a.out_scale / l_tot;
-#pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt) {
-      f32x2 lo2 = {acc[mt][0] * inv, acc[mt][1] * inv};
-      f32x2 hi2 = {acc[mt][2] * inv, acc[mt][3] * inv};
-      *reinterpret_cast<f32x2*>(wrow + mt * 16 + 4 * g) = lo2;
-      *reinterpret_cast<f32x2*>(wrow + mt * 16 + 4 * g + 2) = hi2;
-    }
-    if (g == 0) {
-      wrow[D] = m_run * kLn2;
-      wrow[D + 1] = l_tot;
-    }
-  }
-}
-
 // ---------------------------------------------------------------------------
-// BF16 cache: K and V tiles stream into an LDS ring with direct-to-LDS buffer
-// loads (gfx950 16-byte LDS DMA). Each load instruction moves whole rows:
-// lane l of instruction i fetches row i*RPI + l/CPR of the tile, and the
-// 16-byte chunk (l % CPR) ^ row of it, so the tile lands in LDS row-major
-// with the chunks of row r XOR-permuted by r. Reading K as the MFMA A
-// operand (16 rows, one chunk each) then hits 16 different bank groups, and
-// V is read transposed with ds_read_b64_tr_b16. No VGPRs hold data in
-// flight, so the ring depth is set by LDS alone; the waits on the DMA are
-// explicit (the compiler does not track LDS-DMA writes).
-template <int D>
+// K and V tiles stream into an LDS ring with direct-to-LDS buffer loads
+// (gfx950 LDS DMA, 16 bytes per lane). Each load instruction moves whole rows
+// of the tile: lane l of instruction i fetches row i*RPI + l/CPR and the
+// 16-byte chunk (l % CPR) ^ (row % CPR) of it, so the tile lands in LDS
+// row-major with the chunks of row r XOR-permuted by r. The K reads that feed
+// the MFMA (16 rows, one chunk each) and the transposed V reads then hit
+// different bank groups. NVFP4 tiles carry their group-scale rows behind the
+// codes, fetched by one more load instruction. No VGPRs hold data in flight,
+// so the ring depth is set by LDS alone; the waits on the DMA are explicit
+// (the compiler does not track LDS-DMA writes).
+template <int FMT, int D>
 struct LdsTraits {
-  static constexpr int RB = 2 * D;              // bytes of one (token, head) row
-  static constexpr int CPR = D / 8;             // 16-byte chunks per row
-  static constexpr int RPI = 64 / CPR;          // rows per load instruction (1..8)
-  static constexpr int NI = 16 / RPI;           // load instructions per 16-token tile
-  static constexpr int TILE = 16 * RB;          // bytes of one K or V tile
+  static constexpr int RB = FMT == kBf16 ? 2 * D : (FMT == kFp8 ? D : D / 2);  // row bytes
+  static constexpr int CPR = RB / 16;            // 16-byte chunks per row (2 .. 64)
+  static constexpr int RPI = 64 / CPR;           // rows per load instruction
+  static constexpr int NI = RPI >= 16 ? 1 : 16 / RPI;   // load instructions per tile
+  static constexpr int TILE = NI * 1024;         // LDS bytes of the codes of a tile
+  // NVFP4 group scales: 16 rows of D/16 bytes, one load of 16-byte or 4-byte pieces
+  static constexpr int SC_ROW = D / 16;
+  static constexpr int SC_SIZE = SC_ROW >= 16 ? 16 : 4;
+  static constexpr int SC_LPR = SC_ROW / SC_SIZE;       // lanes per scale row
+  static constexpr int SC_TILE = FMT == kNvfp4 ? 64 * SC_SIZE : 0;
+  static constexpr int KV = TILE + SC_TILE;      // LDS bytes of one K or V tile
+  static constexpr int NDMA = NI + (FMT == kNvfp4 ? 1 : 0);   // load instructions per tile
+  static constexpr int SLOT = 2 * KV;            // K tile + V tile
 #ifndef PKD_LDS_NBUF128
 #define PKD_LDS_NBUF128 1
 #endif
-  static constexpr int NBUF = D <= 64 ? 4 : (D == 128 ? PKD_LDS_NBUF128 : (D == 256 ? 2 : 1));
-  static constexpr int SLOT = 2 * TILE;         // K tile + V tile
-  static constexpr int WAIT = (2 * NBUF - 1) * NI;   // DMA loads allowed in flight at a read
+  // ring depth in tiles: measured best at one 4 KB tile pair per wave with
+  // four waves per CU; small tiles get more slots
+  static constexpr int NBUF =
+      FMT == kBf16 ? (D <= 64 ? 4 : (D == 128 ? PKD_LDS_NBUF128 : (D == 256 ? 2 : 1)))
+                   : (TILE <= 1024 ? 4 : (TILE <= 2048 ? 2 : 1));
+  static constexpr int WAIT = (2 * NBUF - 1) * NDMA;    // loads allowed in flight at a read
+  static constexpr int BRB = 2 * D;              // bytes of a BF16 row (V read transposed)
+  static constexpr int BCPR = D / 8;             // 16-byte chunks of a BF16 row
+  static constexpr int STAGE = FMT == kBf16 ? 16 : 16 * BRB;   // BF16 copy of a quantized V tile
+  static_assert(WAIT < 64, "vmcnt range");
 };
 
 // s_waitcnt that waits for vmcnt <= N only (expcnt / lgkmcnt left at their maximum).
@@ -454,18 +214,28 @@ __device__ __forceinline__ RowLoc find_row(const DecodeArgs& a, uint32_t pos,
   return RowLoc{a.num_seqs, 0, 0, base};
 }
 
-template <int D>
+
+template <int FMT, int D>
 struct StreamLds {
-  __attribute__((aligned(1024))) uint8_t ring[LdsTraits<D>::NBUF * LdsTraits<D>::SLOT];
+  __attribute__((aligned(1024))) uint8_t ring[LdsTraits<FMT, D>::NBUF * LdsTraits<FMT, D>::SLOT];
+  __attribute__((aligned(16))) uint8_t stage[LdsTraits<FMT, D>::STAGE];
 };
 
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+typedef __attribute__((address_space(3))) uint32_t lds_u32;
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
 // One row piece: tiles [tau0, tau1) of row (b, kh), partial state to `slot`.
-template <int D>
-__device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<D>& sh, uint32_t b,
+template <int FMT, int D>
+__device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D>& sh, uint32_t b,
                                           uint32_t kh, uint32_t tau0, uint32_t tau1,
                                           uint32_t slot, bool last, uint32_t L) {
-  using T = LdsTraits<D>;
+  using T = LdsTraits<FMT, D>;
   constexpr int NBUF = T::NBUF;
+  if (slot >= a.num_splits) return;      // only if a sequence outgrows its block table
   const int lane = threadIdx.x;
   const int g = lane >> 4;
   const int n = lane & 15;
@@ -495,10 +265,8 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<D>& sh,
     }
   }
 
-  typedef __attribute__((address_space(3))) uint8_t lds_u8;
-  typedef __attribute__((address_space(3))) void lds_void;
-  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
   lds_u8* const ring3 = (lds_u8*)(sh.ring);
+  lds_u8* const stage3 = (lds_u8*)(sh.stage);
   const int ld_row = lane / T::CPR;                  // + i * RPI
   const int ld_pos = lane % T::CPR;
 
@@ -516,6 +284,10 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<D>& sh,
     const uint32_t ct0 = max(cp * tpp, t0);
     const uint32_t ct1 = min(cpe * tpp, t1);
 
+    // Tile t of kind kv (0 = K, 1 = V) into ring slot s. A tile past the
+    // segment's end gets a zero-length descriptor: zeros land in LDS and no
+    // memory is read. Lanes without a row to fetch use an offset past any
+    // page, which reads nothing either.
     auto issue = [&](int s, int kv, uint32_t t) {
       const bool live = t < ct1;
       const uint32_t page = min(t / tpp, cpe - 1);
@@ -525,13 +297,25 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<D>& sh,
           const_cast<uint8_t*>(pool + uint64_t(phys) * a.page_bytes), 0,
           live ? int(a.page_bytes) : 0, 0x00020000);
       const uint32_t off0 = (t % tpp) * 16;
+      lds_u8* const dst = ring3 + s * T::SLOT + kv * T::KV;
 #pragma unroll
       for (int i = 0; i < T::NI; ++i) {
         const int row = i * T::RPI + ld_row;
         const int chunk = ld_pos ^ (row % T::CPR);
-        const int voff = int(((off0 + row) * a.num_kv_heads + kvh) * T::RB + chunk * 16);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            rsrc, (lds_void*)(ring3 + s * T::SLOT + kv * T::TILE + i * 1024), 16, voff, 0, 0, 2);
+        int voff = int(((off0 + row) * a.num_kv_heads + kvh) * T::RB + chunk * 16);
+        if constexpr (T::RPI > 16) voff = row < 16 ? voff : 0x7FFFFFF0;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + i * 1024), 16, voff,
+                                                 0, 0, 2);
+      }
+      if constexpr (FMT == kNvfp4) {
+        const int srow = lane / T::SC_LPR;
+        const int part = lane % T::SC_LPR;
+        const int voff = srow < 16 ? int(a.data_section) +
+                                         int(((off0 + srow) * a.num_kv_heads + kvh) * T::SC_ROW +
+                                             part * T::SC_SIZE)
+                                   : 0x7FFFFFF0;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + T::TILE), T::SC_SIZE,
+                                                 voff, 0, 0, 2);
       }
     };
 
@@ -548,19 +332,47 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<D>& sh,
         const uint32_t tok0 = t * 16;
         const uint32_t khi = t < ct1 ? L : 0u;
         lds_u8* const kt = ring3 + s * T::SLOT;
-        lds_u8* const vt = kt + T::TILE;
+        lds_u8* const vt = kt + T::KV;
 
-        // ---- S = K Q^T from the LDS tile (row n, chunk 4c+g swizzled by n)
+        // ---- S = K Q^T from the LDS tile (row n, dims 32c + 8g .. +8)
         wait_vmcnt<T::WAIT>();
         wave_lds_fence();
         __builtin_amdgcn_sched_barrier(0);
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (FMT == kBf16) {
 #pragma unroll
-        for (int c = 0; c < D / 32; ++c) {
-          const int chunk = (4 * c + g) ^ (n % T::CPR);
-          const u32x4 kv = *(lds_u32x4*)(kt + n * T::RB + chunk * 16);
-          sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qf[c], sc,
-                                                       0, 0, 0);
+          for (int c = 0; c < D / 32; ++c) {
+            const int chunk = (4 * c + g) ^ (n % T::CPR);
+            const u32x4 kv = *(lds_u32x4*)(kt + n * T::RB + chunk * 16);
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qf[c],
+                                                         sc, 0, 0, 0);
+          }
+        } else if constexpr (FMT == kFp8) {
+#pragma unroll
+          for (int c = 0; c < D / 32; ++c) {
+            const int chunk = (2 * c + (g >> 1)) ^ (n % T::CPR);
+            const u32x2 w = *(lds_u32x2*)(kt + n * T::RB + chunk * 16 + 8 * (g & 1));
+            const u32x4 kv = fp8x8_to_bf16x8(w[0], w[1]);
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qf[c],
+                                                         sc, 0, 0, 0);
+          }
+        } else {
+          // group of dims 32c + 8g is 2c + g/2: byte 2(c & 1) of scale word c/2
+          // once the words are shifted down by g/2 bytes
+          uint32_t sw[(T::SC_ROW + 3) / 4];
+#pragma unroll
+          for (int k = 0; k < (T::SC_ROW + 3) / 4; ++k)
+            sw[k] = *(lds_u32*)(kt + T::TILE + n * T::SC_ROW + 4 * k) >> (8 * (g >> 1));
+#pragma unroll
+          for (int c = 0; c < D / 32; ++c) {
+            const int chunk = c ^ (n % T::CPR);
+            const uint32_t w = *(lds_u32*)(kt + n * T::RB + chunk * 16 + 4 * g);
+            const float S = (c & 1) ? __builtin_amdgcn_cvt_f32_fp8(sw[c / 2], 2)
+                                    : __builtin_amdgcn_cvt_f32_fp8(sw[c / 2], 0);
+            const u32x4 kv = fp4x8_to_bf16x8(w, S);
+            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qf[c],
+                                                         sc, 0, 0, 0);
+          }
         }
         __builtin_amdgcn_sched_barrier(0);
         issue(s, 0, t + NBUF);
@@ -593,57 +405,97 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<D>& sh,
 #pragma unroll
         for (int j = 0; j < 4; ++j) pf[j] = short(pbits[j]);
 
-        // ---- V tile: wait, zero the rows of masked tokens (partial tiles only)
+        // ---- V tile as BF16 rows with masked tokens zeroed: in place for a
+        // BF16 cache (partial tiles only), else dequantized into the stage
         wait_vmcnt<T::WAIT>();
         wave_lds_fence();
         __builtin_amdgcn_sched_barrier(0);
-        if (tok0 < lo || tok0 + 16 > khi) {
+        lds_u8* vsrc;
+        if constexpr (FMT == kBf16) {
+          vsrc = vt;
+          if (tok0 < lo || tok0 + 16 > khi) {
+#pragma unroll
+            for (int i = 0; i < T::NI; ++i) {
+              const uint32_t tok = tok0 + i * T::RPI + ld_row;
+              if (tok < lo || tok >= khi)
+                *(lds_u32x4*)(vt + i * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+            }
+            wave_lds_fence();
+          }
+        } else {
+          vsrc = stage3;
 #pragma unroll
           for (int i = 0; i < T::NI; ++i) {
-            const uint32_t tok = tok0 + i * T::RPI + ld_row;
-            if (tok < lo || tok >= khi)
-              *(lds_u32x4*)(vt + i * 1024 + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+            const int row = i * T::RPI + ld_row;
+            if (T::RPI > 16 && row >= 16) continue;
+            const int pc = ld_pos ^ (row % T::CPR);        // logical chunk at this position
+            const u32x4 raw = *(lds_u32x4*)(vt + i * 1024 + lane * 16);
+            const uint32_t tok = tok0 + row;
+            const bool ok = tok >= lo && tok < khi;
+            lds_u8* const srow = stage3 + row * T::BRB;
+            const int sx = row % T::BCPR;
+            if constexpr (FMT == kFp8) {
+              u32x4 h0 = fp8x8_to_bf16x8(raw[0], raw[1]);
+              u32x4 h1 = fp8x8_to_bf16x8(raw[2], raw[3]);
+              if (!ok) h0 = h1 = u32x4{0u, 0u, 0u, 0u};
+              *(lds_u32x4*)(srow + ((2 * pc) ^ sx) * 16) = h0;
+              *(lds_u32x4*)(srow + ((2 * pc + 1) ^ sx) * 16) = h1;
+            } else {
+              // 32 codes = scale groups 2pc (words 0, 1) and 2pc + 1 (words 2, 3)
+              const uint32_t s2 = *(lds_u16*)(vt + T::TILE + row * T::SC_ROW + 2 * pc);
+              const float S0 = __builtin_amdgcn_cvt_f32_fp8(s2, 0);
+              const float S1 = __builtin_amdgcn_cvt_f32_fp8(s2, 1);
+#pragma unroll
+              for (int w = 0; w < 4; ++w) {
+                u32x4 h = fp4x8_to_bf16x8(raw[w], w < 2 ? S0 : S1);
+                if (!ok) h = u32x4{0u, 0u, 0u, 0u};
+                *(lds_u32x4*)(srow + ((4 * pc + w) ^ sx) * 16) = h;
+              }
+            }
           }
           wave_lds_fence();
+          __builtin_amdgcn_sched_barrier(0);
+          issue(s, 1, t + NBUF);                   // the raw V tile is consumed
         }
         // ---- O^T += V^T P: lane supplies V[4g + n/4][16mt + 4(n%4) .. +4]. The
         // transposed reads are issued as inline asm: the compiler would otherwise
-        // wait for every pending LDS-DMA load before each of them.
+        // wait for every pending LDS-DMA load before each of them. Four reads,
+        // then their four MFMAs, which run while the next reads are in flight.
+        if (rescale) {
+#pragma unroll
+          for (int mt = 0; mt < D / 16; ++mt) acc[mt] *= alpha;
+        }
         {
           const int vtok = 4 * g + (n >> 2);
-          const uint32_t vrow = uint32_t(uintptr_t(vt)) + vtok * T::RB + (n & 1) * 8;
-          u32x2 vv[D / 16];
+          const uint32_t vrow = uint32_t(uintptr_t(vsrc)) + vtok * T::BRB + (n & 1) * 8;
 #pragma unroll
           for (int q4 = 0; q4 < D / 64; ++q4) {
             uint32_t ad[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
               const int mt = 4 * q4 + u;
-              ad[u] = vrow + (((2 * mt + ((n & 3) >> 1)) ^ (vtok % T::CPR)) * 16);
+              ad[u] = vrow + (((2 * mt + ((n & 3) >> 1)) ^ (vtok % T::BCPR)) * 16);
             }
             // four transposed reads and their wait in one statement: the outputs
             // exist only after the wait, so no consumer can be scheduled earlier
+            u32x2 vv[4];
             asm volatile(
                 "ds_read_b64_tr_b16 %0, %4\n\t"
                 "ds_read_b64_tr_b16 %1, %5\n\t"
                 "ds_read_b64_tr_b16 %2, %6\n\t"
                 "ds_read_b64_tr_b16 %3, %7\n\t"
                 "s_waitcnt lgkmcnt(0)"
-                : "=&v"(vv[4 * q4]), "=&v"(vv[4 * q4 + 1]), "=&v"(vv[4 * q4 + 2]), "=&v"(vv[4 * q4 + 3])
+                : "=&v"(vv[0]), "=&v"(vv[1]), "=&v"(vv[2]), "=&v"(vv[3])
                 : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
                 : "memory");
-          }
-          if (rescale) {
 #pragma unroll
-            for (int mt = 0; mt < D / 16; ++mt) acc[mt] *= alpha;
+            for (int u = 0; u < 4; ++u)
+              acc[4 * q4 + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
+                  __builtin_bit_cast(s16x4, vv[u]), pf, acc[4 * q4 + u], 0, 0, 0);
           }
-#pragma unroll
-          for (int mt = 0; mt < D / 16; ++mt)
-            acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, vv[mt]),
-                                                                pf, acc[mt], 0, 0, 0);
         }
         __builtin_amdgcn_sched_barrier(0);
-        issue(s, 1, t + NBUF);
+        if constexpr (FMT == kBf16) issue(s, 1, t + NBUF);
       }
     }
     wait_vmcnt<0>();                               // the ring restarts with the next segment
@@ -675,16 +527,16 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<D>& sh,
   }
 }
 
-template <int D>
-__global__ __launch_bounds__(64) void splitk_bf16_stream(DecodeArgs a) {
-  __shared__ StreamLds<D> sh;
+template <int FMT, int D>
+__global__ __launch_bounds__(64) void splitk_stream(DecodeArgs a) {
+  __shared__ StreamLds<FMT, D> sh;
   const uint32_t R = a.num_kv_heads * a.head_chunks;          // rows per sequence
   if (a.num_splits == 1) {                                    // one wave per row
     const uint32_t b = blockIdx.x / R, kh = blockIdx.x % R;
     const int32_t Ls = a.seq_lens[b];
     const uint32_t L = Ls > 0 ? uint32_t(Ls) : 0u;
     const uint32_t n = row_tiles(L, a.window);
-    if (n) run_piece<D>(a, sh, b, kh, 0, n, 0, true, L);
+    if (n) run_piece<FMT, D>(a, sh, b, kh, 0, n, 0, true, L);
     return;
   }
   const uint32_t P = gridDim.x;
@@ -709,8 +561,8 @@ __global__ __launch_bounds__(64) void splitk_bf16_stream(DecodeArgs a) {
       const uint32_t kh = (pos - excl) / n;
       const uint32_t start = excl + kh * n;
       const uint32_t tau1 = min(n, end - start);
-      run_piece<D>(a, sh, uint32_t(l), kh, pos - start, tau1, pos / c - start / c,
-                   start + n <= end, L);
+      run_piece<FMT, D>(a, sh, uint32_t(l), kh, pos - start, tau1, pos / c - start / c,
+                        start + n <= end, L);
       pos = start + tau1;
     }
     return;
@@ -725,8 +577,8 @@ __global__ __launch_bounds__(64) void splitk_bf16_stream(DecodeArgs a) {
     const uint32_t tau1 = min(r.n, end - r.start);
     const uint32_t slot = pos / c - r.start / c;
     const int32_t Ls = a.seq_lens[r.b];
-    run_piece<D>(a, sh, r.b, r.kh, tau0, tau1, slot, r.start + r.n <= end,
-                 Ls > 0 ? uint32_t(Ls) : 0u);
+    run_piece<FMT, D>(a, sh, r.b, r.kh, tau0, tau1, slot, r.start + r.n <= end,
+                      Ls > 0 ? uint32_t(Ls) : 0u);
     pos = r.start + tau1;
   }
 }
@@ -838,24 +690,34 @@ static int launch_status() {
 }
 
 // Waves the stream kernel launches on the current device: all resident at
-// once (at most the occupancy), cached per device and head_dim.
+// once (at most the occupancy), cached per device, format and head_dim.
+template <int FMT, int D>
+static int stream_occupancy() {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, splitk_stream<FMT, D>, 64, 0) !=
+      hipSuccess)
+    return 0;
+  return per_cu;
+}
+
+template <int FMT>
 static uint64_t stream_capacity(uint32_t head_dim) {
   static uint64_t cache[64][4];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   const int di = head_dim == 64 ? 0 : head_dim == 128 ? 1 : head_dim == 256 ? 2 : 3;
   if (cache[dev][di]) return cache[dev][di];
-  int cus = 0, per_cu = 0;
+  int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  hipError_t e = hipErrorInvalidValue;
+  int per_cu = 0;
   switch (head_dim) {
-    case 64: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, splitk_bf16_stream<64>, 64, 0); break;
-    case 128: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, splitk_bf16_stream<128>, 64, 0); break;
-    case 256: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, splitk_bf16_stream<256>, 64, 0); break;
-    case 512: e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, splitk_bf16_stream<512>, 64, 0); break;
+    case 64: per_cu = stream_occupancy<FMT, 64>(); break;
+    case 128: per_cu = stream_occupancy<FMT, 128>(); break;
+    case 256: per_cu = stream_occupancy<FMT, 256>(); break;
+    case 512: per_cu = stream_occupancy<FMT, 512>(); break;
   }
-  if (e != hipSuccess || per_cu <= 0 || cus <= 0) return 0;
+  if (per_cu <= 0 || cus <= 0) return 0;
 #ifndef PKD_STREAM_WAVES_PER_CU
 #define PKD_STREAM_WAVES_PER_CU 4
 #endif
@@ -869,36 +731,26 @@ static uint64_t stream_capacity(uint32_t head_dim) {
 template <int FMT>
 static int launch_splitk(DecodeArgs a, uint32_t num_seqs, uint32_t head_dim,
                          hipStream_t stream) {
+  // one page must stay addressable by 32-bit buffer offsets
+  if (a.page_bytes > 0x7FFF0000ull) return kUnsupported;
   a.num_seqs = num_seqs;
-  const uint64_t grid = uint64_t(num_seqs) * a.num_kv_heads * a.head_chunks * a.num_splits;
-  if (grid > 0x7FFFFFFFull) return kUnsupported;
-  const dim3 gd = dim3(uint32_t(grid)), bd = dim3(64);
-  if (FMT == kBf16) {
-    const uint32_t rows = num_seqs * a.num_kv_heads * a.head_chunks;
-    uint32_t tile_bound = a.max_blocks * (a.block_size / 16);
-    if (a.window > 0) tile_bound = min(tile_bound, (a.window + 14) / 16 + 1);
-    a.chunk_min = a.num_splits > 1 ? (tile_bound + a.num_splits - 2) / (a.num_splits - 1) : 1;
-    uint64_t waves = rows;
-    if (a.num_splits > 1) {
-      waves = uint64_t(rows) * a.num_splits;
-      const uint64_t cap = stream_capacity(head_dim);
-      if (cap && waves > cap) waves = cap;
-    }
-    const dim3 sgd = dim3(uint32_t(waves));
-    switch (head_dim) {
-      case 64: hipLaunchKernelGGL(splitk_bf16_stream<64>, sgd, bd, 0, stream, a); break;
-      case 128: hipLaunchKernelGGL(splitk_bf16_stream<128>, sgd, bd, 0, stream, a); break;
-      case 256: hipLaunchKernelGGL(splitk_bf16_stream<256>, sgd, bd, 0, stream, a); break;
-      case 512: hipLaunchKernelGGL(splitk_bf16_stream<512>, sgd, bd, 0, stream, a); break;
-      default: return kUnsupported;
-    }
-    return launch_status();
+  const uint64_t rows = uint64_t(num_seqs) * a.num_kv_heads * a.head_chunks;
+  uint32_t tile_bound = a.max_blocks * (a.block_size / 16);
+  if (a.window > 0) tile_bound = min(tile_bound, (a.window + 14) / 16 + 1);
+  a.chunk_min = a.num_splits > 1 ? (tile_bound + a.num_splits - 2) / (a.num_splits - 1) : 1;
+  uint64_t waves = rows;
+  if (a.num_splits > 1) {
+    waves = rows * a.num_splits;
+    const uint64_t cap = stream_capacity<FMT>(head_dim);
+    if (cap && waves > cap) waves = cap;
   }
+  if (waves > 0x7FFFFFFFull) return kUnsupported;
+  const dim3 gd = dim3(uint32_t(waves)), bd = dim3(64);
   switch (head_dim) {
-    case 64: hipLaunchKernelGGL((splitk_kernel<FMT, 64>), gd, bd, 0, stream, a); break;
-    case 128: hipLaunchKernelGGL((splitk_kernel<FMT, 128>), gd, bd, 0, stream, a); break;
-    case 256: hipLaunchKernelGGL((splitk_kernel<FMT, 256>), gd, bd, 0, stream, a); break;
-    case 512: hipLaunchKernelGGL((splitk_kernel<FMT, 512>), gd, bd, 0, stream, a); break;
+    case 64: hipLaunchKernelGGL((splitk_stream<FMT, 64>), gd, bd, 0, stream, a); break;
+    case 128: hipLaunchKernelGGL((splitk_stream<FMT, 128>), gd, bd, 0, stream, a); break;
+    case 256: hipLaunchKernelGGL((splitk_stream<FMT, 256>), gd, bd, 0, stream, a); break;
+    case 512: hipLaunchKernelGGL((splitk_stream<FMT, 512>), gd, bd, 0, stream, a); break;
     default: return kUnsupported;
   }
   return launch_status();
@@ -925,7 +777,6 @@ static DecodeArgs make_args(const uint16_t* q, const void* kc, const void* vc, f
   a.logit_scale = logit_scale;
   a.out_scale = out_scale;
   a.num_splits = S;
-  a.pages_per_split = pages_per_split(max_blocks, bs, window, S);
   a.q_stride = q_stride;
   a.page_bytes = page_bytes;
   a.data_section = data_section;

@@ -87,12 +87,6 @@ inline uint32_t split_page_bound(uint32_t max_blocks_per_seq, uint32_t block_siz
   return bound ? bound : 1;
 }
 
-inline uint32_t pages_per_split(uint32_t max_blocks_per_seq, uint32_t block_size,
-                                uint32_t sliding_window, uint32_t num_splits) {
-  const uint32_t p = split_page_bound(max_blocks_per_seq, block_size, sliding_window);
-  return (p + num_splits - 1) / num_splits;
-}
-
 inline uint32_t head_chunks(uint32_t group) { return (group + 15) / 16; }
 
 inline size_t workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads, uint32_t head_dim,
@@ -100,13 +94,11 @@ inline size_t workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads, uint32_t 
   return size_t(num_seqs) * num_q_heads * num_splits * (size_t(head_dim) + 2) * sizeof(float);
 }
 
-// Split-count heuristic. The BF16 split-K pass launches about 4 waves per CU
-// and balances the batch's tiles evenly over them; num_splits only bounds how
-// many pieces one (sequence, kv head) row may be cut into. It is chosen so
-// that this bound does not force pieces longer than an even share, with room
-// for batches whose sequences are shorter than the block-table width (4x).
-// The FP8 / NVFP4 passes cut each row into num_splits chunks of the page
-// bound, so the same count also gives them several waves per CU.
+// Split-count heuristic. The split-K pass launches about 4 waves per CU and
+// balances the batch's tiles evenly over them; num_splits only bounds how many
+// pieces one (sequence, kv head) row may be cut into. It is chosen so that this
+// bound does not force pieces longer than an even share, with room for batches
+// whose sequences are shorter than the block-table width (4x).
 inline uint32_t num_splits_heuristic(uint32_t num_seqs, uint32_t num_q_heads,
                                      uint32_t num_kv_heads, uint32_t max_blocks_per_seq,
                                      uint32_t block_size, uint32_t sliding_window,

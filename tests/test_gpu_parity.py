@@ -206,6 +206,14 @@ CASES = [
     ("nvfp4", (40, 333), 8, 2, 128, 16, 0, 2),
     ("nvfp4", (40, 333), 8, 2, 64, 32, 0, 2),
     ("nvfp4", (40, 200), 4, 2, 256, 64, 0, 2),
+    ("fp8", (90, 400), 40, 2, 128, 16, 0, 3),           # two head chunks
+    ("fp8", (5, 77, 530), 4, 4, 256, 256, 0, 2),
+    ("fp8", (0, 1, 2, 700), 16, 8, 256, 16, 0, 4),      # empty, one and two keys
+    ("fp8", (33, 600), 8, 2, 512, 32, 300, 3),
+    ("nvfp4", (90, 400, 17), 6, 2, 64, 16, 37, 3),
+    ("nvfp4", (50, 300), 8, 8, 512, 128, 0, 1),
+    ("nvfp4", (0, 1, 2, 700), 16, 2, 512, 16, 0, 4),
+    ("nvfp4", (90, 400), 40, 2, 128, 16, 0, 5),
 ]
 
 
