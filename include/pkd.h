@@ -135,12 +135,13 @@ PKD_API int bf16_absmax(const uint16_t* data, float* out_max, uint64_t n_elems,
  *   dot); output = softmax(s) . V.
  * Splits: the keys of every (b, h) are divided into at most num_splits
  *   pieces, each a contiguous key range; how the launch's work is divided
- *   among waves is internal (the BF16 path balances equal key counts across
- *   the waves it launches, whatever the batch's length mix).
+ *   among waves is internal (equal key counts across the waves it launches,
+ *   whatever the batch's length mix).
  * Workspace: float32 [num_seqs][num_q_heads][num_splits][head_dim + 2]; slot i
  *   of (b, h) holds a piece's o (head_dim values, its softmax-normalized
- *   output), m (its largest logit) and l (sum of exp(s_j - m)). A slot that
- *   holds no keys has l = 0 (m = -inf); a slot with l < 0 is an end marker:
+ *   output), m and l = sum of exp(s_j - m), where m is a reference logit at
+ *   most 8*ln(2) below the piece's largest logit (and never above it). A
+ *   slot that holds no keys has l = 0; a slot with l < 0 is an end marker:
  *   it and every later slot of (b, h) hold no keys, whatever they contain.
  *   The o of a slot without keys is unspecified. Size:
  *   paged_decode_workspace_bytes(). Any contents on entry are fine.
@@ -199,6 +200,63 @@ PKD_API int paged_decode_attn_reduce(const float* workspace, uint16_t* output,
                                      uint32_t head_dim, uint32_t num_splits, uint32_t num_seqs,
                                      hipStream_t stream);
 
+/* ---------------------------------------------------------------- single-launch decode
+ * The whole decode into BF16 output [num_seqs][num_q_heads][head_dim]
+ * (contiguous): the same attention as a split-K call followed by
+ * paged_decode_attn_reduce, in one call. The argument order follows the
+ * non-split launcher paged_decode_attn_nvfp4 of the metrale page (q, caches,
+ * output, block_tables, seq_lens, max_blocks_per_seq, num_seqs, head counts,
+ * head_dim, block_size, scale, q_stride, cache layout); sliding_window,
+ * workspace, counters and num_splits are extensions.
+ *   num_splits == 1: one wave per (sequence, kv head, 16 q heads), output
+ *     written directly, as the non-split launcher does; workspace and
+ *     counters are not used (may be null).
+ *   1 < num_splits <= PKD_FUSED_MAX_SPLITS: one launch; each (sequence, kv
+ *     head, 16 q heads) row is cut into at most num_splits pieces, and the
+ *     last piece of a row to finish merges the row's partials (the combine of
+ *     paged_decode_attn_reduce, in-kernel). workspace: as for the split-K
+ *     calls (paged_decode_workspace_bytes). counters: uint32
+ *     [num_seqs * num_q_heads] (num_seqs * num_kv_heads * ceil(group / 16)
+ *     entries are used), all zero before the first call; every call leaves
+ *     them zero again. Calls that share a counters array must not overlap.
+ *   num_splits > PKD_FUSED_MAX_SPLITS: the split-K pass and the combine as
+ *     two launches on `stream`; counters are not used.
+ * Sequences with seq_lens[b] == 0 get zeros. Other arguments and errors as
+ * for the split-K calls; output must be 16-byte aligned. */
+#define PKD_FUSED_MAX_SPLITS 32u
+
+PKD_API int paged_decode_attn_bf16(const uint16_t* q, const uint16_t* k_cache,
+                                   const uint16_t* v_cache, uint16_t* output,
+                                   const int32_t* block_tables, const int32_t* seq_lens,
+                                   uint32_t max_blocks_per_seq, uint32_t num_seqs,
+                                   uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
+                                   uint32_t block_size, float scale, uint32_t q_stride,
+                                   uint32_t sliding_window, float* workspace, uint32_t* counters,
+                                   uint32_t num_splits, hipStream_t stream);
+
+/* FP8-E4M3FN cache, as paged_decode_attn_splitk_fp8. */
+PKD_API int paged_decode_attn_fp8(const uint16_t* q, const uint8_t* k_cache,
+                                  const uint8_t* v_cache, uint16_t* output,
+                                  const int32_t* block_tables, const int32_t* seq_lens,
+                                  uint32_t max_blocks_per_seq, uint32_t num_seqs,
+                                  uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
+                                  uint32_t block_size, float scale, float k_scale, float v_scale,
+                                  uint32_t q_stride, uint64_t cache_stride,
+                                  uint32_t sliding_window, float* workspace, uint32_t* counters,
+                                  uint32_t num_splits, hipStream_t stream);
+
+/* NVFP4 cache (paged_decode_attn_nvfp4 on the metrale page, extended). */
+PKD_API int paged_decode_attn_nvfp4(const uint16_t* q, const uint8_t* k_cache,
+                                    const uint8_t* v_cache, uint16_t* output,
+                                    const int32_t* block_tables, const int32_t* seq_lens,
+                                    uint32_t max_blocks_per_seq, uint32_t num_seqs,
+                                    uint32_t num_q_heads, uint32_t num_kv_heads,
+                                    uint32_t head_dim, uint32_t block_size, float scale,
+                                    uint32_t q_stride, uint64_t block_stride_bytes,
+                                    uint64_t data_section_bytes, uint32_t sliding_window,
+                                    float* workspace, uint32_t* counters, uint32_t num_splits,
+                                    hipStream_t stream);
+
 /* ---------------------------------------------------------------- host helpers
  * Bytes of the split-K workspace: num_seqs*num_q_heads*num_splits*(head_dim+2)*4. */
 PKD_API size_t paged_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads,
@@ -207,10 +265,10 @@ PKD_API size_t paged_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_he
 /* A split count for the split-K calls: 1 + 4 * (4 * num_cus) / rows, rows =
  * num_seqs * num_kv_heads * ceil(group / 16), capped at the row's tile bound
  * (16-key tiles within max_blocks_per_seq pages, or the window) and at
- * PKD_MAX_SPLITS. The BF16 pass launches about four waves per CU and spreads
+ * PKD_MAX_SPLITS. The split-K pass launches about four waves per CU and spreads
  * the batch's tiles evenly over them, so this count only needs to exceed the
- * pieces a row is cut into; the FP8 / NVFP4 passes give each row num_splits
- * equal page chunks. Pure host arithmetic; num_cus = compute-unit count. */
+ * pieces a row is cut into. Pure host arithmetic; num_cus = compute-unit
+ * count. */
 PKD_API uint32_t paged_decode_num_splits(uint32_t num_seqs, uint32_t num_q_heads,
                                          uint32_t num_kv_heads, uint32_t max_blocks_per_seq,
                                          uint32_t block_size, uint32_t sliding_window,

@@ -29,6 +29,9 @@ def hipcc_command(out=LIB_PATH):
         hipcc, f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
         "-fvisibility=hidden", "-Wall", "-Wno-unused-function",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA results in VGPRs: the accumulators are also scaled by VALU code,
+        # and AGPR-resident ones are copied to VGPRs and back around it
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-I", os.path.join(ROOT, "include"),
         *os.environ.get("PKD_EXTRA_HIPCC_FLAGS", "").split(),
         "-o", out, *sources(),

@@ -33,6 +33,13 @@ namespace pkd {
 
 enum Fmt { kBf16 = 0, kFp8 = 1, kNvfp4 = 2 };
 
+// Largest growth of a head's max (log2 units) absorbed without rescaling.
+constexpr float kLazyMax = 8.0f;
+
+// Single-launch decode: most pieces per row merged in-kernel (more split
+// counts run the split-K pass and the combine as two launches).
+constexpr int kFuseMaxSplits = int(PKD_FUSED_MAX_SPLITS);
+
 struct DecodeArgs {
   const uint16_t* q;
   const uint8_t* k_cache;
@@ -55,14 +62,15 @@ struct DecodeArgs {
   uint32_t window;
   uint32_t num_seqs;
   uint32_t chunk_min;      // least tiles per wave (at most S pieces per row)
+  uint16_t* out;           // single-launch decode: BF16 output (null for the split-K call)
+  uint32_t* counters;      // single-launch decode: finished pieces per row
 };
 
-// Two FP8-E4M3FN codes (bytes 0/1 or 2/3 of w) -> packed BF16 pair (exact;
-// the gfx950 convert decodes E4M3FN, 0x7F / 0xFF giving NaN).
+// Two FP8-E4M3FN codes (bytes 0/1 or 2/3 of w) -> packed BF16 pair, in one
+// gfx950 convert at unit scale (exact: every E4M3FN value is a BF16 value).
 template <bool HI>
 __device__ __forceinline__ uint32_t fp8x2_to_bf16x2(uint32_t w) {
-  const f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8(w, HI);
-  return pack_bf16x2(f[0], f[1]);
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI));
 }
 
 // Eight FP8 codes (little-endian in w) -> eight BF16 values.
@@ -128,16 +136,20 @@ struct LdsTraits {
 #ifndef PKD_LDS_NBUF128
 #define PKD_LDS_NBUF128 1
 #endif
+#ifndef PKD_LDS_NBUF_Q
+#define PKD_LDS_NBUF_Q 1
+#endif
   // ring depth in tiles: measured best at one 4 KB tile pair per wave with
   // four waves per CU; small tiles get more slots
   static constexpr int NBUF =
       FMT == kBf16 ? (D <= 64 ? 4 : (D == 128 ? PKD_LDS_NBUF128 : (D == 256 ? 2 : 1)))
-                   : (TILE <= 1024 ? 4 : (TILE <= 2048 ? 2 : 1));
+                   : (TILE <= 1024 ? 4 : (TILE <= 2048 ? 2 : PKD_LDS_NBUF_Q));
   static constexpr int WAIT = (2 * NBUF - 1) * NDMA;    // loads allowed in flight at a read
   static constexpr int BRB = 2 * D;              // bytes of a BF16 row (V read transposed)
   static constexpr int BCPR = D / 8;             // 16-byte chunks of a BF16 row
   static constexpr int STAGE = FMT == kBf16 ? 16 : 16 * BRB;   // BF16 copy of a quantized V tile
   static_assert(WAIT < 64, "vmcnt range");
+  static_assert(NBUF * SLOT >= 16 * kFuseMaxSplits * 4, "the ring also holds the combine weights");
 };
 
 // s_waitcnt that waits for vmcnt <= N only (expcnt / lgkmcnt left at their maximum).
@@ -228,11 +240,128 @@ typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
+// A quantized V tile (raw codes in the ring) -> BF16 rows in the stage, with
+// the same chunk swizzle as a BF16 tile, rows of keys outside [lo, khi) as
+// zeros (FP8: selected when MASK; NVFP4: always, through a zero scale).
+template <int FMT, int D, bool MASK>
+__device__ __forceinline__ void stage_v(lds_u8* vt, lds_u8* stage, int lane, uint32_t tok0,
+                                        uint32_t lo, uint32_t khi) {
+  using T = LdsTraits<FMT, D>;
+  const int ld_row = lane / T::CPR;
+  const int ld_pos = lane % T::CPR;
+#pragma unroll
+  for (int i = 0; i < T::NI; ++i) {
+    const int row = i * T::RPI + ld_row;
+    if (T::RPI > 16 && row >= 16) continue;
+    const int pc = ld_pos ^ (row % T::CPR);        // logical chunk at this position
+    const u32x4 raw = *(lds_u32x4*)(vt + i * 1024 + lane * 16);
+    const uint32_t tok = tok0 + row;
+    const bool ok = tok >= lo && tok < khi;
+    lds_u8* const srow = stage + row * T::BRB;
+    const int sx = row % T::BCPR;
+    if constexpr (FMT == kFp8) {
+      u32x4 h0 = fp8x8_to_bf16x8(raw[0], raw[1]);
+      u32x4 h1 = fp8x8_to_bf16x8(raw[2], raw[3]);
+      if (MASK && !ok) h0 = h1 = u32x4{0u, 0u, 0u, 0u};
+      *(lds_u32x4*)(srow + ((2 * pc) ^ sx) * 16) = h0;
+      *(lds_u32x4*)(srow + ((2 * pc + 1) ^ sx) * 16) = h1;
+    } else {
+      // 32 codes = scale groups 2pc (words 0, 1) and 2pc + 1 (words 2, 3)
+      const uint32_t s2 = *(lds_u16*)(vt + T::TILE + row * T::SC_ROW + 2 * pc);
+      const float S0 = ok ? __builtin_amdgcn_cvt_f32_fp8(s2, 0) : 0.0f;
+      const float S1 = ok ? __builtin_amdgcn_cvt_f32_fp8(s2, 1) : 0.0f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        *(lds_u32x4*)(srow + ((4 * pc + w) ^ sx) * 16) = fp4x8_to_bf16x8(raw[w], w < 2 ? S0 : S1);
+    }
+  }
+}
+
+// Single-launch decode: the last piece of row (b, kh) to finish merges the
+// row's np workspace slots into the BF16 output, as the combine pass does
+// (weights l_i e^(m_i - M), 1e-20 guard, fixed slot order). Lane (g, n)
+// serves q head n of the chunk: it weighs slots g, g+4, ..., and sums dims
+// 16 mt + 4 g .. +4 over all slots; the weights pass through `wlds` (16 x
+// kFuseMaxSplits floats of LDS the caller no longer uses).
+template <int D>
+__device__ __forceinline__ void combine_row(const DecodeArgs& a, uint32_t b, uint32_t kh,
+                                            uint32_t np, lds_u8* wlds) {
+  constexpr int MAXP = kFuseMaxSplits;
+  constexpr int MT = D / 16;
+  constexpr int CH = MT < 8 ? MT : 8;       // 16-dim tiles per output chunk
+  constexpr int SB = 2;                     // slots per load batch
+  typedef __attribute__((address_space(3))) float lds_f32;
+  lds_f32* const wl = (lds_f32*)wlds;
+  const int lane = threadIdx.x;
+  const int g = lane >> 4, n = lane & 15;
+  const uint32_t kvh = kh / a.head_chunks, hc = kh % a.head_chunks;
+  const uint32_t head_in_group = hc * 16 + n;
+  const bool head_ok = head_in_group < a.group;
+  const uint32_t qh = kvh * a.group + (head_ok ? head_in_group : 0u);
+  const float* base = a.ws + (uint64_t(b) * a.num_q_heads + qh) * a.num_splits * (D + 2);
+  float mv[MAXP / 4], lv[MAXP / 4];
+#pragma unroll
+  for (int k = 0; k < MAXP / 4; ++k) {
+    const int i = g + 4 * k;
+    f32x2 ml = {-__builtin_inff(), 0.0f};
+    if (head_ok && i < int(np)) ml = *reinterpret_cast<const f32x2*>(base + i * (D + 2) + D);
+    mv[k] = ml[0];
+    lv[k] = ml[1];
+  }
+  float M = -__builtin_inff();
+#pragma unroll
+  for (int k = 0; k < MAXP / 4; ++k)
+    if (lv[k] > 0.0f) M = fmaxf(M, mv[k]);
+  M = max_over_rows(M);
+  float wpart = 0.0f;
+#pragma unroll
+  for (int k = 0; k < MAXP / 4; ++k) {
+    const float w = lv[k] > 0.0f ? lv[k] * __builtin_amdgcn_exp2f((mv[k] - M) * kLog2e) : 0.0f;
+    wl[n * MAXP + g + 4 * k] = w;
+    wpart += w;
+  }
+  const float wsum = sum_over_rows(wpart);
+  const float inv = 1.0f / fmaxf(wsum, 1e-20f);
+  wave_lds_fence();
+  uint16_t* orow = a.out + (uint64_t(b) * a.num_q_heads + qh) * D;
+#pragma unroll
+  for (int c0 = 0; c0 < MT; c0 += CH) {
+    f32x4 o[CH];
+#pragma unroll
+    for (int t = 0; t < CH; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i0 = 0; i0 < int(np); i0 += SB) {
+      f32x4 v[SB][CH];
+#pragma unroll
+      for (int u = 0; u < SB; ++u)
+#pragma unroll
+        for (int t = 0; t < CH; ++t) {
+          v[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+          if (head_ok && i0 + u < int(np))
+            v[u][t] = *reinterpret_cast<const f32x4*>(base + (i0 + u) * (D + 2) +
+                                                      16 * (c0 + t) + 4 * g);
+        }
+#pragma unroll
+      for (int u = 0; u < SB; ++u) {
+        const float w = i0 + u < int(np) ? wl[n * MAXP + i0 + u] : 0.0f;
+#pragma unroll
+        for (int t = 0; t < CH; ++t) o[t] += w * v[u][t];
+      }
+    }
+    if (head_ok) {
+#pragma unroll
+      for (int t = 0; t < CH; ++t)
+        *reinterpret_cast<u32x2*>(orow + 16 * (c0 + t) + 4 * g) =
+            u32x2{pack_bf16x2(o[t][0] * inv, o[t][1] * inv), pack_bf16x2(o[t][2] * inv, o[t][3] * inv)};
+    }
+  }
+  wave_lds_fence();
+}
+
 // One row piece: tiles [tau0, tau1) of row (b, kh), partial state to `slot`.
 template <int FMT, int D>
 __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D>& sh, uint32_t b,
                                           uint32_t kh, uint32_t tau0, uint32_t tau1,
-                                          uint32_t slot, bool last, uint32_t L) {
+                                          uint32_t slot, bool last, uint32_t L, uint32_t npieces) {
   using T = LdsTraits<FMT, D>;
   constexpr int NBUF = T::NBUF;
   if (slot >= a.num_splits) return;      // only if a sequence outgrows its block table
@@ -387,16 +516,23 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D>
           mx = fmaxf(mx, sv[j]);
         }
         mx = max_over_rows(mx);
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-        // the accumulator is rescaled only when some head's running max moved
-        const bool rescale = __builtin_amdgcn_ballot_w64(m_new != m_run) != 0;
-        m_run = m_new;
+        // The reference m_run follows the running max lazily: it moves only
+        // when some head's max exceeds it by more than kLazyMax (log2 units),
+        // and only then is the accumulator rescaled. The weights stay below
+        // 2^kLazyMax; (m, l, o) is exact for any reference, so only the
+        // amount of rescaling work changes.
+        const bool rescale = __builtin_amdgcn_ballot_w64(mx > m_run + kLazyMax) != 0;
+        float alpha = 1.0f;
+        if (rescale) {
+          const float m_new = fmaxf(m_run, mx);
+          alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+          m_run = m_new;
+        }
         uint32_t pbits[4];
         float psum = 0.0f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const float p = __builtin_amdgcn_exp2f(sv[j] - m_new);
+          const float p = __builtin_amdgcn_exp2f(sv[j] - m_run);
           pbits[j] = f32_to_bf16_bits(p);
           psum += __uint_as_float(pbits[j] << 16);
         }
@@ -424,35 +560,13 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D>
           }
         } else {
           vsrc = stage3;
-#pragma unroll
-          for (int i = 0; i < T::NI; ++i) {
-            const int row = i * T::RPI + ld_row;
-            if (T::RPI > 16 && row >= 16) continue;
-            const int pc = ld_pos ^ (row % T::CPR);        // logical chunk at this position
-            const u32x4 raw = *(lds_u32x4*)(vt + i * 1024 + lane * 16);
-            const uint32_t tok = tok0 + row;
-            const bool ok = tok >= lo && tok < khi;
-            lds_u8* const srow = stage3 + row * T::BRB;
-            const int sx = row % T::BCPR;
-            if constexpr (FMT == kFp8) {
-              u32x4 h0 = fp8x8_to_bf16x8(raw[0], raw[1]);
-              u32x4 h1 = fp8x8_to_bf16x8(raw[2], raw[3]);
-              if (!ok) h0 = h1 = u32x4{0u, 0u, 0u, 0u};
-              *(lds_u32x4*)(srow + ((2 * pc) ^ sx) * 16) = h0;
-              *(lds_u32x4*)(srow + ((2 * pc + 1) ^ sx) * 16) = h1;
-            } else {
-              // 32 codes = scale groups 2pc (words 0, 1) and 2pc + 1 (words 2, 3)
-              const uint32_t s2 = *(lds_u16*)(vt + T::TILE + row * T::SC_ROW + 2 * pc);
-              const float S0 = __builtin_amdgcn_cvt_f32_fp8(s2, 0);
-              const float S1 = __builtin_amdgcn_cvt_f32_fp8(s2, 1);
-#pragma unroll
-              for (int w = 0; w < 4; ++w) {
-                u32x4 h = fp4x8_to_bf16x8(raw[w], w < 2 ? S0 : S1);
-                if (!ok) h = u32x4{0u, 0u, 0u, 0u};
-                *(lds_u32x4*)(srow + ((4 * pc + w) ^ sx) * 16) = h;
-              }
-            }
-          }
+          // FP8 codes of masked tokens may be anything (NaN included), so
+          // partial tiles select zeros; E2M1 codes are always finite, so a
+          // masked NVFP4 row just takes a zero scale
+          if (FMT == kFp8 && (tok0 < lo || tok0 + 16 > khi))
+            stage_v<FMT, D, true>(vt, stage3, lane, tok0, lo, khi);
+          else
+            stage_v<FMT, D, false>(vt, stage3, lane, tok0, lo, khi);
           wave_lds_fence();
           __builtin_amdgcn_sched_barrier(0);
           issue(s, 1, t + NBUF);                   // the raw V tile is consumed
@@ -503,6 +617,19 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D>
   }
 
   const float l_tot = sum_over_rows(l_run);
+  if (a.out && npieces == 1) {
+    // the whole row in one piece: the normalized output goes straight to BF16
+    if (head_ok) {
+      const float inv = a.out_scale / l_tot;
+      uint16_t* orow = a.out + (uint64_t(b) * a.num_q_heads + qh) * D;
+#pragma unroll
+      for (int mt = 0; mt < D / 16; ++mt)
+        *reinterpret_cast<u32x2*>(orow + 16 * mt + 4 * g) =
+            u32x2{pack_bf16x2(acc[mt][0] * inv, acc[mt][1] * inv),
+                  pack_bf16x2(acc[mt][2] * inv, acc[mt][3] * inv)};
+    }
+    return;
+  }
   if (head_ok) {
     float* wrow = wbase + uint64_t(slot) * (D + 2);
     const float inv = a.out_scale / l_tot;
@@ -519,12 +646,41 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D>
     }
     // the row ends in this piece: an end marker (l = -1) in the next slot
     // tells the combine to ignore that slot and all later ones
-    if (last && g == 0 && slot + 1 < a.num_splits) {
+    if (!a.out && last && g == 0 && slot + 1 < a.num_splits) {
       float* e = wbase + uint64_t(slot + 1) * (D + 2);
       e[D] = -__builtin_inff();
       e[D + 1] = -1.0f;
     }
   }
+  if (a.out) {
+    // single-launch decode: publish the partial, count it in; the row's last
+    // piece to arrive merges all of them and clears the counter for the next
+    // call (release before the count, acquire after it, at device scope)
+    const uint32_t R = a.num_kv_heads * a.head_chunks;
+    uint32_t* const cnt = a.counters + uint64_t(b) * R + kh;
+    __threadfence();
+    uint32_t old = 0;
+    if (lane == 0) old = atomicAdd(cnt, 1u);
+    old = __shfl(old, 0, 64);
+    if (old + 1 == npieces) {
+      __threadfence();
+      combine_row<D>(a, b, kh, min(npieces, a.num_splits), ring3);
+      if (lane == 0) atomicExch(cnt, 0u);
+    }
+  }
+}
+
+// Zeros for the q heads of row (b, kh) of a sequence without keys.
+template <int D>
+__device__ __forceinline__ void zero_row(const DecodeArgs& a, uint32_t b, uint32_t kh) {
+  const int lane = threadIdx.x;
+  const int g = lane >> 4, n = lane & 15;
+  const uint32_t kvh = kh / a.head_chunks, hc = kh % a.head_chunks;
+  const uint32_t head_in_group = hc * 16 + n;
+  if (head_in_group >= a.group) return;
+  uint16_t* orow = a.out + (uint64_t(b) * a.num_q_heads + kvh * a.group + head_in_group) * D;
+#pragma unroll
+  for (int mt = 0; mt < D / 16; ++mt) *reinterpret_cast<u32x2*>(orow + 16 * mt + 4 * g) = u32x2{0u, 0u};
 }
 
 template <int FMT, int D>
@@ -536,10 +692,18 @@ __global__ __launch_bounds__(64) void splitk_stream(DecodeArgs a) {
     const int32_t Ls = a.seq_lens[b];
     const uint32_t L = Ls > 0 ? uint32_t(Ls) : 0u;
     const uint32_t n = row_tiles(L, a.window);
-    if (n) run_piece<FMT, D>(a, sh, b, kh, 0, n, 0, true, L);
+    if (n) run_piece<FMT, D>(a, sh, b, kh, 0, n, 0, true, L, 1);
+    else if (a.out) zero_row<D>(a, b, kh);
     return;
   }
   const uint32_t P = gridDim.x;
+  if (a.out) {
+    // single-launch decode: sequences without keys get zeros here, as no
+    // piece covers them
+    for (uint32_t b = blockIdx.x; b < a.num_seqs; b += P)
+      if (a.seq_lens[b] <= 0)
+        for (uint32_t kh = 0; kh < R; ++kh) zero_row<D>(a, b, kh);
+  }
   if (a.num_seqs <= 64) {
     // one length per lane, loaded once: the tile counts, their prefix sums and
     // every row lookup come from these registers
@@ -562,7 +726,7 @@ __global__ __launch_bounds__(64) void splitk_stream(DecodeArgs a) {
       const uint32_t start = excl + kh * n;
       const uint32_t tau1 = min(n, end - start);
       run_piece<FMT, D>(a, sh, uint32_t(l), kh, pos - start, tau1, pos / c - start / c,
-                        start + n <= end, L);
+                        start + n <= end, L, (start + n - 1) / c - start / c + 1);
       pos = start + tau1;
     }
     return;
@@ -578,7 +742,7 @@ __global__ __launch_bounds__(64) void splitk_stream(DecodeArgs a) {
     const uint32_t slot = pos / c - r.start / c;
     const int32_t Ls = a.seq_lens[r.b];
     run_piece<FMT, D>(a, sh, r.b, r.kh, tau0, tau1, slot, r.start + r.n <= end,
-                      Ls > 0 ? uint32_t(Ls) : 0u);
+                      Ls > 0 ? uint32_t(Ls) : 0u, (r.start + r.n - 1) / c - r.start / c + 1);
     pos = r.start + tau1;
   }
 }
@@ -721,9 +885,15 @@ static uint64_t stream_capacity(uint32_t head_dim) {
 #ifndef PKD_STREAM_WAVES_PER_CU
 #define PKD_STREAM_WAVES_PER_CU 4
 #endif
-  // four long waves per CU stream better than more, shorter ones; the count is
-  // a multiple of the CU count so that every CU gets the same work
-  if (per_cu > PKD_STREAM_WAVES_PER_CU) per_cu = PKD_STREAM_WAVES_PER_CU;
+#ifndef PKD_STREAM_WAVES_PER_CU_Q
+#define PKD_STREAM_WAVES_PER_CU_Q 8
+#endif
+  // BF16: four long waves per CU stream better than more, shorter ones;
+  // quantized tiles carry more ALU work per byte and gain from a second wave
+  // per SIMD where the registers allow it. The count is a multiple of the CU
+  // count so that every CU gets the same work.
+  const int cap = FMT == kBf16 ? PKD_STREAM_WAVES_PER_CU : PKD_STREAM_WAVES_PER_CU_Q;
+  if (per_cu > cap) per_cu = cap;
   cache[dev][di] = uint64_t(per_cu) * uint64_t(cus);
   return cache[dev][di];
 }
@@ -783,7 +953,48 @@ static DecodeArgs make_args(const uint16_t* q, const void* kc, const void* vc, f
   a.window = window;
   a.num_seqs = 0;
   a.chunk_min = 1;
+  a.out = nullptr;
+  a.counters = nullptr;
   return a;
+}
+
+static int launch_reduce(const float* workspace, uint16_t* output, const int32_t* seq_lens,
+                         uint32_t num_q_heads, uint32_t head_dim, uint32_t num_splits,
+                         uint32_t num_seqs, hipStream_t stream) {
+  const uint64_t grid = uint64_t(num_seqs) * num_q_heads;
+  if (grid > 0x7FFFFFFFull) return kUnsupported;
+  const size_t lds = 2 * size_t(num_splits) * sizeof(float);
+  const bool wide = num_splits >= 64;          // many slots: more lanes per (b, h)
+  const dim3 gd = dim3(uint32_t(grid)), bd = dim3(wide ? 1024 : 256);
+#define PKD_REDUCE(DD) \
+  if (wide) hipLaunchKernelGGL((reduce_kernel<DD, 1024>), gd, bd, lds, stream, workspace, output, seq_lens, num_q_heads, num_splits); \
+  else hipLaunchKernelGGL((reduce_kernel<DD, 256>), gd, bd, lds, stream, workspace, output, seq_lens, num_q_heads, num_splits);
+  switch (head_dim) {
+    case 64: PKD_REDUCE(64) break;
+    case 128: PKD_REDUCE(128) break;
+    case 256: PKD_REDUCE(256) break;
+    case 512: PKD_REDUCE(512) break;
+    default: return kUnsupported;
+  }
+#undef PKD_REDUCE
+  return launch_status();
+}
+
+// Single-launch decode: one wave per row (S = 1), the split pass with the
+// combine merged in (S <= kFuseMaxSplits), or the split pass and the combine
+// as two launches (more splits).
+template <int FMT>
+static int launch_decode(DecodeArgs a, uint16_t* output, uint32_t* counters, uint32_t num_seqs,
+                         uint32_t head_dim, hipStream_t stream) {
+  if (a.num_splits > uint32_t(kFuseMaxSplits)) {
+    const int st = launch_splitk<FMT>(a, num_seqs, head_dim, stream);
+    if (st) return st;
+    return launch_reduce(a.ws, output, a.seq_lens, a.num_q_heads, head_dim, a.num_splits,
+                         num_seqs, stream);
+  }
+  a.out = output;
+  a.counters = counters;
+  return launch_splitk<FMT>(a, num_seqs, head_dim, stream);
 }
 
 }  // namespace pkd
@@ -851,6 +1062,68 @@ extern "C" PKD_API int paged_decode_attn_splitk_nvfp4(
   return launch_splitk<kNvfp4>(a, num_seqs, head_dim, stream);
 }
 
+extern "C" PKD_API int paged_decode_attn_bf16(
+    const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, uint16_t* output,
+    const int32_t* block_tables, const int32_t* seq_lens, uint32_t max_blocks_per_seq,
+    uint32_t num_seqs, uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
+    uint32_t block_size, float scale, uint32_t q_stride, uint32_t sliding_window,
+    float* workspace, uint32_t* counters, uint32_t num_splits, hipStream_t stream) {
+  if (num_seqs == 0) return kOk;
+  int st = check_single(q, k_cache, v_cache, output, workspace, counters, block_tables, seq_lens,
+                        max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, block_size,
+                        num_splits, q_stride, kFuseMaxSplits);
+  if (st) return st;
+  const uint64_t page_bytes = uint64_t(block_size) * num_kv_heads * head_dim * 2;
+  DecodeArgs a = make_args(q, k_cache, v_cache, workspace, block_tables, seq_lens,
+                           max_blocks_per_seq, num_q_heads, num_kv_heads, block_size,
+                           scale * kLog2e, 1.0f, num_splits, q_stride, page_bytes, 0,
+                           sliding_window);
+  return launch_decode<kBf16>(a, output, counters, num_seqs, head_dim, stream);
+}
+
+extern "C" PKD_API int paged_decode_attn_fp8(
+    const uint16_t* q, const uint8_t* k_cache, const uint8_t* v_cache, uint16_t* output,
+    const int32_t* block_tables, const int32_t* seq_lens, uint32_t max_blocks_per_seq,
+    uint32_t num_seqs, uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
+    uint32_t block_size, float scale, float k_scale, float v_scale, uint32_t q_stride,
+    uint64_t cache_stride, uint32_t sliding_window, float* workspace, uint32_t* counters,
+    uint32_t num_splits, hipStream_t stream) {
+  if (num_seqs == 0) return kOk;
+  int st = check_single(q, k_cache, v_cache, output, workspace, counters, block_tables, seq_lens,
+                        max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, block_size,
+                        num_splits, q_stride, kFuseMaxSplits);
+  if (st) return st;
+  st = check_fp8_stride(num_kv_heads, head_dim, block_size, cache_stride);
+  if (st) return st;
+  DecodeArgs a = make_args(q, k_cache, v_cache, workspace, block_tables, seq_lens,
+                           max_blocks_per_seq, num_q_heads, num_kv_heads, block_size,
+                           scale * k_scale * kLog2e, v_scale, num_splits, q_stride, cache_stride,
+                           0, sliding_window);
+  return launch_decode<kFp8>(a, output, counters, num_seqs, head_dim, stream);
+}
+
+extern "C" PKD_API int paged_decode_attn_nvfp4(
+    const uint16_t* q, const uint8_t* k_cache, const uint8_t* v_cache, uint16_t* output,
+    const int32_t* block_tables, const int32_t* seq_lens, uint32_t max_blocks_per_seq,
+    uint32_t num_seqs, uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
+    uint32_t block_size, float scale, uint32_t q_stride, uint64_t block_stride_bytes,
+    uint64_t data_section_bytes, uint32_t sliding_window, float* workspace, uint32_t* counters,
+    uint32_t num_splits, hipStream_t stream) {
+  if (num_seqs == 0) return kOk;
+  int st = check_single(q, k_cache, v_cache, output, workspace, counters, block_tables, seq_lens,
+                        max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, block_size,
+                        num_splits, q_stride, kFuseMaxSplits);
+  if (st) return st;
+  st = check_nvfp4_sections(num_kv_heads, head_dim, block_size, block_stride_bytes,
+                            data_section_bytes);
+  if (st) return st;
+  DecodeArgs a = make_args(q, k_cache, v_cache, workspace, block_tables, seq_lens,
+                           max_blocks_per_seq, num_q_heads, num_kv_heads, block_size,
+                           scale * kLog2e, 1.0f, num_splits, q_stride, block_stride_bytes,
+                           data_section_bytes, sliding_window);
+  return launch_decode<kNvfp4>(a, output, counters, num_seqs, head_dim, stream);
+}
+
 extern "C" PKD_API int paged_decode_attn_reduce(const float* workspace, uint16_t* output,
                                                 const int32_t* seq_lens, uint32_t num_q_heads,
                                                 uint32_t head_dim, uint32_t num_splits,
@@ -858,23 +1131,8 @@ extern "C" PKD_API int paged_decode_attn_reduce(const float* workspace, uint16_t
   if (num_seqs == 0) return kOk;
   int st = check_reduce(workspace, output, seq_lens, num_q_heads, head_dim, num_splits);
   if (st) return st;
-  const uint64_t grid = uint64_t(num_seqs) * num_q_heads;
-  if (grid > 0x7FFFFFFFull) return kUnsupported;
-  const size_t lds = 2 * size_t(num_splits) * sizeof(float);
-  const bool wide = num_splits >= 64;          // many slots: more lanes per (b, h)
-  const dim3 gd = dim3(uint32_t(grid)), bd = dim3(wide ? 1024 : 256);
-#define PKD_REDUCE(DD) \
-  if (wide) hipLaunchKernelGGL((reduce_kernel<DD, 1024>), gd, bd, lds, stream, workspace, output, seq_lens, num_q_heads, num_splits); \
-  else hipLaunchKernelGGL((reduce_kernel<DD, 256>), gd, bd, lds, stream, workspace, output, seq_lens, num_q_heads, num_splits);
-  switch (head_dim) {
-    case 64: PKD_REDUCE(64) break;
-    case 128: PKD_REDUCE(128) break;
-    case 256: PKD_REDUCE(256) break;
-    case 512: PKD_REDUCE(512) break;
-    default: return kUnsupported;
-  }
-#undef PKD_REDUCE
-  return launch_status();
+  return launch_reduce(workspace, output, seq_lens, num_q_heads, head_dim, num_splits, num_seqs,
+                       stream);
 }
 
 extern "C" PKD_API size_t paged_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads,

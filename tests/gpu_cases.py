@@ -113,6 +113,38 @@ class DeviceKV:
         return res
 
 
+    def decode_single(self, num_splits, q_bits=None, counters=None, out=None):
+        """The single-launch decode call; returns (output, counters)."""
+        w, g = self.w, self.geom
+        B, Hq, Hkv, D, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+        q_bits = w.q_bits if q_bits is None else q_bits
+        q = u16_to_dev(q_bits.reshape(-1))
+        bt = i32_to_dev(w.block_tables)
+        lens = i32_to_dev(w.seq_lens)
+        ws = None
+        if num_splits > 1:
+            ws = torch.full((pkd.paged_decode_workspace_bytes(B, Hq, D, num_splits) // 4,),
+                            float("nan"), dtype=torch.float32, device=dev())
+        if counters is None:
+            counters = torch.zeros(B * Hq, dtype=torch.int32, device=dev())
+        if out is None:
+            out = torch.full((B, Hq, D), float("nan"), dtype=torch.bfloat16, device=dev())
+        common = (q, self.k, self.v, out, bt, lens, w.max_blocks_per_seq, B, Hq, Hkv, D, bs,
+                  float(w.scale))
+        tail = dict(sliding_window=w.sliding_window, workspace=ws, counters=counters,
+                    num_splits=num_splits)
+        if g.fmt == "bf16":
+            pkd.paged_decode_attn_bf16(*common, Hq * D, **tail)
+        elif g.fmt == "fp8":
+            pkd.paged_decode_attn_fp8(*common, self.k_scale, self.v_scale, Hq * D,
+                                      g.fp8_stride(), **tail)
+        else:
+            stride, data = g.nvfp4_sections()
+            pkd.paged_decode_attn_nvfp4(*common, Hq * D, stride, data, **tail)
+        torch.cuda.synchronize()
+        return out.float().cpu().numpy().astype(np.float64), counters
+
+
 def oracle_pools(w, geom, k_scale=1.0, v_scale=1.0, seqs=None, fill=None):
     """Oracle pools written by the oracle's cache write (all tokens, or only
     the tokens of the sequences in ``seqs``)."""
