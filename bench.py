@@ -2,18 +2,22 @@
 
 A step is the whole decode path for one attention layer over one batch:
 write the new token's K/V through slot_mapping (reshape_and_cache), run the
-split-KV pass and the combine. Inputs are seeded synthetic tensors already
-resident in HBM. Steps rotate over several layers' KV pools whose total size
-is several times the 256 MB Infinity Cache, so every step reads its KV from
-HBM, as the layers of a model do. The timed loop replays a HIP graph of one
-step per layer.
+split-KV pass, then the combine pass. The same step through the single-launch
+decode call (combine merged into the split pass when the split count is at
+most 32) is timed beside it. Inputs are seeded
+synthetic tensors already resident in HBM. Steps rotate over several layers'
+KV pools whose total size is several times the 256 MB Infinity Cache, so
+every step reads its KV from HBM, as the layers of a model do. The timed loop
+replays a HIP graph of one step per layer.
 
 Prints ONE JSON line: KV-read GB/s and us/step on the Llama-3-8B-shaped batch
-(B=32), the B=1 32K-context figures beside it, the roofline of the split-KV
-kernel (live HIP-event timing), and the float64 CPU oracle timed on the host.
+(B=32), the B=1 32K-context figures beside it, the roofline of the step's
+dominant kernel (back-to-back launches timed with HIP events on their
+stream), and the float64 CPU oracle timed on the host.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--extra NAME ...]
   python bench.py --copy-calibration      # plain copy of known size (for rocprof counters)
+  python bench.py --counter-run --workload NAME   # the split-K call alone (for rocprof counters)
 """
 from __future__ import annotations
 
@@ -137,6 +141,7 @@ class Layers:
         self.ws = torch.empty(pkd.paged_decode_workspace_bytes(B, Hq, D, self.num_splits) // 4,
                               dtype=torch.float32, device=self.dev)
         self.out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=self.dev)
+        self.counters = torch.zeros(B * Hq, dtype=torch.int32, device=self.dev)
         torch.cuda.synchronize()
 
     def _write(self, key, val, kp, vp, slots):
@@ -166,7 +171,26 @@ class Layers:
             pkd.paged_decode_attn_splitk_nvfp4(*common, qs, self.block_stride, self.data_section,
                                                w.num_seqs, w.sliding_window)
 
+    def decode(self, layer):
+        """The single-launch decode call (combine merged in when num_splits <= 32)."""
+        import paged_kv_decode_splitk_amd as pkd
+        w = self.w
+        common = (self.q, self.k[layer], self.v[layer], self.out, self.bt, self.lens,
+                  w.max_blocks_per_seq, w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
+                  w.block_size, float(w.scale))
+        tail = dict(sliding_window=w.sliding_window, workspace=self.ws, counters=self.counters,
+                    num_splits=self.num_splits)
+        qs = w.num_q_heads * w.head_dim
+        if w.kv_dtype == "bf16":
+            pkd.paged_decode_attn_bf16(*common, qs, **tail)
+        elif w.kv_dtype == "fp8":
+            pkd.paged_decode_attn_fp8(*common, self.k_scale, self.v_scale, qs, self.page_units,
+                                      **tail)
+        else:
+            pkd.paged_decode_attn_nvfp4(*common, qs, self.block_stride, self.data_section, **tail)
+
     def step(self, layer):
+        """Write the new token's K/V, the split-K pass, then the combine pass."""
         import paged_kv_decode_splitk_amd as pkd
         w = self.w
         self._write(self.new_key, self.new_val, self.k[layer], self.v[layer], self.new_slots)
@@ -174,73 +198,94 @@ class Layers:
         pkd.paged_decode_attn_reduce(self.ws, self.out, self.lens, w.num_q_heads, w.head_dim,
                                      self.num_splits, w.num_seqs)
 
+    def step_single(self, layer):
+        """Write the new token's K/V, then the single-launch decode call."""
+        self._write(self.new_key, self.new_val, self.k[layer], self.v[layer], self.new_slots)
+        self.decode(layer)
 
-def time_workload(name, steps, warmup, kernel_reps=100):
+
+def _graph_time(fn, calls, reps):
+    """ms per call of `fn(i)` for i in range(calls), captured in one HIP graph
+    and replayed `reps` times between two events on the capturing stream."""
+    import torch
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(calls):
+            fn(i)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(reps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    del g
+    return a.elapsed_time(b) / (reps * calls)
+
+
+def time_workload(name, steps, warmup, kernel_reps=100, single=True):
     import torch
     import workloads
     w = workloads.make_workload(name)
     lay = Layers(w)
     NL = lay.num_layers
-    # warm up eagerly (also loads the code objects), then capture one step per layer
+    # warm up eagerly (also loads the code objects), then graphs of one step per layer
     for i in range(max(1, warmup)):
         lay.step(i % NL)
+        if single:
+            lay.step_single(i % NL)
     torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        for layer in range(NL):
-            lay.step(layer)
     reps = max(1, -(-steps // NL))
     steps_run = reps * NL
-    for _ in range(max(1, warmup // NL)):
-        graph.replay()
-    torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
-    start.record()
-    for _ in range(reps):
-        graph.replay()
-    end.record()
-    torch.cuda.synchronize()
+    ms_step = _graph_time(lay.step, NL, reps)
     wall = time.perf_counter() - t0
-    ms_step = start.elapsed_time(end) / steps_run
-
-    # split-KV kernel alone: a graph of back-to-back launches (rotating layers)
-    # between two HIP events on the stream it runs on
-    kgraph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(kgraph):
-        for i in range(kernel_reps):
-            lay.splitk(i % NL)
-    kgraph.replay()
-    torch.cuda.synchronize()
-    ka, kb = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    ka.record()
-    for _ in range(3):
-        kgraph.replay()
-    kb.record()
-    torch.cuda.synchronize()
-    k_ms = ka.elapsed_time(kb) / (3 * kernel_reps)
-    del kgraph
+    nan = float("nan")
+    ms_single = _graph_time(lay.step_single, NL, reps) if single else nan
+    # the kernels alone: back-to-back launches rotating over the layers
+    single_ms = _graph_time(lambda i: lay.decode(i % NL), kernel_reps, 3) if single else nan
+    k_ms = _graph_time(lambda i: lay.splitk(i % NL), kernel_reps, 3)
 
     kv_bytes = attended_tokens(w) * kv_bytes_per_token(w)
+    gbs = lambda ms: kv_bytes / (ms * 1e-3) / 1e9
     res = dict(
         workload=name, description=DESCRIPTIONS.get(name, name), kv_dtype=w.kv_dtype,
         num_seqs=w.num_seqs, num_splits=lay.num_splits, layers_rotated=NL,
         kv_pool_bytes_per_layer=lay.pool_bytes, attended_tokens=attended_tokens(w),
         kv_bytes_per_step=kv_bytes, steps=steps_run, ms_per_step=ms_step,
-        us_per_step=ms_step * 1e3, kv_gbs=kv_bytes / (ms_step * 1e-3) / 1e9,
-        wall_s=wall, splitk_us=k_ms * 1e3, splitk_gbs=kv_bytes / (k_ms * 1e-3) / 1e9,
+        us_per_step=ms_step * 1e3, kv_gbs=gbs(ms_step), wall_s=wall,
+        single_launch_us_per_step=ms_single * 1e3, single_launch_kv_gbs=gbs(ms_single),
+        decode_us=single_ms * 1e3, decode_gbs=gbs(single_ms),
+        decode_merged=lay.num_splits <= 32,
+        splitk_us=k_ms * 1e3, splitk_gbs=gbs(k_ms),
     )
     res["pct_of_peak"] = 100.0 * res["kv_gbs"] / PEAK_HBM_GBS
-    del lay, graph
+    del lay
     torch.cuda.empty_cache()
     return res, w
 
 
-def traffic_record(name):
-    """HBM bytes per split-K launch from the committed rocprofv3 counter
-    summary (profiles/traffic_splitk_<workload>.txt), used only while the
-    kernel sources still hash to what was profiled."""
-    path = os.path.join(ROOT, "profiles", f"traffic_splitk_{name}.txt")
+def counter_run(name, calls=20):
+    """Only the split-K pass, `calls` times over the layers (for rocprofv3
+    counter passes, which profile every dispatch)."""
+    import torch
+    import workloads
+    w = workloads.make_workload(name)
+    lay = Layers(w)
+    torch.cuda.synchronize()
+    for i in range(calls):
+        lay.splitk(i % lay.num_layers)
+    torch.cuda.synchronize()
+    print(json.dumps({"counter_run": name, "calls": calls, "num_splits": lay.num_splits,
+                      "kv_bytes_per_call": attended_tokens(w) * kv_bytes_per_token(w)}))
+
+
+def traffic_record(name, tag):
+    """HBM bytes per launch of the dominant kernel from the committed
+    rocprofv3 counter summary (profiles/traffic_<tag>_<workload>.txt), used
+    only while the kernel sources still hash to what was profiled."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{tag}_{name}.txt")
     if not os.path.exists(path):
         return None
     rec = {}
@@ -316,6 +361,11 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-single", action="store_true",
+                    help="skip the single-launch decode timings (profiles then see only the "
+                         "split-K kernel)")
+    ap.add_argument("--counter-run", action="store_true",
+                    help="only run the split-K pass of --workload 20 times")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -327,27 +377,35 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.counter_run:
+        counter_run(args.workload)
+        return
     print(f"bench: {args.workload} steps={args.steps} warmup={args.warmup}", file=sys.stderr,
           flush=True)
-    main_res, w = time_workload(args.workload, args.steps, args.warmup)
+    main_res, w = time_workload(args.workload, args.steps, args.warmup, single=not args.no_single)
     print(f"bench: {args.workload} {main_res['us_per_step']:.2f} us/step "
           f"{main_res['kv_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
     extras = {}
     for name in args.extra:
-        r, _ = time_workload(name, args.steps, args.warmup)
-        extras[name] = {k: r[k] for k in ("us_per_step", "kv_gbs", "pct_of_peak", "splitk_us",
-                                          "splitk_gbs", "num_splits", "kv_bytes_per_step",
-                                          "layers_rotated")}
+        r, _ = time_workload(name, args.steps, args.warmup, single=not args.no_single)
+        extras[name] = {k: r[k] for k in ("us_per_step", "kv_gbs", "pct_of_peak",
+                                          "single_launch_us_per_step",
+                                          "single_launch_kv_gbs",
+                                          "decode_us", "decode_gbs", "decode_merged",
+                                          "splitk_us", "splitk_gbs", "num_splits",
+                                          "kv_bytes_per_step", "layers_rotated")}
         print(f"bench: {name} {r['us_per_step']:.2f} us/step {r['kv_gbs']:.0f} GB/s",
               file=sys.stderr, flush=True)
 
-    achieved = main_res["splitk_gbs"]
-    traffic = traffic_record(args.workload)
+    # the step's dominant kernel: the split-K pass
+    fmt = main_res["kv_dtype"]
+    kernel, us, tag = f"paged_decode_attn_splitk_{fmt}", main_res["splitk_us"], "splitk"
+    achieved = main_res["kv_bytes_per_step"] / (us * 1e-6) / 1e9
+    traffic = traffic_record(args.workload, tag)
     roofline = dict(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s",
-                    frac=achieved / PEAK_HBM_GBS, traffic=traffic,
-                    kernel=f"paged_decode_attn_splitk_{main_res['kv_dtype']}",
+                    frac=achieved / PEAK_HBM_GBS, traffic=traffic, kernel=kernel,
                     algorithmic_bytes_per_launch=main_res["kv_bytes_per_step"],
-                    avg_launch_us=main_res["splitk_us"])
+                    avg_launch_us=us)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, budget_s=args.cpu_budget)
@@ -371,9 +429,14 @@ def main():
             "num_splits": main_res["num_splits"],
             "layers_rotated": main_res["layers_rotated"],
             "kv_bytes_per_step": main_res["kv_bytes_per_step"],
-            "step": "reshape_and_cache of the new token + split-KV pass + combine, "
+            "step": "reshape_and_cache of the new token + split-KV pass + combine pass, "
                     "HIP-graph replay",
         },
+        "single_launch_step": {k: main_res[k] for k in ("single_launch_us_per_step",
+                                                         "single_launch_kv_gbs",
+                                                         "decode_merged")},
+        "kernels": {k: main_res[k] for k in ("decode_us", "decode_gbs", "splitk_us",
+                                             "splitk_gbs")},
         "roofline": roofline,
         "cpu_baseline": cpu,
     }

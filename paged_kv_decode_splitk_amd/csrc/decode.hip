@@ -107,6 +107,14 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// Cache policy of the single-launch decode's workspace traffic between
+// waves: sc1, the device-scope policy (the memory model gives relaxed
+// device-scope atomics the same bit). Such stores write through the XCD's L2
+// and such loads do not hit stale L2 lines, so partials move between XCDs
+// without a device-scope fence, which would write back and invalidate the
+// whole L2.
+constexpr int kSc1 = 16;
+
 // ---------------------------------------------------------------------------
 // K and V tiles stream into an LDS ring with direct-to-LDS buffer loads
 // (gfx950 LDS DMA, 16 bytes per lane). Each load instruction moves whole rows
@@ -149,7 +157,7 @@ struct LdsTraits {
   static constexpr int BCPR = D / 8;             // 16-byte chunks of a BF16 row
   static constexpr int STAGE = FMT == kBf16 ? 16 : 16 * BRB;   // BF16 copy of a quantized V tile
   static_assert(WAIT < 64, "vmcnt range");
-  static_assert(NBUF * SLOT >= 16 * kFuseMaxSplits * 4, "the ring also holds the combine weights");
+  static_assert(NBUF * SLOT >= (32 * kFuseMaxSplits + 16) * 4, "the ring also holds the combine weights");
 };
 
 // s_waitcnt that waits for vmcnt <= N only (expcnt / lgkmcnt left at their maximum).
@@ -279,79 +287,106 @@ __device__ __forceinline__ void stage_v(lds_u8* vt, lds_u8* stage, int lane, uin
 
 // Single-launch decode: the last piece of row (b, kh) to finish merges the
 // row's np workspace slots into the BF16 output, as the combine pass does
-// (weights l_i e^(m_i - M), 1e-20 guard, fixed slot order). Lane (g, n)
-// serves q head n of the chunk: it weighs slots g, g+4, ..., and sums dims
-// 16 mt + 4 g .. +4 over all slots; the weights pass through `wlds` (16 x
-// kFuseMaxSplits floats of LDS the caller no longer uses).
+// (weights l_i e^(m_i - M), 1e-20 guard, fixed slot order). The chunk's q
+// heads x dim pairs are spread over all 64 lanes, UC pairs per lane and SB
+// slots per round of loads; the weights pass through `wlds` (LDS the caller
+// no longer uses). Workspace reads carry the device-scope cache policy.
 template <int D>
 __device__ __forceinline__ void combine_row(const DecodeArgs& a, uint32_t b, uint32_t kh,
                                             uint32_t np, lds_u8* wlds) {
   constexpr int MAXP = kFuseMaxSplits;
-  constexpr int MT = D / 16;
-  constexpr int CH = MT < 8 ? MT : 8;       // 16-dim tiles per output chunk
-  constexpr int SB = 2;                     // slots per load batch
+  constexpr int UC = 4;                      // dim pairs per lane per pass
+  constexpr int SB = 4;                      // slots per round of loads
   typedef __attribute__((address_space(3))) float lds_f32;
-  lds_f32* const wl = (lds_f32*)wlds;
+  lds_f32* const wl = (lds_f32*)wlds;        // [16][MAXP]: m, then the weights
+  lds_f32* const ll = wl + 16 * MAXP;        // [16][MAXP]: l
+  lds_f32* const il = ll + 16 * MAXP;        // [16]: 1 / sum of the weights
   const int lane = threadIdx.x;
-  const int g = lane >> 4, n = lane & 15;
   const uint32_t kvh = kh / a.head_chunks, hc = kh % a.head_chunks;
-  const uint32_t head_in_group = hc * 16 + n;
-  const bool head_ok = head_in_group < a.group;
-  const uint32_t qh = kvh * a.group + (head_ok ? head_in_group : 0u);
-  const float* base = a.ws + (uint64_t(b) * a.num_q_heads + qh) * a.num_splits * (D + 2);
-  float mv[MAXP / 4], lv[MAXP / 4];
+  const uint32_t gc = min(16u, a.group - hc * 16);           // q heads of this chunk
+  const uint32_t qh0 = kvh * a.group + hc * 16;
+  const uint32_t hs = a.num_splits * (D + 2);                // floats per q head
+  const float* base = a.ws + (uint64_t(b) * a.num_q_heads + qh0) * hs;
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<float*>(base), 0, int(gc * hs * 4), 0x00020000);
+  {
+    // (m, l) of every (head, slot) pair, all loads in flight at once
+    u32x2 ml[16 * MAXP / 64];
 #pragma unroll
-  for (int k = 0; k < MAXP / 4; ++k) {
-    const int i = g + 4 * k;
-    f32x2 ml = {-__builtin_inff(), 0.0f};
-    if (head_ok && i < int(np)) ml = *reinterpret_cast<const f32x2*>(base + i * (D + 2) + D);
-    mv[k] = ml[0];
-    lv[k] = ml[1];
-  }
-  float M = -__builtin_inff();
+    for (int k = 0; k < 16 * MAXP / 64; ++k) {
+      const uint32_t e = lane + 64 * k, h = e / np, i = e % np;
+      ml[k] = u32x2{0u, 0u};
+      if (e < gc * np)
+        ml[k] = __builtin_bit_cast(
+            u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, int((h * hs + i * (D + 2) + D) * 4),
+                                                        0, kSc1));
+    }
 #pragma unroll
-  for (int k = 0; k < MAXP / 4; ++k)
-    if (lv[k] > 0.0f) M = fmaxf(M, mv[k]);
-  M = max_over_rows(M);
-  float wpart = 0.0f;
-#pragma unroll
-  for (int k = 0; k < MAXP / 4; ++k) {
-    const float w = lv[k] > 0.0f ? lv[k] * __builtin_amdgcn_exp2f((mv[k] - M) * kLog2e) : 0.0f;
-    wl[n * MAXP + g + 4 * k] = w;
-    wpart += w;
-  }
-  const float wsum = sum_over_rows(wpart);
-  const float inv = 1.0f / fmaxf(wsum, 1e-20f);
-  wave_lds_fence();
-  uint16_t* orow = a.out + (uint64_t(b) * a.num_q_heads + qh) * D;
-#pragma unroll
-  for (int c0 = 0; c0 < MT; c0 += CH) {
-    f32x4 o[CH];
-#pragma unroll
-    for (int t = 0; t < CH; ++t) o[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int i0 = 0; i0 < int(np); i0 += SB) {
-      f32x4 v[SB][CH];
-#pragma unroll
-      for (int u = 0; u < SB; ++u)
-#pragma unroll
-        for (int t = 0; t < CH; ++t) {
-          v[u][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-          if (head_ok && i0 + u < int(np))
-            v[u][t] = *reinterpret_cast<const f32x4*>(base + (i0 + u) * (D + 2) +
-                                                      16 * (c0 + t) + 4 * g);
-        }
-#pragma unroll
-      for (int u = 0; u < SB; ++u) {
-        const float w = i0 + u < int(np) ? wl[n * MAXP + i0 + u] : 0.0f;
-#pragma unroll
-        for (int t = 0; t < CH; ++t) o[t] += w * v[u][t];
+    for (int k = 0; k < 16 * MAXP / 64; ++k) {
+      const uint32_t e = lane + 64 * k, h = e / np, i = e % np;
+      if (e < gc * np) {
+        wl[h * MAXP + i] = __uint_as_float(ml[k][0]);
+        ll[h * MAXP + i] = __uint_as_float(ml[k][1]);
       }
     }
-    if (head_ok) {
+  }
+  wave_lds_fence();
+  if (uint32_t(lane) < gc) {
+    float M = -__builtin_inff();
+    for (uint32_t i = 0; i < np; ++i)
+      if (ll[lane * MAXP + i] > 0.0f) M = fmaxf(M, wl[lane * MAXP + i]);
+    float wsum = 0.0f;
+    for (uint32_t i = 0; i < np; ++i) {
+      const float l = ll[lane * MAXP + i];
+      const float w = l > 0.0f ? l * __builtin_amdgcn_exp2f((wl[lane * MAXP + i] - M) * kLog2e)
+                               : 0.0f;
+      wl[lane * MAXP + i] = w;
+      wsum += w;
+    }
+    il[lane] = 1.0f / fmaxf(wsum, 1e-20f);
+  }
+  wave_lds_fence();
+  const uint32_t units = gc * (D / 2);                        // (head, dim pair) units
+  for (uint32_t u0 = 0; u0 < units; u0 += 64 * UC) {
+    f32x2 acc[UC];
 #pragma unroll
-      for (int t = 0; t < CH; ++t)
-        *reinterpret_cast<u32x2*>(orow + 16 * (c0 + t) + 4 * g) =
-            u32x2{pack_bf16x2(o[t][0] * inv, o[t][1] * inv), pack_bf16x2(o[t][2] * inv, o[t][3] * inv)};
+    for (int t = 0; t < UC; ++t) acc[t] = f32x2{0.f, 0.f};
+    for (uint32_t i0 = 0; i0 < np; i0 += SB) {
+      u32x2 v[UC][SB];
+#pragma unroll
+      for (int t = 0; t < UC; ++t) {
+        const uint32_t q = u0 + 64 * t + lane;
+        const uint32_t h = q / (D / 2), d2 = q % (D / 2);
+#pragma unroll
+        for (int k = 0; k < SB; ++k) {
+          v[t][k] = u32x2{0u, 0u};
+          if (q < units && i0 + k < np)
+            v[t][k] = __builtin_bit_cast(
+                u32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                           rs, int((h * hs + (i0 + k) * (D + 2) + 2 * d2) * 4), 0, kSc1));
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < UC; ++t) {
+        const uint32_t q = u0 + 64 * t + lane;
+        const uint32_t h = min(q / (D / 2), 15u);
+#pragma unroll
+        for (int k = 0; k < SB; ++k) {
+          const float w = i0 + k < np ? wl[h * MAXP + i0 + k] : 0.0f;
+          acc[t][0] = fmaf(w, __uint_as_float(v[t][k][0]), acc[t][0]);
+          acc[t][1] = fmaf(w, __uint_as_float(v[t][k][1]), acc[t][1]);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < UC; ++t) {
+      const uint32_t q = u0 + 64 * t + lane;
+      if (q < units) {
+        const uint32_t h = q / (D / 2), d2 = q % (D / 2);
+        const float inv = il[h];
+        *reinterpret_cast<uint32_t*>(a.out + (uint64_t(b) * a.num_q_heads + qh0 + h) * D + 2 * d2) =
+            pack_bf16x2(acc[t][0] * inv, acc[t][1] * inv);
+      }
     }
   }
   wave_lds_fence();
@@ -630,7 +665,24 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D>
     }
     return;
   }
-  if (head_ok) {
+  if (head_ok && a.out) {
+    // single-launch decode: the partial goes out with the device-scope cache
+    // policy, so that the merging wave reads it from any XCD
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        wbase + uint64_t(slot) * (D + 2), 0, (D + 2) * 4, 0x00020000);
+    const float inv = a.out_scale / l_tot;
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) {
+      const u32x2 lo2 = {__float_as_uint(acc[mt][0] * inv), __float_as_uint(acc[mt][1] * inv)};
+      const u32x2 hi2 = {__float_as_uint(acc[mt][2] * inv), __float_as_uint(acc[mt][3] * inv)};
+      __builtin_amdgcn_raw_buffer_store_b64(lo2, rs, (mt * 16 + 4 * g) * 4, 0, kSc1);
+      __builtin_amdgcn_raw_buffer_store_b64(hi2, rs, (mt * 16 + 4 * g + 2) * 4, 0, kSc1);
+    }
+    if (g == 0) {
+      const u32x2 ml = {__float_as_uint(m_run * kLn2), __float_as_uint(l_tot)};
+      __builtin_amdgcn_raw_buffer_store_b64(ml, rs, D * 4, 0, kSc1);
+    }
+  } else if (head_ok) {
     float* wrow = wbase + uint64_t(slot) * (D + 2);
     const float inv = a.out_scale / l_tot;
 #pragma unroll
@@ -653,19 +705,21 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D>
     }
   }
   if (a.out) {
-    // single-launch decode: publish the partial, count it in; the row's last
-    // piece to arrive merges all of them and clears the counter for the next
-    // call (release before the count, acquire after it, at device scope)
+    // single-launch decode: once the partial's stores have completed, count
+    // it in (device scope); the row's last piece to arrive merges all of them
+    // and clears the counter for the next call
     const uint32_t R = a.num_kv_heads * a.head_chunks;
     uint32_t* const cnt = a.counters + uint64_t(b) * R + kh;
-    __threadfence();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    wait_vmcnt<0>();
     uint32_t old = 0;
-    if (lane == 0) old = atomicAdd(cnt, 1u);
+    if (lane == 0)
+      old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     old = __shfl(old, 0, 64);
     if (old + 1 == npieces) {
-      __threadfence();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
       combine_row<D>(a, b, kh, min(npieces, a.num_splits), ring3);
-      if (lane == 0) atomicExch(cnt, 0u);
+      if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -683,67 +737,79 @@ __device__ __forceinline__ void zero_row(const DecodeArgs& a, uint32_t b, uint32
   for (int mt = 0; mt < D / 16; ++mt) *reinterpret_cast<u32x2*>(orow + 16 * mt + 4 * g) = u32x2{0u, 0u};
 }
 
+// Waves per SIMD the register budget is held to: quantized tiles up to
+// head_dim 256 run two (their ALU work hides behind the other wave's loads).
 template <int FMT, int D>
-__global__ __launch_bounds__(64) void splitk_stream(DecodeArgs a) {
+constexpr int kWavesPerSimd = (FMT != kBf16 && D <= 256) ? 2 : 1;
+
+template <int FMT, int D>
+__global__ __launch_bounds__(64, (kWavesPerSimd<FMT, D>)) void splitk_stream(DecodeArgs a) {
   __shared__ StreamLds<FMT, D> sh;
   const uint32_t R = a.num_kv_heads * a.head_chunks;          // rows per sequence
-  if (a.num_splits == 1) {                                    // one wave per row
-    const uint32_t b = blockIdx.x / R, kh = blockIdx.x % R;
-    const int32_t Ls = a.seq_lens[b];
-    const uint32_t L = Ls > 0 ? uint32_t(Ls) : 0u;
-    const uint32_t n = row_tiles(L, a.window);
-    if (n) run_piece<FMT, D>(a, sh, b, kh, 0, n, 0, true, L, 1);
-    else if (a.out) zero_row<D>(a, b, kh);
-    return;
-  }
   const uint32_t P = gridDim.x;
-  if (a.out) {
+  const bool whole = a.num_splits == 1;                       // one wave per row
+  if (!whole && a.out) {
     // single-launch decode: sequences without keys get zeros here, as no
     // piece covers them
     for (uint32_t b = blockIdx.x; b < a.num_seqs; b += P)
       if (a.seq_lens[b] <= 0)
         for (uint32_t kh = 0; kh < R; ++kh) zero_row<D>(a, b, kh);
   }
-  if (a.num_seqs <= 64) {
-    // one length per lane, loaded once: the tile counts, their prefix sums and
-    // every row lookup come from these registers
-    const uint32_t lane = threadIdx.x;
-    const int32_t Ls = lane < a.num_seqs ? a.seq_lens[lane] : 0;
-    const uint32_t L_l = Ls > 0 ? uint32_t(Ls) : 0u;
-    const uint32_t n_l = row_tiles(L_l, a.window);
-    const uint32_t incl = wave_scan(n_l * R);
-    const uint32_t T = __shfl(incl, 63, 64);
-    const uint32_t c = max((T + P - 1) / P, a.chunk_min);
-    uint32_t pos = blockIdx.x * c;
-    const uint32_t end = min(pos + c, T);
-    while (pos < end) {
-      const uint64_t hit = __builtin_amdgcn_ballot_w64(incl > pos);
-      const int l = __builtin_ctzll(hit);
-      const uint32_t n = __shfl(n_l, l, 64);
-      const uint32_t excl = __shfl(incl, l, 64) - n * R;
-      const uint32_t L = __shfl(L_l, l, 64);
-      const uint32_t kh = (pos - excl) / n;
-      const uint32_t start = excl + kh * n;
-      const uint32_t tau1 = min(n, end - start);
-      run_piece<FMT, D>(a, sh, uint32_t(l), kh, pos - start, tau1, pos / c - start / c,
-                        start + n <= end, L, (start + n - 1) / c - start / c + 1);
-      pos = start + tau1;
-    }
-    return;
+  // With at most 64 sequences, one length per lane, loaded once: the tile
+  // counts, their prefix sums and every row lookup come from these registers.
+  const bool cached = a.num_seqs <= 64;
+  uint32_t L_l = 0, n_l = 0, incl = 0;
+  if (cached && !whole) {
+    const int32_t Ls = threadIdx.x < a.num_seqs ? a.seq_lens[threadIdx.x] : 0;
+    L_l = Ls > 0 ? uint32_t(Ls) : 0u;
+    n_l = row_tiles(L_l, a.window);
+    incl = wave_scan(n_l * R);
   }
-  const uint32_t T = total_tiles(a, R);
-  const uint32_t c = max((T + P - 1) / P, a.chunk_min);
-  uint32_t pos = blockIdx.x * c;
-  const uint32_t end = min(pos + c, T);
+  uint32_t c = 1, pos = blockIdx.x, end = blockIdx.x + 1;
+  if (!whole) {
+    const uint32_t T = cached ? __shfl(incl, 63, 64) : total_tiles(a, R);
+    c = max((T + P - 1) / P, a.chunk_min);
+    pos = blockIdx.x * c;
+    end = min(pos + c, T);
+  }
   while (pos < end) {
-    const RowLoc r = find_row(a, pos, R);
-    const uint32_t tau0 = pos - r.start;
-    const uint32_t tau1 = min(r.n, end - r.start);
-    const uint32_t slot = pos / c - r.start / c;
-    const int32_t Ls = a.seq_lens[r.b];
-    run_piece<FMT, D>(a, sh, r.b, r.kh, tau0, tau1, slot, r.start + r.n <= end,
-                      Ls > 0 ? uint32_t(Ls) : 0u, (r.start + r.n - 1) / c - r.start / c + 1);
-    pos = r.start + tau1;
+    // the row holding flat tile pos: sequence b, row kh, n tiles from `start`
+    uint32_t b, kh, n, start, L;
+    if (whole) {
+      b = blockIdx.x / R;
+      kh = blockIdx.x % R;
+      const int32_t Ls = a.seq_lens[b];
+      L = Ls > 0 ? uint32_t(Ls) : 0u;
+      n = row_tiles(L, a.window);
+      start = pos;
+      if (n == 0) {
+        if (a.out) zero_row<D>(a, b, kh);
+        break;
+      }
+    } else if (cached) {
+      const int l = __builtin_ctzll(__builtin_amdgcn_ballot_w64(incl > pos));
+      n = __shfl(n_l, l, 64);
+      const uint32_t excl = __shfl(incl, l, 64) - n * R;
+      L = __shfl(L_l, l, 64);
+      b = uint32_t(l);
+      kh = (pos - excl) / n;
+      start = excl + kh * n;
+    } else {
+      const RowLoc r = find_row(a, pos, R);
+      b = r.b;
+      kh = r.kh;
+      n = r.n;
+      start = r.start;
+      const int32_t Ls = a.seq_lens[b];
+      L = Ls > 0 ? uint32_t(Ls) : 0u;
+    }
+    const uint32_t tau0 = whole ? 0u : pos - start;
+    const uint32_t tau1 = whole ? n : min(n, end - start);
+    const uint32_t slot = whole ? 0u : pos / c - start / c;
+    const uint32_t npieces = whole ? 1u : (start + n - 1) / c - start / c + 1;
+    run_piece<FMT, D>(a, sh, b, kh, tau0, tau1, slot, whole || start + n <= end, L, npieces);
+    if (whole) break;
+    pos = start + tau1;
   }
 }
 
