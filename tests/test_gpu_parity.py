@@ -443,3 +443,27 @@ def test_single_launch_full_size(name):
     print(f"[{name}] single launch num_splits={S} max_abs_err={err:.3e}", flush=True)
     del d
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fmt,B,S", [("bf16", 65, 3), ("bf16", 300, 9), ("fp8", 130, 5),
+                                     ("nvfp4", 97, 4), ("bf16", 1000, 2)])
+def test_many_sequences(fmt, B, S):
+    """More than 64 sequences: the rows are found by a scan over the lengths
+    in memory instead of per-lane registers. Lengths include zeros."""
+    rng = np.random.default_rng(B)
+    lens = rng.integers(0, 200, size=B)
+    lens[rng.integers(0, B, size=max(1, B // 10))] = 0
+    D = {"bf16": 128, "fp8": 256, "nvfp4": 512}[fmt]
+    Hq, Hkv = {"bf16": (8, 2), "fp8": (16, 8), "nvfp4": (16, 2)}[fmt]
+    w = workloads.make_workload("tiny", lens=tuple(int(x) for x in lens), num_q_heads=Hq,
+                                num_kv_heads=Hkv, head_dim=D, kv_dtype=fmt, seed=B)
+    geom = geometry(w)
+    ks, vs = _fp8_small_scales(w) if fmt == "fp8" else (1.0, 1.0)
+    d = DeviceKV(w, geom, ks, vs)
+    kc, vc = oracle_pools(w, geom, ks, vs)
+    ref = oracle_decode(w, geom, kc, vc, ks, vs)
+    assert_close(d.decode(S), ref, f"{fmt} B={B} split-K S={S}")
+    got, counters = d.decode_single(S)
+    assert_close(got, ref, f"{fmt} B={B} single launch S={S}")
+    assert int(counters.abs().sum().item()) == 0
+    assert np.all(got[w.seq_lens == 0] == 0)
