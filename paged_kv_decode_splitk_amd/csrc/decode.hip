@@ -119,14 +119,15 @@ constexpr int kSc1 = 16;
 // K and V tiles stream into an LDS ring with direct-to-LDS buffer loads
 // (gfx950 LDS DMA, 16 bytes per lane). Each load instruction moves whole rows
 // of the tile: lane l of instruction i fetches row i*RPI + l/CPR and the
-// 16-byte chunk (l % CPR) ^ (row % CPR) of it, so the tile lands in LDS
-// row-major with the chunks of row r XOR-permuted by r. The K reads that feed
-// the MFMA (16 rows, one chunk each) and the transposed V reads then hit
-// different bank groups. NVFP4 tiles carry their group-scale rows behind the
+// 16-byte chunk (l % CPR) ^ swz(row) of it, so the tile lands in LDS
+// row-major with the chunks of each row XOR-permuted. swz(row) counts the
+// rows that start at the same bank (the 64 banks span 256 bytes), so the K
+// reads that feed the MFMA (16 rows, one chunk each) and the transposed V
+// reads hit 16 different bank groups whatever the row length. NVFP4 tiles carry their group-scale rows behind the
 // codes, fetched by one more load instruction. No VGPRs hold data in flight,
 // so the ring depth is set by LDS alone; the waits on the DMA are explicit
 // (the compiler does not track LDS-DMA writes).
-template <int FMT, int D>
+template <int FMT, int D, int DS = 1>
 struct LdsTraits {
   static constexpr int RB = FMT == kBf16 ? 2 * D : (FMT == kFp8 ? D : D / 2);  // row bytes
   static constexpr int CPR = RB / 16;            // 16-byte chunks per row (2 .. 64)
@@ -149,12 +150,24 @@ struct LdsTraits {
 #endif
   // ring depth in tiles: measured best at one 4 KB tile pair per wave with
   // four waves per CU; small tiles get more slots
+  // (a wave holding half of a split head dim keeps one slot, so that four
+  // two-wave workgroups fit a CU's LDS)
+#ifndef PKD_LDS_NBUF_SPLIT
+#define PKD_LDS_NBUF_SPLIT 1
+#endif
   static constexpr int NBUF =
-      FMT == kBf16 ? (D <= 64 ? 4 : (D == 128 ? PKD_LDS_NBUF128 : (D == 256 ? 2 : 1)))
-                   : (TILE <= 1024 ? 4 : (TILE <= 2048 ? 2 : PKD_LDS_NBUF_Q));
+      DS > 1 ? PKD_LDS_NBUF_SPLIT
+             : FMT == kBf16 ? (D <= 64 ? 4 : (D == 128 ? PKD_LDS_NBUF128 : (D == 256 ? 2 : 1)))
+                            : (TILE <= 1024 ? 4 : (TILE <= 2048 ? 2 : PKD_LDS_NBUF_Q));
   static constexpr int WAIT = (2 * NBUF - 1) * NDMA;    // loads allowed in flight at a read
   static constexpr int BRB = 2 * D;              // bytes of a BF16 row (V read transposed)
   static constexpr int BCPR = D / 8;             // 16-byte chunks of a BF16 row
+  // rows sharing a bank base: RB >= 256 bytes puts every row at the same one
+  static constexpr int SWZ_DIV = RB >= 256 ? 1 : 256 / RB;
+  static constexpr int BSWZ_DIV = BRB >= 256 ? 1 : 256 / BRB;
+  // chunk permutation of row r of a raw tile / of a BF16 V tile
+  __device__ static constexpr int swz(int r) { return (r / SWZ_DIV) % CPR; }
+  __device__ static constexpr int bswz(int r) { return (r / BSWZ_DIV) % BCPR; }
   static constexpr int STAGE = FMT == kBf16 ? 16 : 16 * BRB;   // BF16 copy of a quantized V tile
   static_assert(WAIT < 64, "vmcnt range");
   static_assert(NBUF * SLOT >= (32 * kFuseMaxSplits + 16) * 4, "the ring also holds the combine weights");
@@ -204,7 +217,7 @@ struct RowLoc {
 __device__ __forceinline__ uint32_t total_tiles(const DecodeArgs& a, uint32_t rows_per_seq) {
   uint32_t tot = 0;
   for (uint32_t b0 = 0; b0 < a.num_seqs; b0 += 64) {
-    const uint32_t bb = b0 + threadIdx.x;
+    const uint32_t bb = b0 + (threadIdx.x & 63);
     const int32_t Ls = bb < a.num_seqs ? a.seq_lens[bb] : 0;
     const uint32_t t = row_tiles(Ls > 0 ? uint32_t(Ls) : 0u, a.window) * rows_per_seq;
     tot += __shfl(wave_scan(t), 63, 64);
@@ -217,7 +230,7 @@ __device__ __forceinline__ RowLoc find_row(const DecodeArgs& a, uint32_t pos,
                                            uint32_t rows_per_seq) {
   uint32_t base = 0;
   for (uint32_t b0 = 0; b0 < a.num_seqs; b0 += 64) {
-    const uint32_t bb = b0 + threadIdx.x;
+    const uint32_t bb = b0 + (threadIdx.x & 63);
     const int32_t Ls = bb < a.num_seqs ? a.seq_lens[bb] : 0;
     const uint32_t n = row_tiles(Ls > 0 ? uint32_t(Ls) : 0u, a.window);
     const uint32_t incl = wave_scan(n * rows_per_seq);
@@ -235,10 +248,12 @@ __device__ __forceinline__ RowLoc find_row(const DecodeArgs& a, uint32_t pos,
 }
 
 
-template <int FMT, int D>
+// LDS of one wave: the tile ring and the BF16 copy of a quantized V tile.
+template <int FMT, int DW, int DS>
 struct StreamLds {
-  __attribute__((aligned(1024))) uint8_t ring[LdsTraits<FMT, D>::NBUF * LdsTraits<FMT, D>::SLOT];
-  __attribute__((aligned(16))) uint8_t stage[LdsTraits<FMT, D>::STAGE];
+  __attribute__((aligned(1024))) uint8_t ring[LdsTraits<FMT, DW, DS>::NBUF *
+                                              LdsTraits<FMT, DW, DS>::SLOT];
+  __attribute__((aligned(16))) uint8_t stage[LdsTraits<FMT, DW, DS>::STAGE];
 };
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -248,40 +263,36 @@ typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
-// A quantized V tile (raw codes in the ring) -> BF16 rows in the stage, with
-// the same chunk swizzle as a BF16 tile, rows of keys outside [lo, khi) as
-// zeros (FP8: selected when MASK; NVFP4: always, through a zero scale).
+// A quantized V tile (raw codes in the ring) -> BF16 rows in the stage, laid
+// out as a BF16 tile would be (chunk c of row r at c ^ bswz(r)). Lane l makes
+// BF16 chunks k*64 + l (8 values each), so 16 consecutive lanes write 16
+// consecutive chunks of one row: no bank conflicts. Rows of keys outside
+// [lo, khi) become zeros (FP8: selected when MASK; NVFP4: always, through a
+// zero scale, as E2M1 codes are always finite).
 template <int FMT, int D, bool MASK>
 __device__ __forceinline__ void stage_v(lds_u8* vt, lds_u8* stage, int lane, uint32_t tok0,
                                         uint32_t lo, uint32_t khi) {
   using T = LdsTraits<FMT, D>;
-  const int ld_row = lane / T::CPR;
-  const int ld_pos = lane % T::CPR;
+  constexpr int NQ = 16 * T::BCPR / 64;          // BF16 chunks per lane
 #pragma unroll
-  for (int i = 0; i < T::NI; ++i) {
-    const int row = i * T::RPI + ld_row;
-    if (T::RPI > 16 && row >= 16) continue;
-    const int pc = ld_pos ^ (row % T::CPR);        // logical chunk at this position
-    const u32x4 raw = *(lds_u32x4*)(vt + i * 1024 + lane * 16);
+  for (int k = 0; k < NQ; ++k) {
+    const int q = k * 64 + lane;
+    const int row = q / T::BCPR, c = q % T::BCPR;
     const uint32_t tok = tok0 + row;
     const bool ok = tok >= lo && tok < khi;
-    lds_u8* const srow = stage + row * T::BRB;
-    const int sx = row % T::BCPR;
+    u32x4 h;
     if constexpr (FMT == kFp8) {
-      u32x4 h0 = fp8x8_to_bf16x8(raw[0], raw[1]);
-      u32x4 h1 = fp8x8_to_bf16x8(raw[2], raw[3]);
-      if (MASK && !ok) h0 = h1 = u32x4{0u, 0u, 0u, 0u};
-      *(lds_u32x4*)(srow + ((2 * pc) ^ sx) * 16) = h0;
-      *(lds_u32x4*)(srow + ((2 * pc + 1) ^ sx) * 16) = h1;
+      // codes 8c .. 8c+7: half of raw chunk c/2
+      const u32x2 w = *(lds_u32x2*)(vt + row * T::RB + ((c >> 1) ^ T::swz(row)) * 16 + 8 * (c & 1));
+      h = fp8x8_to_bf16x8(w[0], w[1]);
+      if (MASK && !ok) h = u32x4{0u, 0u, 0u, 0u};
     } else {
-      // 32 codes = scale groups 2pc (words 0, 1) and 2pc + 1 (words 2, 3)
-      const uint32_t s2 = *(lds_u16*)(vt + T::TILE + row * T::SC_ROW + 2 * pc);
-      const float S0 = ok ? __builtin_amdgcn_cvt_f32_fp8(s2, 0) : 0.0f;
-      const float S1 = ok ? __builtin_amdgcn_cvt_f32_fp8(s2, 1) : 0.0f;
-#pragma unroll
-      for (int w = 0; w < 4; ++w)
-        *(lds_u32x4*)(srow + ((4 * pc + w) ^ sx) * 16) = fp4x8_to_bf16x8(raw[w], w < 2 ? S0 : S1);
+      // codes 8c .. 8c+7: a quarter of raw chunk c/4; scale group c/2
+      const uint32_t w = *(lds_u32*)(vt + row * T::RB + ((c >> 2) ^ T::swz(row)) * 16 + 4 * (c & 3));
+      const uint32_t sb = *(lds_u8*)(vt + T::TILE + row * T::SC_ROW + (c >> 1));
+      h = fp4x8_to_bf16x8(w, ok ? __builtin_amdgcn_cvt_f32_fp8(sb, 0) : 0.0f);
     }
+    *(lds_u32x4*)(stage + row * T::BRB + (c ^ T::bswz(row)) * 16) = h;
   }
 }
 
@@ -301,7 +312,7 @@ __device__ __forceinline__ void combine_row(const DecodeArgs& a, uint32_t b, uin
   lds_f32* const wl = (lds_f32*)wlds;        // [16][MAXP]: m, then the weights
   lds_f32* const ll = wl + 16 * MAXP;        // [16][MAXP]: l
   lds_f32* const il = ll + 16 * MAXP;        // [16]: 1 / sum of the weights
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const uint32_t kvh = kh / a.head_chunks, hc = kh % a.head_chunks;
   const uint32_t gc = min(16u, a.group - hc * 16);           // q heads of this chunk
   const uint32_t qh0 = kvh * a.group + hc * 16;
@@ -393,14 +404,22 @@ __device__ __forceinline__ void combine_row(const DecodeArgs& a, uint32_t b, uin
 }
 
 // One row piece: tiles [tau0, tau1) of row (b, kh), partial state to `slot`.
-template <int FMT, int D>
-__device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D>& sh, uint32_t b,
-                                          uint32_t kh, uint32_t tau0, uint32_t tau1,
-                                          uint32_t slot, bool last, uint32_t L, uint32_t npieces) {
-  using T = LdsTraits<FMT, D>;
+// With DS = 2 the workgroup's two waves split the head dim: wave w loads and
+// accumulates dims [w D/2, (w+1) D/2) of K, V, q and o, and the two halves of
+// every tile's logits are added through LDS (`xg`, two buffers used in turn,
+// `xturn` counting the exchanges of the launch).
+template <int FMT, int D, int DS>
+__device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D / DS, DS>& sh,
+                                          lds_u8* xg, uint32_t& xturn, uint32_t b, uint32_t kh,
+                                          uint32_t tau0, uint32_t tau1, uint32_t slot, bool last,
+                                          uint32_t L, uint32_t npieces) {
+  constexpr int DW = D / DS;                     // head dims of this wave
+  using T = LdsTraits<FMT, DW, DS>;              // tile geometry of this wave's half rows
+  using TF = LdsTraits<FMT, D>;                  // full rows (strides in the pools)
   constexpr int NBUF = T::NBUF;
   if (slot >= a.num_splits) return;      // only if a sequence outgrows its block table
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int w = DS > 1 ? int(threadIdx.x >> 6) : 0;
   const int g = lane >> 4;
   const int n = lane & 15;
   const uint32_t kvh = kh / a.head_chunks, hc = kh % a.head_chunks;
@@ -418,11 +437,11 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D>
 
   // q as the B operand of the QK MFMAs: column n = head, dims 32c + 8g .. +8;
   // issued ahead of the tile loads, which only ever wait for later loads.
-  bf16x8 qf[D / 32];
+  bf16x8 qf[DW / 32];
   {
-    const uint16_t* qrow = a.q + uint64_t(b) * a.q_stride + uint64_t(qh) * D;
+    const uint16_t* qrow = a.q + uint64_t(b) * a.q_stride + uint64_t(qh) * D + w * DW;
 #pragma unroll
-    for (int c = 0; c < D / 32; ++c) {
+    for (int c = 0; c < DW / 32; ++c) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (head_ok) v = *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * g);
       qf[c] = __builtin_bit_cast(bf16x8, v);
@@ -434,9 +453,9 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D>
   const int ld_row = lane / T::CPR;                  // + i * RPI
   const int ld_pos = lane % T::CPR;
 
-  f32x4 acc[D / 16];
+  f32x4 acc[DW / 16];
 #pragma unroll
-  for (int mt = 0; mt < D / 16; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < DW / 16; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -__builtin_inff();
   float l_run = 0.0f;
 
@@ -465,8 +484,8 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D>
 #pragma unroll
       for (int i = 0; i < T::NI; ++i) {
         const int row = i * T::RPI + ld_row;
-        const int chunk = ld_pos ^ (row % T::CPR);
-        int voff = int(((off0 + row) * a.num_kv_heads + kvh) * T::RB + chunk * 16);
+        const int chunk = ld_pos ^ T::swz(row);
+        int voff = int(((off0 + row) * a.num_kv_heads + kvh) * TF::RB + w * T::RB + chunk * 16);
         if constexpr (T::RPI > 16) voff = row < 16 ? voff : 0x7FFFFFF0;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + i * 1024), 16, voff,
                                                  0, 0, 2);
@@ -475,8 +494,8 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D>
         const int srow = lane / T::SC_LPR;
         const int part = lane % T::SC_LPR;
         const int voff = srow < 16 ? int(a.data_section) +
-                                         int(((off0 + srow) * a.num_kv_heads + kvh) * T::SC_ROW +
-                                             part * T::SC_SIZE)
+                                         int(((off0 + srow) * a.num_kv_heads + kvh) * TF::SC_ROW +
+                                             w * T::SC_ROW + part * T::SC_SIZE)
                                    : 0x7FFFFFF0;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + T::TILE), T::SC_SIZE,
                                                  voff, 0, 0, 2);
@@ -505,16 +524,16 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D>
         f32x4 sc = {0.f, 0.f, 0.f, 0.f};
         if constexpr (FMT == kBf16) {
 #pragma unroll
-          for (int c = 0; c < D / 32; ++c) {
-            const int chunk = (4 * c + g) ^ (n % T::CPR);
+          for (int c = 0; c < DW / 32; ++c) {
+            const int chunk = (4 * c + g) ^ T::swz(n);
             const u32x4 kv = *(lds_u32x4*)(kt + n * T::RB + chunk * 16);
             sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qf[c],
                                                          sc, 0, 0, 0);
           }
         } else if constexpr (FMT == kFp8) {
 #pragma unroll
-          for (int c = 0; c < D / 32; ++c) {
-            const int chunk = (2 * c + (g >> 1)) ^ (n % T::CPR);
+          for (int c = 0; c < DW / 32; ++c) {
+            const int chunk = (2 * c + (g >> 1)) ^ T::swz(n);
             const u32x2 w = *(lds_u32x2*)(kt + n * T::RB + chunk * 16 + 8 * (g & 1));
             const u32x4 kv = fp8x8_to_bf16x8(w[0], w[1]);
             sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qf[c],
@@ -528,8 +547,8 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D>
           for (int k = 0; k < (T::SC_ROW + 3) / 4; ++k)
             sw[k] = *(lds_u32*)(kt + T::TILE + n * T::SC_ROW + 4 * k) >> (8 * (g >> 1));
 #pragma unroll
-          for (int c = 0; c < D / 32; ++c) {
-            const int chunk = c ^ (n % T::CPR);
+          for (int c = 0; c < DW / 32; ++c) {
+            const int chunk = c ^ T::swz(n);
             const uint32_t w = *(lds_u32*)(kt + n * T::RB + chunk * 16 + 4 * g);
             const float S = (c & 1) ? __builtin_amdgcn_cvt_f32_fp8(sw[c / 2], 2)
                                     : __builtin_amdgcn_cvt_f32_fp8(sw[c / 2], 0);
@@ -537,6 +556,15 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D>
             sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qf[c],
                                                          sc, 0, 0, 0);
           }
+        }
+        if constexpr (DS > 1) {
+          // the other half of the head dim: partial logits through LDS
+          typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+          lds_f32x4* const xs = (lds_f32x4*)xg + (xturn++ & 1) * (DS * 64);
+          xs[w * 64 + lane] = sc;
+          asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+          const f32x4 other = xs[(1 - w) * 64 + lane];
+          sc = w == 0 ? sc + other : other + sc;   // the same sum in both waves
         }
         __builtin_amdgcn_sched_barrier(0);
         issue(s, 0, t + NBUF);
@@ -599,9 +627,9 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D>
           // partial tiles select zeros; E2M1 codes are always finite, so a
           // masked NVFP4 row just takes a zero scale
           if (FMT == kFp8 && (tok0 < lo || tok0 + 16 > khi))
-            stage_v<FMT, D, true>(vt, stage3, lane, tok0, lo, khi);
+            stage_v<FMT, DW, true>(vt, stage3, lane, tok0, lo, khi);
           else
-            stage_v<FMT, D, false>(vt, stage3, lane, tok0, lo, khi);
+            stage_v<FMT, DW, false>(vt, stage3, lane, tok0, lo, khi);
           wave_lds_fence();
           __builtin_amdgcn_sched_barrier(0);
           issue(s, 1, t + NBUF);                   // the raw V tile is consumed
@@ -612,18 +640,18 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D>
         // then their four MFMAs, which run while the next reads are in flight.
         if (rescale) {
 #pragma unroll
-          for (int mt = 0; mt < D / 16; ++mt) acc[mt] *= alpha;
+          for (int mt = 0; mt < DW / 16; ++mt) acc[mt] *= alpha;
         }
         {
           const int vtok = 4 * g + (n >> 2);
           const uint32_t vrow = uint32_t(uintptr_t(vsrc)) + vtok * T::BRB + (n & 1) * 8;
 #pragma unroll
-          for (int q4 = 0; q4 < D / 64; ++q4) {
+          for (int q4 = 0; q4 < DW / 64; ++q4) {
             uint32_t ad[4];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
               const int mt = 4 * q4 + u;
-              ad[u] = vrow + (((2 * mt + ((n & 3) >> 1)) ^ (vtok % T::BCPR)) * 16);
+              ad[u] = vrow + (((2 * mt + ((n & 3) >> 1)) ^ T::bswz(vtok)) * 16);
             }
             // four transposed reads and their wait in one statement: the outputs
             // exist only after the wait, so no consumer can be scheduled earlier
@@ -656,9 +684,9 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D>
     // the whole row in one piece: the normalized output goes straight to BF16
     if (head_ok) {
       const float inv = a.out_scale / l_tot;
-      uint16_t* orow = a.out + (uint64_t(b) * a.num_q_heads + qh) * D;
+      uint16_t* orow = a.out + (uint64_t(b) * a.num_q_heads + qh) * D + w * DW;
 #pragma unroll
-      for (int mt = 0; mt < D / 16; ++mt)
+      for (int mt = 0; mt < DW / 16; ++mt)
         *reinterpret_cast<u32x2*>(orow + 16 * mt + 4 * g) =
             u32x2{pack_bf16x2(acc[mt][0] * inv, acc[mt][1] * inv),
                   pack_bf16x2(acc[mt][2] * inv, acc[mt][3] * inv)};
@@ -672,13 +700,13 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D>
         wbase + uint64_t(slot) * (D + 2), 0, (D + 2) * 4, 0x00020000);
     const float inv = a.out_scale / l_tot;
 #pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt) {
+    for (int mt = 0; mt < DW / 16; ++mt) {
       const u32x2 lo2 = {__float_as_uint(acc[mt][0] * inv), __float_as_uint(acc[mt][1] * inv)};
       const u32x2 hi2 = {__float_as_uint(acc[mt][2] * inv), __float_as_uint(acc[mt][3] * inv)};
-      __builtin_amdgcn_raw_buffer_store_b64(lo2, rs, (mt * 16 + 4 * g) * 4, 0, kSc1);
-      __builtin_amdgcn_raw_buffer_store_b64(hi2, rs, (mt * 16 + 4 * g + 2) * 4, 0, kSc1);
+      __builtin_amdgcn_raw_buffer_store_b64(lo2, rs, (w * DW + mt * 16 + 4 * g) * 4, 0, kSc1);
+      __builtin_amdgcn_raw_buffer_store_b64(hi2, rs, (w * DW + mt * 16 + 4 * g + 2) * 4, 0, kSc1);
     }
-    if (g == 0) {
+    if (g == 0 && w == 0) {
       const u32x2 ml = {__float_as_uint(m_run * kLn2), __float_as_uint(l_tot)};
       __builtin_amdgcn_raw_buffer_store_b64(ml, rs, D * 4, 0, kSc1);
     }
@@ -686,19 +714,19 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D>
     float* wrow = wbase + uint64_t(slot) * (D + 2);
     const float inv = a.out_scale / l_tot;
 #pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt) {
+    for (int mt = 0; mt < DW / 16; ++mt) {
       f32x2 lo2 = {acc[mt][0] * inv, acc[mt][1] * inv};
       f32x2 hi2 = {acc[mt][2] * inv, acc[mt][3] * inv};
-      *reinterpret_cast<f32x2*>(wrow + mt * 16 + 4 * g) = lo2;
-      *reinterpret_cast<f32x2*>(wrow + mt * 16 + 4 * g + 2) = hi2;
+      *reinterpret_cast<f32x2*>(wrow + w * DW + mt * 16 + 4 * g) = lo2;
+      *reinterpret_cast<f32x2*>(wrow + w * DW + mt * 16 + 4 * g + 2) = hi2;
     }
-    if (g == 0) {
+    if (g == 0 && w == 0) {
       wrow[D] = m_run * kLn2;
       wrow[D + 1] = l_tot;
     }
     // the row ends in this piece: an end marker (l = -1) in the next slot
     // tells the combine to ignore that slot and all later ones
-    if (!a.out && last && g == 0 && slot + 1 < a.num_splits) {
+    if (!a.out && last && g == 0 && w == 0 && slot + 1 < a.num_splits) {
       float* e = wbase + uint64_t(slot + 1) * (D + 2);
       e[D] = -__builtin_inff();
       e[D + 1] = -1.0f;
@@ -712,6 +740,11 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D>
     uint32_t* const cnt = a.counters + uint64_t(b) * R + kh;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
     wait_vmcnt<0>();
+    if constexpr (DS > 1) {
+      // both halves stored before the count; the first wave counts and merges
+      asm volatile("s_barrier" ::: "memory");
+      if (w != 0) return;
+    }
     uint32_t old = 0;
     if (lane == 0)
       old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -727,7 +760,7 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D>
 // Zeros for the q heads of row (b, kh) of a sequence without keys.
 template <int D>
 __device__ __forceinline__ void zero_row(const DecodeArgs& a, uint32_t b, uint32_t kh) {
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
   const int g = lane >> 4, n = lane & 15;
   const uint32_t kvh = kh / a.head_chunks, hc = kh % a.head_chunks;
   const uint32_t head_in_group = hc * 16 + n;
@@ -737,18 +770,31 @@ __device__ __forceinline__ void zero_row(const DecodeArgs& a, uint32_t b, uint32
   for (int mt = 0; mt < D / 16; ++mt) *reinterpret_cast<u32x2*>(orow + 16 * mt + 4 * g) = u32x2{0u, 0u};
 }
 
+// Head-dim split: at head_dim 512 a workgroup of two waves shares each row
+// piece, each wave holding half of the dims (the accumulator alone would
+// otherwise take 128 registers of one wave).
+template <int D>
+constexpr int kDSplit = D == 512 ? 2 : 1;
+
 // Waves per SIMD the register budget is held to: quantized tiles up to
-// head_dim 256 run two (their ALU work hides behind the other wave's loads).
+// head_dim 256 and split head dims run two (their ALU work hides behind the
+// other wave's loads).
 template <int FMT, int D>
-constexpr int kWavesPerSimd = (FMT != kBf16 && D <= 256) ? 2 : 1;
+constexpr int kWavesPerSimd = ((FMT != kBf16 && D <= 256) || kDSplit<D> > 1) ? 2 : 1;
 
 template <int FMT, int D>
-__global__ __launch_bounds__(64, (kWavesPerSimd<FMT, D>)) void splitk_stream(DecodeArgs a) {
-  __shared__ StreamLds<FMT, D> sh;
+__global__ __launch_bounds__(64 * kDSplit<D>, (kWavesPerSimd<FMT, D>)) void splitk_stream(
+    DecodeArgs a) {
+  constexpr int DS = kDSplit<D>;
+  __shared__ StreamLds<FMT, D / DS, DS> sh[DS];
+  __shared__ __attribute__((aligned(16))) uint8_t xg[DS > 1 ? 2 * DS * 64 * 16 : 16];
+  StreamLds<FMT, D / DS, DS>& mine = sh[DS > 1 ? threadIdx.x >> 6 : 0];
+  lds_u8* const xg3 = (lds_u8*)xg;
+  uint32_t xturn = 0;
   const uint32_t R = a.num_kv_heads * a.head_chunks;          // rows per sequence
   const uint32_t P = gridDim.x;
   const bool whole = a.num_splits == 1;                       // one wave per row
-  if (!whole && a.out) {
+  if (!whole && a.out && threadIdx.x < 64) {
     // single-launch decode: sequences without keys get zeros here, as no
     // piece covers them
     for (uint32_t b = blockIdx.x; b < a.num_seqs; b += P)
@@ -760,7 +806,8 @@ __global__ __launch_bounds__(64, (kWavesPerSimd<FMT, D>)) void splitk_stream(Dec
   const bool cached = a.num_seqs <= 64;
   uint32_t L_l = 0, n_l = 0, incl = 0;
   if (cached && !whole) {
-    const int32_t Ls = threadIdx.x < a.num_seqs ? a.seq_lens[threadIdx.x] : 0;
+    const uint32_t lane = threadIdx.x & 63;
+    const int32_t Ls = lane < a.num_seqs ? a.seq_lens[lane] : 0;
     L_l = Ls > 0 ? uint32_t(Ls) : 0u;
     n_l = row_tiles(L_l, a.window);
     incl = wave_scan(n_l * R);
@@ -783,7 +830,7 @@ __global__ __launch_bounds__(64, (kWavesPerSimd<FMT, D>)) void splitk_stream(Dec
       n = row_tiles(L, a.window);
       start = pos;
       if (n == 0) {
-        if (a.out) zero_row<D>(a, b, kh);
+        if (a.out && threadIdx.x < 64) zero_row<D>(a, b, kh);
         break;
       }
     } else if (cached) {
@@ -807,7 +854,8 @@ __global__ __launch_bounds__(64, (kWavesPerSimd<FMT, D>)) void splitk_stream(Dec
     const uint32_t tau1 = whole ? n : min(n, end - start);
     const uint32_t slot = whole ? 0u : pos / c - start / c;
     const uint32_t npieces = whole ? 1u : (start + n - 1) / c - start / c + 1;
-    run_piece<FMT, D>(a, sh, b, kh, tau0, tau1, slot, whole || start + n <= end, L, npieces);
+    run_piece<FMT, D, DS>(a, mine, xg3, xturn, b, kh, tau0, tau1, slot,
+                          whole || start + n <= end, L, npieces);
     if (whole) break;
     pos = start + tau1;
   }
@@ -921,13 +969,14 @@ static int launch_status() {
 
 // Waves the stream kernel launches on the current device: all resident at
 // once (at most the occupancy), cached per device, format and head_dim.
+// Resident waves per CU of the stream kernel (workgroups x waves per workgroup).
 template <int FMT, int D>
 static int stream_occupancy() {
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, splitk_stream<FMT, D>, 64, 0) !=
-      hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, splitk_stream<FMT, D>,
+                                                   64 * kDSplit<D>, 0) != hipSuccess)
     return 0;
-  return per_cu;
+  return per_cu * kDSplit<D>;
 }
 
 template <int FMT>
@@ -958,7 +1007,8 @@ static uint64_t stream_capacity(uint32_t head_dim) {
   // quantized tiles carry more ALU work per byte and gain from a second wave
   // per SIMD where the registers allow it. The count is a multiple of the CU
   // count so that every CU gets the same work.
-  const int cap = FMT == kBf16 ? PKD_STREAM_WAVES_PER_CU : PKD_STREAM_WAVES_PER_CU_Q;
+  const int cap = FMT == kBf16 && head_dim < 512 ? PKD_STREAM_WAVES_PER_CU
+                                                 : PKD_STREAM_WAVES_PER_CU_Q;
   if (per_cu > cap) per_cu = cap;
   cache[dev][di] = uint64_t(per_cu) * uint64_t(cus);
   return cache[dev][di];
@@ -974,14 +1024,17 @@ static int launch_splitk(DecodeArgs a, uint32_t num_seqs, uint32_t head_dim,
   uint32_t tile_bound = a.max_blocks * (a.block_size / 16);
   if (a.window > 0) tile_bound = min(tile_bound, (a.window + 14) / 16 + 1);
   a.chunk_min = a.num_splits > 1 ? (tile_bound + a.num_splits - 2) / (a.num_splits - 1) : 1;
-  uint64_t waves = rows;
+  // one workgroup per piece (at most num_splits per row), or as many as stay
+  // resident; a workgroup is one wave, or two sharing a head_dim of 512
+  const uint64_t ds = head_dim == 512 ? 2 : 1;
+  uint64_t groups = rows;
   if (a.num_splits > 1) {
-    waves = rows * a.num_splits;
-    const uint64_t cap = stream_capacity<FMT>(head_dim);
-    if (cap && waves > cap) waves = cap;
+    groups = rows * a.num_splits;
+    const uint64_t cap = stream_capacity<FMT>(head_dim) / ds;
+    if (cap && groups > cap) groups = cap;
   }
-  if (waves > 0x7FFFFFFFull) return kUnsupported;
-  const dim3 gd = dim3(uint32_t(waves)), bd = dim3(64);
+  if (groups > 0x7FFFFFFFull) return kUnsupported;
+  const dim3 gd = dim3(uint32_t(groups)), bd = dim3(uint32_t(64 * ds));
   switch (head_dim) {
     case 64: hipLaunchKernelGGL((splitk_stream<FMT, 64>), gd, bd, 0, stream, a); break;
     case 128: hipLaunchKernelGGL((splitk_stream<FMT, 128>), gd, bd, 0, stream, a); break;
