@@ -79,24 +79,57 @@ __device__ __forceinline__ u32x4 fp8x8_to_bf16x8(uint32_t w0, uint32_t w1) {
                fp8x2_to_bf16x2<false>(w1), fp8x2_to_bf16x2<true>(w1)};
 }
 
-// Two E2M1 codes (byte `sel` of w, low nibble first) times the group scale S
-// -> packed BF16 pair. The fp4 convert takes only the exponent of its scale
-// operand, so it runs at scale 1 and S is applied by a multiply (exact).
-__device__ __forceinline__ uint32_t fp4x2_to_bf16x2(uint32_t w, int sel, float S) {
-  f32x2 f;
-  switch (sel) {
-    case 0: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 0); break;
-    case 1: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 1); break;
-    case 2: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 2); break;
-    default: f = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, 3); break;
-  }
-  return pack_bf16x2(f[0] * S, f[1] * S);
+// NVFP4 runs its MFMAs in FP16: every E2M1 x E4M3 product is an FP16 value
+// (at most 6 significant bits, magnitude 2^-10 .. 2688), so the group scale
+// is applied with one packed FP16 multiply per pair, and P keeps 11 bits.
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+template <int SEL>
+__device__ __forceinline__ uint32_t fp4x2_to_f16x2(uint32_t w, f16x2 S) {
+  const f16x2 x = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+  return __builtin_bit_cast(uint32_t, x * S);
 }
 
-// Eight E2M1 codes (one 32-bit word) of one scale group -> eight BF16 values.
-__device__ __forceinline__ u32x4 fp4x8_to_bf16x8(uint32_t w, float S) {
-  return u32x4{fp4x2_to_bf16x2(w, 0, S), fp4x2_to_bf16x2(w, 1, S), fp4x2_to_bf16x2(w, 2, S),
-               fp4x2_to_bf16x2(w, 3, S)};
+// Eight E2M1 codes (one 32-bit word) of one scale group -> eight FP16 values.
+__device__ __forceinline__ u32x4 fp4x8_to_f16x8(uint32_t w, _Float16 s) {
+  const f16x2 S = {s, s};
+  return u32x4{fp4x2_to_f16x2<0>(w, S), fp4x2_to_f16x2<1>(w, S), fp4x2_to_f16x2<2>(w, S),
+               fp4x2_to_f16x2<3>(w, S)};
+}
+
+// The two MFMAs on raw 16-bit operands: FP16 for NVFP4, BF16 otherwise.
+template <int FMT>
+__device__ __forceinline__ f32x4 mfma_qk(u32x4 k, u32x4 q, f32x4 acc) {
+  if constexpr (FMT == kNvfp4)
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, k),
+                                                  __builtin_bit_cast(f16x8, q), acc, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, k),
+                                                   __builtin_bit_cast(bf16x8, q), acc, 0, 0, 0);
+}
+template <int FMT>
+__device__ __forceinline__ f32x4 mfma_pv(u32x2 v, u32x2 p, f32x4 acc) {
+  if constexpr (FMT == kNvfp4)
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4, v),
+                                                 __builtin_bit_cast(f16x4, p), acc, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, v),
+                                                     __builtin_bit_cast(s16x4, p), acc, 0, 0, 0);
+}
+
+// A softmax weight in the MFMA's 16-bit type (round to nearest even) and the
+// value it holds.
+template <int FMT>
+__device__ __forceinline__ uint32_t p_bits(float p) {
+  if constexpr (FMT == kNvfp4) return __builtin_bit_cast(uint16_t, _Float16(p));
+  else return f32_to_bf16_bits(p);
+}
+template <int FMT>
+__device__ __forceinline__ float p_value(uint32_t bits) {
+  if constexpr (FMT == kNvfp4) return float(__builtin_bit_cast(_Float16, uint16_t(bits)));
+  else return __uint_as_float(bits << 16);
 }
 
 // Orders this wave's LDS accesses for the compiler; a wave's LDS operations
@@ -263,8 +296,9 @@ typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 typedef __attribute__((address_space(3))) uint32_t lds_u32;
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 
-// A quantized V tile (raw codes in the ring) -> BF16 rows in the stage, laid
-// out as a BF16 tile would be (chunk c of row r at c ^ bswz(r)). Lane l makes
+// A quantized V tile (raw codes in the ring) -> 16-bit rows in the stage
+// (BF16 for FP8, FP16 for NVFP4), laid out as a BF16 tile would be (chunk c
+// of row r at c ^ bswz(r)). Lane l makes
 // BF16 chunks k*64 + l (8 values each), so 16 consecutive lanes write 16
 // consecutive chunks of one row: no bank conflicts. Rows of keys outside
 // [lo, khi) become zeros (FP8: selected when MASK; NVFP4: always, through a
@@ -290,7 +324,7 @@ __device__ __forceinline__ void stage_v(lds_u8* vt, lds_u8* stage, int lane, uin
       // codes 8c .. 8c+7: a quarter of raw chunk c/4; scale group c/2
       const uint32_t w = *(lds_u32*)(vt + row * T::RB + ((c >> 2) ^ T::swz(row)) * 16 + 4 * (c & 3));
       const uint32_t sb = *(lds_u8*)(vt + T::TILE + row * T::SC_ROW + (c >> 1));
-      h = fp4x8_to_bf16x8(w, ok ? __builtin_amdgcn_cvt_f32_fp8(sb, 0) : 0.0f);
+      h = fp4x8_to_f16x8(w, ok ? _Float16(__builtin_amdgcn_cvt_f32_fp8(sb, 0)) : _Float16(0.0f));
     }
     *(lds_u32x4*)(stage + row * T::BRB + (c ^ T::bswz(row)) * 16) = h;
   }
@@ -437,14 +471,43 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
 
   // q as the B operand of the QK MFMAs: column n = head, dims 32c + 8g .. +8;
   // issued ahead of the tile loads, which only ever wait for later loads.
-  bf16x8 qf[DW / 32];
+  u32x4 qf[DW / 32];
+  float qup = 1.0f;            // NVFP4: logits of this head's dims are scaled by qup
   {
     const uint16_t* qrow = a.q + uint64_t(b) * a.q_stride + uint64_t(qh) * D + w * DW;
 #pragma unroll
     for (int c = 0; c < DW / 32; ++c) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (head_ok) v = *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * g);
-      qf[c] = __builtin_bit_cast(bf16x8, v);
+      qf[c] = v;
+    }
+    if constexpr (FMT == kNvfp4) {
+      // q in FP16 for the FP16 MFMA: shifted down by 2^k so that the head's
+      // largest |q| stays below 2^15 (exact for every BF16 value in range)
+      uint32_t mlo = 0, mhi = 0;     // largest magnitudes (BF16 bits order as values)
+#pragma unroll
+      for (int c = 0; c < DW / 32; ++c)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          mlo = max(mlo, qf[c][j] & 0x7FFFu);
+          mhi = max(mhi, qf[c][j] & 0x7FFF0000u);
+        }
+      float m = fmaxf(bf16_lo(mlo), bf16_hi(mhi));
+      m = max_over_rows(m);
+      const int e = int((__float_as_uint(m) >> 23) & 255u) - 127;
+      const int k = e > 14 ? e - 14 : 0;
+      const float down = __uint_as_float(uint32_t(127 - k) << 23);
+      qup = __uint_as_float(uint32_t(127 + k) << 23);
+#pragma unroll
+      for (int c = 0; c < DW / 32; ++c) {
+        u32x4 h;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const f32x2 f = {bf16_lo(qf[c][j]) * down, bf16_hi(qf[c][j]) * down};
+          h[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
+        }
+        qf[c] = h;
+      }
     }
   }
 
@@ -527,8 +590,7 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
           for (int c = 0; c < DW / 32; ++c) {
             const int chunk = (4 * c + g) ^ T::swz(n);
             const u32x4 kv = *(lds_u32x4*)(kt + n * T::RB + chunk * 16);
-            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qf[c],
-                                                         sc, 0, 0, 0);
+            sc = mfma_qk<FMT>(kv, qf[c], sc);
           }
         } else if constexpr (FMT == kFp8) {
 #pragma unroll
@@ -536,8 +598,7 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
             const int chunk = (2 * c + (g >> 1)) ^ T::swz(n);
             const u32x2 w = *(lds_u32x2*)(kt + n * T::RB + chunk * 16 + 8 * (g & 1));
             const u32x4 kv = fp8x8_to_bf16x8(w[0], w[1]);
-            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qf[c],
-                                                         sc, 0, 0, 0);
+            sc = mfma_qk<FMT>(kv, qf[c], sc);
           }
         } else {
           // group of dims 32c + 8g is 2c + g/2: byte 2(c & 1) of scale word c/2
@@ -552,10 +613,10 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
             const uint32_t w = *(lds_u32*)(kt + n * T::RB + chunk * 16 + 4 * g);
             const float S = (c & 1) ? __builtin_amdgcn_cvt_f32_fp8(sw[c / 2], 2)
                                     : __builtin_amdgcn_cvt_f32_fp8(sw[c / 2], 0);
-            const u32x4 kv = fp4x8_to_bf16x8(w, S);
-            sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kv), qf[c],
-                                                         sc, 0, 0, 0);
+            const u32x4 kv = fp4x8_to_f16x8(w, _Float16(S));
+            sc = mfma_qk<FMT>(kv, qf[c], sc);
           }
+          sc *= qup;
         }
         if constexpr (DS > 1) {
           // the other half of the head dim: partial logits through LDS
@@ -596,13 +657,11 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const float p = __builtin_amdgcn_exp2f(sv[j] - m_run);
-          pbits[j] = f32_to_bf16_bits(p);
-          psum += __uint_as_float(pbits[j] << 16);
+          pbits[j] = p_bits<FMT>(p);
+          psum += p_value<FMT>(pbits[j]);
         }
         l_run = l_run * alpha + psum;
-        s16x4 pf;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) pf[j] = short(pbits[j]);
+        const u32x2 pf = {pbits[0] | (pbits[1] << 16), pbits[2] | (pbits[3] << 16)};
 
         // ---- V tile as BF16 rows with masked tokens zeroed: in place for a
         // BF16 cache (partial tiles only), else dequantized into the stage
@@ -667,8 +726,7 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
                 : "memory");
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-              acc[4 * q4 + u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(
-                  __builtin_bit_cast(s16x4, vv[u]), pf, acc[4 * q4 + u], 0, 0, 0);
+              acc[4 * q4 + u] = mfma_pv<FMT>(vv[u], pf, acc[4 * q4 + u]);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
