@@ -2,9 +2,8 @@
 
 A step is the whole decode path for one attention layer over one batch:
 write the new token's K/V through slot_mapping (reshape_and_cache), run the
-split-KV pass, then the combine pass. The same step through the single-launch
-decode call (combine merged into the split pass when the split count is at
-most 32) is timed beside it. Inputs are seeded
+split-KV pass, then the combine pass. The same step through the non-split
+decode (one wave per row, one launch, no combine) is timed beside it. Inputs are seeded
 synthetic tensors already resident in HBM. Steps rotate over several layers'
 KV pools whose total size is several times the 256 MB Infinity Cache, so
 every step reads its KV from HBM, as the layers of a model do. The timed loop
@@ -141,7 +140,6 @@ class Layers:
         self.ws = torch.empty(pkd.paged_decode_workspace_bytes(B, Hq, D, self.num_splits) // 4,
                               dtype=torch.float32, device=self.dev)
         self.out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=self.dev)
-        self.counters = torch.zeros(B * Hq, dtype=torch.int32, device=self.dev)
         torch.cuda.synchronize()
 
     def _write(self, key, val, kp, vp, slots):
@@ -172,14 +170,13 @@ class Layers:
                                                w.num_seqs, w.sliding_window)
 
     def decode(self, layer):
-        """The single-launch decode call (combine merged in when num_splits <= 32)."""
+        """The whole-decode call with num_splits 1: one wave per row writes the output."""
         import paged_kv_decode_splitk_amd as pkd
         w = self.w
         common = (self.q, self.k[layer], self.v[layer], self.out, self.bt, self.lens,
                   w.max_blocks_per_seq, w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim,
                   w.block_size, float(w.scale))
-        tail = dict(sliding_window=w.sliding_window, workspace=self.ws, counters=self.counters,
-                    num_splits=self.num_splits)
+        tail = dict(sliding_window=w.sliding_window, workspace=None, num_splits=1)
         qs = w.num_q_heads * w.head_dim
         if w.kv_dtype == "bf16":
             pkd.paged_decode_attn_bf16(*common, qs, **tail)
@@ -199,7 +196,7 @@ class Layers:
                                      self.num_splits, w.num_seqs)
 
     def step_single(self, layer):
-        """Write the new token's K/V, then the single-launch decode call."""
+        """Write the new token's K/V, then the non-split decode (one launch)."""
         self._write(self.new_key, self.new_val, self.k[layer], self.v[layer], self.new_slots)
         self.decode(layer)
 
@@ -255,9 +252,8 @@ def time_workload(name, steps, warmup, kernel_reps=100, single=True):
         kv_pool_bytes_per_layer=lay.pool_bytes, attended_tokens=attended_tokens(w),
         kv_bytes_per_step=kv_bytes, steps=steps_run, ms_per_step=ms_step,
         us_per_step=ms_step * 1e3, kv_gbs=gbs(ms_step), wall_s=wall,
-        single_launch_us_per_step=ms_single * 1e3, single_launch_kv_gbs=gbs(ms_single),
-        decode_us=single_ms * 1e3, decode_gbs=gbs(single_ms),
-        decode_merged=lay.num_splits <= 32,
+        non_split_us_per_step=ms_single * 1e3, non_split_kv_gbs=gbs(ms_single),
+        non_split_kernel_us=single_ms * 1e3, non_split_kernel_gbs=gbs(single_ms),
         splitk_us=k_ms * 1e3, splitk_gbs=gbs(k_ms),
     )
     res["pct_of_peak"] = 100.0 * res["kv_gbs"] / PEAK_HBM_GBS
@@ -362,8 +358,8 @@ def main():
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true")
     ap.add_argument("--no-single", action="store_true",
-                    help="skip the single-launch decode timings (profiles then see only the "
-                         "split-K kernel)")
+                    help="skip the non-split decode timings (profiles then see only the "
+                         "split-K launches of the kernel)")
     ap.add_argument("--counter-run", action="store_true",
                     help="only run the split-K pass of --workload 20 times")
     args = ap.parse_args()
@@ -389,9 +385,9 @@ def main():
     for name in args.extra:
         r, _ = time_workload(name, args.steps, args.warmup, single=not args.no_single)
         extras[name] = {k: r[k] for k in ("us_per_step", "kv_gbs", "pct_of_peak",
-                                          "single_launch_us_per_step",
-                                          "single_launch_kv_gbs",
-                                          "decode_us", "decode_gbs", "decode_merged",
+                                          "non_split_us_per_step",
+                                          "non_split_kv_gbs",
+                                          "non_split_kernel_us", "non_split_kernel_gbs",
                                           "splitk_us", "splitk_gbs", "num_splits",
                                           "kv_bytes_per_step", "layers_rotated")}
         print(f"bench: {name} {r['us_per_step']:.2f} us/step {r['kv_gbs']:.0f} GB/s",
@@ -432,10 +428,9 @@ def main():
             "step": "reshape_and_cache of the new token + split-KV pass + combine pass, "
                     "HIP-graph replay",
         },
-        "single_launch_step": {k: main_res[k] for k in ("single_launch_us_per_step",
-                                                         "single_launch_kv_gbs",
-                                                         "decode_merged")},
-        "kernels": {k: main_res[k] for k in ("decode_us", "decode_gbs", "splitk_us",
+        "non_split_step": {k: main_res[k] for k in ("non_split_us_per_step",
+                                                     "non_split_kv_gbs")},
+        "kernels": {k: main_res[k] for k in ("non_split_kernel_us", "non_split_kernel_gbs", "splitk_us",
                                              "splitk_gbs")},
         "roofline": roofline,
         "cpu_baseline": cpu,

@@ -200,39 +200,30 @@ PKD_API int paged_decode_attn_reduce(const float* workspace, uint16_t* output,
                                      uint32_t head_dim, uint32_t num_splits, uint32_t num_seqs,
                                      hipStream_t stream);
 
-/* ---------------------------------------------------------------- single-launch decode
+/* ---------------------------------------------------------------- whole decode
  * The whole decode into BF16 output [num_seqs][num_q_heads][head_dim]
- * (contiguous): the same attention as a split-K call followed by
- * paged_decode_attn_reduce, in one call. The argument order follows the
- * non-split launcher paged_decode_attn_nvfp4 of the metrale page (q, caches,
- * output, block_tables, seq_lens, max_blocks_per_seq, num_seqs, head counts,
+ * (contiguous), in one call: the same attention as a split-K call followed by
+ * paged_decode_attn_reduce. The argument order follows the non-split launcher
+ * paged_decode_attn_nvfp4 of the metrale page (q, caches, output,
+ * block_tables, seq_lens, max_blocks_per_seq, num_seqs, head counts,
  * head_dim, block_size, scale, q_stride, cache layout); sliding_window,
- * workspace, counters and num_splits are extensions.
- *   num_splits == 1: one wave per (sequence, kv head, 16 q heads), output
- *     written directly, as the non-split launcher does; workspace and
- *     counters are not used (may be null).
- *   1 < num_splits <= PKD_FUSED_MAX_SPLITS: one launch; each (sequence, kv
- *     head, 16 q heads) row is cut into at most num_splits pieces, and the
- *     last piece of a row to finish merges the row's partials (the combine of
- *     paged_decode_attn_reduce, in-kernel). workspace: as for the split-K
- *     calls (paged_decode_workspace_bytes). counters: uint32
- *     [num_seqs * num_q_heads] (num_seqs * num_kv_heads * ceil(group / 16)
- *     entries are used), all zero before the first call; every call leaves
- *     them zero again. Calls that share a counters array must not overlap.
- *   num_splits > PKD_FUSED_MAX_SPLITS: the split-K pass and the combine as
- *     two launches on `stream`; counters are not used.
+ * workspace and num_splits are extensions.
+ *   num_splits == 1: one wave per (sequence, kv head, 16 q heads) row writes
+ *     the output, as the non-split launcher does; workspace is not used
+ *     (may be null).
+ *   num_splits > 1: the split-K pass and the combine, as two launches on
+ *     `stream`; workspace as for the split-K calls
+ *     (paged_decode_workspace_bytes).
  * Sequences with seq_lens[b] == 0 get zeros. Other arguments and errors as
  * for the split-K calls; output must be 16-byte aligned. */
-#define PKD_FUSED_MAX_SPLITS 32u
-
 PKD_API int paged_decode_attn_bf16(const uint16_t* q, const uint16_t* k_cache,
                                    const uint16_t* v_cache, uint16_t* output,
                                    const int32_t* block_tables, const int32_t* seq_lens,
                                    uint32_t max_blocks_per_seq, uint32_t num_seqs,
                                    uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
                                    uint32_t block_size, float scale, uint32_t q_stride,
-                                   uint32_t sliding_window, float* workspace, uint32_t* counters,
-                                   uint32_t num_splits, hipStream_t stream);
+                                   uint32_t sliding_window, float* workspace, uint32_t num_splits,
+                                   hipStream_t stream);
 
 /* FP8-E4M3FN cache, as paged_decode_attn_splitk_fp8. */
 PKD_API int paged_decode_attn_fp8(const uint16_t* q, const uint8_t* k_cache,
@@ -242,8 +233,8 @@ PKD_API int paged_decode_attn_fp8(const uint16_t* q, const uint8_t* k_cache,
                                   uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
                                   uint32_t block_size, float scale, float k_scale, float v_scale,
                                   uint32_t q_stride, uint64_t cache_stride,
-                                  uint32_t sliding_window, float* workspace, uint32_t* counters,
-                                  uint32_t num_splits, hipStream_t stream);
+                                  uint32_t sliding_window, float* workspace, uint32_t num_splits,
+                                  hipStream_t stream);
 
 /* NVFP4 cache (paged_decode_attn_nvfp4 on the metrale page, extended). */
 PKD_API int paged_decode_attn_nvfp4(const uint16_t* q, const uint8_t* k_cache,
@@ -254,8 +245,7 @@ PKD_API int paged_decode_attn_nvfp4(const uint16_t* q, const uint8_t* k_cache,
                                     uint32_t head_dim, uint32_t block_size, float scale,
                                     uint32_t q_stride, uint64_t block_stride_bytes,
                                     uint64_t data_section_bytes, uint32_t sliding_window,
-                                    float* workspace, uint32_t* counters, uint32_t num_splits,
-                                    hipStream_t stream);
+                                    float* workspace, uint32_t num_splits, hipStream_t stream);
 
 /* ---------------------------------------------------------------- host helpers
  * Bytes of the split-K workspace: num_seqs*num_q_heads*num_splits*(head_dim+2)*4. */

@@ -50,11 +50,11 @@ _SIGNATURES = {
                                               _F32, _U32, _U32, _U64, _U64, _U32, _U32, _P]),
     "paged_decode_attn_reduce": (_INT, [_P, _P, _P, _U32, _U32, _U32, _U32, _P]),
     "paged_decode_attn_bf16": (_INT, [_P, _P, _P, _P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32,
-                                      _F32, _U32, _U32, _P, _P, _U32, _P]),
+                                      _F32, _U32, _U32, _P, _U32, _P]),
     "paged_decode_attn_fp8": (_INT, [_P, _P, _P, _P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32,
-                                     _F32, _F32, _F32, _U32, _U64, _U32, _P, _P, _U32, _P]),
+                                     _F32, _F32, _F32, _U32, _U64, _U32, _P, _U32, _P]),
     "paged_decode_attn_nvfp4": (_INT, [_P, _P, _P, _P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32,
-                                       _F32, _U32, _U64, _U64, _U32, _P, _P, _U32, _P]),
+                                       _F32, _U32, _U64, _U64, _U32, _P, _U32, _P]),
     "paged_decode_workspace_bytes": (ctypes.c_size_t, [_U32, _U32, _U32, _U32]),
     "paged_decode_num_splits": (_U32, [_U32, _U32, _U32, _U32, _U32, _U32, _U32]),
     "pkd_status_string": (ctypes.c_char_p, [_INT]),
@@ -221,42 +221,40 @@ def paged_decode_num_splits(num_seqs, num_q_heads, num_kv_heads, max_blocks_per_
                                              num_cus))
 
 
-# ---------------------------------------------------------------- single-launch decode
+# ---------------------------------------------------------------- whole decode
 
 def paged_decode_attn_bf16(q, k_cache, v_cache, output, block_tables, seq_lens,
                            max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads, head_dim,
                            block_size, scale, q_stride, sliding_window=0, workspace=None,
-                           counters=None, num_splits=1, stream=None):
-    _need_gpu(q, k_cache, v_cache, output, block_tables, seq_lens, workspace, counters)
+                           num_splits=1, stream=None):
+    _need_gpu(q, k_cache, v_cache, output, block_tables, seq_lens, workspace)
     _check(lib().paged_decode_attn_bf16(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(output), _ptr(block_tables), _ptr(seq_lens),
         max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
-        float(scale), q_stride, sliding_window, _ptr(workspace), _ptr(counters), num_splits,
+        float(scale), q_stride, sliding_window, _ptr(workspace), num_splits,
         _stream(q, stream)), "paged_decode_attn_bf16")
 
 
 def paged_decode_attn_fp8(q, k_cache, v_cache, output, block_tables, seq_lens,
                           max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads, head_dim,
                           block_size, scale, k_scale, v_scale, q_stride, cache_stride,
-                          sliding_window=0, workspace=None, counters=None, num_splits=1,
-                          stream=None):
-    _need_gpu(q, k_cache, v_cache, output, block_tables, seq_lens, workspace, counters)
+                          sliding_window=0, workspace=None, num_splits=1, stream=None):
+    _need_gpu(q, k_cache, v_cache, output, block_tables, seq_lens, workspace)
     _check(lib().paged_decode_attn_fp8(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(output), _ptr(block_tables), _ptr(seq_lens),
         max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
         float(scale), float(k_scale), float(v_scale), q_stride, cache_stride, sliding_window,
-        _ptr(workspace), _ptr(counters), num_splits, _stream(q, stream)), "paged_decode_attn_fp8")
+        _ptr(workspace), num_splits, _stream(q, stream)), "paged_decode_attn_fp8")
 
 
 def paged_decode_attn_nvfp4(q, k_cache, v_cache, output, block_tables, seq_lens,
                             max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads, head_dim,
                             block_size, scale, q_stride, block_stride_bytes, data_section_bytes,
-                            sliding_window=0, workspace=None, counters=None, num_splits=1,
-                            stream=None):
-    _need_gpu(q, k_cache, v_cache, output, block_tables, seq_lens, workspace, counters)
+                            sliding_window=0, workspace=None, num_splits=1, stream=None):
+    _need_gpu(q, k_cache, v_cache, output, block_tables, seq_lens, workspace)
     _check(lib().paged_decode_attn_nvfp4(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(output), _ptr(block_tables), _ptr(seq_lens),
         max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
         float(scale), q_stride, block_stride_bytes, data_section_bytes, sliding_window,
-        _ptr(workspace), _ptr(counters), num_splits, _stream(q, stream)),
+        _ptr(workspace), num_splits, _stream(q, stream)),
         "paged_decode_attn_nvfp4")

@@ -36,9 +36,6 @@ enum Fmt { kBf16 = 0, kFp8 = 1, kNvfp4 = 2 };
 // Largest growth of a head's max (log2 units) absorbed without rescaling.
 constexpr float kLazyMax = 8.0f;
 
-// Single-launch decode: most pieces per row merged in-kernel (more split
-// counts run the split-K pass and the combine as two launches).
-constexpr int kFuseMaxSplits = int(PKD_FUSED_MAX_SPLITS);
 
 struct DecodeArgs {
   const uint16_t* q;
@@ -62,8 +59,7 @@ struct DecodeArgs {
   uint32_t window;
   uint32_t num_seqs;
   uint32_t chunk_min;      // least tiles per wave (at most S pieces per row)
-  uint16_t* out;           // single-launch decode: BF16 output (null for the split-K call)
-  uint32_t* counters;      // single-launch decode: finished pieces per row
+  uint16_t* out;           // non-split decode (num_splits 1): BF16 output, else null
 };
 
 // Two FP8-E4M3FN codes (bytes 0/1 or 2/3 of w) -> packed BF16 pair, in one
@@ -140,14 +136,6 @@ __device__ __forceinline__ void wave_lds_fence() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Cache policy of the single-launch decode's workspace traffic between
-// waves: sc1, the device-scope policy (the memory model gives relaxed
-// device-scope atomics the same bit). Such stores write through the XCD's L2
-// and such loads do not hit stale L2 lines, so partials move between XCDs
-// without a device-scope fence, which would write back and invalidate the
-// whole L2.
-constexpr int kSc1 = 16;
-
 // ---------------------------------------------------------------------------
 // K and V tiles stream into an LDS ring with direct-to-LDS buffer loads
 // (gfx950 LDS DMA, 16 bytes per lane). Each load instruction moves whole rows
@@ -203,7 +191,6 @@ struct LdsTraits {
   __device__ static constexpr int bswz(int r) { return (r / BSWZ_DIV) % BCPR; }
   static constexpr int STAGE = FMT == kBf16 ? 16 : 16 * BRB;   // BF16 copy of a quantized V tile
   static_assert(WAIT < 64, "vmcnt range");
-  static_assert(NBUF * SLOT >= (32 * kFuseMaxSplits + 16) * 4, "the ring also holds the combine weights");
 };
 
 // s_waitcnt that waits for vmcnt <= N only (expcnt / lgkmcnt left at their maximum).
@@ -330,113 +317,6 @@ __device__ __forceinline__ void stage_v(lds_u8* vt, lds_u8* stage, int lane, uin
   }
 }
 
-// Single-launch decode: the last piece of row (b, kh) to finish merges the
-// row's np workspace slots into the BF16 output, as the combine pass does
-// (weights l_i e^(m_i - M), 1e-20 guard, fixed slot order). The chunk's q
-// heads x dim pairs are spread over all 64 lanes, UC pairs per lane and SB
-// slots per round of loads; the weights pass through `wlds` (LDS the caller
-// no longer uses). Workspace reads carry the device-scope cache policy.
-template <int D>
-__device__ __forceinline__ void combine_row(const DecodeArgs& a, uint32_t b, uint32_t kh,
-                                            uint32_t np, lds_u8* wlds) {
-  constexpr int MAXP = kFuseMaxSplits;
-  constexpr int UC = 4;                      // dim pairs per lane per pass
-  constexpr int SB = 4;                      // slots per round of loads
-  typedef __attribute__((address_space(3))) float lds_f32;
-  lds_f32* const wl = (lds_f32*)wlds;        // [16][MAXP]: m, then the weights
-  lds_f32* const ll = wl + 16 * MAXP;        // [16][MAXP]: l
-  lds_f32* const il = ll + 16 * MAXP;        // [16]: 1 / sum of the weights
-  const int lane = threadIdx.x & 63;
-  const uint32_t kvh = kh / a.head_chunks, hc = kh % a.head_chunks;
-  const uint32_t gc = min(16u, a.group - hc * 16);           // q heads of this chunk
-  const uint32_t qh0 = kvh * a.group + hc * 16;
-  const uint32_t hs = a.num_splits * (D + 2);                // floats per q head
-  const float* base = a.ws + (uint64_t(b) * a.num_q_heads + qh0) * hs;
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<float*>(base), 0, int(gc * hs * 4), 0x00020000);
-  {
-    // (m, l) of every (head, slot) pair, all loads in flight at once
-    u32x2 ml[16 * MAXP / 64];
-#pragma unroll
-    for (int k = 0; k < 16 * MAXP / 64; ++k) {
-      const uint32_t e = lane + 64 * k, h = e / np, i = e % np;
-      ml[k] = u32x2{0u, 0u};
-      if (e < gc * np)
-        ml[k] = __builtin_bit_cast(
-            u32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, int((h * hs + i * (D + 2) + D) * 4),
-                                                        0, kSc1));
-    }
-#pragma unroll
-    for (int k = 0; k < 16 * MAXP / 64; ++k) {
-      const uint32_t e = lane + 64 * k, h = e / np, i = e % np;
-      if (e < gc * np) {
-        wl[h * MAXP + i] = __uint_as_float(ml[k][0]);
-        ll[h * MAXP + i] = __uint_as_float(ml[k][1]);
-      }
-    }
-  }
-  wave_lds_fence();
-  if (uint32_t(lane) < gc) {
-    float M = -__builtin_inff();
-    for (uint32_t i = 0; i < np; ++i)
-      if (ll[lane * MAXP + i] > 0.0f) M = fmaxf(M, wl[lane * MAXP + i]);
-    float wsum = 0.0f;
-    for (uint32_t i = 0; i < np; ++i) {
-      const float l = ll[lane * MAXP + i];
-      const float w = l > 0.0f ? l * __builtin_amdgcn_exp2f((wl[lane * MAXP + i] - M) * kLog2e)
-                               : 0.0f;
-      wl[lane * MAXP + i] = w;
-      wsum += w;
-    }
-    il[lane] = 1.0f / fmaxf(wsum, 1e-20f);
-  }
-  wave_lds_fence();
-  const uint32_t units = gc * (D / 2);                        // (head, dim pair) units
-  for (uint32_t u0 = 0; u0 < units; u0 += 64 * UC) {
-    f32x2 acc[UC];
-#pragma unroll
-    for (int t = 0; t < UC; ++t) acc[t] = f32x2{0.f, 0.f};
-    for (uint32_t i0 = 0; i0 < np; i0 += SB) {
-      u32x2 v[UC][SB];
-#pragma unroll
-      for (int t = 0; t < UC; ++t) {
-        const uint32_t q = u0 + 64 * t + lane;
-        const uint32_t h = q / (D / 2), d2 = q % (D / 2);
-#pragma unroll
-        for (int k = 0; k < SB; ++k) {
-          v[t][k] = u32x2{0u, 0u};
-          if (q < units && i0 + k < np)
-            v[t][k] = __builtin_bit_cast(
-                u32x2, __builtin_amdgcn_raw_buffer_load_b64(
-                           rs, int((h * hs + (i0 + k) * (D + 2) + 2 * d2) * 4), 0, kSc1));
-        }
-      }
-#pragma unroll
-      for (int t = 0; t < UC; ++t) {
-        const uint32_t q = u0 + 64 * t + lane;
-        const uint32_t h = min(q / (D / 2), 15u);
-#pragma unroll
-        for (int k = 0; k < SB; ++k) {
-          const float w = i0 + k < np ? wl[h * MAXP + i0 + k] : 0.0f;
-          acc[t][0] = fmaf(w, __uint_as_float(v[t][k][0]), acc[t][0]);
-          acc[t][1] = fmaf(w, __uint_as_float(v[t][k][1]), acc[t][1]);
-        }
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < UC; ++t) {
-      const uint32_t q = u0 + 64 * t + lane;
-      if (q < units) {
-        const uint32_t h = q / (D / 2), d2 = q % (D / 2);
-        const float inv = il[h];
-        *reinterpret_cast<uint32_t*>(a.out + (uint64_t(b) * a.num_q_heads + qh0 + h) * D + 2 * d2) =
-            pack_bf16x2(acc[t][0] * inv, acc[t][1] * inv);
-      }
-    }
-  }
-  wave_lds_fence();
-}
-
 // One row piece: tiles [tau0, tau1) of row (b, kh), partial state to `slot`.
 // With DS = 2 the workgroup's two waves split the head dim: wave w loads and
 // accumulates dims [w D/2, (w+1) D/2) of K, V, q and o, and the two halves of
@@ -446,7 +326,7 @@ template <int FMT, int D, int DS>
 __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D / DS, DS>& sh,
                                           lds_u8* xg, uint32_t& xturn, uint32_t b, uint32_t kh,
                                           uint32_t tau0, uint32_t tau1, uint32_t slot, bool last,
-                                          uint32_t L, uint32_t npieces) {
+                                          uint32_t L) {
   constexpr int DW = D / DS;                     // head dims of this wave
   using T = LdsTraits<FMT, DW, DS>;              // tile geometry of this wave's half rows
   using TF = LdsTraits<FMT, D>;                  // full rows (strides in the pools)
@@ -738,8 +618,9 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
   }
 
   const float l_tot = sum_over_rows(l_run);
-  if (a.out && npieces == 1) {
-    // the whole row in one piece: the normalized output goes straight to BF16
+  if (a.out) {
+    // non-split decode: the whole row in one piece, the normalized output
+    // straight to BF16
     if (head_ok) {
       const float inv = a.out_scale / l_tot;
       uint16_t* orow = a.out + (uint64_t(b) * a.num_q_heads + qh) * D + w * DW;
@@ -751,24 +632,7 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
     }
     return;
   }
-  if (head_ok && a.out) {
-    // single-launch decode: the partial goes out with the device-scope cache
-    // policy, so that the merging wave reads it from any XCD
-    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        wbase + uint64_t(slot) * (D + 2), 0, (D + 2) * 4, 0x00020000);
-    const float inv = a.out_scale / l_tot;
-#pragma unroll
-    for (int mt = 0; mt < DW / 16; ++mt) {
-      const u32x2 lo2 = {__float_as_uint(acc[mt][0] * inv), __float_as_uint(acc[mt][1] * inv)};
-      const u32x2 hi2 = {__float_as_uint(acc[mt][2] * inv), __float_as_uint(acc[mt][3] * inv)};
-      __builtin_amdgcn_raw_buffer_store_b64(lo2, rs, (w * DW + mt * 16 + 4 * g) * 4, 0, kSc1);
-      __builtin_amdgcn_raw_buffer_store_b64(hi2, rs, (w * DW + mt * 16 + 4 * g + 2) * 4, 0, kSc1);
-    }
-    if (g == 0 && w == 0) {
-      const u32x2 ml = {__float_as_uint(m_run * kLn2), __float_as_uint(l_tot)};
-      __builtin_amdgcn_raw_buffer_store_b64(ml, rs, D * 4, 0, kSc1);
-    }
-  } else if (head_ok) {
+  if (head_ok) {
     float* wrow = wbase + uint64_t(slot) * (D + 2);
     const float inv = a.out_scale / l_tot;
 #pragma unroll
@@ -784,33 +648,10 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
     }
     // the row ends in this piece: an end marker (l = -1) in the next slot
     // tells the combine to ignore that slot and all later ones
-    if (!a.out && last && g == 0 && w == 0 && slot + 1 < a.num_splits) {
+    if (last && g == 0 && w == 0 && slot + 1 < a.num_splits) {
       float* e = wbase + uint64_t(slot + 1) * (D + 2);
       e[D] = -__builtin_inff();
       e[D + 1] = -1.0f;
-    }
-  }
-  if (a.out) {
-    // single-launch decode: once the partial's stores have completed, count
-    // it in (device scope); the row's last piece to arrive merges all of them
-    // and clears the counter for the next call
-    const uint32_t R = a.num_kv_heads * a.head_chunks;
-    uint32_t* const cnt = a.counters + uint64_t(b) * R + kh;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
-    wait_vmcnt<0>();
-    if constexpr (DS > 1) {
-      // both halves stored before the count; the first wave counts and merges
-      asm volatile("s_barrier" ::: "memory");
-      if (w != 0) return;
-    }
-    uint32_t old = 0;
-    if (lane == 0)
-      old = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    old = __shfl(old, 0, 64);
-    if (old + 1 == npieces) {
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
-      combine_row<D>(a, b, kh, min(npieces, a.num_splits), ring3);
-      if (lane == 0) __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
@@ -852,13 +693,6 @@ __global__ __launch_bounds__(64 * kDSplit<D>, (kWavesPerSimd<FMT, D>)) void spli
   const uint32_t R = a.num_kv_heads * a.head_chunks;          // rows per sequence
   const uint32_t P = gridDim.x;
   const bool whole = a.num_splits == 1;                       // one wave per row
-  if (!whole && a.out && threadIdx.x < 64) {
-    // single-launch decode: sequences without keys get zeros here, as no
-    // piece covers them
-    for (uint32_t b = blockIdx.x; b < a.num_seqs; b += P)
-      if (a.seq_lens[b] <= 0)
-        for (uint32_t kh = 0; kh < R; ++kh) zero_row<D>(a, b, kh);
-  }
   // With at most 64 sequences, one length per lane, loaded once: the tile
   // counts, their prefix sums and every row lookup come from these registers.
   const bool cached = a.num_seqs <= 64;
@@ -911,9 +745,8 @@ __global__ __launch_bounds__(64 * kDSplit<D>, (kWavesPerSimd<FMT, D>)) void spli
     const uint32_t tau0 = whole ? 0u : pos - start;
     const uint32_t tau1 = whole ? n : min(n, end - start);
     const uint32_t slot = whole ? 0u : pos / c - start / c;
-    const uint32_t npieces = whole ? 1u : (start + n - 1) / c - start / c + 1;
     run_piece<FMT, D, DS>(a, mine, xg3, xturn, b, kh, tau0, tau1, slot,
-                          whole || start + n <= end, L, npieces);
+                          whole || start + n <= end, L);
     if (whole) break;
     pos = start + tau1;
   }
@@ -1018,6 +851,74 @@ __global__ __launch_bounds__(NT) void reduce_kernel(const float* ws, uint16_t* o
     const uint32_t packed = pack_bf16x2(sum[0] * inv, sum[1] * inv);
     *reinterpret_cast<uint32_t*>(o + 2 * tid) = packed;
   }
+}
+
+// Combine with at most 64 slots: one wave per (sequence, q head), every
+// reduction in registers. Lane i reads slot i's (m, l); the end marker and the
+// largest m come from a ballot and a cross-lane max, the sum of the weights is
+// taken in slot order. Lane c then sums float2 column c (and c + 64, ...) over
+// the slots in slot order, eight loads in flight: the same arithmetic, in the
+// same order, as the merged combine of the single-launch decode.
+template <int D>
+__global__ __launch_bounds__(64) void reduce_wave_kernel(const float* ws, uint16_t* out,
+                                                         const int32_t* seq_lens,
+                                                         uint32_t num_q_heads,
+                                                         uint32_t num_splits) {
+  constexpr int COLS = D / 2;                      // float2 columns of a slot
+  constexpr int NC = COLS >= 64 ? COLS / 64 : 1;   // columns per lane
+  const int lane = threadIdx.x;
+  const uint32_t bh = blockIdx.x;
+  const float* base = ws + uint64_t(bh) * num_splits * (D + 2);
+  uint16_t* o = out + uint64_t(bh) * D;
+  f32x2 ml = {-__builtin_inff(), 0.0f};
+  if (uint32_t(lane) < num_splits) ml = *reinterpret_cast<const f32x2*>(base + lane * (D + 2) + D);
+  const int32_t L = seq_lens[bh / num_q_heads];
+  const uint64_t marks = __builtin_amdgcn_ballot_w64(uint32_t(lane) < num_splits && ml[1] < 0.0f);
+  uint32_t stop = marks ? uint32_t(__builtin_ctzll(marks)) : num_splits;
+  if (L <= 0) stop = 0;
+  const bool live = uint32_t(lane) < stop && ml[1] > 0.0f;
+  const float M = wave_max(live ? ml[0] : -__builtin_inff());
+  if (M == -__builtin_inff()) {                    // no slot holds a key
+    for (int d = lane; d < D / 2; d += 64) reinterpret_cast<uint32_t*>(o)[d] = 0u;
+    return;
+  }
+  const float w = live ? ml[1] * __builtin_amdgcn_exp2f((ml[0] - M) * kLog2e) : 0.0f;
+  float wsum = 0.0f;
+  for (uint32_t i = 0; i < stop; ++i)
+    wsum += __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), int(i)));
+  f32x2 acc[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) acc[c] = f32x2{0.0f, 0.0f};
+  for (uint32_t i0 = 0; i0 < stop; i0 += 8) {
+    f32x2 v[8][NC];
+    float wi[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint32_t i = i0 + u;
+      // the slot's weight from its lane (a slot holding no keys weighs 0)
+      wi[u] = i < stop ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
+                                                       __builtin_bit_cast(int, w), int(i)))
+                       : 0.0f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        v[u][c] = f32x2{0.0f, 0.0f};
+        if (wi[u] != 0.0f && lane + 64 * c < COLS)
+          v[u][c] = *reinterpret_cast<const f32x2*>(base + i * (D + 2) + 2 * (lane + 64 * c));
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        acc[c][0] = fmaf(wi[u], v[u][c][0], acc[c][0]);
+        acc[c][1] = fmaf(wi[u], v[u][c][1], acc[c][1]);
+      }
+  }
+  const float inv = 1.0f / fmaxf(wsum, 1e-20f);
+#pragma unroll
+  for (int c = 0; c < NC; ++c)
+    if (lane + 64 * c < COLS)
+      reinterpret_cast<uint32_t*>(o)[lane + 64 * c] = pack_bf16x2(acc[c][0] * inv, acc[c][1] * inv);
 }
 
 static int launch_status() {
@@ -1131,7 +1032,6 @@ static DecodeArgs make_args(const uint16_t* q, const void* kc, const void* vc, f
   a.num_seqs = 0;
   a.chunk_min = 1;
   a.out = nullptr;
-  a.counters = nullptr;
   return a;
 }
 
@@ -1140,9 +1040,21 @@ static int launch_reduce(const float* workspace, uint16_t* output, const int32_t
                          uint32_t num_seqs, hipStream_t stream) {
   const uint64_t grid = uint64_t(num_seqs) * num_q_heads;
   if (grid > 0x7FFFFFFFull) return kUnsupported;
+  const dim3 gd = dim3(uint32_t(grid));
+  if (num_splits <= 64) {                      // one wave per (b, h), registers only
+    const dim3 bw = dim3(64);
+    switch (head_dim) {
+      case 64: hipLaunchKernelGGL((reduce_wave_kernel<64>), gd, bw, 0, stream, workspace, output, seq_lens, num_q_heads, num_splits); break;
+      case 128: hipLaunchKernelGGL((reduce_wave_kernel<128>), gd, bw, 0, stream, workspace, output, seq_lens, num_q_heads, num_splits); break;
+      case 256: hipLaunchKernelGGL((reduce_wave_kernel<256>), gd, bw, 0, stream, workspace, output, seq_lens, num_q_heads, num_splits); break;
+      case 512: hipLaunchKernelGGL((reduce_wave_kernel<512>), gd, bw, 0, stream, workspace, output, seq_lens, num_q_heads, num_splits); break;
+      default: return kUnsupported;
+    }
+    return launch_status();
+  }
   const size_t lds = 2 * size_t(num_splits) * sizeof(float);
   const bool wide = num_splits >= 64;          // many slots: more lanes per (b, h)
-  const dim3 gd = dim3(uint32_t(grid)), bd = dim3(wide ? 1024 : 256);
+  const dim3 bd = dim3(wide ? 1024 : 256);
 #define PKD_REDUCE(DD) \
   if (wide) hipLaunchKernelGGL((reduce_kernel<DD, 1024>), gd, bd, lds, stream, workspace, output, seq_lens, num_q_heads, num_splits); \
   else hipLaunchKernelGGL((reduce_kernel<DD, 256>), gd, bd, lds, stream, workspace, output, seq_lens, num_q_heads, num_splits);
@@ -1157,20 +1069,18 @@ static int launch_reduce(const float* workspace, uint16_t* output, const int32_t
   return launch_status();
 }
 
-// Single-launch decode: one wave per row (S = 1), the split pass with the
-// combine merged in (S <= kFuseMaxSplits), or the split pass and the combine
-// as two launches (more splits).
+// Non-split decode (num_splits 1): one wave per row writes the output. More
+// splits: the split-K pass and the combine, as two launches.
 template <int FMT>
-static int launch_decode(DecodeArgs a, uint16_t* output, uint32_t* counters, uint32_t num_seqs,
-                         uint32_t head_dim, hipStream_t stream) {
-  if (a.num_splits > uint32_t(kFuseMaxSplits)) {
+static int launch_decode(DecodeArgs a, uint16_t* output, uint32_t num_seqs, uint32_t head_dim,
+                         hipStream_t stream) {
+  if (a.num_splits > 1) {
     const int st = launch_splitk<FMT>(a, num_seqs, head_dim, stream);
     if (st) return st;
     return launch_reduce(a.ws, output, a.seq_lens, a.num_q_heads, head_dim, a.num_splits,
                          num_seqs, stream);
   }
   a.out = output;
-  a.counters = counters;
   return launch_splitk<FMT>(a, num_seqs, head_dim, stream);
 }
 
@@ -1244,18 +1154,18 @@ extern "C" PKD_API int paged_decode_attn_bf16(
     const int32_t* block_tables, const int32_t* seq_lens, uint32_t max_blocks_per_seq,
     uint32_t num_seqs, uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
     uint32_t block_size, float scale, uint32_t q_stride, uint32_t sliding_window,
-    float* workspace, uint32_t* counters, uint32_t num_splits, hipStream_t stream) {
+    float* workspace, uint32_t num_splits, hipStream_t stream) {
   if (num_seqs == 0) return kOk;
-  int st = check_single(q, k_cache, v_cache, output, workspace, counters, block_tables, seq_lens,
+  int st = check_single(q, k_cache, v_cache, output, workspace, block_tables, seq_lens,
                         max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, block_size,
-                        num_splits, q_stride, kFuseMaxSplits);
+                        num_splits, q_stride);
   if (st) return st;
   const uint64_t page_bytes = uint64_t(block_size) * num_kv_heads * head_dim * 2;
   DecodeArgs a = make_args(q, k_cache, v_cache, workspace, block_tables, seq_lens,
                            max_blocks_per_seq, num_q_heads, num_kv_heads, block_size,
                            scale * kLog2e, 1.0f, num_splits, q_stride, page_bytes, 0,
                            sliding_window);
-  return launch_decode<kBf16>(a, output, counters, num_seqs, head_dim, stream);
+  return launch_decode<kBf16>(a, output, num_seqs, head_dim, stream);
 }
 
 extern "C" PKD_API int paged_decode_attn_fp8(
@@ -1263,12 +1173,12 @@ extern "C" PKD_API int paged_decode_attn_fp8(
     const int32_t* block_tables, const int32_t* seq_lens, uint32_t max_blocks_per_seq,
     uint32_t num_seqs, uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
     uint32_t block_size, float scale, float k_scale, float v_scale, uint32_t q_stride,
-    uint64_t cache_stride, uint32_t sliding_window, float* workspace, uint32_t* counters,
-    uint32_t num_splits, hipStream_t stream) {
+    uint64_t cache_stride, uint32_t sliding_window, float* workspace, uint32_t num_splits,
+    hipStream_t stream) {
   if (num_seqs == 0) return kOk;
-  int st = check_single(q, k_cache, v_cache, output, workspace, counters, block_tables, seq_lens,
+  int st = check_single(q, k_cache, v_cache, output, workspace, block_tables, seq_lens,
                         max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, block_size,
-                        num_splits, q_stride, kFuseMaxSplits);
+                        num_splits, q_stride);
   if (st) return st;
   st = check_fp8_stride(num_kv_heads, head_dim, block_size, cache_stride);
   if (st) return st;
@@ -1276,7 +1186,7 @@ extern "C" PKD_API int paged_decode_attn_fp8(
                            max_blocks_per_seq, num_q_heads, num_kv_heads, block_size,
                            scale * k_scale * kLog2e, v_scale, num_splits, q_stride, cache_stride,
                            0, sliding_window);
-  return launch_decode<kFp8>(a, output, counters, num_seqs, head_dim, stream);
+  return launch_decode<kFp8>(a, output, num_seqs, head_dim, stream);
 }
 
 extern "C" PKD_API int paged_decode_attn_nvfp4(
@@ -1284,12 +1194,12 @@ extern "C" PKD_API int paged_decode_attn_nvfp4(
     const int32_t* block_tables, const int32_t* seq_lens, uint32_t max_blocks_per_seq,
     uint32_t num_seqs, uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
     uint32_t block_size, float scale, uint32_t q_stride, uint64_t block_stride_bytes,
-    uint64_t data_section_bytes, uint32_t sliding_window, float* workspace, uint32_t* counters,
-    uint32_t num_splits, hipStream_t stream) {
+    uint64_t data_section_bytes, uint32_t sliding_window, float* workspace, uint32_t num_splits,
+    hipStream_t stream) {
   if (num_seqs == 0) return kOk;
-  int st = check_single(q, k_cache, v_cache, output, workspace, counters, block_tables, seq_lens,
+  int st = check_single(q, k_cache, v_cache, output, workspace, block_tables, seq_lens,
                         max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, block_size,
-                        num_splits, q_stride, kFuseMaxSplits);
+                        num_splits, q_stride);
   if (st) return st;
   st = check_nvfp4_sections(num_kv_heads, head_dim, block_size, block_stride_bytes,
                             data_section_bytes);
@@ -1298,7 +1208,7 @@ extern "C" PKD_API int paged_decode_attn_nvfp4(
                            max_blocks_per_seq, num_q_heads, num_kv_heads, block_size,
                            scale * kLog2e, 1.0f, num_splits, q_stride, block_stride_bytes,
                            data_section_bytes, sliding_window);
-  return launch_decode<kNvfp4>(a, output, counters, num_seqs, head_dim, stream);
+  return launch_decode<kNvfp4>(a, output, num_seqs, head_dim, stream);
 }
 
 extern "C" PKD_API int paged_decode_attn_reduce(const float* workspace, uint16_t* output,

@@ -66,23 +66,19 @@ inline int check_decode(const void* q, const void* kc, const void* vc, const voi
   return kOk;
 }
 
-// Checks of the single-launch decode calls: the split-K checks, then the
-// output always, the workspace when num_splits > 1 and the counters when the
-// combine runs inside the launch (1 < num_splits <= fuse_max).
+// Checks of the whole-decode calls: the split-K checks (the workspace only
+// when num_splits > 1), then the output.
 inline int check_single(const void* q, const void* kc, const void* vc, const void* out,
-                        const void* ws, const void* counters, const void* bt, const void* lens,
+                        const void* ws, const void* bt, const void* lens,
                         uint32_t max_blocks_per_seq, uint32_t num_q_heads, uint32_t num_kv_heads,
                         uint32_t head_dim, uint32_t block_size, uint32_t num_splits,
-                        uint32_t q_stride, uint32_t fuse_max) {
+                        uint32_t q_stride) {
   static const uint64_t kAligned = 16;   // stands in for a workspace the call does not use
   const void* ws_or = num_splits > 1 ? ws : reinterpret_cast<const void*>(kAligned);
   const int st = check_decode(q, kc, vc, ws_or, bt, lens, max_blocks_per_seq, num_q_heads,
                               num_kv_heads, head_dim, block_size, num_splits, q_stride);
   if (st) return st;
   if (!out || !aligned16(out)) return kInvalid;
-  if (num_splits > 1 && num_splits <= fuse_max) {
-    if (!counters || (reinterpret_cast<uintptr_t>(counters) & 3u)) return kInvalid;
-  }
   return kOk;
 }
 

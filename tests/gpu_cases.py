@@ -113,8 +113,8 @@ class DeviceKV:
         return res
 
 
-    def decode_single(self, num_splits, q_bits=None, counters=None, out=None):
-        """The single-launch decode call; returns (output, counters)."""
+    def decode_single(self, num_splits, q_bits=None, out=None):
+        """The whole-decode call (one wave per row when num_splits is 1)."""
         w, g = self.w, self.geom
         B, Hq, Hkv, D, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
         q_bits = w.q_bits if q_bits is None else q_bits
@@ -125,14 +125,11 @@ class DeviceKV:
         if num_splits > 1:
             ws = torch.full((pkd.paged_decode_workspace_bytes(B, Hq, D, num_splits) // 4,),
                             float("nan"), dtype=torch.float32, device=dev())
-        if counters is None:
-            counters = torch.zeros(B * Hq, dtype=torch.int32, device=dev())
         if out is None:
             out = torch.full((B, Hq, D), float("nan"), dtype=torch.bfloat16, device=dev())
         common = (q, self.k, self.v, out, bt, lens, w.max_blocks_per_seq, B, Hq, Hkv, D, bs,
                   float(w.scale))
-        tail = dict(sliding_window=w.sliding_window, workspace=ws, counters=counters,
-                    num_splits=num_splits)
+        tail = dict(sliding_window=w.sliding_window, workspace=ws, num_splits=num_splits)
         if g.fmt == "bf16":
             pkd.paged_decode_attn_bf16(*common, Hq * D, **tail)
         elif g.fmt == "fp8":
@@ -142,7 +139,7 @@ class DeviceKV:
             stride, data = g.nvfp4_sections()
             pkd.paged_decode_attn_nvfp4(*common, Hq * D, stride, data, **tail)
         torch.cuda.synchronize()
-        return out.float().cpu().numpy().astype(np.float64), counters
+        return out.float().cpu().numpy().astype(np.float64)
 
 
 def oracle_pools(w, geom, k_scale=1.0, v_scale=1.0, seqs=None, fill=None):

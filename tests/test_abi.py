@@ -131,33 +131,31 @@ def test_fp8_nvfp4_specific_validation(lib):
     assert lib.paged_decode_attn_reduce(A16, A16, None, 4, 64, 1, 2, None) == -1
 
 
-def test_single_launch_validation(lib):
+def test_whole_decode_validation(lib):
     f = lib.paged_decode_attn_bf16
-    # q, k, v, out, bt, lens, maxb, B, Hq, Hkv, D, bs, scale, q_stride, W, ws, counters, S
-    base = [A16, A16, A16, A16, A16, A16, 4, 2, 4, 2, 64, 16, 0.125, 256, 0, A16, A16, 2, None]
+    # q, k, v, out, bt, lens, maxb, B, Hq, Hkv, D, bs, scale, q_stride, W, ws, S
+    base = [A16, A16, A16, A16, A16, A16, 4, 2, 4, 2, 64, 16, 0.125, 256, 0, A16, 2, None]
 
     def call(**kw):
         a = list(base)
         for k, v in kw.items():
-            a[{"out": 3, "ws": 15, "cnt": 16, "S": 17, "Hq": 8, "D": 10, "q": 0}[k]] = v
+            a[{"out": 3, "ws": 15, "S": 16, "Hq": 8, "D": 10, "q": 0}[k]] = v
         return f(*a)
 
     assert call(out=None) == -1                 # the output is always needed
     assert call(out=A16 + 8) == -1              # 16-byte aligned
-    assert call(cnt=None) == -1                 # merged combine: counters needed
-    assert call(cnt=A16 + 2) == -1              # 4-byte aligned
     assert call(ws=None) == -1                  # num_splits > 1: workspace needed
     assert call(S=0) == -2
     assert call(S=4097) == -2
     assert call(Hq=5) == -1
     assert call(D=96) == -2
     assert call(q=None) == -1
-    assert f(None, None, None, None, None, None, 4, 0, 4, 2, 64, 16, 0.125, 256, 0, None, None, 1,
+    assert f(None, None, None, None, None, None, 4, 0, 4, 2, 64, 16, 0.125, 256, 0, None, 1,
              None) == 0                         # no sequences: a no-op
     f8 = lib.paged_decode_attn_fp8
     assert f8(A16, A16, A16, A16, A16, A16, 4, 2, 4, 2, 64, 16, 0.125, 1.0, 1.0, 256,
-              16 * 2 * 64 - 16, 0, A16, A16, 2, None) == -1          # cache stride too short
+              16 * 2 * 64 - 16, 0, A16, 2, None) == -1               # cache stride too short
     n4 = lib.paged_decode_attn_nvfp4
     data = 16 * 2 * 64 // 2
     assert n4(A16, A16, A16, A16, A16, A16, 4, 2, 4, 2, 64, 16, 0.125, 256, data + 64, data, 0,
-              A16, A16, 2, None) == -1                                 # no room for the scales
+              A16, 2, None) == -1                                      # no room for the scales

@@ -341,16 +341,16 @@ def test_full_size_b1_long_context(name):
     _full_size(name, lambda w: [0])
 
 
-# ------------------------------------------------------------------ single-launch decode
+# ------------------------------------------------------------------ whole-decode call
 
 SINGLE_CASES = [CASES[i] for i in (1, 2, 6, 7, 9, 10, 13, 14, 15, 17, 19, 21, 23, 25)]
 
 
 @pytest.mark.parametrize("case", SINGLE_CASES,
                          ids=[f"{c[0]}-D{c[4]}-G{c[2]//c[3]}-bs{c[5]}-W{c[6]}" for c in SINGLE_CASES])
-def test_single_launch_matches_oracle(case):
-    """One wave per row (S=1), the merged combine (S <= 32, twice in a row:
-    the counters must come back to zero) and the two-launch form (S > 32)."""
+def test_whole_decode_matches_oracle(case):
+    """One wave per row (S=1, the non-split decode) and the split-K pass plus
+    the combine behind the one call (S > 1)."""
     fmt, lens, Hq, Hkv, D, bs, window, S = case
     w = workloads.make_workload("tiny", lens=lens, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
                                 block_size=bs, sliding_window=window, kv_dtype=fmt, seed=D + S)
@@ -359,88 +359,73 @@ def test_single_launch_matches_oracle(case):
     d = DeviceKV(w, geom, ks, vs)
     kc, vc = oracle_pools(w, geom, ks, vs)
     ref = oracle_decode(w, geom, kc, vc, ks, vs)
-    for n_splits in (1, 2, S, 32, 40):
-        counters = None
-        for rep in range(2):
-            got, counters = d.decode_single(n_splits, counters=counters)
-            assert_close(got, ref, f"{case} single S={n_splits} rep {rep}")
-            assert int(counters.abs().sum().item()) == 0
+    for n_splits in (1, 2, S, 40):
+        assert_close(d.decode_single(n_splits), ref, f"{case} whole decode S={n_splits}")
 
 
-def test_single_launch_empty_and_single_key():
+def test_whole_decode_empty_and_single_key():
     w = workloads.make_workload("tiny", lens=(0, 1, 0, 1, 300), num_q_heads=8, num_kv_heads=2,
                                 head_dim=128, seed=3)
     geom = geometry(w)
     d = DeviceKV(w, geom)
     V = oracle.bf16_to_f64(w.v_bits)
     for S in (1, 3, 17, 33):
-        got, _ = d.decode_single(S)
+        got = d.decode_single(S)
         assert np.all(got[[0, 2]] == 0)
         for i, b in enumerate((1, 3)):
             for h in range(8):
                 assert np.array_equal(got[b, h], V[i, h // 4])
 
 
-def test_single_launch_matches_split_k_bitwise():
-    """The merged combine weighs the same partials in the same slot order as
-    the combine pass: identical bits."""
-    w = workloads.make_workload("tiny", lens=(100, 513, 40, 7), num_q_heads=16, num_kv_heads=4,
-                                head_dim=128, seed=13)
-    d = DeviceKV(w, geometry(w))
-    for S in (2, 5, 17, 32):
-        a = d.decode(S)
-        b, _ = d.decode_single(S)
-        assert np.array_equal(a, b), S
-
-
-def test_single_launch_graph_replay():
+def test_whole_decode_graph_replay():
     """Captured once, replayed with eager work in between: every replay gives
-    the eager output (the counters reset themselves inside the launch)."""
+    the eager output, for the non-split form and the two-launch form."""
     w = workloads.make_workload("tiny", lens=(100, 513, 40, 7, 1200), num_q_heads=32,
                                 num_kv_heads=8, head_dim=128, seed=14)
     d = DeviceKV(w, geometry(w))
-    eager, counters = d.decode_single(9)
     B, Hq, D = w.num_seqs, w.num_q_heads, w.head_dim
     q = u16_to_dev(w.q_bits.reshape(-1))
     bt, lens = i32_to_dev(w.block_tables), i32_to_dev(w.seq_lens)
-    ws = torch.empty(pkd.paged_decode_workspace_bytes(B, Hq, D, 9) // 4, dtype=torch.float32,
-                     device=dev())
-    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev())
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.stream(s):
-        with torch.cuda.graph(graph, stream=s):
-            pkd.paged_decode_attn_bf16(q, d.k, d.v, out, bt, lens, w.max_blocks_per_seq, B, Hq,
-                                       w.num_kv_heads, D, w.block_size, float(w.scale), Hq * D,
-                                       0, ws, counters, 9)
-    torch.cuda.synchronize()
-    for rep in range(3):
-        out.fill_(float("nan"))
-        ws.fill_(float("nan"))
-        graph.replay()
+    for S in (1, 9):
+        eager = d.decode_single(S)
+        ws = torch.empty(pkd.paged_decode_workspace_bytes(B, Hq, D, S) // 4, dtype=torch.float32,
+                         device=dev())
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev())
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(graph, stream=s):
+                pkd.paged_decode_attn_bf16(q, d.k, d.v, out, bt, lens, w.max_blocks_per_seq, B,
+                                           Hq, w.num_kv_heads, D, w.block_size, float(w.scale),
+                                           Hq * D, 0, ws, S)
         torch.cuda.synchronize()
-        got = out.float().cpu().numpy().astype(np.float64)
-        assert np.array_equal(got, eager), rep
-        assert int(counters.abs().sum().item()) == 0
-        d.decode(3)                                      # eager work between replays
+        for rep in range(3):
+            out.fill_(float("nan"))
+            ws.fill_(float("nan"))
+            graph.replay()
+            torch.cuda.synchronize()
+            got = out.float().cpu().numpy().astype(np.float64)
+            assert np.array_equal(got, eager), (S, rep)
+            d.decode(3)                                      # eager work between replays
+        del graph
 
 
 @pytest.mark.parametrize("name", ["llama8b", "b1_32k"])
-def test_single_launch_full_size(name):
+def test_whole_decode_full_size(name):
     w = workloads.make_workload(name)
     geom = geometry(w)
     d = DeviceKV(w, geom)
     S = pkd.paged_decode_num_splits(w.num_seqs, w.num_q_heads, w.num_kv_heads,
                                     w.max_blocks_per_seq, w.block_size, w.sliding_window,
                                     _num_cus())
-    got, counters = d.decode_single(S)
-    assert int(counters.abs().sum().item()) == 0
     seqs = _spread(w) if w.num_seqs > 1 else [0]
     kc, vc = oracle_pools(w, geom, seqs=seqs)
     ref = oracle_decode(w, geom, kc, vc, seqs=seqs)
-    err = assert_close(got[seqs], ref, name)
-    print(f"[{name}] single launch num_splits={S} max_abs_err={err:.3e}", flush=True)
+    for n_splits in (1, S):
+        got = d.decode_single(n_splits)
+        err = assert_close(got[seqs], ref, f"{name} S={n_splits}")
+        print(f"[{name}] whole decode num_splits={n_splits} max_abs_err={err:.3e}", flush=True)
     del d
     torch.cuda.empty_cache()
 
@@ -463,7 +448,7 @@ def test_many_sequences(fmt, B, S):
     kc, vc = oracle_pools(w, geom, ks, vs)
     ref = oracle_decode(w, geom, kc, vc, ks, vs)
     assert_close(d.decode(S), ref, f"{fmt} B={B} split-K S={S}")
-    got, counters = d.decode_single(S)
-    assert_close(got, ref, f"{fmt} B={B} single launch S={S}")
-    assert int(counters.abs().sum().item()) == 0
-    assert np.all(got[w.seq_lens == 0] == 0)
+    for n_splits in (1, S):
+        got = d.decode_single(n_splits)
+        assert_close(got, ref, f"{fmt} B={B} whole decode S={n_splits}")
+        assert np.all(got[w.seq_lens == 0] == 0)
