@@ -1,9 +1,11 @@
 """Benchmark of one paged decode step on one MI355X.
 
-A step is the whole decode path for one attention layer over one batch:
-write the new token's K/V through slot_mapping (reshape_and_cache), run the
-split-KV pass, then the combine pass. The same step through the non-split
-decode (one wave per row, one launch, no combine) is timed beside it. Inputs are seeded
+A step is the whole decode path for one attention layer over one batch: the
+new token's K/V go into the cache, the split-KV pass runs, then the combine.
+The headline step does it in two launches (the split-K pass that appends the
+new token itself, then the combine); the same step with a separate
+reshape_and_cache launch, and the non-split decode (one wave per row), are
+timed beside it. Inputs are seeded
 synthetic tensors already resident in HBM. Steps rotate over several layers'
 KV pools whose total size is several times the 256 MB Infinity Cache, so
 every step reads its KV from HBM, as the layers of a model do. The timed loop
@@ -16,7 +18,7 @@ stream), and the float64 CPU oracle timed on the host.
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--extra NAME ...]
   python bench.py --copy-calibration      # plain copy of known size (for rocprof counters)
-  python bench.py --counter-run --workload NAME   # the split-K call alone (for rocprof counters)
+  python bench.py --counter-run --workload NAME   # the split-K append call alone (rocprof counters)
 """
 from __future__ import annotations
 
@@ -126,10 +128,10 @@ class Layers:
             self.k.append(kp)
             self.v.append(vp)
         last = w.last_token_index()
-        live = last >= 0
-        self.new_key = key[torch.from_numpy(last[live]).to(self.dev)].contiguous()
-        self.new_val = val[torch.from_numpy(last[live]).to(self.dev)].contiguous()
-        self.new_slots = slots[torch.from_numpy(last[live]).to(self.dev)].contiguous()
+        assert (last >= 0).all(), "every sequence of a decode step appends one token"
+        self.new_key = key[torch.from_numpy(last).to(self.dev)].contiguous()
+        self.new_val = val[torch.from_numpy(last).to(self.dev)].contiguous()
+        self.new_slots = slots[torch.from_numpy(last).to(self.dev)].contiguous()
         del key, val, slots
         self.q = u16(w.q_bits.reshape(-1))
         self.bt = torch.from_numpy(w.block_tables).to(self.dev)
@@ -186,8 +188,36 @@ class Layers:
         else:
             pkd.paged_decode_attn_nvfp4(*common, qs, self.block_stride, self.data_section, **tail)
 
+    def splitk_append(self, layer):
+        """The split-K pass that first appends each sequence's new token."""
+        import paged_kv_decode_splitk_amd as pkd
+        w = self.w
+        common = (self.q, self.new_key, self.new_val, self.k[layer], self.v[layer], self.ws,
+                  self.bt, self.lens, w.max_blocks_per_seq, w.num_q_heads, w.num_kv_heads,
+                  w.head_dim, w.block_size, float(w.scale), self.num_splits)
+        qs = w.num_q_heads * w.head_dim
+        if w.kv_dtype == "bf16":
+            pkd.paged_decode_attn_splitk_append_bf16(*common, qs, w.num_seqs, w.sliding_window)
+        elif w.kv_dtype == "fp8":
+            pkd.paged_decode_attn_splitk_append_fp8(*common, self.k_scale, self.v_scale, qs,
+                                                    self.page_units, w.num_seqs,
+                                                    w.sliding_window)
+        else:
+            pkd.paged_decode_attn_splitk_append_nvfp4(*common, qs, self.block_stride,
+                                                      self.data_section, w.num_seqs,
+                                                      w.sliding_window)
+
     def step(self, layer):
-        """Write the new token's K/V, the split-K pass, then the combine pass."""
+        """The decode step in two launches: the split-K pass that appends the
+        new token's K/V, then the combine pass."""
+        import paged_kv_decode_splitk_amd as pkd
+        w = self.w
+        self.splitk_append(layer)
+        pkd.paged_decode_attn_reduce(self.ws, self.out, self.lens, w.num_q_heads, w.head_dim,
+                                     self.num_splits, w.num_seqs)
+
+    def step_separate(self, layer):
+        """The decode step in three launches: cache write, split-K, combine."""
         import paged_kv_decode_splitk_amd as pkd
         w = self.w
         self._write(self.new_key, self.new_val, self.k[layer], self.v[layer], self.new_slots)
@@ -230,6 +260,7 @@ def time_workload(name, steps, warmup, kernel_reps=100, single=True):
     # warm up eagerly (also loads the code objects), then graphs of one step per layer
     for i in range(max(1, warmup)):
         lay.step(i % NL)
+        lay.step_separate(i % NL)
         if single:
             lay.step_single(i % NL)
     torch.cuda.synchronize()
@@ -238,11 +269,13 @@ def time_workload(name, steps, warmup, kernel_reps=100, single=True):
     t0 = time.perf_counter()
     ms_step = _graph_time(lay.step, NL, reps)
     wall = time.perf_counter() - t0
+    ms_sep = _graph_time(lay.step_separate, NL, reps)
     nan = float("nan")
     ms_single = _graph_time(lay.step_single, NL, reps) if single else nan
     # the kernels alone: back-to-back launches rotating over the layers
     single_ms = _graph_time(lambda i: lay.decode(i % NL), kernel_reps, 3) if single else nan
-    k_ms = _graph_time(lambda i: lay.splitk(i % NL), kernel_reps, 3)
+    k_ms = _graph_time(lambda i: lay.splitk_append(i % NL), kernel_reps, 3)
+    plain_ms = _graph_time(lambda i: lay.splitk(i % NL), kernel_reps, 3)
 
     kv_bytes = attended_tokens(w) * kv_bytes_per_token(w)
     gbs = lambda ms: kv_bytes / (ms * 1e-3) / 1e9
@@ -252,6 +285,8 @@ def time_workload(name, steps, warmup, kernel_reps=100, single=True):
         kv_pool_bytes_per_layer=lay.pool_bytes, attended_tokens=attended_tokens(w),
         kv_bytes_per_step=kv_bytes, steps=steps_run, ms_per_step=ms_step,
         us_per_step=ms_step * 1e3, kv_gbs=gbs(ms_step), wall_s=wall,
+        separate_write_us_per_step=ms_sep * 1e3, separate_write_kv_gbs=gbs(ms_sep),
+        splitk_plain_us=plain_ms * 1e3, splitk_plain_gbs=gbs(plain_ms),
         non_split_us_per_step=ms_single * 1e3, non_split_kv_gbs=gbs(ms_single),
         non_split_kernel_us=single_ms * 1e3, non_split_kernel_gbs=gbs(single_ms),
         splitk_us=k_ms * 1e3, splitk_gbs=gbs(k_ms),
@@ -263,15 +298,15 @@ def time_workload(name, steps, warmup, kernel_reps=100, single=True):
 
 
 def counter_run(name, calls=20):
-    """Only the split-K pass, `calls` times over the layers (for rocprofv3
-    counter passes, which profile every dispatch)."""
+    """Only the split-K pass with the append, `calls` times over the layers
+    (for rocprofv3 counter passes, which profile every dispatch)."""
     import torch
     import workloads
     w = workloads.make_workload(name)
     lay = Layers(w)
     torch.cuda.synchronize()
     for i in range(calls):
-        lay.splitk(i % lay.num_layers)
+        lay.splitk_append(i % lay.num_layers)
     torch.cuda.synchronize()
     print(json.dumps({"counter_run": name, "calls": calls, "num_splits": lay.num_splits,
                       "kv_bytes_per_call": attended_tokens(w) * kv_bytes_per_token(w)}))
@@ -385,6 +420,9 @@ def main():
     for name in args.extra:
         r, _ = time_workload(name, args.steps, args.warmup, single=not args.no_single)
         extras[name] = {k: r[k] for k in ("us_per_step", "kv_gbs", "pct_of_peak",
+                                          "separate_write_us_per_step",
+                                          "separate_write_kv_gbs",
+                                          "splitk_plain_us", "splitk_plain_gbs",
                                           "non_split_us_per_step",
                                           "non_split_kv_gbs",
                                           "non_split_kernel_us", "non_split_kernel_gbs",
@@ -393,9 +431,9 @@ def main():
         print(f"bench: {name} {r['us_per_step']:.2f} us/step {r['kv_gbs']:.0f} GB/s",
               file=sys.stderr, flush=True)
 
-    # the step's dominant kernel: the split-K pass
+    # the step's dominant kernel: the split-K pass (with the append)
     fmt = main_res["kv_dtype"]
-    kernel, us, tag = f"paged_decode_attn_splitk_{fmt}", main_res["splitk_us"], "splitk"
+    kernel, us, tag = f"paged_decode_attn_splitk_append_{fmt}", main_res["splitk_us"], "splitk"
     achieved = main_res["kv_bytes_per_step"] / (us * 1e-6) / 1e9
     traffic = traffic_record(args.workload, tag)
     roofline = dict(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s",
@@ -425,12 +463,15 @@ def main():
             "num_splits": main_res["num_splits"],
             "layers_rotated": main_res["layers_rotated"],
             "kv_bytes_per_step": main_res["kv_bytes_per_step"],
-            "step": "reshape_and_cache of the new token + split-KV pass + combine pass, "
-                    "HIP-graph replay",
+            "step": "split-KV pass that first appends the new token's K/V (the cache write) "
+                    "+ combine pass, HIP-graph replay",
         },
+        "separate_write_step": {k: main_res[k] for k in ("separate_write_us_per_step",
+                                                          "separate_write_kv_gbs")},
         "non_split_step": {k: main_res[k] for k in ("non_split_us_per_step",
                                                      "non_split_kv_gbs")},
-        "kernels": {k: main_res[k] for k in ("non_split_kernel_us", "non_split_kernel_gbs", "splitk_us",
+        "kernels": {k: main_res[k] for k in ("non_split_kernel_us", "non_split_kernel_gbs",
+                                             "splitk_plain_us", "splitk_plain_gbs", "splitk_us",
                                              "splitk_gbs")},
         "roofline": roofline,
         "cpu_baseline": cpu,

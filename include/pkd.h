@@ -186,6 +186,43 @@ PKD_API int paged_decode_attn_splitk_nvfp4(const uint16_t* q, const uint8_t* k_c
                                            uint64_t data_section_bytes, uint32_t num_seqs,
                                            uint32_t sliding_window, hipStream_t stream);
 
+/* ---------------------------------------------------------------- split-K with append
+ * The decode step's cache write and split-K pass in one launch, for the usual
+ * decode case where every sequence appends one token at its last position:
+ * the new token of sequence b (row b of `key` / `value`: num_kv_heads *
+ * head_dim BF16 values at key + b * key_stride) is written to position
+ * seq_lens[b] - 1, i.e. page block_tables[b][(L-1) / block_size], offset
+ * (L-1) % block_size, encoded exactly as reshape_and_cache_{bf16,fp8,nvfp4}
+ * encode it; then the same pass as paged_decode_attn_splitk_* runs over keys
+ * [lo, L), the new one included. Equivalent to reshape_and_cache_* of those
+ * tokens (slot_mapping[b] = that position's slot) followed by
+ * paged_decode_attn_splitk_*. Sequences with seq_lens[b] == 0 append
+ * nothing. Follow with paged_decode_attn_reduce. */
+PKD_API int paged_decode_attn_splitk_append_bf16(
+    const uint16_t* q, const uint16_t* key, const uint16_t* value, uint16_t* k_cache,
+    uint16_t* v_cache, float* workspace, const int32_t* block_tables, const int32_t* seq_lens,
+    uint32_t max_blocks_per_seq, uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
+    uint32_t block_size, float scale, uint32_t num_splits, uint32_t q_stride, uint32_t key_stride,
+    uint32_t value_stride, uint32_t num_seqs, uint32_t sliding_window, hipStream_t stream);
+
+/* FP8-E4M3FN cache: codes of x / k_scale and x / v_scale. */
+PKD_API int paged_decode_attn_splitk_append_fp8(
+    const uint16_t* q, const uint16_t* key, const uint16_t* value, uint8_t* k_cache,
+    uint8_t* v_cache, float* workspace, const int32_t* block_tables, const int32_t* seq_lens,
+    uint32_t max_blocks_per_seq, uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
+    uint32_t block_size, float scale, uint32_t num_splits, float k_scale, float v_scale,
+    uint32_t q_stride, uint32_t key_stride, uint32_t value_stride, uint64_t cache_stride,
+    uint32_t num_seqs, uint32_t sliding_window, hipStream_t stream);
+
+/* NVFP4 cache: E2M1 codes with one E4M3 scale per 16 values. */
+PKD_API int paged_decode_attn_splitk_append_nvfp4(
+    const uint16_t* q, const uint16_t* key, const uint16_t* value, uint8_t* k_cache,
+    uint8_t* v_cache, float* workspace, const int32_t* block_tables, const int32_t* seq_lens,
+    uint32_t max_blocks_per_seq, uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
+    uint32_t block_size, float scale, uint32_t num_splits, uint32_t q_stride, uint32_t key_stride,
+    uint32_t value_stride, uint64_t block_stride_bytes, uint64_t data_section_bytes,
+    uint32_t num_seqs, uint32_t sliding_window, hipStream_t stream);
+
 /* ---------------------------------------------------------------- combine
  * Merge the split partials of every (b, h) into output BF16
  * [num_seqs][num_q_heads][head_dim] (contiguous), one combine for every cache

@@ -21,7 +21,9 @@ __all__ = [
     "LIB_PATH", "lib", "reshape_and_cache_bf16", "reshape_and_cache_fp8",
     "reshape_and_cache_nvfp4", "bf16_absmax", "paged_decode_attn_splitk_bf16",
     "paged_decode_attn_splitk_fp8", "paged_decode_attn_splitk_nvfp4",
-    "paged_decode_attn_reduce", "paged_decode_attn_bf16", "paged_decode_attn_fp8",
+    "paged_decode_attn_reduce", "paged_decode_attn_splitk_append_bf16",
+    "paged_decode_attn_splitk_append_fp8", "paged_decode_attn_splitk_append_nvfp4",
+    "paged_decode_attn_bf16", "paged_decode_attn_fp8",
     "paged_decode_attn_nvfp4", "paged_decode_workspace_bytes", "paged_decode_num_splits",
     "pkd_status_string", "EXPORTED_SYMBOLS", "PkdError",
 ]
@@ -49,6 +51,15 @@ _SIGNATURES = {
     "paged_decode_attn_splitk_nvfp4": (_INT, [_P, _P, _P, _P, _P, _P, _U32, _U32, _U32, _U32, _U32,
                                               _F32, _U32, _U32, _U64, _U64, _U32, _U32, _P]),
     "paged_decode_attn_reduce": (_INT, [_P, _P, _P, _U32, _U32, _U32, _U32, _P]),
+    "paged_decode_attn_splitk_append_bf16": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _U32, _U32,
+                                                    _U32, _U32, _U32, _F32, _U32, _U32, _U32,
+                                                    _U32, _U32, _U32, _P]),
+    "paged_decode_attn_splitk_append_fp8": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _U32, _U32,
+                                                   _U32, _U32, _U32, _F32, _U32, _F32, _F32,
+                                                   _U32, _U32, _U32, _U64, _U32, _U32, _P]),
+    "paged_decode_attn_splitk_append_nvfp4": (_INT, [_P, _P, _P, _P, _P, _P, _P, _P, _U32, _U32,
+                                                     _U32, _U32, _U32, _F32, _U32, _U32, _U32,
+                                                     _U32, _U64, _U64, _U32, _U32, _P]),
     "paged_decode_attn_bf16": (_INT, [_P, _P, _P, _P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32,
                                       _F32, _U32, _U32, _P, _U32, _P]),
     "paged_decode_attn_fp8": (_INT, [_P, _P, _P, _P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32,
@@ -258,3 +269,53 @@ def paged_decode_attn_nvfp4(q, k_cache, v_cache, output, block_tables, seq_lens,
         float(scale), q_stride, block_stride_bytes, data_section_bytes, sliding_window,
         _ptr(workspace), num_splits, _stream(q, stream)),
         "paged_decode_attn_nvfp4")
+
+
+# ---------------------------------------------------------------- split-K with append
+
+def paged_decode_attn_splitk_append_bf16(q, key, value, k_cache, v_cache, workspace,
+                                         block_tables, seq_lens, max_blocks_per_seq, num_q_heads,
+                                         num_kv_heads, head_dim, block_size, scale, num_splits,
+                                         q_stride, num_seqs, sliding_window=0, key_stride=None,
+                                         value_stride=None, stream=None):
+    _need_gpu(q, key, value, k_cache, v_cache, workspace, block_tables, seq_lens)
+    ks = num_kv_heads * head_dim if key_stride is None else key_stride
+    vs = num_kv_heads * head_dim if value_stride is None else value_stride
+    _check(lib().paged_decode_attn_splitk_append_bf16(
+        _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(workspace),
+        _ptr(block_tables), _ptr(seq_lens), max_blocks_per_seq, num_q_heads, num_kv_heads,
+        head_dim, block_size, float(scale), num_splits, q_stride, ks, vs, num_seqs,
+        sliding_window, _stream(q, stream)), "paged_decode_attn_splitk_append_bf16")
+
+
+def paged_decode_attn_splitk_append_fp8(q, key, value, k_cache, v_cache, workspace, block_tables,
+                                        seq_lens, max_blocks_per_seq, num_q_heads, num_kv_heads,
+                                        head_dim, block_size, scale, num_splits, k_scale, v_scale,
+                                        q_stride, cache_stride, num_seqs, sliding_window=0,
+                                        key_stride=None, value_stride=None, stream=None):
+    _need_gpu(q, key, value, k_cache, v_cache, workspace, block_tables, seq_lens)
+    ks = num_kv_heads * head_dim if key_stride is None else key_stride
+    vs = num_kv_heads * head_dim if value_stride is None else value_stride
+    _check(lib().paged_decode_attn_splitk_append_fp8(
+        _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(workspace),
+        _ptr(block_tables), _ptr(seq_lens), max_blocks_per_seq, num_q_heads, num_kv_heads,
+        head_dim, block_size, float(scale), num_splits, float(k_scale), float(v_scale), q_stride,
+        ks, vs, cache_stride, num_seqs, sliding_window, _stream(q, stream)),
+        "paged_decode_attn_splitk_append_fp8")
+
+
+def paged_decode_attn_splitk_append_nvfp4(q, key, value, k_cache, v_cache, workspace,
+                                          block_tables, seq_lens, max_blocks_per_seq,
+                                          num_q_heads, num_kv_heads, head_dim, block_size, scale,
+                                          num_splits, q_stride, block_stride_bytes,
+                                          data_section_bytes, num_seqs, sliding_window=0,
+                                          key_stride=None, value_stride=None, stream=None):
+    _need_gpu(q, key, value, k_cache, v_cache, workspace, block_tables, seq_lens)
+    ks = num_kv_heads * head_dim if key_stride is None else key_stride
+    vs = num_kv_heads * head_dim if value_stride is None else value_stride
+    _check(lib().paged_decode_attn_splitk_append_nvfp4(
+        _ptr(q), _ptr(key), _ptr(value), _ptr(k_cache), _ptr(v_cache), _ptr(workspace),
+        _ptr(block_tables), _ptr(seq_lens), max_blocks_per_seq, num_q_heads, num_kv_heads,
+        head_dim, block_size, float(scale), num_splits, q_stride, ks, vs, block_stride_bytes,
+        data_section_bytes, num_seqs, sliding_window, _stream(q, stream)),
+        "paged_decode_attn_splitk_append_nvfp4")

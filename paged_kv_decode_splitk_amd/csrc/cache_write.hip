@@ -51,20 +51,7 @@ __device__ __forceinline__ void write_rows(const WriteArgs& a, const uint16_t* s
     uint8_t* dst = cache + page_base + uint64_t(off) * row;
     for (uint32_t c = threadIdx.x; c < row / 8; c += blockDim.x) {
       const u32x4 v = *reinterpret_cast<const u32x4*>(src + row_base_elem + c * 8);
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const uint32_t w = v[i];
-        const uint32_t c0 = scale == 0.0f ? 0u : e4m3_from_f32(bf16_lo(w) / scale);
-        const uint32_t c1 = scale == 0.0f ? 0u : e4m3_from_f32(bf16_hi(w) / scale);
-        const uint32_t pair = c0 | (c1 << 8);
-        if (i < 2) lo |= pair << (16 * i);
-        else hi |= pair << (16 * (i - 2));
-      }
-      u32x2 out;
-      out[0] = lo;
-      out[1] = hi;
-      *reinterpret_cast<u32x2*>(dst + c * 8) = out;
+      *reinterpret_cast<u32x2*>(dst + c * 8) = fp8_encode8(v, scale);
     }
   } else {
     uint8_t* data = cache + page_base + uint64_t(off) * (row / 2);
@@ -72,30 +59,8 @@ __device__ __forceinline__ void write_rows(const WriteArgs& a, const uint16_t* s
     for (uint32_t g = threadIdx.x; g < row / 16; g += blockDim.x) {
       const u32x4 v0 = *reinterpret_cast<const u32x4*>(src + row_base_elem + g * 16);
       const u32x4 v1 = *reinterpret_cast<const u32x4*>(src + row_base_elem + g * 16 + 8);
-      float x[16];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x[2 * i] = bf16_lo(v0[i]);
-        x[2 * i + 1] = bf16_hi(v0[i]);
-        x[8 + 2 * i] = bf16_lo(v1[i]);
-        x[8 + 2 * i + 1] = bf16_hi(v1[i]);
-      }
-      float amax = 0.0f;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) amax = fmaxf(amax, __builtin_fabsf(x[i]));
-      const uint32_t s_code = e4m3_from_f32(amax / 6.0f);
-      const float S = e4m3_to_f32(s_code);
-      uint32_t w0 = 0, w1 = 0;
-      if (S != 0.0f) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w0 |= e2m1_from_f32(x[i] / S) << (4 * i);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) w1 |= e2m1_from_f32(x[8 + i] / S) << (4 * i);
-      }
-      u32x2 out;
-      out[0] = w0;
-      out[1] = w1;
-      *reinterpret_cast<u32x2*>(data + g * 8) = out;
+      uint32_t s_code;
+      *reinterpret_cast<u32x2*>(data + g * 8) = nvfp4_encode16(v0, v1, s_code);
       scales[g] = uint8_t(s_code);
     }
   }

@@ -60,6 +60,14 @@ struct DecodeArgs {
   uint32_t num_seqs;
   uint32_t chunk_min;      // least tiles per wave (at most S pieces per row)
   uint16_t* out;           // non-split decode (num_splits 1): BF16 output, else null
+  // append: each sequence's new token, written to position L - 1 by the
+  // piece that ends the row, before that piece loads its last tile
+  const uint16_t* new_k;   // null: no append
+  const uint16_t* new_v;
+  uint32_t new_k_stride;   // elements between the rows of consecutive sequences
+  uint32_t new_v_stride;
+  float enc_k_scale;       // FP8 cache encode scales
+  float enc_v_scale;
 };
 
 // Two FP8-E4M3FN codes (bytes 0/1 or 2/3 of w) -> packed BF16 pair, in one
@@ -317,6 +325,40 @@ __device__ __forceinline__ void stage_v(lds_u8* vt, lds_u8* stage, int lane, uin
   }
 }
 
+// Append: this wave's half of the head dims (all of them when DS = 1) of
+// sequence b's new token, kv head kvh, into position L - 1 of its K and V
+// pages, encoded as reshape_and_cache_{bf16,fp8,nvfp4} encode it. Lanes 0-31
+// write K and lanes 32-63 write V. The caller waits for the stores before it
+// requests the tile that holds position L - 1.
+template <int FMT, int D, int DS>
+__device__ __forceinline__ void append_token(const DecodeArgs& a, uint32_t b, uint32_t kvh,
+                                             uint32_t L, int w, int lane) {
+  constexpr int DW = D / DS;
+  constexpr int PER = FMT == kNvfp4 ? 16 : 8;     // values a lane encodes
+  static_assert(DW / PER <= 32, "one lane half covers a row");
+  const int kv = lane >> 5, j = lane & 31;
+  if (j >= DW / PER) return;
+  const uint32_t pos = L - 1;
+  const uint32_t phys = uint32_t(a.block_tables[uint64_t(b) * a.max_blocks + pos / a.block_size]);
+  const uint64_t row = uint64_t(pos % a.block_size) * a.num_kv_heads + kvh;   // (offset, head)
+  const uint16_t* src = (kv ? a.new_v + uint64_t(b) * a.new_v_stride
+                            : a.new_k + uint64_t(b) * a.new_k_stride) + kvh * D + w * DW + PER * j;
+  uint8_t* const pool = const_cast<uint8_t*>(kv ? a.v_cache : a.k_cache) + uint64_t(phys) * a.page_bytes;
+  if constexpr (FMT == kBf16) {
+    *reinterpret_cast<u32x4*>(pool + (row * D + w * DW + 8 * j) * 2) =
+        *reinterpret_cast<const u32x4*>(src);
+  } else if constexpr (FMT == kFp8) {
+    *reinterpret_cast<u32x2*>(pool + row * D + w * DW + 8 * j) =
+        fp8_encode8(*reinterpret_cast<const u32x4*>(src), kv ? a.enc_v_scale : a.enc_k_scale);
+  } else {
+    uint32_t sc;
+    const u32x2 codes = nvfp4_encode16(*reinterpret_cast<const u32x4*>(src),
+                                       *reinterpret_cast<const u32x4*>(src + 8), sc);
+    *reinterpret_cast<u32x2*>(pool + row * (D / 2) + (w * DW) / 2 + 8 * j) = codes;
+    pool[a.data_section + row * (D / 16) + (w * DW) / 16 + j] = uint8_t(sc);
+  }
+}
+
 // One row piece: tiles [tau0, tau1) of row (b, kh), partial state to `slot`.
 // With DS = 2 the workgroup's two waves split the head dim: wave w loads and
 // accumulates dims [w D/2, (w+1) D/2) of K, V, q and o, and the two halves of
@@ -348,6 +390,9 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
   const uint32_t qh = kvh * a.group + head_in_group;
   float* const wbase = a.ws + (uint64_t(b) * a.num_q_heads + qh) * a.num_splits * (D + 2);
   const int32_t* bt = a.block_tables + uint64_t(b) * a.max_blocks;
+  // append: written now, waited for only when the row's last tile is requested
+  bool pend = a.new_k != nullptr && last;
+  if (pend) append_token<FMT, D, DS>(a, b, kvh, L, w, lane);
 
   // q as the B operand of the QK MFMAs: column n = head, dims 32c + 8g .. +8;
   // issued ahead of the tile loads, which only ever wait for later loads.
@@ -416,6 +461,12 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
     // page, which reads nothing either.
     auto issue = [&](int s, int kv, uint32_t t) {
       const bool live = t < ct1;
+      if (pend && live && t + 1 == t1) {
+        // the tile with the appended token: its stores must have landed
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        wait_vmcnt<0>();
+        pend = false;
+      }
       const uint32_t page = min(t / tpp, cpe - 1);
       const uint32_t phys = uint32_t(__builtin_amdgcn_readlane(bt_reg, int(page - cp)));
       const uint8_t* pool = kv ? a.v_cache : a.k_cache;
@@ -1032,6 +1083,12 @@ static DecodeArgs make_args(const uint16_t* q, const void* kc, const void* vc, f
   a.num_seqs = 0;
   a.chunk_min = 1;
   a.out = nullptr;
+  a.new_k = nullptr;
+  a.new_v = nullptr;
+  a.new_k_stride = 0;
+  a.new_v_stride = 0;
+  a.enc_k_scale = 1.0f;
+  a.enc_v_scale = 1.0f;
   return a;
 }
 
@@ -1146,6 +1203,78 @@ extern "C" PKD_API int paged_decode_attn_splitk_nvfp4(
                            max_blocks_per_seq, num_q_heads, num_kv_heads, block_size,
                            scale * kLog2e, 1.0f, num_splits, q_stride, block_stride_bytes,
                            data_section_bytes, sliding_window);
+  return launch_splitk<kNvfp4>(a, num_seqs, head_dim, stream);
+}
+
+extern "C" PKD_API int paged_decode_attn_splitk_append_bf16(
+    const uint16_t* q, const uint16_t* key, const uint16_t* value, uint16_t* k_cache,
+    uint16_t* v_cache, float* workspace, const int32_t* block_tables, const int32_t* seq_lens,
+    uint32_t max_blocks_per_seq, uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
+    uint32_t block_size, float scale, uint32_t num_splits, uint32_t q_stride, uint32_t key_stride,
+    uint32_t value_stride, uint32_t num_seqs, uint32_t sliding_window, hipStream_t stream) {
+  if (num_seqs == 0) return kOk;
+  int st = check_decode(q, k_cache, v_cache, workspace, block_tables, seq_lens,
+                        max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, block_size,
+                        num_splits, q_stride);
+  if (st) return st;
+  st = check_append(key, value, num_kv_heads, head_dim, key_stride, value_stride);
+  if (st) return st;
+  const uint64_t page_bytes = uint64_t(block_size) * num_kv_heads * head_dim * 2;
+  DecodeArgs a = make_args(q, k_cache, v_cache, workspace, block_tables, seq_lens,
+                           max_blocks_per_seq, num_q_heads, num_kv_heads, block_size,
+                           scale * kLog2e, 1.0f, num_splits, q_stride, page_bytes, 0,
+                           sliding_window);
+  a.new_k = key; a.new_v = value; a.new_k_stride = key_stride; a.new_v_stride = value_stride;
+  return launch_splitk<kBf16>(a, num_seqs, head_dim, stream);
+}
+
+extern "C" PKD_API int paged_decode_attn_splitk_append_fp8(
+    const uint16_t* q, const uint16_t* key, const uint16_t* value, uint8_t* k_cache,
+    uint8_t* v_cache, float* workspace, const int32_t* block_tables, const int32_t* seq_lens,
+    uint32_t max_blocks_per_seq, uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
+    uint32_t block_size, float scale, uint32_t num_splits, float k_scale, float v_scale,
+    uint32_t q_stride, uint32_t key_stride, uint32_t value_stride, uint64_t cache_stride,
+    uint32_t num_seqs, uint32_t sliding_window, hipStream_t stream) {
+  if (num_seqs == 0) return kOk;
+  int st = check_decode(q, k_cache, v_cache, workspace, block_tables, seq_lens,
+                        max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, block_size,
+                        num_splits, q_stride);
+  if (st) return st;
+  st = check_fp8_stride(num_kv_heads, head_dim, block_size, cache_stride);
+  if (st) return st;
+  st = check_append(key, value, num_kv_heads, head_dim, key_stride, value_stride);
+  if (st) return st;
+  DecodeArgs a = make_args(q, k_cache, v_cache, workspace, block_tables, seq_lens,
+                           max_blocks_per_seq, num_q_heads, num_kv_heads, block_size,
+                           scale * k_scale * kLog2e, v_scale, num_splits, q_stride, cache_stride,
+                           0, sliding_window);
+  a.new_k = key; a.new_v = value; a.new_k_stride = key_stride; a.new_v_stride = value_stride;
+  a.enc_k_scale = k_scale; a.enc_v_scale = v_scale;
+  return launch_splitk<kFp8>(a, num_seqs, head_dim, stream);
+}
+
+extern "C" PKD_API int paged_decode_attn_splitk_append_nvfp4(
+    const uint16_t* q, const uint16_t* key, const uint16_t* value, uint8_t* k_cache,
+    uint8_t* v_cache, float* workspace, const int32_t* block_tables, const int32_t* seq_lens,
+    uint32_t max_blocks_per_seq, uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
+    uint32_t block_size, float scale, uint32_t num_splits, uint32_t q_stride, uint32_t key_stride,
+    uint32_t value_stride, uint64_t block_stride_bytes, uint64_t data_section_bytes,
+    uint32_t num_seqs, uint32_t sliding_window, hipStream_t stream) {
+  if (num_seqs == 0) return kOk;
+  int st = check_decode(q, k_cache, v_cache, workspace, block_tables, seq_lens,
+                        max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, block_size,
+                        num_splits, q_stride);
+  if (st) return st;
+  st = check_nvfp4_sections(num_kv_heads, head_dim, block_size, block_stride_bytes,
+                            data_section_bytes);
+  if (st) return st;
+  st = check_append(key, value, num_kv_heads, head_dim, key_stride, value_stride);
+  if (st) return st;
+  DecodeArgs a = make_args(q, k_cache, v_cache, workspace, block_tables, seq_lens,
+                           max_blocks_per_seq, num_q_heads, num_kv_heads, block_size,
+                           scale * kLog2e, 1.0f, num_splits, q_stride, block_stride_bytes,
+                           data_section_bytes, sliding_window);
+  a.new_k = key; a.new_v = value; a.new_k_stride = key_stride; a.new_v_stride = value_stride;
   return launch_splitk<kNvfp4>(a, num_seqs, head_dim, stream);
 }
 

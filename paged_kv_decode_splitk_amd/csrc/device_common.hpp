@@ -87,6 +87,49 @@ __device__ __forceinline__ uint32_t e2m1_from_f32(float y) {
   return sign | c;
 }
 
+// Eight BF16 values (one 16-byte load) -> eight E4M3FN codes of x / scale
+// (IEEE float32 division; scale 0 gives code 0), little-endian in 8 bytes.
+__device__ __forceinline__ u32x2 fp8_encode8(u32x4 v, float scale) {
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t w = v[i];
+    const uint32_t c0 = scale == 0.0f ? 0u : e4m3_from_f32(bf16_lo(w) / scale);
+    const uint32_t c1 = scale == 0.0f ? 0u : e4m3_from_f32(bf16_hi(w) / scale);
+    const uint32_t pair = c0 | (c1 << 8);
+    if (i < 2) lo |= pair << (16 * i);
+    else hi |= pair << (16 * (i - 2));
+  }
+  return u32x2{lo, hi};
+}
+
+// One NVFP4 group: sixteen BF16 values (two 16-byte loads) -> eight code
+// bytes (element 2k in the low nibble of byte k) and the E4M3FN group scale
+// E4M3(amax / 6); a scale that decodes to 0 gives all-zero codes.
+__device__ __forceinline__ u32x2 nvfp4_encode16(u32x4 v0, u32x4 v1, uint32_t& scale_code) {
+  float x[16];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16_lo(v0[i]);
+    x[2 * i + 1] = bf16_hi(v0[i]);
+    x[8 + 2 * i] = bf16_lo(v1[i]);
+    x[8 + 2 * i + 1] = bf16_hi(v1[i]);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, __builtin_fabsf(x[i]));
+  scale_code = e4m3_from_f32(amax / 6.0f);
+  const float S = e4m3_to_f32(scale_code);
+  uint32_t w0 = 0, w1 = 0;
+  if (S != 0.0f) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w0 |= e2m1_from_f32(x[i] / S) << (4 * i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w1 |= e2m1_from_f32(x[8 + i] / S) << (4 * i);
+  }
+  return u32x2{w0, w1};
+}
+
 // Max / sum over the four 16-lane rows of a wave (lanes n, n+16, n+32, n+48),
 // with the gfx950 row-swap permutes (VALU only, no LDS round trip).
 __device__ __forceinline__ float max_over_rows(float x) {

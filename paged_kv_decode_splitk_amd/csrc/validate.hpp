@@ -82,6 +82,16 @@ inline int check_single(const void* q, const void* kc, const void* vc, const voi
   return kOk;
 }
 
+// The new-token rows of the append calls.
+inline int check_append(const void* key, const void* value, uint32_t num_kv_heads,
+                        uint32_t head_dim, uint32_t key_stride, uint32_t value_stride) {
+  const uint64_t row = uint64_t(num_kv_heads) * head_dim;
+  if (!key || !value || !aligned16(key) || !aligned16(value)) return kInvalid;
+  if (key_stride < row || value_stride < row || (key_stride % 8) || (value_stride % 8))
+    return kInvalid;
+  return kOk;
+}
+
 inline int check_reduce(const void* ws, const void* out, const void* lens, uint32_t num_q_heads,
                         uint32_t head_dim, uint32_t num_splits) {
   if (num_q_heads == 0) return kInvalid;

@@ -452,3 +452,88 @@ def test_many_sequences(fmt, B, S):
         got = d.decode_single(n_splits)
         assert_close(got, ref, f"{fmt} B={B} whole decode S={n_splits}")
         assert np.all(got[w.seq_lens == 0] == 0)
+
+
+# ------------------------------------------------------------------ split-K with append
+
+def _append_decode(w, geom, ks, vs, S):
+    """Pools holding every token but each sequence's last; the append call
+    writes the last ones and attends. Returns (output, device pools)."""
+    last = w.last_token_index()
+    keep = np.setdiff1d(np.arange(w.num_tokens), last[last >= 0])
+    d = DeviceKV(w, geom, ks, vs, tokens=keep)
+    B, Hq, Hkv, D, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    rows = np.zeros((B, Hkv * D), np.uint16)
+    rows_v = np.zeros((B, Hkv * D), np.uint16)
+    live = last >= 0
+    rows[live] = w.k_bits[last[live]].reshape(-1, Hkv * D)
+    rows_v[live] = w.v_bits[last[live]].reshape(-1, Hkv * D)
+    key, val = u16_to_dev(rows.reshape(-1)), u16_to_dev(rows_v.reshape(-1))
+    q = u16_to_dev(w.q_bits.reshape(-1))
+    bt, lens = i32_to_dev(w.block_tables), i32_to_dev(w.seq_lens)
+    ws = torch.full((pkd.paged_decode_workspace_bytes(B, Hq, D, S) // 4,), float("nan"),
+                    dtype=torch.float32, device=dev())
+    out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev())
+    common = (q, key, val, d.k, d.v, ws, bt, lens, w.max_blocks_per_seq, Hq, Hkv, D, bs,
+              float(w.scale), S)
+    if geom.fmt == "bf16":
+        pkd.paged_decode_attn_splitk_append_bf16(*common, Hq * D, B, w.sliding_window)
+    elif geom.fmt == "fp8":
+        pkd.paged_decode_attn_splitk_append_fp8(*common, ks, vs, Hq * D, geom.fp8_stride(), B,
+                                                w.sliding_window)
+    else:
+        stride, data = geom.nvfp4_sections()
+        pkd.paged_decode_attn_splitk_append_nvfp4(*common, Hq * D, stride, data, B,
+                                                  w.sliding_window)
+    pkd.paged_decode_attn_reduce(ws, out, lens, Hq, D, S, B)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), d
+
+
+APPEND_CASES = [
+    ("bf16", (1, 15, 16, 17, 100, 300), 8, 2, 128, 16, 0, 4),
+    ("bf16", (33, 0, 257, 1000), 40, 2, 128, 16, 0, 7),      # two head chunks, an empty row
+    ("bf16", (90, 400, 17), 6, 2, 64, 32, 37, 3),
+    ("bf16", (50, 180), 8, 1, 512, 16, 0, 2),                # head dim split over two waves
+    ("bf16", (300, 700), 8, 2, 128, 16, 0, 1),               # one wave per row
+    ("fp8", (1, 17, 300, 1000), 16, 8, 256, 16, 129, 5),
+    ("fp8", (40, 100), 16, 2, 512, 16, 0, 2),
+    ("nvfp4", (1, 17, 300, 700), 16, 2, 512, 16, 200, 4),
+    ("nvfp4", (40, 333), 8, 2, 64, 32, 0, 2),
+]
+
+
+@pytest.mark.parametrize("case", APPEND_CASES,
+                         ids=[f"{c[0]}-D{c[4]}-G{c[2]//c[3]}-bs{c[5]}-W{c[6]}-S{c[7]}"
+                              for c in APPEND_CASES])
+def test_split_k_append(case):
+    """The appended tokens land bit for bit where reshape_and_cache puts them,
+    and the output is bit for bit that of the separate write + split-K."""
+    fmt, lens, Hq, Hkv, D, bs, window, S = case
+    w = workloads.make_workload("tiny", lens=lens, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                                block_size=bs, sliding_window=window, kv_dtype=fmt, seed=D + S)
+    geom = geometry(w)
+    ks, vs = _fp8_small_scales(w) if fmt == "fp8" else (1.0, 1.0)
+    got, d = _append_decode(w, geom, ks, vs, S)
+    kc, vc = oracle_pools(w, geom, ks, vs)
+    assert np.array_equal(pool_to_np(d.k, fmt), kc) and np.array_equal(pool_to_np(d.v, fmt), vc)
+    ref = oracle_decode(w, geom, kc, vc, ks, vs)
+    assert_close(got, ref, f"append {case}")
+    full = DeviceKV(w, geom, ks, vs)
+    assert np.array_equal(got, full.decode(S))
+
+
+def test_split_k_append_full_size():
+    w = workloads.make_workload("llama8b")
+    geom = geometry(w)
+    S = pkd.paged_decode_num_splits(w.num_seqs, w.num_q_heads, w.num_kv_heads,
+                                    w.max_blocks_per_seq, w.block_size, w.sliding_window,
+                                    _num_cus())
+    got, d = _append_decode(w, geom, 1.0, 1.0, S)
+    seqs = _spread(w)
+    kc, vc = oracle_pools(w, geom, seqs=seqs)
+    ref = oracle_decode(w, geom, kc, vc, seqs=seqs)
+    err = assert_close(got[seqs], ref, "llama8b append")
+    print(f"[llama8b] append num_splits={S} max_abs_err={err:.3e}", flush=True)
+    del d
+    torch.cuda.empty_cache()
