@@ -159,3 +159,30 @@ def test_whole_decode_validation(lib):
     data = 16 * 2 * 64 // 2
     assert n4(A16, A16, A16, A16, A16, A16, 4, 2, 4, 2, 64, 16, 0.125, 256, data + 64, data, 0,
               A16, 2, None) == -1                                      # no room for the scales
+
+
+def test_append_validation(lib):
+    f = lib.paged_decode_attn_splitk_append_bf16
+    # q, key, value, kc, vc, ws, bt, lens, maxb, Hq, Hkv, D, bs, scale, S, q_stride, ks, vs, B, W
+    base = [A16, A16, A16, A16, A16, A16, A16, A16, 4, 4, 2, 64, 16, 0.125, 2, 256, 128, 128, 2, 0,
+            None]
+
+    def call(**kw):
+        a = list(base)
+        for k, v in kw.items():
+            a[{"key": 1, "value": 2, "ks": 16, "vs": 17, "B": 18, "D": 11}[k]] = v
+        return f(*a)
+
+    assert call(key=None) == -1
+    assert call(value=A16 + 4) == -1            # 16-byte aligned
+    assert call(ks=120) == -1                   # shorter than num_kv_heads * head_dim
+    assert call(vs=132) == -1                   # not a multiple of 8
+    assert call(D=96) == -2
+    assert call(B=0, key=None) == 0             # no sequences: a no-op
+    f8 = lib.paged_decode_attn_splitk_append_fp8
+    assert f8(A16, None, A16, A16, A16, A16, A16, A16, 4, 4, 2, 64, 16, 0.125, 2, 1.0, 1.0, 256,
+              128, 128, 2048, 2, 0, None) == -1
+    n4 = lib.paged_decode_attn_splitk_append_nvfp4
+    data = 16 * 2 * 64 // 2
+    assert n4(A16, A16, A16, A16, A16, A16, A16, A16, 4, 4, 2, 64, 16, 0.125, 2, 256, 128, 128,
+              data + 64, data, 2, 0, None) == -1                    # no room for the scales
