@@ -12,8 +12,9 @@ import torch
 import oracle
 import paged_kv_decode_splitk_amd as pkd
 import workloads
-from gpu_cases import (DeviceKV, POISON, assert_close, dev, fp8_scales, geometry, gpu_absmax,
-                       i32_to_dev, oracle_decode, oracle_pools, pool_to_np, u16_to_dev)
+from gpu_cases import (DeviceKV, POISON, alloc_pool, assert_close, dev, fp8_scales, geometry,
+                       gpu_absmax, i32_to_dev, oracle_decode, oracle_pools, pool_to_np,
+                       u16_to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -537,3 +538,60 @@ def test_split_k_append_full_size():
     print(f"[llama8b] append num_splits={S} max_abs_err={err:.3e}", flush=True)
     del d
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fmt,pad", [("fp8", 48), ("fp8", 4096), ("nvfp4", 32), ("nvfp4", 256)])
+def test_decode_padded_pages(fmt, pad):
+    """Pages with room between them (and NVFP4 scale sections that do not
+    follow the codes directly): the split-K pass, the whole-decode call and
+    the append call all address them through the strides."""
+    w = workloads.make_workload("tiny", lens=(30, 333, 1, 70), num_q_heads=8, num_kv_heads=2,
+                                head_dim=128, kv_dtype=fmt, seed=21)
+    rows = 16 * 2 * 128
+    if fmt == "fp8":
+        geom = geometry(w, cache_stride=rows + pad)
+        ks, vs = _fp8_small_scales(w)
+    else:
+        geom = geometry(w, data_section_bytes=rows // 2 + pad,
+                        block_stride_bytes=rows // 2 + pad + rows // 16 + pad)
+        ks = vs = 1.0
+    d = DeviceKV(w, geom, ks, vs)
+    kc, vc = oracle_pools(w, geom, ks, vs)
+    assert np.array_equal(pool_to_np(d.k, fmt), kc)
+    ref = oracle_decode(w, geom, kc, vc, ks, vs)
+    assert_close(d.decode(3), ref, f"{fmt} pad {pad} split-K")
+    assert_close(d.decode_single(1), ref, f"{fmt} pad {pad} non-split")
+    got, da = _append_decode(w, geom, ks, vs, 3)
+    assert np.array_equal(pool_to_np(da.k, fmt), kc) and np.array_equal(pool_to_np(da.v, fmt), vc)
+    assert_close(got, ref, f"{fmt} pad {pad} append")
+
+
+@pytest.mark.parametrize("fmt", ["bf16", "fp8", "nvfp4"])
+def test_cache_write_from_strided_rows(fmt):
+    """K and V as slices of a fused QKV row (key_stride, value_stride larger
+    than a row): the bytes written are those of the packed rows."""
+    w = workloads.make_workload("tiny", lens=(17, 40, 5), num_q_heads=8, num_kv_heads=2,
+                                head_dim=64, kv_dtype=fmt, sigma=1.5, seed=12)
+    geom = geometry(w)
+    ks, vs = _fp8_small_scales(w) if fmt == "fp8" else (1.0, 1.0)
+    Hq, Hkv, D, T = w.num_q_heads, w.num_kv_heads, w.head_dim, w.num_tokens
+    row = Hkv * D
+    width = Hq * D + 2 * row + 8                    # q | k | v | padding, per token
+    qkv = np.full((T, width), 0x7FC0, np.uint16)
+    qkv[:, Hq * D:Hq * D + row] = w.k_bits.reshape(T, row)
+    qkv[:, Hq * D + row:Hq * D + 2 * row] = w.v_bits.reshape(T, row)
+    buf = u16_to_dev(qkv.reshape(-1))
+    key, val = buf[Hq * D:], buf[Hq * D + row:]
+    kd, vd = alloc_pool(geom, POISON[fmt]), alloc_pool(geom, POISON[fmt])
+    slots = i32_to_dev(w.slot_mapping)
+    if fmt == "bf16":
+        pkd.reshape_and_cache_bf16(key, val, kd, vd, slots, Hkv, D, w.block_size, width, width)
+    elif fmt == "fp8":
+        pkd.reshape_and_cache_fp8(key, val, kd, vd, slots, Hkv, D, w.block_size, ks, vs,
+                                  key_stride=width, value_stride=width)
+    else:
+        pkd.reshape_and_cache_nvfp4(key, val, kd, vd, slots, Hkv, D, w.block_size,
+                                    key_stride=width, value_stride=width)
+    torch.cuda.synchronize()
+    kc, vc = oracle_pools(w, geom, ks, vs)
+    assert np.array_equal(pool_to_np(kd, fmt), kc) and np.array_equal(pool_to_np(vd, fmt), vc)
