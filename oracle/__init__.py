@@ -55,6 +55,8 @@ from .attention import (
     split_page_bound,
     split_partials,
     combine_partials,
+    query_range,
+    paged_prefill_attention,
 )
 
 __all__ = [
@@ -63,5 +65,6 @@ __all__ = [
     "nvfp4_encode_groups", "nvfp4_decode_groups", "CacheGeometry", "new_cache",
     "reshape_and_cache", "bf16_absmax", "read_kv_rows", "window_start",
     "paged_decode_attention", "attention_rows", "split_page_bound",
-    "split_partials", "combine_partials",
+    "split_partials", "combine_partials", "query_range",
+    "paged_prefill_attention",
 ]

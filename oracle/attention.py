@@ -141,3 +141,68 @@ def combine_partials(o: np.ndarray, m: np.ndarray, l: np.ndarray) -> np.ndarray:
     num = (w[..., None] * o).sum(axis=-2)
     den = np.maximum(w.sum(axis=-1), 1e-20)
     return num / den[..., None]
+
+
+def query_range(seq_len: int, q_len: int, i: int, causal: bool, sliding_window: int):
+    """Keys [lo, hi) that query token i of a q_len-token block attends.
+
+    Multi-token paged attention (chunked prefill, speculative verify) over the
+    same block table [pegainfer #1008: the paged prefill launch body; AstrAI
+    log: unified causal_offset, -1 = off, >= 0 = the first query position]:
+    the block's tokens are the sequence's newest, already in the cache, so in
+    a batch of ragged lengths the first query position of sequence b is
+    L_b - q_len and token i sits at p = L - q_len + i (R26). Causal: keys
+    0..p, the last W of them with a window W > 0. Not causal (the offset -1):
+    every token attends what a one-token decode of the sequence would,
+    [window_start(L, W), L). A token at a negative position attends nothing."""
+    if not causal:
+        return window_start(seq_len, sliding_window), seq_len
+    p = seq_len - q_len + i
+    hi = max(p + 1, 0)
+    lo = max(0, p + 1 - sliding_window) if sliding_window > 0 else 0
+    return min(lo, hi), hi
+
+
+def _prefill_q_rows(q_bits, b, i, Hq, D, q_stride, q_token_stride):
+    flat = np.asarray(q_bits, dtype=np.uint16).reshape(-1)
+    idx = b * q_stride + i * q_token_stride + np.arange(Hq)[:, None] * D + np.arange(D)[None, :]
+    return bf16_to_f64(flat[idx])
+
+
+def paged_prefill_attention(geom: CacheGeometry, q_bits, k_cache, v_cache, block_tables,
+                            seq_lens, num_q_heads, q_len, scale, causal=True, q_stride=None,
+                            q_token_stride=None, sliding_window=0, k_scale=1.0, v_scale=1.0,
+                            seqs=None, return_state=False):
+    """Exact output [len(seqs), q_len, Hq, D] (float64) of multi-token paged
+    attention: for each sequence and each of its q_len query tokens, gather
+    the token's key range (``query_range``) through the block table,
+    dequantize, softmax. q token i of sequence b is the BF16 row block at
+    b * q_stride + i * q_token_stride (elements; defaults: contiguous
+    [B, q_len, Hq, D]). With ``return_state`` also the largest scaled logit m
+    and the sum l of exp(s - m) of every query row (-inf and 0 when the row
+    attends nothing)."""
+    D = geom.head_dim
+    Hq = num_q_heads
+    G = Hq // geom.num_kv_heads
+    q_token_stride = Hq * D if q_token_stride is None else q_token_stride
+    q_stride = q_len * q_token_stride if q_stride is None else q_stride
+    seq_lens = np.asarray(seq_lens).reshape(-1)
+    seqs = list(range(len(seq_lens)) if seqs is None else seqs)
+    out = np.zeros((len(seqs), q_len, Hq, D))
+    m = np.full((len(seqs), q_len, Hq), -np.inf)
+    l = np.zeros((len(seqs), q_len, Hq))
+    for r, b in enumerate(seqs):
+        L = int(seq_lens[b])
+        for i in range(q_len):
+            lo, hi = query_range(L, q_len, i, causal, sliding_window)
+            K, V = _seq_kv(geom, k_cache, v_cache, block_tables, b, lo, hi, k_scale, v_scale)
+            q = _prefill_q_rows(q_bits, b, i, Hq, D, q_stride, q_token_stride)
+            out[r, i] = attention_rows(q, K, V, scale)
+            if return_state and hi > lo:
+                for h in range(Hq):
+                    s = (K[:, h // G, :] @ q[h]) * float(scale)
+                    m[r, i, h] = s.max()
+                    l[r, i, h] = np.exp(s - s.max()).sum()
+    if return_state:
+        return out, m, l
+    return out
