@@ -14,9 +14,12 @@ replays a HIP graph of one step per layer.
 Prints ONE JSON line: KV-read GB/s and us/step on the Llama-3-8B-shaped batch
 (B=32), the B=1 32K-context figures beside it, the roofline of the step's
 dominant kernel (back-to-back launches timed with HIP events on their
-stream), and the float64 CPU oracle timed on the host.
+stream), and the float64 CPU oracle timed on the host. Beside them: a causal
+query block of q_len tokens per sequence (speculative verify) over the same
+batch, through the multi-token call (--verify workload:q_len).
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--extra NAME ...]
+  python bench.py --verify-only --verify llama8b:4   # the multi-token call alone
   python bench.py --copy-calibration      # plain copy of known size (for rocprof counters)
   python bench.py --counter-run --workload NAME   # the split-K append call alone (rocprof counters)
 """
@@ -297,6 +300,96 @@ def time_workload(name, steps, warmup, kernel_reps=100, single=True):
     return res, w
 
 
+def verify_tokens(w, q_len) -> int:
+    """Keys the rows of a causal q_len-token block read: the whole sequence,
+    or with a window W the last W + q_len - 1 keys."""
+    L = w.seq_lens.astype(np.int64)
+    if w.sliding_window > 0:
+        return int(np.minimum(L, w.sliding_window + q_len - 1).sum())
+    return int(L.sum())
+
+
+class VerifyBlock:
+    """A causal q_len-token query block per sequence over a workload's
+    layers (speculative verify / chunked prefill): the multi-token call at
+    the split count the library's heuristic picks."""
+
+    def __init__(self, lay, q_len):
+        import torch
+        import paged_kv_decode_splitk_amd as pkd
+        import workloads
+        w = self.w = lay.w
+        self.lay, self.q_len = lay, q_len
+        B, Hq, D = w.num_seqs, w.num_q_heads, w.head_dim
+        qb = workloads.query_block(w, q_len, seed=1)
+        self.q = torch.from_numpy(qb.reshape(-1).view(np.int16)).to(lay.dev)
+        cus = torch.cuda.get_device_properties(lay.dev).multi_processor_count
+        self.num_splits = pkd.paged_prefill_num_splits(B, q_len, Hq, w.num_kv_heads,
+                                                       w.max_blocks_per_seq, w.block_size, True,
+                                                       w.sliding_window, cus)
+        self.ws = torch.empty(pkd.paged_decode_workspace_bytes(B, Hq * q_len, D,
+                                                               self.num_splits) // 4,
+                              dtype=torch.float32, device=lay.dev)
+        self.out = torch.empty((B, q_len, Hq, D), dtype=torch.bfloat16, device=lay.dev)
+
+    def call(self, layer):
+        import paged_kv_decode_splitk_amd as pkd
+        w, lay = self.w, self.lay
+        common = (self.q, lay.k[layer], lay.v[layer], self.out, lay.bt, lay.lens,
+                  w.max_blocks_per_seq, w.num_seqs, self.q_len, w.num_q_heads, w.num_kv_heads,
+                  w.head_dim, w.block_size, float(w.scale))
+        tail = dict(causal=True, sliding_window=w.sliding_window, workspace=self.ws,
+                    num_splits=self.num_splits)
+        if w.kv_dtype == "bf16":
+            pkd.paged_prefill_attn_bf16(*common, **tail)
+        elif w.kv_dtype == "fp8":
+            pkd.paged_prefill_attn_fp8(*common, lay.k_scale, lay.v_scale, lay.page_units, **tail)
+        else:
+            pkd.paged_prefill_attn_nvfp4(*common, lay.block_stride, lay.data_section, **tail)
+
+    def reduce(self, layer):
+        import paged_kv_decode_splitk_amd as pkd
+        w = self.w
+        pkd.paged_decode_attn_reduce(self.ws, self.out, self.lay.lens,
+                                     w.num_q_heads * self.q_len, w.head_dim, self.num_splits,
+                                     w.num_seqs)
+
+
+def time_verify(name, q_lens, steps, warmup, kernel_reps=100):
+    """us per multi-token call (split-K pass + combine, HIP-graph replay over
+    the layers) for each q_len, and the split-K pass alone (the call minus
+    the combine, both timed back to back)."""
+    import torch
+    import workloads
+    w = workloads.make_workload(name)
+    lay = Layers(w)
+    NL = lay.num_layers
+    res = {}
+    for n in q_lens:
+        vb = VerifyBlock(lay, n)
+        for i in range(max(1, warmup)):
+            vb.call(i % NL)
+        torch.cuda.synchronize()
+        reps = max(1, -(-steps // NL))
+        ms = _graph_time(vb.call, NL, reps)
+        red_ms = _graph_time(lambda i: vb.reduce(i % NL), kernel_reps, 3)
+        kv_bytes = verify_tokens(w, n) * kv_bytes_per_token(w)
+        split_us = (ms - red_ms) * 1e3
+        chunks = -(-(w.group * n) // 16)
+        res[f"{name}_q{n}"] = dict(
+            q_len=n, causal=True, num_splits=vb.num_splits, query_rows=w.num_seqs * n * w.num_q_heads,
+            column_chunks_per_kv_head=chunks, kv_bytes_per_step=kv_bytes,
+            us_per_step=ms * 1e3, kv_gbs=kv_bytes / (ms * 1e-3) / 1e9,
+            pct_of_peak=100.0 * kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            combine_us=red_ms * 1e3, splitk_us=split_us,
+            splitk_gbs=kv_bytes / (split_us * 1e-6) / 1e9,
+            query_tokens_per_s=w.num_seqs * n / (ms * 1e-3))
+        del vb
+    del lay
+    torch.cuda.empty_cache()
+    return res
+
+
 def counter_run(name, calls=20):
     """Only the split-K pass with the append, `calls` times over the layers
     (for rocprofv3 counter passes, which profile every dispatch)."""
@@ -395,6 +488,10 @@ def main():
     ap.add_argument("--no-single", action="store_true",
                     help="skip the non-split decode timings (profiles then see only the "
                          "split-K launches of the kernel)")
+    ap.add_argument("--verify", nargs="*", default=["llama8b:4", "llama8b:8"],
+                    help="multi-token (causal query block) timings, as workload:q_len")
+    ap.add_argument("--verify-only", action="store_true",
+                    help="only the --verify timings (for kernel statistics of that call)")
     ap.add_argument("--counter-run", action="store_true",
                     help="only run the split-K pass of --workload 20 times")
     args = ap.parse_args()
@@ -410,6 +507,13 @@ def main():
         return
     if args.counter_run:
         counter_run(args.workload)
+        return
+    if args.verify_only:
+        out = {}
+        for spec in args.verify:
+            nm, n = spec.split(":")
+            out.update(time_verify(nm, [int(n)], args.steps, args.warmup))
+        print(json.dumps({"verify": out}))
         return
     print(f"bench: {args.workload} steps={args.steps} warmup={args.warmup}", file=sys.stderr,
           flush=True)
@@ -430,6 +534,18 @@ def main():
                                           "kv_bytes_per_step", "layers_rotated")}
         print(f"bench: {name} {r['us_per_step']:.2f} us/step {r['kv_gbs']:.0f} GB/s",
               file=sys.stderr, flush=True)
+
+    verify = {}
+    by_name = {}
+    for spec in args.verify:
+        nm, n = spec.split(":")
+        by_name.setdefault(nm, []).append(int(n))
+    for nm, ns in by_name.items():
+        r = time_verify(nm, ns, args.steps, args.warmup)
+        for k, v in r.items():
+            print(f"bench: verify {k} {v['us_per_step']:.2f} us/step {v['kv_gbs']:.0f} GB/s",
+                  file=sys.stderr, flush=True)
+        verify.update(r)
 
     # the step's dominant kernel: the split-K pass (with the append)
     fmt = main_res["kv_dtype"]
@@ -478,6 +594,8 @@ def main():
     }
     for name, r in extras.items():
         line[name] = r
+    if verify:
+        line["verify"] = verify
     print(json.dumps(line))
 
 

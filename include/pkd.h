@@ -284,6 +284,81 @@ PKD_API int paged_decode_attn_nvfp4(const uint16_t* q, const uint8_t* k_cache,
                                     uint64_t data_section_bytes, uint32_t sliding_window,
                                     float* workspace, uint32_t num_splits, hipStream_t stream);
 
+/* ---------------------------------------------------------------- query blocks
+ * Multi-token paged attention over the same block table: q_len query tokens
+ * per sequence (chunked prefill, speculative verify), each attending the
+ * sequence's paged keys (pegainfer issue #1008, the paged prefill launch body
+ * of its Description; AstrAI csrc/tests commit log, the causal_offset,
+ * stride-addressing and layout bullets). The block is the sequence's newest
+ * q_len tokens, already written to the cache (a reshape_and_cache call
+ * first), so token i of sequence b sits at position p = seq_lens[b] - q_len
+ * + i, the per-sequence form of a causal offset that names the first query
+ * position.
+ *   causal != 0: token i attends keys max(0, p + 1 - W) .. p, W =
+ *     sliding_window (0: from key 0). A token with p < 0 gets zeros.
+ *   causal == 0 (the causal offset -1): every token attends what a
+ *     one-token decode would, keys [max(0, L - W), L).
+ * q: BF16, token i of sequence b at q + b*q_stride + i*q_token_stride
+ *   (elements, multiples of 8; q_token_stride >= num_q_heads*head_dim when
+ *   q_len > 1), heads head_dim apart, 16-byte aligned.
+ * output: BF16 [num_seqs][q_len][num_q_heads][head_dim], contiguous.
+ * num_splits == 1: one pass writes the output (workspace unused, may be
+ *   null). num_splits > 1: the split-K pass and the combine, two launches;
+ *   workspace of paged_decode_workspace_bytes(num_seqs, num_q_heads * q_len,
+ *   head_dim, num_splits) bytes, laid out [num_seqs][q_len][num_q_heads]
+ *   [num_splits][head_dim + 2] (the combine is paged_decode_attn_reduce with
+ *   num_q_heads * q_len query rows per sequence).
+ * The q heads of one kv head and the block's tokens share the kv head's one
+ * pass over its pages, group * q_len query rows per 16-column tile; blocks
+ * with group * q_len > 16 take ceil(group * q_len / 16) passes.
+ * Errors: as for the whole-decode calls; PKD_ERR_INVALID_ARG for q_len == 0 or a
+ * query stride too small, PKD_ERR_UNSUPPORTED for q_len > 4096. */
+PKD_API int paged_prefill_attn_bf16(const uint16_t* q, const uint16_t* k_cache,
+                                    const uint16_t* v_cache, uint16_t* output,
+                                    const int32_t* block_tables, const int32_t* seq_lens,
+                                    uint32_t max_blocks_per_seq, uint32_t num_seqs,
+                                    uint32_t q_len, uint32_t num_q_heads, uint32_t num_kv_heads,
+                                    uint32_t head_dim, uint32_t block_size, float scale,
+                                    uint32_t q_stride, uint32_t q_token_stride, uint32_t causal,
+                                    uint32_t sliding_window, float* workspace,
+                                    uint32_t num_splits, hipStream_t stream);
+
+/* FP8-E4M3FN cache: k_scale, v_scale and cache_stride as for
+ * paged_decode_attn_splitk_fp8. */
+PKD_API int paged_prefill_attn_fp8(const uint16_t* q, const uint8_t* k_cache,
+                                   const uint8_t* v_cache, uint16_t* output,
+                                   const int32_t* block_tables, const int32_t* seq_lens,
+                                   uint32_t max_blocks_per_seq, uint32_t num_seqs,
+                                   uint32_t q_len, uint32_t num_q_heads, uint32_t num_kv_heads,
+                                   uint32_t head_dim, uint32_t block_size, float scale,
+                                   float k_scale, float v_scale, uint32_t q_stride,
+                                   uint32_t q_token_stride, uint64_t cache_stride,
+                                   uint32_t causal, uint32_t sliding_window, float* workspace,
+                                   uint32_t num_splits, hipStream_t stream);
+
+/* NVFP4 cache: block_stride_bytes and data_section_bytes as for
+ * paged_decode_attn_splitk_nvfp4. */
+PKD_API int paged_prefill_attn_nvfp4(const uint16_t* q, const uint8_t* k_cache,
+                                     const uint8_t* v_cache, uint16_t* output,
+                                     const int32_t* block_tables, const int32_t* seq_lens,
+                                     uint32_t max_blocks_per_seq, uint32_t num_seqs,
+                                     uint32_t q_len, uint32_t num_q_heads, uint32_t num_kv_heads,
+                                     uint32_t head_dim, uint32_t block_size, float scale,
+                                     uint32_t q_stride, uint32_t q_token_stride,
+                                     uint64_t block_stride_bytes, uint64_t data_section_bytes,
+                                     uint32_t causal, uint32_t sliding_window, float* workspace,
+                                     uint32_t num_splits, hipStream_t stream);
+
+/* A split count for the query-block calls: paged_decode_num_splits with
+ * num_q_heads * q_len query heads and, for a causal window W, a window of
+ * W + q_len - 1 keys (the keys one row of the block can touch). Returns 1
+ * for q_len outside 1 .. 4096. */
+PKD_API uint32_t paged_prefill_num_splits(uint32_t num_seqs, uint32_t q_len,
+                                          uint32_t num_q_heads, uint32_t num_kv_heads,
+                                          uint32_t max_blocks_per_seq, uint32_t block_size,
+                                          uint32_t causal, uint32_t sliding_window,
+                                          uint32_t num_cus);
+
 /* ---------------------------------------------------------------- host helpers
  * Bytes of the split-K workspace: num_seqs*num_q_heads*num_splits*(head_dim+2)*4. */
 PKD_API size_t paged_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads,

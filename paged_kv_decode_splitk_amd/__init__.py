@@ -24,7 +24,9 @@ __all__ = [
     "paged_decode_attn_reduce", "paged_decode_attn_splitk_append_bf16",
     "paged_decode_attn_splitk_append_fp8", "paged_decode_attn_splitk_append_nvfp4",
     "paged_decode_attn_bf16", "paged_decode_attn_fp8",
-    "paged_decode_attn_nvfp4", "paged_decode_workspace_bytes", "paged_decode_num_splits",
+    "paged_decode_attn_nvfp4", "paged_prefill_attn_bf16", "paged_prefill_attn_fp8",
+    "paged_prefill_attn_nvfp4", "paged_prefill_num_splits",
+    "paged_decode_workspace_bytes", "paged_decode_num_splits",
     "pkd_status_string", "EXPORTED_SYMBOLS", "PkdError",
 ]
 
@@ -66,6 +68,15 @@ _SIGNATURES = {
                                      _F32, _F32, _F32, _U32, _U64, _U32, _P, _U32, _P]),
     "paged_decode_attn_nvfp4": (_INT, [_P, _P, _P, _P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32,
                                        _F32, _U32, _U64, _U64, _U32, _P, _U32, _P]),
+    "paged_prefill_attn_bf16": (_INT, [_P, _P, _P, _P, _P, _P, _U32, _U32, _U32, _U32, _U32,
+                                       _U32, _U32, _F32, _U32, _U32, _U32, _U32, _P, _U32, _P]),
+    "paged_prefill_attn_fp8": (_INT, [_P, _P, _P, _P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32,
+                                      _U32, _F32, _F32, _F32, _U32, _U32, _U64, _U32, _U32, _P,
+                                      _U32, _P]),
+    "paged_prefill_attn_nvfp4": (_INT, [_P, _P, _P, _P, _P, _P, _U32, _U32, _U32, _U32, _U32,
+                                        _U32, _U32, _F32, _U32, _U32, _U64, _U64, _U32, _U32, _P,
+                                        _U32, _P]),
+    "paged_prefill_num_splits": (_U32, [_U32, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _U32]),
     "paged_decode_workspace_bytes": (ctypes.c_size_t, [_U32, _U32, _U32, _U32]),
     "paged_decode_num_splits": (_U32, [_U32, _U32, _U32, _U32, _U32, _U32, _U32]),
     "pkd_status_string": (ctypes.c_char_p, [_INT]),
@@ -319,3 +330,62 @@ def paged_decode_attn_splitk_append_nvfp4(q, key, value, k_cache, v_cache, works
         head_dim, block_size, float(scale), num_splits, q_stride, ks, vs, block_stride_bytes,
         data_section_bytes, num_seqs, sliding_window, _stream(q, stream)),
         "paged_decode_attn_splitk_append_nvfp4")
+
+
+# ---------------------------------------------------------------- query blocks
+
+def _q_strides(num_q_heads, head_dim, q_len, q_stride, q_token_stride):
+    ts = num_q_heads * head_dim if q_token_stride is None else q_token_stride
+    qs = q_len * ts if q_stride is None else q_stride
+    return qs, ts
+
+
+def paged_prefill_attn_bf16(q, k_cache, v_cache, output, block_tables, seq_lens,
+                            max_blocks_per_seq, num_seqs, q_len, num_q_heads, num_kv_heads,
+                            head_dim, block_size, scale, causal=True, sliding_window=0,
+                            q_stride=None, q_token_stride=None, workspace=None, num_splits=1,
+                            stream=None):
+    _need_gpu(q, k_cache, v_cache, output, block_tables, seq_lens, workspace)
+    qs, ts = _q_strides(num_q_heads, head_dim, q_len, q_stride, q_token_stride)
+    _check(lib().paged_prefill_attn_bf16(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(output), _ptr(block_tables), _ptr(seq_lens),
+        max_blocks_per_seq, num_seqs, q_len, num_q_heads, num_kv_heads, head_dim, block_size,
+        float(scale), qs, ts, int(bool(causal)), sliding_window, _ptr(workspace), num_splits,
+        _stream(q, stream)), "paged_prefill_attn_bf16")
+
+
+def paged_prefill_attn_fp8(q, k_cache, v_cache, output, block_tables, seq_lens,
+                           max_blocks_per_seq, num_seqs, q_len, num_q_heads, num_kv_heads,
+                           head_dim, block_size, scale, k_scale, v_scale, cache_stride,
+                           causal=True, sliding_window=0, q_stride=None, q_token_stride=None,
+                           workspace=None, num_splits=1, stream=None):
+    _need_gpu(q, k_cache, v_cache, output, block_tables, seq_lens, workspace)
+    qs, ts = _q_strides(num_q_heads, head_dim, q_len, q_stride, q_token_stride)
+    _check(lib().paged_prefill_attn_fp8(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(output), _ptr(block_tables), _ptr(seq_lens),
+        max_blocks_per_seq, num_seqs, q_len, num_q_heads, num_kv_heads, head_dim, block_size,
+        float(scale), float(k_scale), float(v_scale), qs, ts, cache_stride, int(bool(causal)),
+        sliding_window, _ptr(workspace), num_splits, _stream(q, stream)),
+        "paged_prefill_attn_fp8")
+
+
+def paged_prefill_attn_nvfp4(q, k_cache, v_cache, output, block_tables, seq_lens,
+                             max_blocks_per_seq, num_seqs, q_len, num_q_heads, num_kv_heads,
+                             head_dim, block_size, scale, block_stride_bytes, data_section_bytes,
+                             causal=True, sliding_window=0, q_stride=None, q_token_stride=None,
+                             workspace=None, num_splits=1, stream=None):
+    _need_gpu(q, k_cache, v_cache, output, block_tables, seq_lens, workspace)
+    qs, ts = _q_strides(num_q_heads, head_dim, q_len, q_stride, q_token_stride)
+    _check(lib().paged_prefill_attn_nvfp4(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(output), _ptr(block_tables), _ptr(seq_lens),
+        max_blocks_per_seq, num_seqs, q_len, num_q_heads, num_kv_heads, head_dim, block_size,
+        float(scale), qs, ts, block_stride_bytes, data_section_bytes, int(bool(causal)),
+        sliding_window, _ptr(workspace), num_splits, _stream(q, stream)),
+        "paged_prefill_attn_nvfp4")
+
+
+def paged_prefill_num_splits(num_seqs, q_len, num_q_heads, num_kv_heads, max_blocks_per_seq,
+                             block_size, causal=True, sliding_window=0, num_cus=256) -> int:
+    return int(lib().paged_prefill_num_splits(num_seqs, q_len, num_q_heads, num_kv_heads,
+                                              max_blocks_per_seq, block_size, int(bool(causal)),
+                                              sliding_window, num_cus))

@@ -9,15 +9,17 @@
 // combine merges them into BF16 with a 1e-20 guard on the denominator.
 //
 // Work unit: one wavefront per piece of a (sequence, kv head, chunk of up to
-// 16 q heads of that kv head's group) row. All q heads sharing a kv head are
-// served by the one pass over its pages, so each K/V byte leaves HBM once per
-// step.
+// 16 query columns) row. A kv head's columns are its group's q heads, times
+// the q_len tokens of a query block (pegainfer issue #1008, the paged prefill
+// launch; AstrAI log, the unified causal offset): all of them are served by
+// the one pass over its pages, so each K/V byte leaves HBM once per step
+// while group * q_len <= 16. A causal column masks the keys after its token.
 //
 // Per 16-token tile (a page holds block_size/16 tiles):
 //  * K and V tiles stream from HBM into an LDS ring with direct-to-LDS buffer
 //    loads, one block-table lookup per tile.
-//  * S = K . Q^T on v_mfma_f32_16x16x32_bf16 (M = tokens, N = q heads, K =
-//    head_dim; q heads beyond the group are zero columns). FP8 / NVFP4 K codes
+//  * S = K . Q^T on v_mfma_f32_16x16x32_bf16 (M = keys, N = query columns,
+//    K = head_dim; columns beyond the group's are zero). FP8 / NVFP4 K codes
 //    are dequantized to BF16 in registers on their way from LDS to the MFMA
 //    (exact: every E4M3 value and every E2M1 x E4M3 product is a BF16 value).
 //  * Online softmax in fp32 on the MFMA output layout (lane l: head l%16,
@@ -35,6 +37,9 @@ enum Fmt { kBf16 = 0, kFp8 = 1, kNvfp4 = 2 };
 
 // Largest growth of a head's max (log2 units) absorbed without rescaling.
 constexpr float kLazyMax = 8.0f;
+// Starting reference max (log2 units): below any finite scaled logit that
+// matters, yet finite.
+constexpr float kMaxFloor = -3.0e38f;
 
 
 struct DecodeArgs {
@@ -48,7 +53,7 @@ struct DecodeArgs {
   uint32_t num_q_heads;
   uint32_t num_kv_heads;
   uint32_t group;          // q heads per kv head
-  uint32_t head_chunks;    // ceil(group / 16)
+  uint32_t head_chunks;    // ceil(group * q_len / 16): 16-column chunks of a kv head's queries
   uint32_t block_size;
   float logit_scale;       // scale * log2(e) (* k_scale for FP8)
   float out_scale;         // v_scale for FP8, 1 otherwise
@@ -56,7 +61,7 @@ struct DecodeArgs {
   uint32_t q_stride;
   uint64_t page_bytes;     // bytes per page of one pool
   uint64_t data_section;   // NVFP4: byte offset of the scales within a page
-  uint32_t window;
+  uint32_t window;         // keys of a row: the last `window` (0: all)
   uint32_t num_seqs;
   uint32_t chunk_min;      // least tiles per wave (at most S pieces per row)
   uint16_t* out;           // non-split decode (num_splits 1): BF16 output, else null
@@ -68,6 +73,12 @@ struct DecodeArgs {
   uint32_t new_v_stride;
   float enc_k_scale;       // FP8 cache encode scales
   float enc_v_scale;
+  // query blocks: q_len tokens per sequence, column c of a kv head's row is
+  // token c / group, q head c % group of the group
+  uint32_t q_len;          // 1 for decode
+  uint32_t q_tok_stride;   // elements between the rows of consecutive tokens
+  uint32_t causal;         // token i sits at L - q_len + i and sees keys up to it
+  uint32_t q_window;       // keys a token sees with causal: the last q_window up to it
 };
 
 // Two FP8-E4M3FN codes (bytes 0/1 or 2/3 of w) -> packed BF16 pair, in one
@@ -385,10 +396,21 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
   const uint32_t t0 = lo / 16 + tau0, t1 = lo / 16 + tau1;   // tiles of the sequence
   const uint32_t pa = t0 / tpp, pb = (t1 + tpp - 1) / tpp;
 
-  const uint32_t head_in_group = hc * 16 + n;
-  const bool head_ok = head_in_group < a.group;
-  const uint32_t qh = kvh * a.group + head_in_group;
-  float* const wbase = a.ws + (uint64_t(b) * a.num_q_heads + qh) * a.num_splits * (D + 2);
+  // column n: query token qi, q head qh; its output / workspace row qrow
+  const uint32_t col = hc * 16 + n;
+  const bool head_ok = col < a.group * a.q_len;
+  const uint32_t qi = head_ok ? col / a.group : 0u;
+  const uint32_t qh = kvh * a.group + (col - qi * a.group);
+  const uint64_t qrow = (uint64_t(b) * a.q_len + qi) * a.num_q_heads + qh;
+  float* const wbase = a.ws + qrow * a.num_splits * (D + 2);
+  // the keys [c_lo, c_hi) this column attends: the row's range, or with
+  // causal the keys up to the token's position (the last q_window of them)
+  uint32_t c_lo = lo, c_hi = L;
+  if (a.causal && head_ok) {
+    const int p1 = int(L) - int(a.q_len) + int(qi) + 1;     // position + 1
+    c_hi = p1 > 0 ? uint32_t(p1) : 0u;
+    c_lo = (a.q_window > 0 && c_hi > a.q_window) ? c_hi - a.q_window : 0u;
+  }
   const int32_t* bt = a.block_tables + uint64_t(b) * a.max_blocks;
   // append: written now, waited for only when the row's last tile is requested
   bool pend = a.new_k != nullptr && last;
@@ -399,11 +421,12 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
   u32x4 qf[DW / 32];
   float qup = 1.0f;            // NVFP4: logits of this head's dims are scaled by qup
   {
-    const uint16_t* qrow = a.q + uint64_t(b) * a.q_stride + uint64_t(qh) * D + w * DW;
+    const uint16_t* qsrc = a.q + uint64_t(b) * a.q_stride + uint64_t(qi) * a.q_tok_stride +
+                           uint64_t(qh) * D + w * DW;
 #pragma unroll
     for (int c = 0; c < DW / 32; ++c) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (head_ok) v = *reinterpret_cast<const u32x4*>(qrow + 32 * c + 8 * g);
+      if (head_ok) v = *reinterpret_cast<const u32x4*>(qsrc + 32 * c + 8 * g);
       qf[c] = v;
     }
     if constexpr (FMT == kNvfp4) {
@@ -444,7 +467,10 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
   f32x4 acc[DW / 16];
 #pragma unroll
   for (int mt = 0; mt < DW / 16; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -__builtin_inff();
+  // The reference max starts at a finite floor rather than -inf, so that a
+  // column whose keys in this piece are all masked keeps weights exp2(-inf -
+  // floor) = 0 and rescale factors 1 (never exp2(-inf + inf)).
+  float m_run = kMaxFloor;
   float l_run = 0.0f;
 
   // Segments of up to 64 pages: the block-table entries of a segment sit in
@@ -508,6 +534,7 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
         const uint32_t t = tb + s;               // t >= ct1: phantom tile, all keys masked
         const uint32_t tok0 = t * 16;
         const uint32_t khi = t < ct1 ? L : 0u;
+        const uint32_t c_khi = t < ct1 ? c_hi : 0u;
         lds_u8* const kt = ring3 + s * T::SLOT;
         lds_u8* const vt = kt + T::KV;
 
@@ -567,7 +594,7 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const uint32_t tok = tok0 + 4 * g + j;
-          sv[j] = (tok >= lo && tok < khi) ? sc[j] * a.logit_scale : -__builtin_inff();
+          sv[j] = (tok >= c_lo && tok < c_khi) ? sc[j] * a.logit_scale : -__builtin_inff();
           mx = fmaxf(mx, sv[j]);
         }
         mx = max_over_rows(mx);
@@ -669,12 +696,13 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
   }
 
   const float l_tot = sum_over_rows(l_run);
+  // a column without keys (l = 0) writes zeros
+  const float inv = l_tot > 0.0f ? a.out_scale / l_tot : 0.0f;
   if (a.out) {
     // non-split decode: the whole row in one piece, the normalized output
     // straight to BF16
     if (head_ok) {
-      const float inv = a.out_scale / l_tot;
-      uint16_t* orow = a.out + (uint64_t(b) * a.num_q_heads + qh) * D + w * DW;
+      uint16_t* orow = a.out + qrow * D + w * DW;
 #pragma unroll
       for (int mt = 0; mt < DW / 16; ++mt)
         *reinterpret_cast<u32x2*>(orow + 16 * mt + 4 * g) =
@@ -685,7 +713,6 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
   }
   if (head_ok) {
     float* wrow = wbase + uint64_t(slot) * (D + 2);
-    const float inv = a.out_scale / l_tot;
 #pragma unroll
     for (int mt = 0; mt < DW / 16; ++mt) {
       f32x2 lo2 = {acc[mt][0] * inv, acc[mt][1] * inv};
@@ -713,9 +740,11 @@ __device__ __forceinline__ void zero_row(const DecodeArgs& a, uint32_t b, uint32
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, n = lane & 15;
   const uint32_t kvh = kh / a.head_chunks, hc = kh % a.head_chunks;
-  const uint32_t head_in_group = hc * 16 + n;
-  if (head_in_group >= a.group) return;
-  uint16_t* orow = a.out + (uint64_t(b) * a.num_q_heads + kvh * a.group + head_in_group) * D;
+  const uint32_t col = hc * 16 + n;
+  if (col >= a.group * a.q_len) return;
+  const uint32_t qi = col / a.group;
+  uint16_t* orow =
+      a.out + ((uint64_t(b) * a.q_len + qi) * a.num_q_heads + kvh * a.group + col - qi * a.group) * D;
 #pragma unroll
   for (int mt = 0; mt < D / 16; ++mt) *reinterpret_cast<u32x2*>(orow + 16 * mt + 4 * g) = u32x2{0u, 0u};
 }
@@ -1089,6 +1118,10 @@ static DecodeArgs make_args(const uint16_t* q, const void* kc, const void* vc, f
   a.new_v_stride = 0;
   a.enc_k_scale = 1.0f;
   a.enc_v_scale = 1.0f;
+  a.q_len = 1;
+  a.q_tok_stride = 0;
+  a.causal = 0;
+  a.q_window = window;
   return a;
 }
 
@@ -1134,8 +1167,8 @@ static int launch_decode(DecodeArgs a, uint16_t* output, uint32_t num_seqs, uint
   if (a.num_splits > 1) {
     const int st = launch_splitk<FMT>(a, num_seqs, head_dim, stream);
     if (st) return st;
-    return launch_reduce(a.ws, output, a.seq_lens, a.num_q_heads, head_dim, a.num_splits,
-                         num_seqs, stream);
+    return launch_reduce(a.ws, output, a.seq_lens, a.num_q_heads * a.q_len, head_dim,
+                         a.num_splits, num_seqs, stream);
   }
   a.out = output;
   return launch_splitk<FMT>(a, num_seqs, head_dim, stream);
@@ -1338,6 +1371,104 @@ extern "C" PKD_API int paged_decode_attn_nvfp4(
                            scale * kLog2e, 1.0f, num_splits, q_stride, block_stride_bytes,
                            data_section_bytes, sliding_window);
   return launch_decode<kNvfp4>(a, output, num_seqs, head_dim, stream);
+}
+
+// Query-block arguments on top of the decode arguments: head_chunks over
+// the group's q_len x group columns, the row window widened for a causal
+// window (the first token's keys through the last token's).
+static void set_query_block(DecodeArgs& a, uint32_t q_len, uint32_t q_token_stride,
+                            uint32_t causal, uint32_t sliding_window) {
+  a.q_len = q_len;
+  a.q_tok_stride = q_token_stride;
+  a.causal = causal ? 1u : 0u;
+  a.q_window = sliding_window;
+  a.window = prefill_row_window(q_len, a.causal, sliding_window);
+  a.head_chunks = head_chunks(a.group * q_len);
+}
+
+extern "C" PKD_API int paged_prefill_attn_bf16(
+    const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, uint16_t* output,
+    const int32_t* block_tables, const int32_t* seq_lens, uint32_t max_blocks_per_seq,
+    uint32_t num_seqs, uint32_t q_len, uint32_t num_q_heads, uint32_t num_kv_heads,
+    uint32_t head_dim, uint32_t block_size, float scale, uint32_t q_stride,
+    uint32_t q_token_stride, uint32_t causal, uint32_t sliding_window, float* workspace,
+    uint32_t num_splits, hipStream_t stream) {
+  if (num_seqs == 0) return kOk;
+  int st = check_single(q, k_cache, v_cache, output, workspace, block_tables, seq_lens,
+                        max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, block_size,
+                        num_splits, q_stride);
+  if (st) return st;
+  st = check_prefill(q_len, num_q_heads, head_dim, q_stride, q_token_stride);
+  if (st) return st;
+  const uint64_t page_bytes = uint64_t(block_size) * num_kv_heads * head_dim * 2;
+  DecodeArgs a = make_args(q, k_cache, v_cache, workspace, block_tables, seq_lens,
+                           max_blocks_per_seq, num_q_heads, num_kv_heads, block_size,
+                           scale * kLog2e, 1.0f, num_splits, q_stride, page_bytes, 0,
+                           sliding_window);
+  set_query_block(a, q_len, q_token_stride, causal, sliding_window);
+  return launch_decode<kBf16>(a, output, num_seqs, head_dim, stream);
+}
+
+extern "C" PKD_API int paged_prefill_attn_fp8(
+    const uint16_t* q, const uint8_t* k_cache, const uint8_t* v_cache, uint16_t* output,
+    const int32_t* block_tables, const int32_t* seq_lens, uint32_t max_blocks_per_seq,
+    uint32_t num_seqs, uint32_t q_len, uint32_t num_q_heads, uint32_t num_kv_heads,
+    uint32_t head_dim, uint32_t block_size, float scale, float k_scale, float v_scale,
+    uint32_t q_stride, uint32_t q_token_stride, uint64_t cache_stride, uint32_t causal,
+    uint32_t sliding_window, float* workspace, uint32_t num_splits, hipStream_t stream) {
+  if (num_seqs == 0) return kOk;
+  int st = check_single(q, k_cache, v_cache, output, workspace, block_tables, seq_lens,
+                        max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, block_size,
+                        num_splits, q_stride);
+  if (st) return st;
+  st = check_prefill(q_len, num_q_heads, head_dim, q_stride, q_token_stride);
+  if (st) return st;
+  st = check_fp8_stride(num_kv_heads, head_dim, block_size, cache_stride);
+  if (st) return st;
+  DecodeArgs a = make_args(q, k_cache, v_cache, workspace, block_tables, seq_lens,
+                           max_blocks_per_seq, num_q_heads, num_kv_heads, block_size,
+                           scale * k_scale * kLog2e, v_scale, num_splits, q_stride, cache_stride,
+                           0, sliding_window);
+  set_query_block(a, q_len, q_token_stride, causal, sliding_window);
+  return launch_decode<kFp8>(a, output, num_seqs, head_dim, stream);
+}
+
+extern "C" PKD_API int paged_prefill_attn_nvfp4(
+    const uint16_t* q, const uint8_t* k_cache, const uint8_t* v_cache, uint16_t* output,
+    const int32_t* block_tables, const int32_t* seq_lens, uint32_t max_blocks_per_seq,
+    uint32_t num_seqs, uint32_t q_len, uint32_t num_q_heads, uint32_t num_kv_heads,
+    uint32_t head_dim, uint32_t block_size, float scale, uint32_t q_stride,
+    uint32_t q_token_stride, uint64_t block_stride_bytes, uint64_t data_section_bytes,
+    uint32_t causal, uint32_t sliding_window, float* workspace, uint32_t num_splits,
+    hipStream_t stream) {
+  if (num_seqs == 0) return kOk;
+  int st = check_single(q, k_cache, v_cache, output, workspace, block_tables, seq_lens,
+                        max_blocks_per_seq, num_q_heads, num_kv_heads, head_dim, block_size,
+                        num_splits, q_stride);
+  if (st) return st;
+  st = check_prefill(q_len, num_q_heads, head_dim, q_stride, q_token_stride);
+  if (st) return st;
+  st = check_nvfp4_sections(num_kv_heads, head_dim, block_size, block_stride_bytes,
+                            data_section_bytes);
+  if (st) return st;
+  DecodeArgs a = make_args(q, k_cache, v_cache, workspace, block_tables, seq_lens,
+                           max_blocks_per_seq, num_q_heads, num_kv_heads, block_size,
+                           scale * kLog2e, 1.0f, num_splits, q_stride, block_stride_bytes,
+                           data_section_bytes, sliding_window);
+  set_query_block(a, q_len, q_token_stride, causal, sliding_window);
+  return launch_decode<kNvfp4>(a, output, num_seqs, head_dim, stream);
+}
+
+extern "C" PKD_API uint32_t paged_prefill_num_splits(uint32_t num_seqs, uint32_t q_len,
+                                                     uint32_t num_q_heads, uint32_t num_kv_heads,
+                                                     uint32_t max_blocks_per_seq,
+                                                     uint32_t block_size, uint32_t causal,
+                                                     uint32_t sliding_window, uint32_t num_cus) {
+  if (q_len == 0 || q_len > kMaxQueryLen || uint64_t(num_q_heads) * q_len > 0x7FFFFFFFull)
+    return 1;
+  return num_splits_heuristic(num_seqs, num_q_heads * q_len, num_kv_heads, max_blocks_per_seq,
+                              block_size, prefill_row_window(q_len, causal, sliding_window),
+                              num_cus);
 }
 
 extern "C" PKD_API int paged_decode_attn_reduce(const float* workspace, uint16_t* output,

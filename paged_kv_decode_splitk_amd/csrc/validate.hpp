@@ -92,6 +92,28 @@ inline int check_append(const void* key, const void* value, uint32_t num_kv_head
   return kOk;
 }
 
+// The query block of the multi-token calls: q_len >= 1 tokens per sequence,
+// token rows q_token_stride elements apart inside a sequence's q_stride.
+constexpr uint32_t kMaxQueryLen = 4096;
+inline int check_prefill(uint32_t q_len, uint32_t num_q_heads, uint32_t head_dim,
+                         uint32_t q_stride, uint32_t q_token_stride) {
+  if (q_len == 0) return kInvalid;
+  if (q_len > kMaxQueryLen || uint64_t(num_q_heads) * q_len > 0x7FFFFFFFull) return kUnsupported;
+  const uint64_t row = uint64_t(num_q_heads) * head_dim;
+  if (q_token_stride % 8) return kInvalid;
+  if (q_len > 1 && q_token_stride < row) return kInvalid;
+  if (uint64_t(q_stride) < uint64_t(q_len - 1) * q_token_stride + row) return kInvalid;
+  return kOk;
+}
+
+// Keys one row of a query block may touch: with a causal window W the first
+// token's W keys plus the q_len - 1 after it; 0 (no bound) if that overflows.
+inline uint32_t prefill_row_window(uint32_t q_len, uint32_t causal, uint32_t sliding_window) {
+  if (!causal || sliding_window == 0) return sliding_window;
+  const uint64_t w = uint64_t(sliding_window) + q_len - 1;
+  return w > 0xFFFFFFFFull ? 0u : uint32_t(w);
+}
+
 inline int check_reduce(const void* ws, const void* out, const void* lens, uint32_t num_q_heads,
                         uint32_t head_dim, uint32_t num_splits) {
   if (num_q_heads == 0) return kInvalid;

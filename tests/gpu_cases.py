@@ -142,6 +142,38 @@ class DeviceKV:
         return out.float().cpu().numpy().astype(np.float64)
 
 
+    def prefill(self, q_bits, q_len, num_splits, causal=True, sliding_window=None,
+                q_stride=None, q_token_stride=None, return_ws=False, ws_fill=float("nan")):
+        """The multi-token call: q_bits holds q_len tokens per sequence."""
+        w, g = self.w, self.geom
+        B, Hq, Hkv, D, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+        window = w.sliding_window if sliding_window is None else sliding_window
+        q = u16_to_dev(np.asarray(q_bits).reshape(-1))
+        bt = i32_to_dev(w.block_tables)
+        lens = i32_to_dev(w.seq_lens)
+        ws = None
+        if num_splits > 1:
+            ws = torch.full((pkd.paged_decode_workspace_bytes(B, Hq * q_len, D, num_splits) // 4,),
+                            ws_fill, dtype=torch.float32, device=dev())
+        out = torch.full((B, q_len, Hq, D), float("nan"), dtype=torch.bfloat16, device=dev())
+        common = (q, self.k, self.v, out, bt, lens, w.max_blocks_per_seq, B, q_len, Hq, Hkv, D,
+                  bs, float(w.scale))
+        tail = dict(causal=causal, sliding_window=window, q_stride=q_stride,
+                    q_token_stride=q_token_stride, workspace=ws, num_splits=num_splits)
+        if g.fmt == "bf16":
+            pkd.paged_prefill_attn_bf16(*common, **tail)
+        elif g.fmt == "fp8":
+            pkd.paged_prefill_attn_fp8(*common, self.k_scale, self.v_scale, g.fp8_stride(), **tail)
+        else:
+            stride, data = g.nvfp4_sections()
+            pkd.paged_prefill_attn_nvfp4(*common, stride, data, **tail)
+        torch.cuda.synchronize()
+        res = out.float().cpu().numpy().astype(np.float64)
+        if return_ws:
+            return res, ws.cpu().numpy().reshape(B, q_len, Hq, num_splits, D + 2)
+        return res
+
+
 def oracle_pools(w, geom, k_scale=1.0, v_scale=1.0, seqs=None, fill=None):
     """Oracle pools written by the oracle's cache write (all tokens, or only
     the tokens of the sequences in ``seqs``)."""
@@ -190,3 +222,11 @@ def fp8_scales(w):
         v_ref = oracle.bf16_absmax(flat_v[i:i + step], v_ref)
     assert np.float32(k_gpu) == k_ref and np.float32(v_gpu) == v_ref
     return np.float32(k_ref) / np.float32(448.0), np.float32(v_ref) / np.float32(448.0)
+
+
+def oracle_prefill(w, geom, kc, vc, q_bits, q_len, causal=True, k_scale=1.0, v_scale=1.0,
+                   seqs=None, sliding_window=None, return_state=False):
+    return oracle.paged_prefill_attention(
+        geom, q_bits, kc, vc, w.block_tables, w.seq_lens, w.num_q_heads, q_len, w.scale,
+        causal=causal, sliding_window=w.sliding_window if sliding_window is None else sliding_window,
+        k_scale=k_scale, v_scale=v_scale, seqs=seqs, return_state=return_state)

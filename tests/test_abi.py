@@ -186,3 +186,48 @@ def test_append_validation(lib):
     data = 16 * 2 * 64 // 2
     assert n4(A16, A16, A16, A16, A16, A16, A16, A16, 4, 4, 2, 64, 16, 0.125, 2, 256, 128, 128,
               data + 64, data, 2, 0, None) == -1                    # no room for the scales
+
+
+def test_prefill_validation(lib):
+    f = lib.paged_prefill_attn_bf16
+    # q, k, v, out, bt, lens, maxb, B, q_len, Hq, Hkv, D, bs, scale, q_stride, tok_stride,
+    # causal, W, ws, S
+    base = [A16, A16, A16, A16, A16, A16, 4, 2, 3, 4, 2, 64, 16, 0.125, 3 * 256, 256, 1, 0, A16,
+            2, None]
+
+    def call(**kw):
+        a = list(base)
+        for k, v in kw.items():
+            a[{"out": 3, "B": 7, "n": 8, "Hq": 9, "D": 11, "qs": 14, "ts": 15, "ws": 18,
+               "S": 19}[k]] = v
+        return f(*a)
+
+    assert call(n=0) == -1                      # no query tokens
+    assert call(n=4097, qs=4097 * 256) == -2    # longer than the supported block
+    assert call(ts=248) == -1                   # token rows overlap
+    assert call(ts=260) == -1                   # not a multiple of 8
+    assert call(qs=3 * 256 - 8) == -1           # the last token runs past the sequence stride
+    assert call(out=None) == -1
+    assert call(ws=None) == -1                  # num_splits > 1: workspace needed
+    assert call(D=96) == -2
+    assert call(Hq=5) == -1
+    assert call(B=0, out=None) == 0             # no sequences: a no-op
+    f8 = lib.paged_prefill_attn_fp8
+    assert f8(A16, A16, A16, A16, A16, A16, 4, 2, 3, 4, 2, 64, 16, 0.125, 1.0, 1.0, 768, 256,
+              16 * 2 * 64 - 16, 1, 0, A16, 2, None) == -1           # cache stride too short
+    n4 = lib.paged_prefill_attn_nvfp4
+    data = 16 * 2 * 64 // 2
+    assert n4(A16, A16, A16, A16, A16, A16, 4, 2, 3, 4, 2, 64, 16, 0.125, 768, 256, data + 64,
+              data, 1, 0, A16, 2, None) == -1                       # no room for the scales
+
+
+def test_prefill_num_splits(lib):
+    ns = lib.paged_prefill_num_splits
+    dec = lib.paged_decode_num_splits
+    # q_len tokens of G heads count as q_len * G query heads
+    assert ns(32, 4, 32, 8, 256, 16, 1, 0, 256) == dec(32, 128, 8, 256, 16, 0, 256)
+    assert ns(1, 1, 32, 8, 2048, 16, 1, 0, 256) == dec(1, 32, 8, 2048, 16, 0, 256)
+    # a causal window widens by q_len - 1 keys; a plain one does not
+    assert ns(1, 8, 32, 8, 2048, 16, 1, 64, 256) == dec(1, 256, 8, 2048, 16, 71, 256)
+    assert ns(1, 8, 32, 8, 2048, 16, 0, 64, 256) == dec(1, 256, 8, 2048, 16, 64, 256)
+    assert ns(1, 0, 32, 8, 2048, 16, 1, 0, 256) == 1

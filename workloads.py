@@ -37,6 +37,7 @@ __all__ = [
     "make_workload",
     "bf16_bits_from_f32",
     "workload_names",
+    "query_block",
 ]
 
 
@@ -196,3 +197,14 @@ def make_workload(
         slot_mapping=slot_mapping, token_seq=token_seq, token_pos=token_pos,
         num_splits=tuple(splits),
     )
+
+
+def query_block(w: DecodeWorkload, q_len: int, seed: int = 0) -> np.ndarray:
+    """q_len query tokens per sequence for multi-token attention over the
+    workload's cache (a speculative-verify or chunked-prefill block): BF16
+    patterns [B, q_len, Hq, D] of N(0, 1) draws, from a generator of its own
+    (seeded by ``seed`` and q_len) so the workload's other draws are
+    unchanged."""
+    rng = np.random.default_rng([seed, q_len, 7])
+    x = rng.standard_normal((w.num_seqs, q_len, w.num_q_heads, w.head_dim), dtype=np.float32)
+    return bf16_bits_from_f32(x)
