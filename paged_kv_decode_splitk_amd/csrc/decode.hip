@@ -53,7 +53,8 @@ struct DecodeArgs {
   uint32_t num_q_heads;
   uint32_t num_kv_heads;
   uint32_t group;          // q heads per kv head
-  uint32_t head_chunks;    // ceil(group * q_len / 16): 16-column chunks of a kv head's queries
+  uint32_t col_chunks;     // ceil(group * q_len / 16): 16-column chunks of a kv head's queries
+  uint32_t head_chunks;    // rows per kv head: col_chunks / (chunks per wave), rounded up
   uint32_t block_size;
   float logit_scale;       // scale * log2(e) (* k_scale for FP8)
   float out_scale;         // v_scale for FP8, 1 otherwise
@@ -371,15 +372,18 @@ __device__ __forceinline__ void append_token(const DecodeArgs& a, uint32_t b, ui
 }
 
 // One row piece: tiles [tau0, tau1) of row (b, kh), partial state to `slot`.
+// The row's NC chunks of 16 query columns share every K/V tile: each K or V
+// read from LDS feeds NC MFMAs.
 // With DS = 2 the workgroup's two waves split the head dim: wave w loads and
 // accumulates dims [w D/2, (w+1) D/2) of K, V, q and o, and the two halves of
 // every tile's logits are added through LDS (`xg`, two buffers used in turn,
 // `xturn` counting the exchanges of the launch).
-template <int FMT, int D, int DS>
+template <int FMT, int D, int DS, int NC>
 __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D / DS, DS>& sh,
                                           lds_u8* xg, uint32_t& xturn, uint32_t b, uint32_t kh,
                                           uint32_t tau0, uint32_t tau1, uint32_t slot, bool last,
                                           uint32_t L) {
+  static_assert(DS == 1 || NC == 1, "a split head dim carries one column chunk");
   constexpr int DW = D / DS;                     // head dims of this wave
   using T = LdsTraits<FMT, DW, DS>;              // tile geometry of this wave's half rows
   using TF = LdsTraits<FMT, D>;                  // full rows (strides in the pools)
@@ -396,65 +400,74 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
   const uint32_t t0 = lo / 16 + tau0, t1 = lo / 16 + tau1;   // tiles of the sequence
   const uint32_t pa = t0 / tpp, pb = (t1 + tpp - 1) / tpp;
 
-  // column n: query token qi, q head qh; its output / workspace row qrow
-  const uint32_t col = hc * 16 + n;
-  const bool head_ok = col < a.group * a.q_len;
-  const uint32_t qi = head_ok ? col / a.group : 0u;
-  const uint32_t qh = kvh * a.group + (col - qi * a.group);
-  const uint64_t qrow = (uint64_t(b) * a.q_len + qi) * a.num_q_heads + qh;
-  float* const wbase = a.ws + qrow * a.num_splits * (D + 2);
-  // the keys [c_lo, c_hi) this column attends: the row's range, or with
-  // causal the keys up to the token's position (the last q_window of them)
-  uint32_t c_lo = lo, c_hi = L;
-  if (a.causal && head_ok) {
-    const int p1 = int(L) - int(a.q_len) + int(qi) + 1;     // position + 1
-    c_hi = p1 > 0 ? uint32_t(p1) : 0u;
-    c_lo = (a.q_window > 0 && c_hi > a.q_window) ? c_hi - a.q_window : 0u;
+  // column n of chunk k: query token qi, q head qh, read from q + qoff; its
+  // output / workspace row qrow; the keys [c_lo, c_hi) it attends: the row's
+  // range, or with causal the keys up to the token's position (the last
+  // q_window of them)
+  bool head_ok[NC];
+  uint64_t qrow[NC], qoff[NC];
+  uint32_t c_lo[NC], c_hi[NC];
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const uint32_t col = (hc * NC + k) * 16 + n;
+    head_ok[k] = col < a.group * a.q_len;
+    const uint32_t qi = head_ok[k] ? col / a.group : 0u;
+    const uint32_t qh = kvh * a.group + (col - qi * a.group);
+    qrow[k] = (uint64_t(b) * a.q_len + qi) * a.num_q_heads + qh;
+    qoff[k] = uint64_t(b) * a.q_stride + uint64_t(qi) * a.q_tok_stride + uint64_t(qh) * D + w * DW;
+    c_lo[k] = lo;
+    c_hi[k] = L;
+    if (a.causal && head_ok[k]) {
+      const int p1 = int(L) - int(a.q_len) + int(qi) + 1;     // position + 1
+      c_hi[k] = p1 > 0 ? uint32_t(p1) : 0u;
+      c_lo[k] = (a.q_window > 0 && c_hi[k] > a.q_window) ? c_hi[k] - a.q_window : 0u;
+    }
   }
   const int32_t* bt = a.block_tables + uint64_t(b) * a.max_blocks;
   // append: written now, waited for only when the row's last tile is requested
   bool pend = a.new_k != nullptr && last;
   if (pend) append_token<FMT, D, DS>(a, b, kvh, L, w, lane);
 
-  // q as the B operand of the QK MFMAs: column n = head, dims 32c + 8g .. +8;
+  // q as the B operand of the QK MFMAs: column n, dims 32c + 8g .. +8;
   // issued ahead of the tile loads, which only ever wait for later loads.
-  u32x4 qf[DW / 32];
-  float qup = 1.0f;            // NVFP4: logits of this head's dims are scaled by qup
-  {
-    const uint16_t* qsrc = a.q + uint64_t(b) * a.q_stride + uint64_t(qi) * a.q_tok_stride +
-                           uint64_t(qh) * D + w * DW;
+  u32x4 qf[NC][DW / 32];
+  float qup[NC];               // NVFP4: logits of this column's dims are scaled by qup
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    qup[k] = 1.0f;
+    const uint16_t* qsrc = a.q + qoff[k];
 #pragma unroll
     for (int c = 0; c < DW / 32; ++c) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (head_ok) v = *reinterpret_cast<const u32x4*>(qsrc + 32 * c + 8 * g);
-      qf[c] = v;
+      if (head_ok[k]) v = *reinterpret_cast<const u32x4*>(qsrc + 32 * c + 8 * g);
+      qf[k][c] = v;
     }
     if constexpr (FMT == kNvfp4) {
-      // q in FP16 for the FP16 MFMA: shifted down by 2^k so that the head's
-      // largest |q| stays below 2^15 (exact for every BF16 value in range)
+      // q in FP16 for the FP16 MFMA: shifted down by 2^e so that the
+      // column's largest |q| stays below 2^15 (exact for every BF16 value in range)
       uint32_t mlo = 0, mhi = 0;     // largest magnitudes (BF16 bits order as values)
 #pragma unroll
       for (int c = 0; c < DW / 32; ++c)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          mlo = max(mlo, qf[c][j] & 0x7FFFu);
-          mhi = max(mhi, qf[c][j] & 0x7FFF0000u);
+          mlo = max(mlo, qf[k][c][j] & 0x7FFFu);
+          mhi = max(mhi, qf[k][c][j] & 0x7FFF0000u);
         }
       float m = fmaxf(bf16_lo(mlo), bf16_hi(mhi));
       m = max_over_rows(m);
       const int e = int((__float_as_uint(m) >> 23) & 255u) - 127;
-      const int k = e > 14 ? e - 14 : 0;
-      const float down = __uint_as_float(uint32_t(127 - k) << 23);
-      qup = __uint_as_float(uint32_t(127 + k) << 23);
+      const int sh2 = e > 14 ? e - 14 : 0;
+      const float down = __uint_as_float(uint32_t(127 - sh2) << 23);
+      qup[k] = __uint_as_float(uint32_t(127 + sh2) << 23);
 #pragma unroll
       for (int c = 0; c < DW / 32; ++c) {
         u32x4 h;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const f32x2 f = {bf16_lo(qf[c][j]) * down, bf16_hi(qf[c][j]) * down};
+          const f32x2 f = {bf16_lo(qf[k][c][j]) * down, bf16_hi(qf[k][c][j]) * down};
           h[j] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f, f16x2));
         }
-        qf[c] = h;
+        qf[k][c] = h;
       }
     }
   }
@@ -464,14 +477,20 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
   const int ld_row = lane / T::CPR;                  // + i * RPI
   const int ld_pos = lane % T::CPR;
 
-  f32x4 acc[DW / 16];
+  f32x4 acc[NC][DW / 16];
 #pragma unroll
-  for (int mt = 0; mt < DW / 16; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < NC; ++k)
+#pragma unroll
+    for (int mt = 0; mt < DW / 16; ++mt) acc[k][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   // The reference max starts at a finite floor rather than -inf, so that a
   // column whose keys in this piece are all masked keeps weights exp2(-inf -
   // floor) = 0 and rescale factors 1 (never exp2(-inf + inf)).
-  float m_run = kMaxFloor;
-  float l_run = 0.0f;
+  float m_run[NC], l_run[NC];
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    m_run[k] = kMaxFloor;
+    l_run[k] = 0.0f;
+  }
 
   // Segments of up to 64 pages: the block-table entries of a segment sit in
   // one VGPR (entry per lane); the DMA ring restarts at every segment.
@@ -534,7 +553,6 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
         const uint32_t t = tb + s;               // t >= ct1: phantom tile, all keys masked
         const uint32_t tok0 = t * 16;
         const uint32_t khi = t < ct1 ? L : 0u;
-        const uint32_t c_khi = t < ct1 ? c_hi : 0u;
         lds_u8* const kt = ring3 + s * T::SLOT;
         lds_u8* const vt = kt + T::KV;
 
@@ -542,13 +560,16 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
         wait_vmcnt<T::WAIT>();
         wave_lds_fence();
         __builtin_amdgcn_sched_barrier(0);
-        f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+        f32x4 sc[NC];
+#pragma unroll
+        for (int k = 0; k < NC; ++k) sc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
         if constexpr (FMT == kBf16) {
 #pragma unroll
           for (int c = 0; c < DW / 32; ++c) {
             const int chunk = (4 * c + g) ^ T::swz(n);
             const u32x4 kv = *(lds_u32x4*)(kt + n * T::RB + chunk * 16);
-            sc = mfma_qk<FMT>(kv, qf[c], sc);
+#pragma unroll
+            for (int k = 0; k < NC; ++k) sc[k] = mfma_qk<FMT>(kv, qf[k][c], sc[k]);
           }
         } else if constexpr (FMT == kFp8) {
 #pragma unroll
@@ -556,15 +577,16 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
             const int chunk = (2 * c + (g >> 1)) ^ T::swz(n);
             const u32x2 w = *(lds_u32x2*)(kt + n * T::RB + chunk * 16 + 8 * (g & 1));
             const u32x4 kv = fp8x8_to_bf16x8(w[0], w[1]);
-            sc = mfma_qk<FMT>(kv, qf[c], sc);
+#pragma unroll
+            for (int k = 0; k < NC; ++k) sc[k] = mfma_qk<FMT>(kv, qf[k][c], sc[k]);
           }
         } else {
           // group of dims 32c + 8g is 2c + g/2: byte 2(c & 1) of scale word c/2
           // once the words are shifted down by g/2 bytes
           uint32_t sw[(T::SC_ROW + 3) / 4];
 #pragma unroll
-          for (int k = 0; k < (T::SC_ROW + 3) / 4; ++k)
-            sw[k] = *(lds_u32*)(kt + T::TILE + n * T::SC_ROW + 4 * k) >> (8 * (g >> 1));
+          for (int i = 0; i < (T::SC_ROW + 3) / 4; ++i)
+            sw[i] = *(lds_u32*)(kt + T::TILE + n * T::SC_ROW + 4 * i) >> (8 * (g >> 1));
 #pragma unroll
           for (int c = 0; c < DW / 32; ++c) {
             const int chunk = c ^ T::swz(n);
@@ -572,54 +594,63 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
             const float S = (c & 1) ? __builtin_amdgcn_cvt_f32_fp8(sw[c / 2], 2)
                                     : __builtin_amdgcn_cvt_f32_fp8(sw[c / 2], 0);
             const u32x4 kv = fp4x8_to_f16x8(w, _Float16(S));
-            sc = mfma_qk<FMT>(kv, qf[c], sc);
+#pragma unroll
+            for (int k = 0; k < NC; ++k) sc[k] = mfma_qk<FMT>(kv, qf[k][c], sc[k]);
           }
-          sc *= qup;
+#pragma unroll
+          for (int k = 0; k < NC; ++k) sc[k] *= qup[k];
         }
         if constexpr (DS > 1) {
           // the other half of the head dim: partial logits through LDS
           typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
           lds_f32x4* const xs = (lds_f32x4*)xg + (xturn++ & 1) * (DS * 64);
-          xs[w * 64 + lane] = sc;
+          xs[w * 64 + lane] = sc[0];
           asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
           const f32x4 other = xs[(1 - w) * 64 + lane];
-          sc = w == 0 ? sc + other : other + sc;   // the same sum in both waves
+          sc[0] = w == 0 ? sc[0] + other : other + sc[0];   // the same sum in both waves
         }
         __builtin_amdgcn_sched_barrier(0);
         issue(s, 0, t + NBUF);
 
-        // ---- online softmax (lane: head n, tokens tok0 + 4g + j)
-        float sv[4];
-        float mx = -__builtin_inff();
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const uint32_t tok = tok0 + 4 * g + j;
-          sv[j] = (tok >= c_lo && tok < c_khi) ? sc[j] * a.logit_scale : -__builtin_inff();
-          mx = fmaxf(mx, sv[j]);
-        }
-        mx = max_over_rows(mx);
+        // ---- online softmax (lane: column n, tokens tok0 + 4g + j)
         // The reference m_run follows the running max lazily: it moves only
-        // when some head's max exceeds it by more than kLazyMax (log2 units),
-        // and only then is the accumulator rescaled. The weights stay below
-        // 2^kLazyMax; (m, l, o) is exact for any reference, so only the
+        // when some column's max exceeds it by more than kLazyMax (log2
+        // units), and only then is the accumulator rescaled. The weights stay
+        // below 2^kLazyMax; (m, l, o) is exact for any reference, so only the
         // amount of rescaling work changes.
-        const bool rescale = __builtin_amdgcn_ballot_w64(mx > m_run + kLazyMax) != 0;
-        float alpha = 1.0f;
-        if (rescale) {
-          const float m_new = fmaxf(m_run, mx);
-          alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-          m_run = m_new;
-        }
-        uint32_t pbits[4];
-        float psum = 0.0f;
+        bool rescale[NC];
+        float alpha[NC];
+        u32x2 pf[NC];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const float p = __builtin_amdgcn_exp2f(sv[j] - m_run);
-          pbits[j] = p_bits<FMT>(p);
-          psum += p_value<FMT>(pbits[j]);
+        for (int k = 0; k < NC; ++k) {
+          const uint32_t c_khi = t < ct1 ? c_hi[k] : 0u;
+          float sv[4];
+          float mx = -__builtin_inff();
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t tok = tok0 + 4 * g + j;
+            sv[j] = (tok >= c_lo[k] && tok < c_khi) ? sc[k][j] * a.logit_scale : -__builtin_inff();
+            mx = fmaxf(mx, sv[j]);
+          }
+          mx = max_over_rows(mx);
+          rescale[k] = __builtin_amdgcn_ballot_w64(mx > m_run[k] + kLazyMax) != 0;
+          alpha[k] = 1.0f;
+          if (rescale[k]) {
+            const float m_new = fmaxf(m_run[k], mx);
+            alpha[k] = __builtin_amdgcn_exp2f(m_run[k] - m_new);
+            m_run[k] = m_new;
+          }
+          uint32_t pbits[4];
+          float psum = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const float p = __builtin_amdgcn_exp2f(sv[j] - m_run[k]);
+            pbits[j] = p_bits<FMT>(p);
+            psum += p_value<FMT>(pbits[j]);
+          }
+          l_run[k] = l_run[k] * alpha[k] + psum;
+          pf[k] = u32x2{pbits[0] | (pbits[1] << 16), pbits[2] | (pbits[3] << 16)};
         }
-        l_run = l_run * alpha + psum;
-        const u32x2 pf = {pbits[0] | (pbits[1] << 16), pbits[2] | (pbits[3] << 16)};
 
         // ---- V tile as BF16 rows with masked tokens zeroed: in place for a
         // BF16 cache (partial tiles only), else dequantized into the stage
@@ -654,11 +685,13 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
         // ---- O^T += V^T P: lane supplies V[4g + n/4][16mt + 4(n%4) .. +4]. The
         // transposed reads are issued as inline asm: the compiler would otherwise
         // wait for every pending LDS-DMA load before each of them. Four reads,
-        // then their four MFMAs, which run while the next reads are in flight.
-        if (rescale) {
+        // then their MFMAs, which run while the next reads are in flight.
 #pragma unroll
-          for (int mt = 0; mt < DW / 16; ++mt) acc[mt] *= alpha;
-        }
+        for (int k = 0; k < NC; ++k)
+          if (rescale[k]) {
+#pragma unroll
+            for (int mt = 0; mt < DW / 16; ++mt) acc[k][mt] *= alpha[k];
+          }
         {
           const int vtok = 4 * g + (n >> 2);
           const uint32_t vrow = uint32_t(uintptr_t(vsrc)) + vtok * T::BRB + (n & 1) * 8;
@@ -684,7 +717,9 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
                 : "memory");
 #pragma unroll
             for (int u = 0; u < 4; ++u)
-              acc[4 * q4 + u] = mfma_pv<FMT>(vv[u], pf, acc[4 * q4 + u]);
+#pragma unroll
+              for (int k = 0; k < NC; ++k)
+                acc[k][4 * q4 + u] = mfma_pv<FMT>(vv[u], pf[k], acc[k][4 * q4 + u]);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -695,33 +730,34 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
     wave_lds_fence();
   }
 
-  const float l_tot = sum_over_rows(l_run);
-  // a column without keys (l = 0) writes zeros
-  const float inv = l_tot > 0.0f ? a.out_scale / l_tot : 0.0f;
-  if (a.out) {
-    // non-split decode: the whole row in one piece, the normalized output
-    // straight to BF16
-    if (head_ok) {
-      uint16_t* orow = a.out + qrow * D + w * DW;
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const float l_tot = sum_over_rows(l_run[k]);
+    // a column without keys (l = 0) writes zeros
+    const float inv = l_tot > 0.0f ? a.out_scale / l_tot : 0.0f;
+    if (!head_ok[k]) continue;
+    if (a.out) {
+      // non-split: the whole row in one piece, the normalized output
+      // straight to BF16
+      uint16_t* orow = a.out + qrow[k] * D + w * DW;
 #pragma unroll
       for (int mt = 0; mt < DW / 16; ++mt)
         *reinterpret_cast<u32x2*>(orow + 16 * mt + 4 * g) =
-            u32x2{pack_bf16x2(acc[mt][0] * inv, acc[mt][1] * inv),
-                  pack_bf16x2(acc[mt][2] * inv, acc[mt][3] * inv)};
+            u32x2{pack_bf16x2(acc[k][mt][0] * inv, acc[k][mt][1] * inv),
+                  pack_bf16x2(acc[k][mt][2] * inv, acc[k][mt][3] * inv)};
+      continue;
     }
-    return;
-  }
-  if (head_ok) {
+    float* const wbase = a.ws + qrow[k] * a.num_splits * (D + 2);
     float* wrow = wbase + uint64_t(slot) * (D + 2);
 #pragma unroll
     for (int mt = 0; mt < DW / 16; ++mt) {
-      f32x2 lo2 = {acc[mt][0] * inv, acc[mt][1] * inv};
-      f32x2 hi2 = {acc[mt][2] * inv, acc[mt][3] * inv};
+      f32x2 lo2 = {acc[k][mt][0] * inv, acc[k][mt][1] * inv};
+      f32x2 hi2 = {acc[k][mt][2] * inv, acc[k][mt][3] * inv};
       *reinterpret_cast<f32x2*>(wrow + w * DW + mt * 16 + 4 * g) = lo2;
       *reinterpret_cast<f32x2*>(wrow + w * DW + mt * 16 + 4 * g + 2) = hi2;
     }
     if (g == 0 && w == 0) {
-      wrow[D] = m_run * kLn2;
+      wrow[D] = m_run[k] * kLn2;
       wrow[D + 1] = l_tot;
     }
     // the row ends in this piece: an end marker (l = -1) in the next slot
@@ -734,19 +770,23 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
   }
 }
 
-// Zeros for the q heads of row (b, kh) of a sequence without keys.
-template <int D>
+// Zeros for the query columns of row (b, kh) of a sequence without keys.
+template <int D, int NC>
 __device__ __forceinline__ void zero_row(const DecodeArgs& a, uint32_t b, uint32_t kh) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, n = lane & 15;
   const uint32_t kvh = kh / a.head_chunks, hc = kh % a.head_chunks;
-  const uint32_t col = hc * 16 + n;
-  if (col >= a.group * a.q_len) return;
-  const uint32_t qi = col / a.group;
-  uint16_t* orow =
-      a.out + ((uint64_t(b) * a.q_len + qi) * a.num_q_heads + kvh * a.group + col - qi * a.group) * D;
 #pragma unroll
-  for (int mt = 0; mt < D / 16; ++mt) *reinterpret_cast<u32x2*>(orow + 16 * mt + 4 * g) = u32x2{0u, 0u};
+  for (int k = 0; k < NC; ++k) {
+    const uint32_t col = (hc * NC + k) * 16 + n;
+    if (col >= a.group * a.q_len) continue;
+    const uint32_t qi = col / a.group;
+    uint16_t* orow = a.out + ((uint64_t(b) * a.q_len + qi) * a.num_q_heads + kvh * a.group +
+                              col - qi * a.group) * D;
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt)
+      *reinterpret_cast<u32x2*>(orow + 16 * mt + 4 * g) = u32x2{0u, 0u};
+  }
 }
 
 // Head-dim split: at head_dim 512 a workgroup of two waves shares each row
@@ -761,7 +801,12 @@ constexpr int kDSplit = D == 512 ? 2 : 1;
 template <int FMT, int D>
 constexpr int kWavesPerSimd = ((FMT != kBf16 && D <= 256) || kDSplit<D> > 1) ? 2 : 1;
 
+// Column chunks one wave can carry: two for BF16 tiles up to head_dim 128
+// (a second accumulator and q fit the registers), else one.
 template <int FMT, int D>
+constexpr int kMaxChunks = (FMT == kBf16 && D <= 128) ? 2 : 1;
+
+template <int FMT, int D, int NC>
 __global__ __launch_bounds__(64 * kDSplit<D>, (kWavesPerSimd<FMT, D>)) void splitk_stream(
     DecodeArgs a) {
   constexpr int DS = kDSplit<D>;
@@ -802,7 +847,7 @@ __global__ __launch_bounds__(64 * kDSplit<D>, (kWavesPerSimd<FMT, D>)) void spli
       n = row_tiles(L, a.window);
       start = pos;
       if (n == 0) {
-        if (a.out && threadIdx.x < 64) zero_row<D>(a, b, kh);
+        if (a.out && threadIdx.x < 64) zero_row<D, NC>(a, b, kh);
         break;
       }
     } else if (cached) {
@@ -825,7 +870,7 @@ __global__ __launch_bounds__(64 * kDSplit<D>, (kWavesPerSimd<FMT, D>)) void spli
     const uint32_t tau0 = whole ? 0u : pos - start;
     const uint32_t tau1 = whole ? n : min(n, end - start);
     const uint32_t slot = whole ? 0u : pos / c - start / c;
-    run_piece<FMT, D, DS>(a, mine, xg3, xturn, b, kh, tau0, tau1, slot,
+    run_piece<FMT, D, DS, NC>(a, mine, xg3, xturn, b, kh, tau0, tau1, slot,
                           whole || start + n <= end, L);
     if (whole) break;
     pos = start + tau1;
@@ -1006,35 +1051,29 @@ static int launch_status() {
   return e == hipSuccess ? kOk : kLaunch;
 }
 
-// Waves the stream kernel launches on the current device: all resident at
-// once (at most the occupancy), cached per device, format and head_dim.
 // Resident waves per CU of the stream kernel (workgroups x waves per workgroup).
-template <int FMT, int D>
+template <int FMT, int D, int NC>
 static int stream_occupancy() {
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, splitk_stream<FMT, D>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, splitk_stream<FMT, D, NC>,
                                                    64 * kDSplit<D>, 0) != hipSuccess)
     return 0;
   return per_cu * kDSplit<D>;
 }
 
-template <int FMT>
-static uint64_t stream_capacity(uint32_t head_dim) {
-  static uint64_t cache[64][4];
+// Waves the stream kernel launches on the current device: all resident at
+// once (at most the occupancy), cached per device, format, head_dim and
+// chunks per wave.
+template <int FMT, int D, int NC>
+static uint64_t stream_capacity() {
+  static uint64_t cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  const int di = head_dim == 64 ? 0 : head_dim == 128 ? 1 : head_dim == 256 ? 2 : 3;
-  if (cache[dev][di]) return cache[dev][di];
+  if (cache[dev]) return cache[dev];
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  int per_cu = 0;
-  switch (head_dim) {
-    case 64: per_cu = stream_occupancy<FMT, 64>(); break;
-    case 128: per_cu = stream_occupancy<FMT, 128>(); break;
-    case 256: per_cu = stream_occupancy<FMT, 256>(); break;
-    case 512: per_cu = stream_occupancy<FMT, 512>(); break;
-  }
+  int per_cu = stream_occupancy<FMT, D, NC>();
   if (per_cu <= 0 || cus <= 0) return 0;
 #ifndef PKD_STREAM_WAVES_PER_CU
 #define PKD_STREAM_WAVES_PER_CU 4
@@ -1046,11 +1085,47 @@ static uint64_t stream_capacity(uint32_t head_dim) {
   // quantized tiles carry more ALU work per byte and gain from a second wave
   // per SIMD where the registers allow it. The count is a multiple of the CU
   // count so that every CU gets the same work.
-  const int cap = FMT == kBf16 && head_dim < 512 ? PKD_STREAM_WAVES_PER_CU
-                                                 : PKD_STREAM_WAVES_PER_CU_Q;
+#ifndef PKD_STREAM_WAVES_PER_CU_NC
+#define PKD_STREAM_WAVES_PER_CU_NC 4
+#endif
+  const int cap = FMT == kBf16 && D < 512
+                      ? (NC > 1 ? PKD_STREAM_WAVES_PER_CU_NC : PKD_STREAM_WAVES_PER_CU)
+                      : PKD_STREAM_WAVES_PER_CU_Q;
   if (per_cu > cap) per_cu = cap;
-  cache[dev][di] = uint64_t(per_cu) * uint64_t(cus);
-  return cache[dev][di];
+  cache[dev] = uint64_t(per_cu) * uint64_t(cus);
+  return cache[dev];
+}
+
+// One launch of the stream kernel with NC column chunks per wave.
+template <int FMT, int D, int NC>
+static int launch_stream(DecodeArgs a, hipStream_t stream) {
+  constexpr uint64_t ds = kDSplit<D>;
+  a.head_chunks = (a.col_chunks + NC - 1) / NC;
+  const uint64_t rows = uint64_t(a.num_seqs) * a.num_kv_heads * a.head_chunks;
+  uint32_t tile_bound = a.max_blocks * (a.block_size / 16);
+  if (a.window > 0) tile_bound = min(tile_bound, (a.window + 14) / 16 + 1);
+  a.chunk_min = a.num_splits > 1 ? (tile_bound + a.num_splits - 2) / (a.num_splits - 1) : 1;
+  // one workgroup per piece (at most num_splits per row), or as many as stay
+  // resident; a workgroup is one wave, or two sharing a head_dim of 512
+  uint64_t groups = rows;
+  if (a.num_splits > 1) {
+    groups = rows * a.num_splits;
+    const uint64_t cap = stream_capacity<FMT, D, NC>() / ds;
+    if (cap && groups > cap) groups = cap;
+  }
+  if (groups > 0x7FFFFFFFull) return kUnsupported;
+  hipLaunchKernelGGL((splitk_stream<FMT, D, NC>), dim3(uint32_t(groups)), dim3(uint32_t(64 * ds)),
+                     0, stream, a);
+  return launch_status();
+}
+
+// Two chunks per wave when the row has them and the registers allow it.
+template <int FMT, int D>
+static int launch_stream_nc(const DecodeArgs& a, hipStream_t stream) {
+  if constexpr (kMaxChunks<FMT, D> >= 2) {
+    if (a.col_chunks >= 2) return launch_stream<FMT, D, 2>(a, stream);
+  }
+  return launch_stream<FMT, D, 1>(a, stream);
 }
 
 template <int FMT>
@@ -1059,29 +1134,13 @@ static int launch_splitk(DecodeArgs a, uint32_t num_seqs, uint32_t head_dim,
   // one page must stay addressable by 32-bit buffer offsets
   if (a.page_bytes > 0x7FFF0000ull) return kUnsupported;
   a.num_seqs = num_seqs;
-  const uint64_t rows = uint64_t(num_seqs) * a.num_kv_heads * a.head_chunks;
-  uint32_t tile_bound = a.max_blocks * (a.block_size / 16);
-  if (a.window > 0) tile_bound = min(tile_bound, (a.window + 14) / 16 + 1);
-  a.chunk_min = a.num_splits > 1 ? (tile_bound + a.num_splits - 2) / (a.num_splits - 1) : 1;
-  // one workgroup per piece (at most num_splits per row), or as many as stay
-  // resident; a workgroup is one wave, or two sharing a head_dim of 512
-  const uint64_t ds = head_dim == 512 ? 2 : 1;
-  uint64_t groups = rows;
-  if (a.num_splits > 1) {
-    groups = rows * a.num_splits;
-    const uint64_t cap = stream_capacity<FMT>(head_dim) / ds;
-    if (cap && groups > cap) groups = cap;
-  }
-  if (groups > 0x7FFFFFFFull) return kUnsupported;
-  const dim3 gd = dim3(uint32_t(groups)), bd = dim3(uint32_t(64 * ds));
   switch (head_dim) {
-    case 64: hipLaunchKernelGGL((splitk_stream<FMT, 64>), gd, bd, 0, stream, a); break;
-    case 128: hipLaunchKernelGGL((splitk_stream<FMT, 128>), gd, bd, 0, stream, a); break;
-    case 256: hipLaunchKernelGGL((splitk_stream<FMT, 256>), gd, bd, 0, stream, a); break;
-    case 512: hipLaunchKernelGGL((splitk_stream<FMT, 512>), gd, bd, 0, stream, a); break;
+    case 64: return launch_stream_nc<FMT, 64>(a, stream);
+    case 128: return launch_stream_nc<FMT, 128>(a, stream);
+    case 256: return launch_stream_nc<FMT, 256>(a, stream);
+    case 512: return launch_stream_nc<FMT, 512>(a, stream);
     default: return kUnsupported;
   }
-  return launch_status();
 }
 
 static DecodeArgs make_args(const uint16_t* q, const void* kc, const void* vc, float* ws,
@@ -1100,7 +1159,8 @@ static DecodeArgs make_args(const uint16_t* q, const void* kc, const void* vc, f
   a.num_q_heads = Hq;
   a.num_kv_heads = Hkv;
   a.group = Hq / Hkv;
-  a.head_chunks = head_chunks(a.group);
+  a.col_chunks = head_chunks(a.group);
+  a.head_chunks = a.col_chunks;
   a.block_size = bs;
   a.logit_scale = logit_scale;
   a.out_scale = out_scale;
@@ -1373,7 +1433,7 @@ extern "C" PKD_API int paged_decode_attn_nvfp4(
   return launch_decode<kNvfp4>(a, output, num_seqs, head_dim, stream);
 }
 
-// Query-block arguments on top of the decode arguments: head_chunks over
+// Query-block arguments on top of the decode arguments: column chunks over
 // the group's q_len x group columns, the row window widened for a causal
 // window (the first token's keys through the last token's).
 static void set_query_block(DecodeArgs& a, uint32_t q_len, uint32_t q_token_stride,
@@ -1383,7 +1443,7 @@ static void set_query_block(DecodeArgs& a, uint32_t q_len, uint32_t q_token_stri
   a.causal = causal ? 1u : 0u;
   a.q_window = sliding_window;
   a.window = prefill_row_window(q_len, a.causal, sliding_window);
-  a.head_chunks = head_chunks(a.group * q_len);
+  a.col_chunks = head_chunks(a.group * q_len);
 }
 
 extern "C" PKD_API int paged_prefill_attn_bf16(

@@ -51,6 +51,9 @@ CASES = [
     ("bf16", (90, 400, 17), 5, 6, 2, 64, 16, 1, 37, 3),                  # causal window
     ("bf16", (90, 400, 17), 5, 6, 2, 64, 128, 0, 37, 2),                 # plain window
     ("bf16", (90, 400, 17), 33, 6, 2, 64, 16, 1, 20, 4),                 # window < q_len
+    ("bf16", (0, 5, 40), 8, 8, 2, 64, 16, 1, 0, 1),                     # two chunks per wave
+    ("bf16", (0, 5, 40, 300), 12, 8, 2, 128, 16, 1, 0, 4),              # three chunks: 2 + 1
+    ("bf16", (100, 700), 16, 32, 8, 128, 16, 1, 100, 3),                # four chunks, window
     ("fp8", (1, 17, 300, 1000), 2, 16, 8, 256, 16, 1, 0, 3),
     ("fp8", (1, 17, 300, 1000), 3, 16, 8, 256, 16, 1, 129, 5),
     ("fp8", (40, 333), 4, 8, 1, 128, 16, 1, 60, 2),
