@@ -57,6 +57,8 @@ from .attention import (
     combine_partials,
     query_range,
     paged_prefill_attention,
+    contiguous_kv_rows,
+    contiguous_attention,
 )
 
 __all__ = [
@@ -66,5 +68,5 @@ __all__ = [
     "reshape_and_cache", "bf16_absmax", "read_kv_rows", "window_start",
     "paged_decode_attention", "attention_rows", "split_page_bound",
     "split_partials", "combine_partials", "query_range",
-    "paged_prefill_attention",
+    "paged_prefill_attention", "contiguous_kv_rows", "contiguous_attention",
 ]

@@ -27,7 +27,7 @@ import math
 import numpy as np
 
 from .cache import CacheGeometry, read_kv_rows
-from .formats import bf16_to_f64
+from .formats import bf16_to_f64, e4m3_decode
 
 
 def window_start(seq_len: int, sliding_window: int) -> int:
@@ -205,4 +205,50 @@ def paged_prefill_attention(geom: CacheGeometry, q_bits, k_cache, v_cache, block
                     l[r, i, h] = np.exp(s - s.max()).sum()
     if return_state:
         return out, m, l
+    return out
+
+
+def contiguous_kv_rows(fmt: str, data, b: int, lo: int, hi: int, num_kv_heads: int,
+                       head_dim: int, strides, scale=1.0) -> np.ndarray:
+    """Rows [hi - lo, Hkv, D] (float64, exact) of keys lo .. hi-1 of sequence b
+    in a contiguous K or V tensor (no block table) [AstrAI log: the ContigKV
+    source policy; stride-based Q/KV/O addressing]: element
+    b*strides[0] + j*strides[1] + h*strides[2] + d. BF16 bits, or E4M3 codes
+    times the per-tensor scale."""
+    flat = np.asarray(data).reshape(-1)
+    j = np.arange(lo, hi, dtype=np.int64)[:, None, None]
+    h = np.arange(num_kv_heads, dtype=np.int64)[None, :, None]
+    d = np.arange(head_dim, dtype=np.int64)[None, None, :]
+    idx = b * int(strides[0]) + j * int(strides[1]) + h * int(strides[2]) + d
+    if fmt == "bf16":
+        return bf16_to_f64(flat[idx])
+    if fmt == "fp8":
+        return e4m3_decode(flat[idx]) * float(np.float32(scale))
+    raise ValueError(f"contiguous K/V rows are BF16 or FP8, not {fmt}")
+
+
+def contiguous_attention(fmt: str, q_bits, k_data, v_data, seq_lens, num_q_heads: int,
+                         num_kv_heads: int, head_dim: int, q_len: int, scale, q_strides,
+                         k_strides, v_strides, causal=True, sliding_window=0, k_scale=1.0,
+                         v_scale=1.0, seqs=None) -> np.ndarray:
+    """Exact output [len(seqs), q_len, Hq, D] (float64) of multi-token
+    attention over contiguous K/V tensors: q token i of sequence b, head h at
+    b*q_strides[0] + i*q_strides[1] + h*q_strides[2]; the keys each token
+    attends as in ``query_range``; softmax as in ``attention_rows``."""
+    D, Hq = head_dim, num_q_heads
+    qflat = np.asarray(q_bits, dtype=np.uint16).reshape(-1)
+    seq_lens = np.asarray(seq_lens).reshape(-1)
+    seqs = list(range(len(seq_lens)) if seqs is None else seqs)
+    out = np.zeros((len(seqs), q_len, Hq, D))
+    hq = np.arange(Hq, dtype=np.int64)[:, None]
+    d = np.arange(D, dtype=np.int64)[None, :]
+    for r, b in enumerate(seqs):
+        L = int(seq_lens[b])
+        for i in range(q_len):
+            lo, hi = query_range(L, q_len, i, causal, sliding_window)
+            K = contiguous_kv_rows(fmt, k_data, b, lo, hi, num_kv_heads, D, k_strides, k_scale)
+            V = contiguous_kv_rows(fmt, v_data, b, lo, hi, num_kv_heads, D, v_strides, v_scale)
+            q = bf16_to_f64(qflat[b * int(q_strides[0]) + i * int(q_strides[1]) +
+                                  hq * int(q_strides[2]) + d])
+            out[r, i] = attention_rows(q, K, V, scale)
     return out
