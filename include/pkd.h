@@ -359,6 +359,46 @@ PKD_API uint32_t paged_prefill_num_splits(uint32_t num_seqs, uint32_t q_len,
                                           uint32_t causal, uint32_t sliding_window,
                                           uint32_t num_cus);
 
+/* ---------------------------------------------------------------- contiguous K/V
+ * The multi-token attention above over contiguous K/V tensors instead of a
+ * paged cache (AstrAI csrc/tests commit log: the ContigKV / PagedKV source
+ * policy, stride-based Q/KV/O addressing, the bhld / blhd layouts): key j of
+ * sequence b, kv head h is the row at element
+ *   b*strides[3] + j*strides[4] + h*strides[5]   of k  (BF16, or E4M3FN codes)
+ *   b*strides[6] + j*strides[7] + h*strides[8]   of v
+ * q token i, head h at b*strides[0] + i*strides[1] + h*strides[2]; the output
+ * row at b*strides[9] + i*strides[10] + h*strides[11] (BF16). strides: a host
+ * array of 12 element strides, each a multiple of 16 bytes. So (b, l, h, d)
+ * and (b, h, l, d) tensors, padded rows and views are all read in place.
+ * Keys j < seq_lens[b] <= max_seq_len are read; causal, sliding_window,
+ * num_splits and workspace as for paged_prefill_attn_bf16 (workspace of
+ * paged_decode_workspace_bytes(num_seqs, num_q_heads * q_len, head_dim,
+ * num_splits) bytes). q_len = 1 is plain decode.
+ * The paged kernels run with the block-table lookup replaced by the strides:
+ * the same tiles, order and arithmetic, so a paged cache holding the same
+ * rows gives bit-identical outputs.
+ * Errors: PKD_ERR_INVALID_ARG for a null or misaligned buffer, a stride not
+ * a multiple of 16 bytes, max_seq_len == 0 or q_len == 0;
+ * PKD_ERR_UNSUPPORTED for head_dim / num_splits outside the supported set,
+ * q_len > 4096 or a K/V token stride so large that 16 rows pass 2^31 bytes. */
+PKD_API int contig_kv_attn_bf16(const uint16_t* q, const uint16_t* k, const uint16_t* v,
+                                uint16_t* output, const int32_t* seq_lens, uint32_t num_seqs,
+                                uint32_t q_len, uint32_t max_seq_len, uint32_t num_q_heads,
+                                uint32_t num_kv_heads, uint32_t head_dim, float scale,
+                                const uint64_t* strides, uint32_t causal,
+                                uint32_t sliding_window, float* workspace, uint32_t num_splits,
+                                hipStream_t stream);
+
+/* FP8-E4M3FN K/V codes with per-tensor k_scale, v_scale (values are
+ * code * scale, as in the paged FP8 cache). */
+PKD_API int contig_kv_attn_fp8(const uint16_t* q, const uint8_t* k, const uint8_t* v,
+                               uint16_t* output, const int32_t* seq_lens, uint32_t num_seqs,
+                               uint32_t q_len, uint32_t max_seq_len, uint32_t num_q_heads,
+                               uint32_t num_kv_heads, uint32_t head_dim, float scale,
+                               float k_scale, float v_scale, const uint64_t* strides,
+                               uint32_t causal, uint32_t sliding_window, float* workspace,
+                               uint32_t num_splits, hipStream_t stream);
+
 /* ---------------------------------------------------------------- host helpers
  * Bytes of the split-K workspace: num_seqs*num_q_heads*num_splits*(head_dim+2)*4. */
 PKD_API size_t paged_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads,

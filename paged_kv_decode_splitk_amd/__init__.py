@@ -25,7 +25,8 @@ __all__ = [
     "paged_decode_attn_splitk_append_fp8", "paged_decode_attn_splitk_append_nvfp4",
     "paged_decode_attn_bf16", "paged_decode_attn_fp8",
     "paged_decode_attn_nvfp4", "paged_prefill_attn_bf16", "paged_prefill_attn_fp8",
-    "paged_prefill_attn_nvfp4", "paged_prefill_num_splits",
+    "paged_prefill_attn_nvfp4", "paged_prefill_num_splits", "contig_kv_attn_bf16",
+    "contig_kv_attn_fp8", "layout_strides",
     "paged_decode_workspace_bytes", "paged_decode_num_splits",
     "pkd_status_string", "EXPORTED_SYMBOLS", "PkdError",
 ]
@@ -76,6 +77,10 @@ _SIGNATURES = {
     "paged_prefill_attn_nvfp4": (_INT, [_P, _P, _P, _P, _P, _P, _U32, _U32, _U32, _U32, _U32,
                                         _U32, _U32, _F32, _U32, _U32, _U64, _U64, _U32, _U32, _P,
                                         _U32, _P]),
+    "contig_kv_attn_bf16": (_INT, [_P, _P, _P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32, _F32,
+                                   _P, _U32, _U32, _P, _U32, _P]),
+    "contig_kv_attn_fp8": (_INT, [_P, _P, _P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32, _F32,
+                                  _F32, _F32, _P, _U32, _U32, _P, _U32, _P]),
     "paged_prefill_num_splits": (_U32, [_U32, _U32, _U32, _U32, _U32, _U32, _U32, _U32, _U32]),
     "paged_decode_workspace_bytes": (ctypes.c_size_t, [_U32, _U32, _U32, _U32]),
     "paged_decode_num_splits": (_U32, [_U32, _U32, _U32, _U32, _U32, _U32, _U32]),
@@ -389,3 +394,47 @@ def paged_prefill_num_splits(num_seqs, q_len, num_q_heads, num_kv_heads, max_blo
     return int(lib().paged_prefill_num_splits(num_seqs, q_len, num_q_heads, num_kv_heads,
                                               max_blocks_per_seq, block_size, int(bool(causal)),
                                               sliding_window, num_cus))
+
+
+# ---------------------------------------------------------------- contiguous K/V
+
+def layout_strides(layout, num_seqs, length, num_heads, head_dim):
+    """Element strides (sequence, token, head) of a dense tensor in the
+    "blhd" (b, l, h, d) or "bhld" (b, h, l, d) layout."""
+    if layout == "blhd":
+        return (length * num_heads * head_dim, num_heads * head_dim, head_dim)
+    if layout == "bhld":
+        return (num_heads * length * head_dim, head_dim, length * head_dim)
+    raise PkdError(f"unknown layout {layout!r} (blhd or bhld)")
+
+
+def _strides_arg(q_strides, k_strides, v_strides, o_strides):
+    vals = [int(x) for x in (*q_strides, *k_strides, *v_strides, *o_strides)]
+    if len(vals) != 12:
+        raise PkdError("three strides each for q, k, v and the output")
+    return (ctypes.c_uint64 * 12)(*vals)
+
+
+def contig_kv_attn_bf16(q, k, v, output, seq_lens, num_seqs, q_len, max_seq_len, num_q_heads,
+                        num_kv_heads, head_dim, scale, q_strides, k_strides, v_strides,
+                        o_strides, causal=True, sliding_window=0, workspace=None, num_splits=1,
+                        stream=None):
+    _need_gpu(q, k, v, output, seq_lens, workspace)
+    st = _strides_arg(q_strides, k_strides, v_strides, o_strides)
+    _check(lib().contig_kv_attn_bf16(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(output), _ptr(seq_lens), num_seqs, q_len, max_seq_len,
+        num_q_heads, num_kv_heads, head_dim, float(scale), st, int(bool(causal)),
+        sliding_window, _ptr(workspace), num_splits, _stream(q, stream)), "contig_kv_attn_bf16")
+
+
+def contig_kv_attn_fp8(q, k, v, output, seq_lens, num_seqs, q_len, max_seq_len, num_q_heads,
+                       num_kv_heads, head_dim, scale, k_scale, v_scale, q_strides, k_strides,
+                       v_strides, o_strides, causal=True, sliding_window=0, workspace=None,
+                       num_splits=1, stream=None):
+    _need_gpu(q, k, v, output, seq_lens, workspace)
+    st = _strides_arg(q_strides, k_strides, v_strides, o_strides)
+    _check(lib().contig_kv_attn_fp8(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(output), _ptr(seq_lens), num_seqs, q_len, max_seq_len,
+        num_q_heads, num_kv_heads, head_dim, float(scale), float(k_scale), float(v_scale), st,
+        int(bool(causal)), sliding_window, _ptr(workspace), num_splits, _stream(q, stream)),
+        "contig_kv_attn_fp8")

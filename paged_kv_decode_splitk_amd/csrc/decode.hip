@@ -80,6 +80,11 @@ struct DecodeArgs {
   uint32_t q_tok_stride;   // elements between the rows of consecutive tokens
   uint32_t causal;         // token i sits at L - q_len + i and sees keys up to it
   uint32_t q_window;       // keys a token sees with causal: the last q_window up to it
+  uint32_t q_head_stride;  // elements between the q rows of consecutive heads (D by default)
+  uint64_t o_seq, o_tok, o_head;   // output element strides (sequence, token, head)
+  // contiguous K/V (no block table): byte strides of sequence, token, kv head
+  uint64_t k_strides[3];
+  uint64_t v_strides[3];
 };
 
 // Two FP8-E4M3FN codes (bytes 0/1 or 2/3 of w) -> packed BF16 pair, in one
@@ -371,6 +376,16 @@ __device__ __forceinline__ void append_token(const DecodeArgs& a, uint32_t b, ui
   }
 }
 
+// Query column col of kv head kvh: token qi = col / group and q head qh of
+// that token; false past the group * q_len columns (then qi = 0).
+__device__ __forceinline__ bool column_of(const DecodeArgs& a, uint32_t kvh, uint32_t col,
+                                          uint32_t& qi, uint32_t& qh) {
+  const bool ok = col < a.group * a.q_len;
+  qi = ok ? col / a.group : 0u;
+  qh = kvh * a.group + (col - qi * a.group);
+  return ok;
+}
+
 // One row piece: tiles [tau0, tau1) of row (b, kh), partial state to `slot`.
 // The row's NC chunks of 16 query columns share every K/V tile: each K or V
 // read from LDS feeds NC MFMAs.
@@ -378,12 +393,22 @@ __device__ __forceinline__ void append_token(const DecodeArgs& a, uint32_t b, ui
 // accumulates dims [w D/2, (w+1) D/2) of K, V, q and o, and the two halves of
 // every tile's logits are added through LDS (`xg`, two buffers used in turn,
 // `xturn` counting the exchanges of the launch).
-template <int FMT, int D, int DS, int NC>
+template <int FMT, int D, int DS, int NC, bool CONTIG>
 __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D / DS, DS>& sh,
                                           lds_u8* xg, uint32_t& xturn, uint32_t b, uint32_t kh,
                                           uint32_t tau0, uint32_t tau1, uint32_t slot, bool last,
                                           uint32_t L) {
   static_assert(DS == 1 || NC == 1, "a split head dim carries one column chunk");
+  static_assert(!CONTIG || FMT != kNvfp4, "contiguous K/V: BF16 and FP8 rows only");
+  // The piece is the same for every lane; saying so keeps the tile loop, the
+  // block-table walk and the load descriptors in scalar registers (a
+  // descriptor the compiler cannot prove uniform costs a loop per load).
+  b = __builtin_amdgcn_readfirstlane(b);
+  kh = __builtin_amdgcn_readfirstlane(kh);
+  tau0 = __builtin_amdgcn_readfirstlane(tau0);
+  tau1 = __builtin_amdgcn_readfirstlane(tau1);
+  slot = __builtin_amdgcn_readfirstlane(slot);
+  L = __builtin_amdgcn_readfirstlane(L);
   constexpr int DW = D / DS;                     // head dims of this wave
   using T = LdsTraits<FMT, DW, DS>;              // tile geometry of this wave's half rows
   using TF = LdsTraits<FMT, D>;                  // full rows (strides in the pools)
@@ -400,21 +425,18 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
   const uint32_t t0 = lo / 16 + tau0, t1 = lo / 16 + tau1;   // tiles of the sequence
   const uint32_t pa = t0 / tpp, pb = (t1 + tpp - 1) / tpp;
 
-  // column n of chunk k: query token qi, q head qh, read from q + qoff; its
-  // output / workspace row qrow; the keys [c_lo, c_hi) it attends: the row's
-  // range, or with causal the keys up to the token's position (the last
-  // q_window of them)
+  // column n of chunk k: query token qi, q head qh (column_of), read from
+  // q + qoff; the keys [c_lo, c_hi) it attends: the row's range, or with
+  // causal the keys up to the token's position (the last q_window of them)
   bool head_ok[NC];
-  uint64_t qrow[NC], qoff[NC];
+  uint64_t qoff[NC];
   uint32_t c_lo[NC], c_hi[NC];
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
-    const uint32_t col = (hc * NC + k) * 16 + n;
-    head_ok[k] = col < a.group * a.q_len;
-    const uint32_t qi = head_ok[k] ? col / a.group : 0u;
-    const uint32_t qh = kvh * a.group + (col - qi * a.group);
-    qrow[k] = (uint64_t(b) * a.q_len + qi) * a.num_q_heads + qh;
-    qoff[k] = uint64_t(b) * a.q_stride + uint64_t(qi) * a.q_tok_stride + uint64_t(qh) * D + w * DW;
+    uint32_t qi, qh;
+    head_ok[k] = column_of(a, kvh, (hc * NC + k) * 16 + n, qi, qh);
+    qoff[k] = uint64_t(b) * a.q_stride + uint64_t(qi) * a.q_tok_stride +
+              uint64_t(qh) * a.q_head_stride + w * DW;
     c_lo[k] = lo;
     c_hi[k] = L;
     if (a.causal && head_ok[k]) {
@@ -425,8 +447,10 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
   }
   const int32_t* bt = a.block_tables + uint64_t(b) * a.max_blocks;
   // append: written now, waited for only when the row's last tile is requested
-  bool pend = a.new_k != nullptr && last;
-  if (pend) append_token<FMT, D, DS>(a, b, kvh, L, w, lane);
+  bool pend = !CONTIG && a.new_k != nullptr && last;
+  if constexpr (!CONTIG) {
+    if (pend) append_token<FMT, D, DS>(a, b, kvh, L, w, lane);
+  }
 
   // q as the B operand of the QK MFMAs: column n, dims 32c + 8g .. +8;
   // issued ahead of the tile loads, which only ever wait for later loads.
@@ -494,9 +518,11 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
 
   // Segments of up to 64 pages: the block-table entries of a segment sit in
   // one VGPR (entry per lane); the DMA ring restarts at every segment.
-  for (uint32_t cp = pa; cp < pb; cp += 64) {
-    const uint32_t cpe = min(cp + 64, pb);
-    const int32_t bt_reg = (cp + lane < cpe) ? bt[cp + lane] : 0;
+  // Contiguous K/V: one segment of 16-key tiles.
+  for (uint32_t cp = pa; cp < pb;) {
+    const uint32_t cpe = CONTIG ? pb : min(cp + 64, pb);
+    int32_t bt_reg = 0;
+    if constexpr (!CONTIG) bt_reg = (cp + lane < cpe) ? bt[cp + lane] : 0;
     const uint32_t ct0 = max(cp * tpp, t0);
     const uint32_t ct1 = min(cpe * tpp, t1);
 
@@ -512,19 +538,36 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
         wait_vmcnt<0>();
         pend = false;
       }
-      const uint32_t page = min(t / tpp, cpe - 1);
-      const uint32_t phys = uint32_t(__builtin_amdgcn_readlane(bt_reg, int(page - cp)));
       const uint8_t* pool = kv ? a.v_cache : a.k_cache;
-      const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-          const_cast<uint8_t*>(pool + uint64_t(phys) * a.page_bytes), 0,
-          live ? int(a.page_bytes) : 0, 0x00020000);
-      const uint32_t off0 = (t % tpp) * 16;
+      __amdgpu_buffer_rsrc_t rsrc;
+      uint32_t off0 = 0, rstride = 0;       // paged: first row of the tile; contiguous: row bytes
+      if constexpr (CONTIG) {
+        // keys 16t .. 16t + 15 of sequence b, kv head kvh: the descriptor
+        // spans the tile's rows below L only
+        const uint64_t* st = kv ? a.v_strides : a.k_strides;
+        const uint32_t tok0 = t * 16;
+        const uint32_t nv = live ? min(16u, L - tok0) : 0u;
+        rstride = uint32_t(st[1]);
+        rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(pool + uint64_t(b) * st[0] + uint64_t(tok0) * st[1] +
+                                 uint64_t(kvh) * st[2]),
+            0, nv ? int((nv - 1) * rstride + TF::RB) : 0, 0x00020000);
+      } else {
+        const uint32_t page = min(t / tpp, cpe - 1);
+        const uint32_t phys = uint32_t(__builtin_amdgcn_readlane(bt_reg, int(page - cp)));
+        rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(pool + uint64_t(phys) * a.page_bytes), 0,
+            live ? int(a.page_bytes) : 0, 0x00020000);
+        off0 = (t % tpp) * 16;
+      }
       lds_u8* const dst = ring3 + s * T::SLOT + kv * T::KV;
 #pragma unroll
       for (int i = 0; i < T::NI; ++i) {
         const int row = i * T::RPI + ld_row;
         const int chunk = ld_pos ^ T::swz(row);
-        int voff = int(((off0 + row) * a.num_kv_heads + kvh) * TF::RB + w * T::RB + chunk * 16);
+        int voff = CONTIG ? int(row * rstride + w * T::RB + chunk * 16)
+                          : int(((off0 + row) * a.num_kv_heads + kvh) * TF::RB + w * T::RB +
+                                chunk * 16);
         if constexpr (T::RPI > 16) voff = row < 16 ? voff : 0x7FFFFFF0;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(dst + i * 1024), 16, voff,
                                                  0, 0, 2);
@@ -728,6 +771,7 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
     }
     wait_vmcnt<0>();                               // the ring restarts with the next segment
     wave_lds_fence();
+    cp = cpe;
   }
 
 #pragma unroll
@@ -736,10 +780,13 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
     // a column without keys (l = 0) writes zeros
     const float inv = l_tot > 0.0f ? a.out_scale / l_tot : 0.0f;
     if (!head_ok[k]) continue;
+    uint32_t qi, qh;
+    column_of(a, kvh, (hc * NC + k) * 16 + n, qi, qh);
     if (a.out) {
       // non-split: the whole row in one piece, the normalized output
       // straight to BF16
-      uint16_t* orow = a.out + qrow[k] * D + w * DW;
+      uint16_t* orow = a.out + uint64_t(b) * a.o_seq + uint64_t(qi) * a.o_tok +
+                       uint64_t(qh) * a.o_head + w * DW;
 #pragma unroll
       for (int mt = 0; mt < DW / 16; ++mt)
         *reinterpret_cast<u32x2*>(orow + 16 * mt + 4 * g) =
@@ -747,7 +794,9 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
                   pack_bf16x2(acc[k][mt][2] * inv, acc[k][mt][3] * inv)};
       continue;
     }
-    float* const wbase = a.ws + qrow[k] * a.num_splits * (D + 2);
+    // workspace row of the column: [B][q_len][Hq] order
+    const uint64_t qrow = (uint64_t(b) * a.q_len + qi) * a.num_q_heads + qh;
+    float* const wbase = a.ws + qrow * a.num_splits * (D + 2);
     float* wrow = wbase + uint64_t(slot) * (D + 2);
 #pragma unroll
     for (int mt = 0; mt < DW / 16; ++mt) {
@@ -778,11 +827,9 @@ __device__ __forceinline__ void zero_row(const DecodeArgs& a, uint32_t b, uint32
   const uint32_t kvh = kh / a.head_chunks, hc = kh % a.head_chunks;
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
-    const uint32_t col = (hc * NC + k) * 16 + n;
-    if (col >= a.group * a.q_len) continue;
-    const uint32_t qi = col / a.group;
-    uint16_t* orow = a.out + ((uint64_t(b) * a.q_len + qi) * a.num_q_heads + kvh * a.group +
-                              col - qi * a.group) * D;
+    uint32_t qi, qh;
+    if (!column_of(a, kvh, (hc * NC + k) * 16 + n, qi, qh)) continue;
+    uint16_t* orow = a.out + uint64_t(b) * a.o_seq + uint64_t(qi) * a.o_tok + uint64_t(qh) * a.o_head;
 #pragma unroll
     for (int mt = 0; mt < D / 16; ++mt)
       *reinterpret_cast<u32x2*>(orow + 16 * mt + 4 * g) = u32x2{0u, 0u};
@@ -806,7 +853,7 @@ constexpr int kWavesPerSimd = ((FMT != kBf16 && D <= 256) || kDSplit<D> > 1) ? 2
 template <int FMT, int D>
 constexpr int kMaxChunks = (FMT == kBf16 && D <= 128) ? 2 : 1;
 
-template <int FMT, int D, int NC>
+template <int FMT, int D, int NC, bool CONTIG>
 __global__ __launch_bounds__(64 * kDSplit<D>, (kWavesPerSimd<FMT, D>)) void splitk_stream(
     DecodeArgs a) {
   constexpr int DS = kDSplit<D>;
@@ -870,11 +917,24 @@ __global__ __launch_bounds__(64 * kDSplit<D>, (kWavesPerSimd<FMT, D>)) void spli
     const uint32_t tau0 = whole ? 0u : pos - start;
     const uint32_t tau1 = whole ? n : min(n, end - start);
     const uint32_t slot = whole ? 0u : pos / c - start / c;
-    run_piece<FMT, D, DS, NC>(a, mine, xg3, xturn, b, kh, tau0, tau1, slot,
+    run_piece<FMT, D, DS, NC, CONTIG>(a, mine, xg3, xturn, b, kh, tau0, tau1, slot,
                           whole || start + n <= end, L);
     if (whole) break;
     pos = start + tau1;
   }
+}
+
+// Where the combine writes query row bh (sequence-major: per_seq rows per
+// sequence, heads rows per token): element strides of sequence, token, head.
+struct OutMap {
+  uint64_t seq, tok, head;
+  uint32_t per_seq, heads;
+};
+
+__device__ __forceinline__ uint16_t* out_row(uint16_t* out, const OutMap& om, uint32_t bh) {
+  const uint32_t b = bh / om.per_seq, r = bh - b * om.per_seq;
+  const uint32_t i = r / om.heads, h = r - i * om.heads;
+  return out + uint64_t(b) * om.seq + uint64_t(i) * om.tok + uint64_t(h) * om.head;
 }
 
 // Combine: one workgroup of NT lanes per (sequence, q head); NT = 1024 when
@@ -885,8 +945,8 @@ __global__ __launch_bounds__(64 * kDSplit<D>, (kWavesPerSimd<FMT, D>)) void spli
 // partial sums are added in a fixed order (deterministic).
 template <int D, int NT>
 __global__ __launch_bounds__(NT) void reduce_kernel(const float* ws, uint16_t* out,
-                                                    const int32_t* seq_lens,
-                                                    uint32_t num_q_heads, uint32_t num_splits) {
+                                                    const int32_t* seq_lens, OutMap om,
+                                                    uint32_t num_splits) {
   constexpr int COLS = D / 2;                 // float2 columns of one split row
   constexpr int KS = NT / COLS;               // split lanes
   constexpr int NW = NT / 64;                 // waves
@@ -896,8 +956,8 @@ __global__ __launch_bounds__(NT) void reduce_kernel(const float* ws, uint16_t* o
   __shared__ f32x2 part[KS][COLS];
   const int tid = threadIdx.x;
   const uint32_t bh = blockIdx.x;
-  const uint32_t b = bh / num_q_heads;
-  uint16_t* o = out + uint64_t(bh) * D;
+  const uint32_t b = bh / om.per_seq;
+  uint16_t* o = out_row(out, om, bh);
   const float* base = ws + uint64_t(bh) * num_splits * (D + 2);
 
   // slot i counts if l_i > 0 and no earlier slot holds an end marker (l < 0)
@@ -986,18 +1046,17 @@ __global__ __launch_bounds__(NT) void reduce_kernel(const float* ws, uint16_t* o
 // same order, as the merged combine of the single-launch decode.
 template <int D>
 __global__ __launch_bounds__(64) void reduce_wave_kernel(const float* ws, uint16_t* out,
-                                                         const int32_t* seq_lens,
-                                                         uint32_t num_q_heads,
+                                                         const int32_t* seq_lens, OutMap om,
                                                          uint32_t num_splits) {
   constexpr int COLS = D / 2;                      // float2 columns of a slot
   constexpr int NC = COLS >= 64 ? COLS / 64 : 1;   // columns per lane
   const int lane = threadIdx.x;
   const uint32_t bh = blockIdx.x;
   const float* base = ws + uint64_t(bh) * num_splits * (D + 2);
-  uint16_t* o = out + uint64_t(bh) * D;
+  uint16_t* o = out_row(out, om, bh);
   f32x2 ml = {-__builtin_inff(), 0.0f};
   if (uint32_t(lane) < num_splits) ml = *reinterpret_cast<const f32x2*>(base + lane * (D + 2) + D);
-  const int32_t L = seq_lens[bh / num_q_heads];
+  const int32_t L = seq_lens[bh / om.per_seq];
   const uint64_t marks = __builtin_amdgcn_ballot_w64(uint32_t(lane) < num_splits && ml[1] < 0.0f);
   uint32_t stop = marks ? uint32_t(__builtin_ctzll(marks)) : num_splits;
   if (L <= 0) stop = 0;
@@ -1052,19 +1111,18 @@ static int launch_status() {
 }
 
 // Resident waves per CU of the stream kernel (workgroups x waves per workgroup).
-template <int FMT, int D, int NC>
+template <int FMT, int D, int NC, bool CONTIG>
 static int stream_occupancy() {
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, splitk_stream<FMT, D, NC>,
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, splitk_stream<FMT, D, NC, CONTIG>,
                                                    64 * kDSplit<D>, 0) != hipSuccess)
     return 0;
   return per_cu * kDSplit<D>;
 }
 
 // Waves the stream kernel launches on the current device: all resident at
-// once (at most the occupancy), cached per device, format, head_dim and
-// chunks per wave.
-template <int FMT, int D, int NC>
+// once (at most the occupancy), cached per device and kernel instance.
+template <int FMT, int D, int NC, bool CONTIG>
 static uint64_t stream_capacity() {
   static uint64_t cache[64];
   int dev = 0;
@@ -1073,7 +1131,7 @@ static uint64_t stream_capacity() {
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  int per_cu = stream_occupancy<FMT, D, NC>();
+  int per_cu = stream_occupancy<FMT, D, NC, CONTIG>();
   if (per_cu <= 0 || cus <= 0) return 0;
 #ifndef PKD_STREAM_WAVES_PER_CU
 #define PKD_STREAM_WAVES_PER_CU 4
@@ -1097,7 +1155,7 @@ static uint64_t stream_capacity() {
 }
 
 // One launch of the stream kernel with NC column chunks per wave.
-template <int FMT, int D, int NC>
+template <int FMT, int D, int NC, bool CONTIG>
 static int launch_stream(DecodeArgs a, hipStream_t stream) {
   constexpr uint64_t ds = kDSplit<D>;
   a.head_chunks = (a.col_chunks + NC - 1) / NC;
@@ -1110,35 +1168,35 @@ static int launch_stream(DecodeArgs a, hipStream_t stream) {
   uint64_t groups = rows;
   if (a.num_splits > 1) {
     groups = rows * a.num_splits;
-    const uint64_t cap = stream_capacity<FMT, D, NC>() / ds;
+    const uint64_t cap = stream_capacity<FMT, D, NC, CONTIG>() / ds;
     if (cap && groups > cap) groups = cap;
   }
   if (groups > 0x7FFFFFFFull) return kUnsupported;
-  hipLaunchKernelGGL((splitk_stream<FMT, D, NC>), dim3(uint32_t(groups)), dim3(uint32_t(64 * ds)),
-                     0, stream, a);
+  hipLaunchKernelGGL((splitk_stream<FMT, D, NC, CONTIG>), dim3(uint32_t(groups)),
+                     dim3(uint32_t(64 * ds)), 0, stream, a);
   return launch_status();
 }
 
 // Two chunks per wave when the row has them and the registers allow it.
-template <int FMT, int D>
+template <int FMT, int D, bool CONTIG>
 static int launch_stream_nc(const DecodeArgs& a, hipStream_t stream) {
   if constexpr (kMaxChunks<FMT, D> >= 2) {
-    if (a.col_chunks >= 2) return launch_stream<FMT, D, 2>(a, stream);
+    if (a.col_chunks >= 2) return launch_stream<FMT, D, 2, CONTIG>(a, stream);
   }
-  return launch_stream<FMT, D, 1>(a, stream);
+  return launch_stream<FMT, D, 1, CONTIG>(a, stream);
 }
 
-template <int FMT>
+template <int FMT, bool CONTIG = false>
 static int launch_splitk(DecodeArgs a, uint32_t num_seqs, uint32_t head_dim,
                          hipStream_t stream) {
   // one page must stay addressable by 32-bit buffer offsets
   if (a.page_bytes > 0x7FFF0000ull) return kUnsupported;
   a.num_seqs = num_seqs;
   switch (head_dim) {
-    case 64: return launch_stream_nc<FMT, 64>(a, stream);
-    case 128: return launch_stream_nc<FMT, 128>(a, stream);
-    case 256: return launch_stream_nc<FMT, 256>(a, stream);
-    case 512: return launch_stream_nc<FMT, 512>(a, stream);
+    case 64: return launch_stream_nc<FMT, 64, CONTIG>(a, stream);
+    case 128: return launch_stream_nc<FMT, 128, CONTIG>(a, stream);
+    case 256: return launch_stream_nc<FMT, 256, CONTIG>(a, stream);
+    case 512: return launch_stream_nc<FMT, 512, CONTIG>(a, stream);
     default: return kUnsupported;
   }
 }
@@ -1147,7 +1205,7 @@ static DecodeArgs make_args(const uint16_t* q, const void* kc, const void* vc, f
                             const int32_t* bt, const int32_t* lens, uint32_t max_blocks,
                             uint32_t Hq, uint32_t Hkv, uint32_t bs, float logit_scale,
                             float out_scale, uint32_t S, uint32_t q_stride, uint64_t page_bytes,
-                            uint64_t data_section, uint32_t window) {
+                            uint64_t data_section, uint32_t window, uint32_t head_dim) {
   DecodeArgs a;
   a.q = q;
   a.k_cache = static_cast<const uint8_t*>(kc);
@@ -1182,22 +1240,27 @@ static DecodeArgs make_args(const uint16_t* q, const void* kc, const void* vc, f
   a.q_tok_stride = 0;
   a.causal = 0;
   a.q_window = window;
+  a.q_head_stride = head_dim;
+  a.o_head = head_dim;                        // output [B][q_len][Hq][D], contiguous
+  a.o_tok = uint64_t(Hq) * head_dim;
+  a.o_seq = a.o_tok;
+  for (int i = 0; i < 3; ++i) a.k_strides[i] = a.v_strides[i] = 0;
   return a;
 }
 
 static int launch_reduce(const float* workspace, uint16_t* output, const int32_t* seq_lens,
-                         uint32_t num_q_heads, uint32_t head_dim, uint32_t num_splits,
+                         const OutMap& om, uint32_t head_dim, uint32_t num_splits,
                          uint32_t num_seqs, hipStream_t stream) {
-  const uint64_t grid = uint64_t(num_seqs) * num_q_heads;
+  const uint64_t grid = uint64_t(num_seqs) * om.per_seq;
   if (grid > 0x7FFFFFFFull) return kUnsupported;
   const dim3 gd = dim3(uint32_t(grid));
   if (num_splits <= 64) {                      // one wave per (b, h), registers only
     const dim3 bw = dim3(64);
     switch (head_dim) {
-      case 64: hipLaunchKernelGGL((reduce_wave_kernel<64>), gd, bw, 0, stream, workspace, output, seq_lens, num_q_heads, num_splits); break;
-      case 128: hipLaunchKernelGGL((reduce_wave_kernel<128>), gd, bw, 0, stream, workspace, output, seq_lens, num_q_heads, num_splits); break;
-      case 256: hipLaunchKernelGGL((reduce_wave_kernel<256>), gd, bw, 0, stream, workspace, output, seq_lens, num_q_heads, num_splits); break;
-      case 512: hipLaunchKernelGGL((reduce_wave_kernel<512>), gd, bw, 0, stream, workspace, output, seq_lens, num_q_heads, num_splits); break;
+      case 64: hipLaunchKernelGGL((reduce_wave_kernel<64>), gd, bw, 0, stream, workspace, output, seq_lens, om, num_splits); break;
+      case 128: hipLaunchKernelGGL((reduce_wave_kernel<128>), gd, bw, 0, stream, workspace, output, seq_lens, om, num_splits); break;
+      case 256: hipLaunchKernelGGL((reduce_wave_kernel<256>), gd, bw, 0, stream, workspace, output, seq_lens, om, num_splits); break;
+      case 512: hipLaunchKernelGGL((reduce_wave_kernel<512>), gd, bw, 0, stream, workspace, output, seq_lens, om, num_splits); break;
       default: return kUnsupported;
     }
     return launch_status();
@@ -1206,8 +1269,8 @@ static int launch_reduce(const float* workspace, uint16_t* output, const int32_t
   const bool wide = num_splits >= 64;          // many slots: more lanes per (b, h)
   const dim3 bd = dim3(wide ? 1024 : 256);
 #define PKD_REDUCE(DD) \
-  if (wide) hipLaunchKernelGGL((reduce_kernel<DD, 1024>), gd, bd, lds, stream, workspace, output, seq_lens, num_q_heads, num_splits); \
-  else hipLaunchKernelGGL((reduce_kernel<DD, 256>), gd, bd, lds, stream, workspace, output, seq_lens, num_q_heads, num_splits);
+  if (wide) hipLaunchKernelGGL((reduce_kernel<DD, 1024>), gd, bd, lds, stream, workspace, output, seq_lens, om, num_splits); \
+  else hipLaunchKernelGGL((reduce_kernel<DD, 256>), gd, bd, lds, stream, workspace, output, seq_lens, om, num_splits);
   switch (head_dim) {
     case 64: PKD_REDUCE(64) break;
     case 128: PKD_REDUCE(128) break;
@@ -1221,17 +1284,17 @@ static int launch_reduce(const float* workspace, uint16_t* output, const int32_t
 
 // Non-split decode (num_splits 1): one wave per row writes the output. More
 // splits: the split-K pass and the combine, as two launches.
-template <int FMT>
+template <int FMT, bool CONTIG = false>
 static int launch_decode(DecodeArgs a, uint16_t* output, uint32_t num_seqs, uint32_t head_dim,
                          hipStream_t stream) {
   if (a.num_splits > 1) {
-    const int st = launch_splitk<FMT>(a, num_seqs, head_dim, stream);
+    const int st = launch_splitk<FMT, CONTIG>(a, num_seqs, head_dim, stream);
     if (st) return st;
-    return launch_reduce(a.ws, output, a.seq_lens, a.num_q_heads * a.q_len, head_dim,
-                         a.num_splits, num_seqs, stream);
+    const OutMap om = {a.o_seq, a.o_tok, a.o_head, a.num_q_heads * a.q_len, a.num_q_heads};
+    return launch_reduce(a.ws, output, a.seq_lens, om, head_dim, a.num_splits, num_seqs, stream);
   }
   a.out = output;
-  return launch_splitk<FMT>(a, num_seqs, head_dim, stream);
+  return launch_splitk<FMT, CONTIG>(a, num_seqs, head_dim, stream);
 }
 
 }  // namespace pkd
@@ -1253,7 +1316,7 @@ extern "C" PKD_API int paged_decode_attn_splitk_bf16(
   DecodeArgs a = make_args(q, k_cache, v_cache, workspace, block_tables, seq_lens,
                            max_blocks_per_seq, num_q_heads, num_kv_heads, block_size,
                            scale * kLog2e, 1.0f, num_splits, q_stride, page_bytes, 0,
-                           sliding_window);
+                           sliding_window, head_dim);
   return launch_splitk<kBf16>(a, num_seqs, head_dim, stream);
 }
 
@@ -1273,7 +1336,7 @@ extern "C" PKD_API int paged_decode_attn_splitk_fp8(
   DecodeArgs a = make_args(q, k_cache, v_cache, workspace, block_tables, seq_lens,
                            max_blocks_per_seq, num_q_heads, num_kv_heads, block_size,
                            scale * k_scale * kLog2e, v_scale, num_splits, q_stride, cache_stride,
-                           0, sliding_window);
+                           0, sliding_window, head_dim);
   return launch_splitk<kFp8>(a, num_seqs, head_dim, stream);
 }
 
@@ -1295,7 +1358,7 @@ extern "C" PKD_API int paged_decode_attn_splitk_nvfp4(
   DecodeArgs a = make_args(q, k_cache, v_cache, workspace, block_tables, seq_lens,
                            max_blocks_per_seq, num_q_heads, num_kv_heads, block_size,
                            scale * kLog2e, 1.0f, num_splits, q_stride, block_stride_bytes,
-                           data_section_bytes, sliding_window);
+                           data_section_bytes, sliding_window, head_dim);
   return launch_splitk<kNvfp4>(a, num_seqs, head_dim, stream);
 }
 
@@ -1316,7 +1379,7 @@ extern "C" PKD_API int paged_decode_attn_splitk_append_bf16(
   DecodeArgs a = make_args(q, k_cache, v_cache, workspace, block_tables, seq_lens,
                            max_blocks_per_seq, num_q_heads, num_kv_heads, block_size,
                            scale * kLog2e, 1.0f, num_splits, q_stride, page_bytes, 0,
-                           sliding_window);
+                           sliding_window, head_dim);
   a.new_k = key; a.new_v = value; a.new_k_stride = key_stride; a.new_v_stride = value_stride;
   return launch_splitk<kBf16>(a, num_seqs, head_dim, stream);
 }
@@ -1340,7 +1403,7 @@ extern "C" PKD_API int paged_decode_attn_splitk_append_fp8(
   DecodeArgs a = make_args(q, k_cache, v_cache, workspace, block_tables, seq_lens,
                            max_blocks_per_seq, num_q_heads, num_kv_heads, block_size,
                            scale * k_scale * kLog2e, v_scale, num_splits, q_stride, cache_stride,
-                           0, sliding_window);
+                           0, sliding_window, head_dim);
   a.new_k = key; a.new_v = value; a.new_k_stride = key_stride; a.new_v_stride = value_stride;
   a.enc_k_scale = k_scale; a.enc_v_scale = v_scale;
   return launch_splitk<kFp8>(a, num_seqs, head_dim, stream);
@@ -1366,7 +1429,7 @@ extern "C" PKD_API int paged_decode_attn_splitk_append_nvfp4(
   DecodeArgs a = make_args(q, k_cache, v_cache, workspace, block_tables, seq_lens,
                            max_blocks_per_seq, num_q_heads, num_kv_heads, block_size,
                            scale * kLog2e, 1.0f, num_splits, q_stride, block_stride_bytes,
-                           data_section_bytes, sliding_window);
+                           data_section_bytes, sliding_window, head_dim);
   a.new_k = key; a.new_v = value; a.new_k_stride = key_stride; a.new_v_stride = value_stride;
   return launch_splitk<kNvfp4>(a, num_seqs, head_dim, stream);
 }
@@ -1386,7 +1449,7 @@ extern "C" PKD_API int paged_decode_attn_bf16(
   DecodeArgs a = make_args(q, k_cache, v_cache, workspace, block_tables, seq_lens,
                            max_blocks_per_seq, num_q_heads, num_kv_heads, block_size,
                            scale * kLog2e, 1.0f, num_splits, q_stride, page_bytes, 0,
-                           sliding_window);
+                           sliding_window, head_dim);
   return launch_decode<kBf16>(a, output, num_seqs, head_dim, stream);
 }
 
@@ -1407,7 +1470,7 @@ extern "C" PKD_API int paged_decode_attn_fp8(
   DecodeArgs a = make_args(q, k_cache, v_cache, workspace, block_tables, seq_lens,
                            max_blocks_per_seq, num_q_heads, num_kv_heads, block_size,
                            scale * k_scale * kLog2e, v_scale, num_splits, q_stride, cache_stride,
-                           0, sliding_window);
+                           0, sliding_window, head_dim);
   return launch_decode<kFp8>(a, output, num_seqs, head_dim, stream);
 }
 
@@ -1429,7 +1492,7 @@ extern "C" PKD_API int paged_decode_attn_nvfp4(
   DecodeArgs a = make_args(q, k_cache, v_cache, workspace, block_tables, seq_lens,
                            max_blocks_per_seq, num_q_heads, num_kv_heads, block_size,
                            scale * kLog2e, 1.0f, num_splits, q_stride, block_stride_bytes,
-                           data_section_bytes, sliding_window);
+                           data_section_bytes, sliding_window, head_dim);
   return launch_decode<kNvfp4>(a, output, num_seqs, head_dim, stream);
 }
 
@@ -1444,6 +1507,7 @@ static void set_query_block(DecodeArgs& a, uint32_t q_len, uint32_t q_token_stri
   a.q_window = sliding_window;
   a.window = prefill_row_window(q_len, a.causal, sliding_window);
   a.col_chunks = head_chunks(a.group * q_len);
+  a.o_seq = uint64_t(q_len) * a.o_tok;
 }
 
 extern "C" PKD_API int paged_prefill_attn_bf16(
@@ -1464,7 +1528,7 @@ extern "C" PKD_API int paged_prefill_attn_bf16(
   DecodeArgs a = make_args(q, k_cache, v_cache, workspace, block_tables, seq_lens,
                            max_blocks_per_seq, num_q_heads, num_kv_heads, block_size,
                            scale * kLog2e, 1.0f, num_splits, q_stride, page_bytes, 0,
-                           sliding_window);
+                           sliding_window, head_dim);
   set_query_block(a, q_len, q_token_stride, causal, sliding_window);
   return launch_decode<kBf16>(a, output, num_seqs, head_dim, stream);
 }
@@ -1488,7 +1552,7 @@ extern "C" PKD_API int paged_prefill_attn_fp8(
   DecodeArgs a = make_args(q, k_cache, v_cache, workspace, block_tables, seq_lens,
                            max_blocks_per_seq, num_q_heads, num_kv_heads, block_size,
                            scale * k_scale * kLog2e, v_scale, num_splits, q_stride, cache_stride,
-                           0, sliding_window);
+                           0, sliding_window, head_dim);
   set_query_block(a, q_len, q_token_stride, causal, sliding_window);
   return launch_decode<kFp8>(a, output, num_seqs, head_dim, stream);
 }
@@ -1514,9 +1578,61 @@ extern "C" PKD_API int paged_prefill_attn_nvfp4(
   DecodeArgs a = make_args(q, k_cache, v_cache, workspace, block_tables, seq_lens,
                            max_blocks_per_seq, num_q_heads, num_kv_heads, block_size,
                            scale * kLog2e, 1.0f, num_splits, q_stride, block_stride_bytes,
-                           data_section_bytes, sliding_window);
+                           data_section_bytes, sliding_window, head_dim);
   set_query_block(a, q_len, q_token_stride, causal, sliding_window);
   return launch_decode<kNvfp4>(a, output, num_seqs, head_dim, stream);
+}
+
+// Contiguous K/V: 16-key tiles addressed through the caller's strides; the
+// tile bound comes from max_seq_len. Strides: q (seq, token, head), k, v,
+// output, in elements.
+template <int FMT>
+static int contig_attn(const uint16_t* q, const void* k, const void* v, uint16_t* output,
+                       const int32_t* seq_lens, uint32_t num_seqs, uint32_t q_len,
+                       uint32_t max_seq_len, uint32_t num_q_heads, uint32_t num_kv_heads,
+                       uint32_t head_dim, float logit_scale, float out_scale,
+                       const uint64_t* strides, uint32_t causal, uint32_t sliding_window,
+                       float* workspace, uint32_t num_splits, hipStream_t stream) {
+  if (num_seqs == 0) return kOk;
+  const uint32_t esize = FMT == kBf16 ? 2 : 1;
+  int st = check_contig(q, k, v, output, workspace, seq_lens, strides, num_seqs, q_len,
+                        max_seq_len, num_q_heads, num_kv_heads, head_dim, esize, num_splits);
+  if (st) return st;
+  DecodeArgs a = make_args(q, k, v, workspace, nullptr, seq_lens, (max_seq_len + 15) / 16,
+                           num_q_heads, num_kv_heads, 16, logit_scale, out_scale, num_splits,
+                           uint32_t(strides[0]), 0, 0, sliding_window, head_dim);
+  set_query_block(a, q_len, uint32_t(strides[1]), causal, sliding_window);
+  a.q_head_stride = uint32_t(strides[2]);
+  for (int i = 0; i < 3; ++i) {
+    a.k_strides[i] = strides[3 + i] * esize;
+    a.v_strides[i] = strides[6 + i] * esize;
+  }
+  a.o_seq = strides[9];
+  a.o_tok = strides[10];
+  a.o_head = strides[11];
+  return launch_decode<FMT, true>(a, output, num_seqs, head_dim, stream);
+}
+
+extern "C" PKD_API int contig_kv_attn_bf16(
+    const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* output,
+    const int32_t* seq_lens, uint32_t num_seqs, uint32_t q_len, uint32_t max_seq_len,
+    uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim, float scale,
+    const uint64_t* strides, uint32_t causal, uint32_t sliding_window, float* workspace,
+    uint32_t num_splits, hipStream_t stream) {
+  return contig_attn<kBf16>(q, k, v, output, seq_lens, num_seqs, q_len, max_seq_len,
+                            num_q_heads, num_kv_heads, head_dim, scale * kLog2e, 1.0f, strides,
+                            causal, sliding_window, workspace, num_splits, stream);
+}
+
+extern "C" PKD_API int contig_kv_attn_fp8(
+    const uint16_t* q, const uint8_t* k, const uint8_t* v, uint16_t* output,
+    const int32_t* seq_lens, uint32_t num_seqs, uint32_t q_len, uint32_t max_seq_len,
+    uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim, float scale, float k_scale,
+    float v_scale, const uint64_t* strides, uint32_t causal, uint32_t sliding_window,
+    float* workspace, uint32_t num_splits, hipStream_t stream) {
+  return contig_attn<kFp8>(q, k, v, output, seq_lens, num_seqs, q_len, max_seq_len, num_q_heads,
+                           num_kv_heads, head_dim, scale * k_scale * kLog2e, v_scale, strides,
+                           causal, sliding_window, workspace, num_splits, stream);
 }
 
 extern "C" PKD_API uint32_t paged_prefill_num_splits(uint32_t num_seqs, uint32_t q_len,
@@ -1538,8 +1654,8 @@ extern "C" PKD_API int paged_decode_attn_reduce(const float* workspace, uint16_t
   if (num_seqs == 0) return kOk;
   int st = check_reduce(workspace, output, seq_lens, num_q_heads, head_dim, num_splits);
   if (st) return st;
-  return launch_reduce(workspace, output, seq_lens, num_q_heads, head_dim, num_splits, num_seqs,
-                       stream);
+  const OutMap om = {uint64_t(num_q_heads) * head_dim, 0, head_dim, num_q_heads, num_q_heads};
+  return launch_reduce(workspace, output, seq_lens, om, head_dim, num_splits, num_seqs, stream);
 }
 
 extern "C" PKD_API size_t paged_decode_workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads,

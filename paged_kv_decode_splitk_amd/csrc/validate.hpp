@@ -114,6 +114,39 @@ inline uint32_t prefill_row_window(uint32_t q_len, uint32_t causal, uint32_t sli
   return w > 0xFFFFFFFFull ? 0u : uint32_t(w);
 }
 
+// The contiguous-K/V calls. strides: 12 element strides, q (seq, token,
+// head), k, v, output; every one a multiple of 16 bytes, so that rows stay
+// 16-byte aligned; a K/V token stride small enough that 16 rows stay within
+// 32-bit buffer offsets.
+inline int check_contig(const void* q, const void* k, const void* v, const void* out,
+                        const void* ws, const void* lens, const uint64_t* strides,
+                        uint32_t num_seqs, uint32_t q_len, uint32_t max_seq_len,
+                        uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
+                        uint32_t kv_elem_bytes, uint32_t num_splits) {
+  if (num_kv_heads == 0 || num_q_heads == 0 || num_q_heads % num_kv_heads) return kInvalid;
+  if (!supported_head_dim(head_dim)) return kUnsupported;
+  if (num_splits == 0 || num_splits > kMaxSplits) return kUnsupported;
+  if (q_len == 0) return kInvalid;
+  if (q_len > kMaxQueryLen || uint64_t(num_q_heads) * q_len > 0x7FFFFFFFull) return kUnsupported;
+  if (max_seq_len == 0 || max_seq_len > 0x7FFFFFF0u) return kInvalid;
+  if (!strides || !q || !k || !v || !out || !lens || (num_splits > 1 && !ws)) return kInvalid;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return kInvalid;
+  if (num_splits > 1 && !aligned16(ws)) return kInvalid;
+  for (int i = 0; i < 12; ++i) {
+    const uint64_t bytes = (i >= 3 && i < 9) ? kv_elem_bytes : 2;
+    if ((strides[i] * bytes) % 16) return kInvalid;
+  }
+  // q / output strides fit the kernel's 32-bit q fields; K/V tiles of 16 rows
+  // stay within 32-bit buffer offsets
+  if (strides[0] > 0xFFFFFFFFull || strides[1] > 0xFFFFFFFFull || strides[2] > 0xFFFFFFFFull)
+    return kUnsupported;
+  const uint64_t row = uint64_t(head_dim) * kv_elem_bytes;
+  for (int i : {4, 7})
+    if (strides[i] * kv_elem_bytes * 15 + row > 0x7FFFFFF0ull) return kUnsupported;
+  (void)num_seqs;
+  return kOk;
+}
+
 inline int check_reduce(const void* ws, const void* out, const void* lens, uint32_t num_q_heads,
                         uint32_t head_dim, uint32_t num_splits) {
   if (num_q_heads == 0) return kInvalid;

@@ -231,3 +231,40 @@ def test_prefill_num_splits(lib):
     assert ns(1, 8, 32, 8, 2048, 16, 1, 64, 256) == dec(1, 256, 8, 2048, 16, 71, 256)
     assert ns(1, 8, 32, 8, 2048, 16, 0, 64, 256) == dec(1, 256, 8, 2048, 16, 64, 256)
     assert ns(1, 0, 32, 8, 2048, 16, 1, 0, 256) == 1
+
+
+def test_contig_validation(lib):
+    import ctypes
+    f = lib.contig_kv_attn_bf16
+    good = [2 * 4 * 256, 256, 64, 48 * 128, 128, 64, 48 * 128, 128, 64, 4 * 256, 256, 64]
+
+    def arr(v):
+        return (ctypes.c_uint64 * 12)(*v)
+
+    # q, k, v, out, lens, B, q_len, max_len, Hq, Hkv, D, scale, strides, causal, W, ws, S
+    def call(strides=good, **kw):
+        a = [A16, A16, A16, A16, A16, 2, 4, 48, 4, 2, 64, 0.125, arr(strides), 1, 0, A16, 2, None]
+        for k, v in kw.items():
+            a[{"q": 0, "out": 3, "B": 5, "n": 6, "maxlen": 7, "D": 10, "ws": 15, "S": 16}[k]] = v
+        return f(*a)
+
+    for i in range(12):                       # every stride a multiple of 16 bytes
+        bad = list(good)
+        bad[i] += 4
+        assert call(bad) == -1, i
+    huge = list(good)
+    huge[4] = 1 << 28                         # 16 K rows past 2^31 bytes
+    assert call(huge) == -2
+    assert call(n=0) == -1
+    assert call(maxlen=0) == -1
+    assert call(D=96) == -2
+    assert call(out=None) == -1
+    assert call(ws=None) == -1                # num_splits > 1 needs the workspace
+    assert call(q=A16 + 2) == -1
+    assert call(B=0, out=None) == 0           # no sequences: a no-op
+    assert f(A16, A16, A16, A16, A16, 2, 4, 48, 4, 2, 64, 0.125, None, 1, 0, A16, 2, None) == -1
+    f8 = lib.contig_kv_attn_fp8
+    odd = list(good)
+    odd[4] = 72                               # 72 one-byte codes: not a multiple of 16 bytes
+    assert f8(A16, A16, A16, A16, A16, 2, 4, 48, 4, 2, 64, 0.125, 1.0, 1.0, arr(odd), 1, 0, A16,
+              2, None) == -1
