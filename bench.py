@@ -16,7 +16,8 @@ Prints ONE JSON line: KV-read GB/s and us/step on the Llama-3-8B-shaped batch
 dominant kernel (back-to-back launches timed with HIP events on their
 stream), and the float64 CPU oracle timed on the host. Beside them: a causal
 query block of q_len tokens per sequence (speculative verify) over the same
-batch, through the multi-token call (--verify workload:q_len).
+batch, through the multi-token call (--verify workload:q_len), and the same
+decode over contiguous K/V tensors (--contig workload:layout).
 
   python bench.py [--steps K] [--warmup W] [--workload NAME] [--extra NAME ...]
   python bench.py --verify-only --verify llama8b:4   # the multi-token call alone
@@ -254,6 +255,40 @@ def _graph_time(fn, calls, reps):
     return a.elapsed_time(b) / (reps * calls)
 
 
+STEPS_PER_GRAPH = 32
+
+
+def _steps_time(fn, NL, steps):
+    """ms per step of exactly `steps` steps fn(layer), cycling over the NL
+    layers. The steps are captured as a model's layers are, many to a graph
+    (whole cycles of at least STEPS_PER_GRAPH steps, plus one graph for the
+    remainder), so that the host's graph launches stay off the step time;
+    every kernel boundary inside a graph is still in it."""
+    import torch
+    per_graph = NL * max(1, -(-STEPS_PER_GRAPH // NL))
+    full, rem = divmod(steps, per_graph)
+    graphs = []
+    for count, n in ((full, per_graph), (1 if rem else 0, rem)):
+        if count == 0:
+            continue
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(n):
+                fn(i % NL)
+        g.replay()
+        graphs.append((g, count))
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for g, count in graphs:
+        for _ in range(count):
+            g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    del graphs
+    return a.elapsed_time(b) / steps
+
+
 def time_workload(name, steps, warmup, kernel_reps=100, single=True):
     import torch
     import workloads
@@ -267,14 +302,13 @@ def time_workload(name, steps, warmup, kernel_reps=100, single=True):
         if single:
             lay.step_single(i % NL)
     torch.cuda.synchronize()
-    reps = max(1, -(-steps // NL))
-    steps_run = reps * NL
+    steps_run = steps
     t0 = time.perf_counter()
-    ms_step = _graph_time(lay.step, NL, reps)
+    ms_step = _steps_time(lay.step, NL, steps)
     wall = time.perf_counter() - t0
-    ms_sep = _graph_time(lay.step_separate, NL, reps)
+    ms_sep = _steps_time(lay.step_separate, NL, steps)
     nan = float("nan")
-    ms_single = _graph_time(lay.step_single, NL, reps) if single else nan
+    ms_single = _steps_time(lay.step_single, NL, steps) if single else nan
     # the kernels alone: back-to-back launches rotating over the layers
     single_ms = _graph_time(lambda i: lay.decode(i % NL), kernel_reps, 3) if single else nan
     k_ms = _graph_time(lambda i: lay.splitk_append(i % NL), kernel_reps, 3)
@@ -370,8 +404,7 @@ def time_verify(name, q_lens, steps, warmup, kernel_reps=100):
         for i in range(max(1, warmup)):
             vb.call(i % NL)
         torch.cuda.synchronize()
-        reps = max(1, -(-steps // NL))
-        ms = _graph_time(vb.call, NL, reps)
+        ms = _steps_time(vb.call, NL, steps)
         red_ms = _graph_time(lambda i: vb.reduce(i % NL), kernel_reps, 3)
         kv_bytes = verify_tokens(w, n) * kv_bytes_per_token(w)
         split_us = (ms - red_ms) * 1e3
@@ -386,6 +419,90 @@ def time_verify(name, q_lens, steps, warmup, kernel_reps=100):
             query_tokens_per_s=w.num_seqs * n / (ms * 1e-3))
         del vb
     del lay
+    torch.cuda.empty_cache()
+    return res
+
+
+class ContigLayers:
+    """A workload's K/V as contiguous (b, h, l, d) or (b, l, h, d) tensors
+    with l = the block-table capacity, NL layers of them (rotated like the
+    paged pools), and the contiguous-K/V call over them (decode, q_len 1)."""
+
+    def __init__(self, w, layout="bhld", dev="cuda:0"):
+        import torch
+        import paged_kv_decode_splitk_amd as pkd
+        assert w.kv_dtype == "bf16", "contiguous timing: BF16 workloads"
+        self.w, self.dev, self.layout = w, torch.device(dev), layout
+        B, Hq, Hkv, D = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim
+        self.Lmax = w.max_blocks_per_seq * w.block_size
+        per_layer = 2 * B * self.Lmax * Hkv * D * 2
+        self.num_layers = max(2, int(np.ceil(4 * MALL_BYTES / per_layer)))
+        self.pool_bytes = per_layer
+        rows = torch.from_numpy(w.token_seq.astype(np.int64) * self.Lmax +
+                                w.token_pos.astype(np.int64)).to(self.dev)
+
+        def dense(bits):
+            src = torch.from_numpy(bits.reshape(w.num_tokens, -1).view(np.int16)).to(self.dev)
+            t = torch.zeros((B * self.Lmax, Hkv * D), dtype=torch.int16, device=self.dev)
+            t[rows] = src
+            t = t.view(B, self.Lmax, Hkv, D)
+            if layout == "bhld":
+                t = t.permute(0, 2, 1, 3).contiguous()
+            return t.reshape(-1)
+
+        self.k = [dense(w.k_bits) for _ in range(self.num_layers)]
+        self.v = [dense(w.v_bits) for _ in range(self.num_layers)]
+        self.kv_strides = pkd.layout_strides(layout, B, self.Lmax, Hkv, D)
+        self.q = torch.from_numpy(w.q_bits.reshape(-1).view(np.int16)).to(self.dev)
+        self.lens = torch.from_numpy(w.seq_lens).to(self.dev)
+        cus = torch.cuda.get_device_properties(self.dev).multi_processor_count
+        self.num_splits = pkd.paged_decode_num_splits(B, Hq, Hkv, w.max_blocks_per_seq,
+                                                      w.block_size, w.sliding_window, cus)
+        self.ws = torch.empty(pkd.paged_decode_workspace_bytes(B, Hq, D, self.num_splits) // 4,
+                              dtype=torch.float32, device=self.dev)
+        self.out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=self.dev)
+        torch.cuda.synchronize()
+
+    def call(self, layer):
+        import paged_kv_decode_splitk_amd as pkd
+        w = self.w
+        B, Hq, Hkv, D = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim
+        qs = (Hq * D, Hq * D, D)
+        pkd.contig_kv_attn_bf16(self.q, self.k[layer], self.v[layer], self.out, self.lens, B, 1,
+                                self.Lmax, Hq, Hkv, D, float(w.scale), qs, self.kv_strides,
+                                self.kv_strides, qs, causal=True,
+                                sliding_window=w.sliding_window, workspace=self.ws,
+                                num_splits=self.num_splits)
+
+    def reduce(self, layer):
+        import paged_kv_decode_splitk_amd as pkd
+        w = self.w
+        pkd.paged_decode_attn_reduce(self.ws, self.out, self.lens, w.num_q_heads, w.head_dim,
+                                     self.num_splits, w.num_seqs)
+
+
+def time_contig(name, layout, steps, warmup, kernel_reps=100):
+    """us per contiguous-K/V decode call (split-K pass + combine, graph
+    replay over the layers) and the split-K pass alone (call minus combine)."""
+    import torch
+    import workloads
+    w = workloads.make_workload(name)
+    cl = ContigLayers(w, layout)
+    NL = cl.num_layers
+    for i in range(max(1, warmup)):
+        cl.call(i % NL)
+    torch.cuda.synchronize()
+    ms = _steps_time(cl.call, NL, steps)
+    red_ms = _graph_time(lambda i: cl.reduce(i % NL), kernel_reps, 3)
+    kv_bytes = attended_tokens(w) * kv_bytes_per_token(w)
+    split_us = (ms - red_ms) * 1e3
+    res = dict(layout=layout, num_splits=cl.num_splits, layers_rotated=NL,
+               kv_bytes_per_step=kv_bytes, us_per_step=ms * 1e3,
+               kv_gbs=kv_bytes / (ms * 1e-3) / 1e9,
+               pct_of_peak=100.0 * kv_bytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS,
+               combine_us=red_ms * 1e3, splitk_us=split_us,
+               splitk_gbs=kv_bytes / (split_us * 1e-6) / 1e9)
+    del cl
     torch.cuda.empty_cache()
     return res
 
@@ -490,6 +607,8 @@ def main():
                          "split-K launches of the kernel)")
     ap.add_argument("--verify", nargs="*", default=["llama8b:4", "llama8b:8"],
                     help="multi-token (causal query block) timings, as workload:q_len")
+    ap.add_argument("--contig", nargs="*", default=["llama8b:bhld"],
+                    help="contiguous-K/V decode timings, as workload:layout (BF16)")
     ap.add_argument("--verify-only", action="store_true",
                     help="only the --verify timings (for kernel statistics of that call)")
     ap.add_argument("--counter-run", action="store_true",
@@ -513,6 +632,9 @@ def main():
         for spec in args.verify:
             nm, n = spec.split(":")
             out.update(time_verify(nm, [int(n)], args.steps, args.warmup))
+        for spec in args.contig:
+            nm, lay = spec.split(":")
+            out[f"contig_{nm}_{lay}"] = time_contig(nm, lay, args.steps, args.warmup)
         print(json.dumps({"verify": out}))
         return
     print(f"bench: {args.workload} steps={args.steps} warmup={args.warmup}", file=sys.stderr,
@@ -546,6 +668,13 @@ def main():
             print(f"bench: verify {k} {v['us_per_step']:.2f} us/step {v['kv_gbs']:.0f} GB/s",
                   file=sys.stderr, flush=True)
         verify.update(r)
+    contig = {}
+    for spec in args.contig:
+        nm, lay = spec.split(":")
+        r = time_contig(nm, lay, args.steps, args.warmup)
+        print(f"bench: contiguous {nm} {lay} {r['us_per_step']:.2f} us/step "
+              f"{r['kv_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
+        contig[f"{nm}_{lay}"] = r
 
     # the step's dominant kernel: the split-K pass (with the append)
     fmt = main_res["kv_dtype"]
@@ -596,6 +725,8 @@ def main():
         line[name] = r
     if verify:
         line["verify"] = verify
+    if contig:
+        line["contiguous_kv"] = contig
     print(json.dumps(line))
 
 
