@@ -599,6 +599,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="llama8b")
     ap.add_argument("--extra", nargs="*", default=["b1_32k"])
+    ap.add_argument("--sweep", nargs="*", default=["b1_1k", "b1_4k", "b1_8k", "b1_16k"],
+                    help="B=1 context sweep: step and split-K kernel per context")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -657,6 +659,15 @@ def main():
         print(f"bench: {name} {r['us_per_step']:.2f} us/step {r['kv_gbs']:.0f} GB/s",
               file=sys.stderr, flush=True)
 
+    sweep = {}
+    for name in args.sweep:
+        r, _ = time_workload(name, args.steps, args.warmup, single=False)
+        sweep[name] = {k: r[k] for k in ("us_per_step", "kv_gbs", "pct_of_peak", "splitk_us",
+                                         "splitk_gbs", "splitk_plain_us", "splitk_plain_gbs",
+                                         "num_splits", "kv_bytes_per_step")}
+        print(f"bench: sweep {name} {r['us_per_step']:.2f} us/step, split-K "
+              f"{r['splitk_plain_us']:.2f} us {r['splitk_plain_gbs']:.0f} GB/s",
+              file=sys.stderr, flush=True)
     verify = {}
     by_name = {}
     for spec in args.verify:
@@ -723,6 +734,8 @@ def main():
     }
     for name, r in extras.items():
         line[name] = r
+    if sweep:
+        line["b1_sweep"] = sweep
     if verify:
         line["verify"] = verify
     if contig:

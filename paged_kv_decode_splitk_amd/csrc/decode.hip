@@ -1146,9 +1146,13 @@ static uint64_t stream_capacity() {
 #ifndef PKD_STREAM_WAVES_PER_CU_NC
 #define PKD_STREAM_WAVES_PER_CU_NC 4
 #endif
+#ifndef PKD_STREAM_WAVES_PER_CU_FP8
+#define PKD_STREAM_WAVES_PER_CU_FP8 4
+#endif
   const int cap = FMT == kBf16 && D < 512
                       ? (NC > 1 ? PKD_STREAM_WAVES_PER_CU_NC : PKD_STREAM_WAVES_PER_CU)
-                      : PKD_STREAM_WAVES_PER_CU_Q;
+                      : (FMT == kFp8 && D < 512 ? PKD_STREAM_WAVES_PER_CU_FP8
+                                                : PKD_STREAM_WAVES_PER_CU_Q);
   if (per_cu > cap) per_cu = cap;
   cache[dev] = uint64_t(per_cu) * uint64_t(cus);
   return cache[dev];
