@@ -57,5 +57,26 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+STANDALONE_SRC = os.path.join(ROOT, "tests", "standalone", "decode_tiny.cpp")
+STANDALONE_BIN = os.path.join(ROOT, "tests", "standalone", "decode_tiny")
+
+
+def build_standalone(verbose: bool = False) -> str:
+    """Compile the standalone C++ test of the C ABI (host code only), linked
+    against the in-tree library with an rpath to it."""
+    hipcc = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+    cmd = [hipcc, "-O2", "-std=c++17", "-Wall", "-I", os.path.join(ROOT, "include"),
+           STANDALONE_SRC, "-L", HERE, "-lpkd",
+           "-Wl,-rpath,$ORIGIN/../../paged_kv_decode_splitk_amd", "-o", STANDALONE_BIN]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, cwd=ROOT, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"hipcc (standalone test) failed with status {res.returncode}")
+    return STANDALONE_BIN
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_standalone(verbose=True))
