@@ -644,13 +644,19 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
           for (int k = 0; k < NC; ++k) sc[k] *= qup[k];
         }
         if constexpr (DS > 1) {
-          // the other half of the head dim: partial logits through LDS
+          // the other parts of the head dim: partial logits through LDS,
+          // summed in wave order so that every wave gets the same sum
           typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
           lds_f32x4* const xs = (lds_f32x4*)xg + (xturn++ & 1) * (DS * 64);
           xs[w * 64 + lane] = sc[0];
           asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-          const f32x4 other = xs[(1 - w) * 64 + lane];
-          sc[0] = w == 0 ? sc[0] + other : other + sc[0];   // the same sum in both waves
+          f32x4 part[DS];
+#pragma unroll
+          for (int u = 0; u < DS; ++u) part[u] = u == w ? sc[0] : xs[u * 64 + lane];
+          f32x4 sum = part[0];
+#pragma unroll
+          for (int u = 1; u < DS; ++u) sum += part[u];
+          sc[0] = sum;
         }
         __builtin_amdgcn_sched_barrier(0);
         issue(s, 0, t + NBUF);
@@ -836,17 +842,23 @@ __device__ __forceinline__ void zero_row(const DecodeArgs& a, uint32_t b, uint32
   }
 }
 
-// Head-dim split: at head_dim 512 a workgroup of two waves shares each row
-// piece, each wave holding half of the dims (the accumulator alone would
-// otherwise take 128 registers of one wave).
-template <int D>
-constexpr int kDSplit = D == 512 ? 2 : 1;
+// Head-dim split: at head_dim 512 a workgroup of DS waves shares each row
+// piece, each wave holding D/DS of the dims (the accumulator alone would
+// otherwise take 128 registers of one wave): two waves, or four for NVFP4
+// tiles (PKD_NVFP4_DSPLIT), whose dequant work wants more waves per CU than
+// half-dim registers allow.
+#ifndef PKD_NVFP4_DSPLIT
+#define PKD_NVFP4_DSPLIT 2
+#endif
+template <int FMT, int D>
+constexpr int kDSplit = D == 512 ? (FMT == kNvfp4 ? PKD_NVFP4_DSPLIT : 2) : 1;
 
 // Waves per SIMD the register budget is held to: quantized tiles up to
 // head_dim 256 and split head dims run two (their ALU work hides behind the
 // other wave's loads).
 template <int FMT, int D>
-constexpr int kWavesPerSimd = ((FMT != kBf16 && D <= 256) || kDSplit<D> > 1) ? 2 : 1;
+constexpr int kWavesPerSimd =
+    kDSplit<FMT, D> > 2 ? 3 : (((FMT != kBf16 && D <= 256) || kDSplit<FMT, D> > 1) ? 2 : 1);
 
 // Column chunks one wave can carry: two for BF16 tiles up to head_dim 128
 // (a second accumulator and q fit the registers), else one.
@@ -854,9 +866,9 @@ template <int FMT, int D>
 constexpr int kMaxChunks = (FMT == kBf16 && D <= 128) ? 2 : 1;
 
 template <int FMT, int D, int NC, bool CONTIG>
-__global__ __launch_bounds__(64 * kDSplit<D>, (kWavesPerSimd<FMT, D>)) void splitk_stream(
+__global__ __launch_bounds__((64 * kDSplit<FMT, D>), (kWavesPerSimd<FMT, D>)) void splitk_stream(
     DecodeArgs a) {
-  constexpr int DS = kDSplit<D>;
+  constexpr int DS = kDSplit<FMT, D>;
   __shared__ StreamLds<FMT, D / DS, DS> sh[DS];
   __shared__ __attribute__((aligned(16))) uint8_t xg[DS > 1 ? 2 * DS * 64 * 16 : 16];
   StreamLds<FMT, D / DS, DS>& mine = sh[DS > 1 ? threadIdx.x >> 6 : 0];
@@ -1115,9 +1127,9 @@ template <int FMT, int D, int NC, bool CONTIG>
 static int stream_occupancy() {
   int per_cu = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, splitk_stream<FMT, D, NC, CONTIG>,
-                                                   64 * kDSplit<D>, 0) != hipSuccess)
+                                                   64 * kDSplit<FMT, D>, 0) != hipSuccess)
     return 0;
-  return per_cu * kDSplit<D>;
+  return per_cu * kDSplit<FMT, D>;
 }
 
 // Waves the stream kernel launches on the current device: all resident at
@@ -1149,9 +1161,13 @@ static uint64_t stream_capacity() {
 #ifndef PKD_STREAM_WAVES_PER_CU_FP8
 #define PKD_STREAM_WAVES_PER_CU_FP8 4
 #endif
+#ifndef PKD_STREAM_WAVES_PER_CU_Q4
+#define PKD_STREAM_WAVES_PER_CU_Q4 12
+#endif
   const int cap = FMT == kBf16 && D < 512
                       ? (NC > 1 ? PKD_STREAM_WAVES_PER_CU_NC : PKD_STREAM_WAVES_PER_CU)
                       : (FMT == kFp8 && D < 512 ? PKD_STREAM_WAVES_PER_CU_FP8
+                         : kDSplit<FMT, D> > 2  ? PKD_STREAM_WAVES_PER_CU_Q4
                                                 : PKD_STREAM_WAVES_PER_CU_Q);
   if (per_cu > cap) per_cu = cap;
   cache[dev] = uint64_t(per_cu) * uint64_t(cus);
@@ -1161,7 +1177,7 @@ static uint64_t stream_capacity() {
 // One launch of the stream kernel with NC column chunks per wave.
 template <int FMT, int D, int NC, bool CONTIG>
 static int launch_stream(DecodeArgs a, hipStream_t stream) {
-  constexpr uint64_t ds = kDSplit<D>;
+  constexpr uint64_t ds = kDSplit<FMT, D>;
   a.head_chunks = (a.col_chunks + NC - 1) / NC;
   const uint64_t rows = uint64_t(a.num_seqs) * a.num_kv_heads * a.head_chunks;
   uint32_t tile_bound = a.max_blocks * (a.block_size / 16);
