@@ -9,99 +9,9 @@ import torch
 import oracle
 import paged_kv_decode_splitk_amd as pkd
 import workloads
-from gpu_cases import (DeviceKV, assert_close, dev, geometry, i32_to_dev, oracle_pools,
-                       u16_to_dev)
+from gpu_cases import Contig, DeviceKV, assert_close, geometry
 
 pytestmark = pytest.mark.gpu
-
-
-def _tensor(rows, layout, Lmax, fill, dtype):
-    """Per-sequence rows [L, Hkv, D] laid into (b, l, h, d) or (b, h, l, d)."""
-    B = len(rows)
-    Hkv, D = rows[0].shape[1], rows[0].shape[2]
-    t = np.full((B, Lmax, Hkv, D), fill, dtype)
-    for b, r in enumerate(rows):
-        t[b, :len(r)] = r
-    if layout == "bhld":
-        t = np.ascontiguousarray(t.transpose(0, 2, 1, 3))
-    return t, pkd.layout_strides(layout, B, Lmax, Hkv, D)
-
-
-def _seq_rows(w, bits):
-    out, start = [], 0
-    for L in w.seq_lens:
-        out.append(bits[start:start + int(L)])
-        start += int(L)
-    return out
-
-
-class Contig:
-    """A workload's K/V as contiguous device tensors (BF16, or FP8 codes from
-    the oracle's encoder: inputs, read the same by both sides)."""
-
-    def __init__(self, w, layout, fmt="bf16", k_scale=1.0, v_scale=1.0, pad=3, Lmax=None):
-        self.w, self.fmt = w, fmt
-        self.Lmax = int(max(1, w.seq_lens.max(initial=1))) + pad if Lmax is None else Lmax
-        kr, vr = _seq_rows(w, w.k_bits), _seq_rows(w, w.v_bits)
-        if fmt == "fp8":
-            kr = [oracle.e4m3_encode(oracle.bf16_to_f64(r).astype(np.float32), k_scale) for r in kr]
-            vr = [oracle.e4m3_encode(oracle.bf16_to_f64(r).astype(np.float32), v_scale) for r in vr]
-            fill, dt = 0x7F, np.uint8                          # NaN codes in the padding
-        else:
-            fill, dt = 0x7FC0, np.uint16
-        self.k_np, self.ks = _tensor(kr, layout, self.Lmax, fill, dt)
-        self.v_np, self.vs = _tensor(vr, layout, self.Lmax, fill, dt)
-        if fmt == "fp8":
-            self.k = torch.from_numpy(self.k_np.reshape(-1)).to(dev())
-            self.v = torch.from_numpy(self.v_np.reshape(-1)).to(dev())
-        else:
-            self.k = u16_to_dev(self.k_np.reshape(-1))
-            self.v = u16_to_dev(self.v_np.reshape(-1))
-        self.k_scale, self.v_scale = k_scale, v_scale
-
-    def run(self, q, q_len, num_splits, causal=True, window=None, q_strides=None,
-            o_layout="blhd", o_pad=0):
-        w = self.w
-        B, Hq, Hkv, D = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim
-        window = w.sliding_window if window is None else window
-        if q_strides is None:
-            q_strides = (q_len * Hq * D, Hq * D, D)
-        # output: (b, i, h, d) or (b, h, i, d), each head row padded by o_pad elements
-        row = D + o_pad
-        if o_layout == "blhd":
-            os_ = (q_len * Hq * row, Hq * row, row)
-        else:
-            os_ = (Hq * q_len * row, row, q_len * row)
-        out = torch.full((B * q_len * Hq * row,), float("nan"), dtype=torch.bfloat16, device=dev())
-        ws = None
-        if num_splits > 1:
-            ws = torch.full((pkd.paged_decode_workspace_bytes(B, Hq * q_len, D, num_splits) // 4,),
-                            float("nan"), dtype=torch.float32, device=dev())
-        qd = u16_to_dev(np.asarray(q).reshape(-1))
-        lens = i32_to_dev(w.seq_lens)
-        args = (qd, self.k, self.v, out, lens, B, q_len, self.Lmax, Hq, Hkv, D, float(w.scale))
-        kw = dict(causal=causal, sliding_window=window, workspace=ws, num_splits=num_splits)
-        if self.fmt == "fp8":
-            pkd.contig_kv_attn_fp8(*args, self.k_scale, self.v_scale, q_strides, self.ks, self.vs,
-                                   os_, **kw)
-        else:
-            pkd.contig_kv_attn_bf16(*args, q_strides, self.ks, self.vs, os_, **kw)
-        torch.cuda.synchronize()
-        o = out.float().cpu().numpy().astype(np.float64)
-        idx = (np.arange(B)[:, None, None, None] * os_[0] + np.arange(q_len)[None, :, None, None] * os_[1]
-               + np.arange(Hq)[None, None, :, None] * os_[2] + np.arange(D)[None, None, None, :])
-        return o[idx]
-
-    def oracle(self, q, q_len, causal=True, window=None, q_strides=None, seqs=None):
-        w = self.w
-        Hq, D = w.num_q_heads, w.head_dim
-        if q_strides is None:
-            q_strides = (q_len * Hq * D, Hq * D, D)
-        return oracle.contiguous_attention(
-            self.fmt, q, self.k_np, self.v_np, w.seq_lens, Hq, w.num_kv_heads, D, q_len, w.scale,
-            q_strides, self.ks, self.vs, causal=causal,
-            sliding_window=w.sliding_window if window is None else window,
-            k_scale=self.k_scale, v_scale=self.v_scale, seqs=seqs)
 
 
 CASES = [
