@@ -313,8 +313,8 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 // of row r at c ^ bswz(r)). Lane l makes
 // BF16 chunks k*64 + l (8 values each), so 16 consecutive lanes write 16
 // consecutive chunks of one row: no bank conflicts. Rows of keys outside
-// [lo, khi) become zeros (FP8: selected when MASK; NVFP4: always, through a
-// zero scale, as E2M1 codes are always finite).
+// [lo, khi) become zeros for FP8 (selected when MASK: its codes may be NaN);
+// NVFP4 rows only have NaN scales cleared (their weight is zero).
 template <int FMT, int D, bool MASK>
 __device__ __forceinline__ void stage_v(lds_u8* vt, lds_u8* stage, int lane, uint32_t tok0,
                                         uint32_t lo, uint32_t khi) {
@@ -333,10 +333,16 @@ __device__ __forceinline__ void stage_v(lds_u8* vt, lds_u8* stage, int lane, uin
       h = fp8x8_to_bf16x8(w[0], w[1]);
       if (MASK && !ok) h = u32x4{0u, 0u, 0u, 0u};
     } else {
-      // codes 8c .. 8c+7: a quarter of raw chunk c/4; scale group c/2
+      // codes 8c .. 8c+7: a quarter of raw chunk c/4; scale group c/2. E2M1
+      // codes are always finite, so only the scale can poison a row past the
+      // keys: a NaN scale code (0x7F / 0xFF) becomes 0, every row decodes to
+      // finite values, and the zero weight of a masked key removes it. No
+      // per-row test, so the LDS reads of all chunks issue together.
+      (void)ok;
       const uint32_t w = *(lds_u32*)(vt + row * T::RB + ((c >> 2) ^ T::swz(row)) * 16 + 4 * (c & 3));
-      const uint32_t sb = *(lds_u8*)(vt + T::TILE + row * T::SC_ROW + (c >> 1));
-      h = fp4x8_to_f16x8(w, ok ? _Float16(__builtin_amdgcn_cvt_f32_fp8(sb, 0)) : _Float16(0.0f));
+      const uint32_t sraw = *(lds_u8*)(vt + T::TILE + row * T::SC_ROW + (c >> 1));
+      const uint32_t sb = (sraw & 0x7Fu) == 0x7Fu ? 0u : sraw;
+      h = fp4x8_to_f16x8(w, _Float16(__builtin_amdgcn_cvt_f32_fp8(sb, 0)));
     }
     *(lds_u32x4*)(stage + row * T::BRB + (c ^ T::bswz(row)) * 16) = h;
   }
