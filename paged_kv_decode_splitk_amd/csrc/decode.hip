@@ -392,6 +392,17 @@ __device__ __forceinline__ bool column_of(const DecodeArgs& a, uint32_t kvh, uin
   return ok;
 }
 
+// First of the eight head dims (within this wave's share) that lane group g
+// feeds to QK MFMA c. The dot product sums over all dims, so any order works
+// as long as K and q agree: BF16 / FP8 / NVFP4 tiles below 128 dims take
+// dims 32c + 8g .. +8; NVFP4 from 128 dims takes word c % 4 of the 16-byte
+// code chunk 4 (c / 4) + g, so that a lane reads whole chunks.
+template <int FMT, int DW>
+__device__ __forceinline__ constexpr int qk_dim(int c, int g) {
+  if constexpr (FMT == kNvfp4 && DW >= 128) return 32 * (4 * (c / 4) + g) + 8 * (c % 4);
+  return 32 * c + 8 * g;
+}
+
 // One row piece: tiles [tau0, tau1) of row (b, kh), partial state to `slot`.
 // The row's NC chunks of 16 query columns share every K/V tile: each K or V
 // read from LDS feeds NC MFMAs.
@@ -469,7 +480,7 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
 #pragma unroll
     for (int c = 0; c < DW / 32; ++c) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (head_ok[k]) v = *reinterpret_cast<const u32x4*>(qsrc + 32 * c + 8 * g);
+      if (head_ok[k]) v = *reinterpret_cast<const u32x4*>(qsrc + qk_dim<FMT, DW>(c, g));
       qf[k][c] = v;
     }
     if constexpr (FMT == kNvfp4) {
@@ -630,21 +641,42 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
             for (int k = 0; k < NC; ++k) sc[k] = mfma_qk<FMT>(kv, qf[k][c], sc[k]);
           }
         } else {
-          // group of dims 32c + 8g is 2c + g/2: byte 2(c & 1) of scale word c/2
-          // once the words are shifted down by g/2 bytes
-          uint32_t sw[(T::SC_ROW + 3) / 4];
+          if constexpr (DW >= 128) {
+            // lane group g takes whole 16-byte chunks 4h + g (32 codes, the
+            // dims of two scale groups): MFMA 4h + u uses its word u, so a
+            // lane makes one 16-byte and one 2-byte read per chunk (q is
+            // loaded in the same dim order, qk_dim)
 #pragma unroll
-          for (int i = 0; i < (T::SC_ROW + 3) / 4; ++i)
-            sw[i] = *(lds_u32*)(kt + T::TILE + n * T::SC_ROW + 4 * i) >> (8 * (g >> 1));
+            for (int h = 0; h < DW / 128; ++h) {
+              const int j = 4 * h + g;
+              const u32x4 cw = *(lds_u32x4*)(kt + n * T::RB + (j ^ T::swz(n)) * 16);
+              const uint32_t s2 = *(lds_u16*)(kt + T::TILE + n * T::SC_ROW + 2 * j);
+              const _Float16 S0 = _Float16(__builtin_amdgcn_cvt_f32_fp8(s2, 0));
+              const _Float16 S1 = _Float16(__builtin_amdgcn_cvt_f32_fp8(s2, 1));
 #pragma unroll
-          for (int c = 0; c < DW / 32; ++c) {
-            const int chunk = c ^ T::swz(n);
-            const uint32_t w = *(lds_u32*)(kt + n * T::RB + chunk * 16 + 4 * g);
-            const float S = (c & 1) ? __builtin_amdgcn_cvt_f32_fp8(sw[c / 2], 2)
-                                    : __builtin_amdgcn_cvt_f32_fp8(sw[c / 2], 0);
-            const u32x4 kv = fp4x8_to_f16x8(w, _Float16(S));
+              for (int u = 0; u < 4; ++u) {
+                const u32x4 kv = fp4x8_to_f16x8(cw[u], u < 2 ? S0 : S1);
 #pragma unroll
-            for (int k = 0; k < NC; ++k) sc[k] = mfma_qk<FMT>(kv, qf[k][c], sc[k]);
+                for (int k = 0; k < NC; ++k) sc[k] = mfma_qk<FMT>(kv, qf[k][4 * h + u], sc[k]);
+              }
+            }
+          } else {
+            // group of dims 32c + 8g is 2c + g/2: byte 2(c & 1) of scale word
+            // c/2 once the words are shifted down by g/2 bytes
+            uint32_t sw[(T::SC_ROW + 3) / 4];
+#pragma unroll
+            for (int i = 0; i < (T::SC_ROW + 3) / 4; ++i)
+              sw[i] = *(lds_u32*)(kt + T::TILE + n * T::SC_ROW + 4 * i) >> (8 * (g >> 1));
+#pragma unroll
+            for (int c = 0; c < DW / 32; ++c) {
+              const int chunk = c ^ T::swz(n);
+              const uint32_t w = *(lds_u32*)(kt + n * T::RB + chunk * 16 + 4 * g);
+              const float S = (c & 1) ? __builtin_amdgcn_cvt_f32_fp8(sw[c / 2], 2)
+                                      : __builtin_amdgcn_cvt_f32_fp8(sw[c / 2], 0);
+              const u32x4 kv = fp4x8_to_f16x8(w, _Float16(S));
+#pragma unroll
+              for (int k = 0; k < NC; ++k) sc[k] = mfma_qk<FMT>(kv, qf[k][c], sc[k]);
+            }
           }
 #pragma unroll
           for (int k = 0; k < NC; ++k) sc[k] *= qup[k];
