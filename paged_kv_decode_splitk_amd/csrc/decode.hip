@@ -394,12 +394,15 @@ __device__ __forceinline__ bool column_of(const DecodeArgs& a, uint32_t kvh, uin
 
 // First of the eight head dims (within this wave's share) that lane group g
 // feeds to QK MFMA c. The dot product sums over all dims, so any order works
-// as long as K and q agree: BF16 / FP8 / NVFP4 tiles below 128 dims take
-// dims 32c + 8g .. +8; NVFP4 from 128 dims takes word c % 4 of the 16-byte
-// code chunk 4 (c / 4) + g, so that a lane reads whole chunks.
+// as long as K and q agree. A lane reads whole 16-byte K chunks: BF16 tiles
+// (8 dims a chunk) take dims 32c + 8g .. +8; FP8 takes half c % 2 of chunk
+// 4 (c / 2) + g (16 dims a chunk); NVFP4 from 128 dims takes word c % 4
+// of chunk 4 (c / 4) + g (32 dims a chunk); narrower NVFP4 tiles keep the
+// BF16 order.
 template <int FMT, int DW>
 __device__ __forceinline__ constexpr int qk_dim(int c, int g) {
   if constexpr (FMT == kNvfp4 && DW >= 128) return 32 * (4 * (c / 4) + g) + 8 * (c % 4);
+  if constexpr (FMT == kFp8) return 16 * (4 * (c / 2) + g) + 8 * (c % 2);
   return 32 * c + 8 * g;
 }
 
@@ -632,13 +635,17 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
             for (int k = 0; k < NC; ++k) sc[k] = mfma_qk<FMT>(kv, qf[k][c], sc[k]);
           }
         } else if constexpr (FMT == kFp8) {
+          // lane group g takes whole 16-byte chunks 4h + g (16 codes): MFMA
+          // 2h + u uses its half u (q is loaded in the same dim order, qk_dim)
 #pragma unroll
-          for (int c = 0; c < DW / 32; ++c) {
-            const int chunk = (2 * c + (g >> 1)) ^ T::swz(n);
-            const u32x2 w = *(lds_u32x2*)(kt + n * T::RB + chunk * 16 + 8 * (g & 1));
-            const u32x4 kv = fp8x8_to_bf16x8(w[0], w[1]);
+          for (int h = 0; h < DW / 64; ++h) {
+            const u32x4 cw = *(lds_u32x4*)(kt + n * T::RB + ((4 * h + g) ^ T::swz(n)) * 16);
 #pragma unroll
-            for (int k = 0; k < NC; ++k) sc[k] = mfma_qk<FMT>(kv, qf[k][c], sc[k]);
+            for (int u = 0; u < 2; ++u) {
+              const u32x4 kv = fp8x8_to_bf16x8(cw[2 * u], cw[2 * u + 1]);
+#pragma unroll
+              for (int k = 0; k < NC; ++k) sc[k] = mfma_qk<FMT>(kv, qf[k][2 * h + u], sc[k]);
+            }
           }
         } else {
           if constexpr (DW >= 128) {
