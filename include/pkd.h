@@ -349,10 +349,12 @@ PKD_API int paged_prefill_attn_nvfp4(const uint16_t* q, const uint8_t* k_cache,
                                      uint32_t causal, uint32_t sliding_window, float* workspace,
                                      uint32_t num_splits, hipStream_t stream);
 
-/* A split count for the query-block calls: paged_decode_num_splits with
- * num_q_heads * q_len query heads and, for a causal window W, a window of
- * W + q_len - 1 keys (the keys one row of the block can touch). Returns 1
- * for q_len outside 1 .. 4096. */
+/* A split count for the query-block calls: as paged_decode_num_splits, with
+ * rows of up to 16 query columns (group x tokens) for blocks of at most 32
+ * columns and of up to 128 columns for wider ones (BF16 blocks that wide are
+ * streamed by four waves sharing each K/V tile), and, for a causal window W,
+ * a window of W + q_len - 1 keys (the keys one row of the block can touch).
+ * Returns 1 for q_len outside 1 .. 4096. */
 PKD_API uint32_t paged_prefill_num_splits(uint32_t num_seqs, uint32_t q_len,
                                           uint32_t num_q_heads, uint32_t num_kv_heads,
                                           uint32_t max_blocks_per_seq, uint32_t block_size,

@@ -870,16 +870,271 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Query blocks wider than one wave (BF16 tiles): WQ waves of a workgroup
+// share every K/V tile of the row's pages through one LDS ring, each wave
+// owning NC chunks of 16 query columns, so the pages are read once per
+// WQ * NC * 16 columns instead of once per NC * 16. Each wave issues its
+// share of a tile's DMA loads; rows at or past the sequence length get an
+// offset past the page and read as zeros, so no wave ever writes the shared
+// tiles. One workgroup barrier per tile makes the tile visible to all waves
+// and frees the slot of the previous tile, which is refilled right after it.
+#ifndef PKD_SHARED_NB
+#define PKD_SHARED_NB 3
+#endif
+template <int D>
+struct SharedLds {
+  static constexpr int NB = PKD_SHARED_NB;       // tile-pair slots of the ring
+  __attribute__((aligned(1024))) uint8_t ring[NB * LdsTraits<kBf16, D>::SLOT];
+};
+
+template <int D, int NC, int WQ>
+__device__ __forceinline__ void run_piece_shared(const DecodeArgs& a, SharedLds<D>& sh,
+                                                 uint32_t b, uint32_t kh, uint32_t tau0,
+                                                 uint32_t tau1, uint32_t slot, bool last,
+                                                 uint32_t L) {
+  using T = LdsTraits<kBf16, D>;
+  constexpr int NB = SharedLds<D>::NB;
+  constexpr int NLD = 2 * T::NI;                 // load instructions of a K + V tile pair
+  static_assert(NLD % WQ == 0, "the tile loads split evenly over the waves");
+  constexpr int LPW = NLD / WQ;                  // load instructions per wave and tile
+  b = __builtin_amdgcn_readfirstlane(b);
+  kh = __builtin_amdgcn_readfirstlane(kh);
+  tau0 = __builtin_amdgcn_readfirstlane(tau0);
+  tau1 = __builtin_amdgcn_readfirstlane(tau1);
+  slot = __builtin_amdgcn_readfirstlane(slot);
+  L = __builtin_amdgcn_readfirstlane(L);
+  if (slot >= a.num_splits) return;      // the same for every wave of the workgroup
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int g = lane >> 4;
+  const int n = lane & 15;
+  const uint32_t kvh = kh / a.head_chunks, hc = kh % a.head_chunks;
+  const uint32_t lo = (a.window > 0 && L > a.window) ? L - a.window : 0u;
+  const uint32_t tpp = a.block_size / 16;
+  const uint32_t t0 = lo / 16 + tau0, t1 = lo / 16 + tau1;
+  const uint32_t pa = t0 / tpp, pb = (t1 + tpp - 1) / tpp;
+  const uint32_t chunk0 = (hc * WQ + w) * NC;    // this wave's first column chunk
+
+  bool head_ok[NC];
+  uint64_t qoff[NC];
+  uint32_t c_lo[NC], c_hi[NC];
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    uint32_t qi, qh;
+    head_ok[k] = column_of(a, kvh, (chunk0 + k) * 16 + n, qi, qh);
+    qoff[k] = uint64_t(b) * a.q_stride + uint64_t(qi) * a.q_tok_stride +
+              uint64_t(qh) * a.q_head_stride;
+    c_lo[k] = lo;
+    c_hi[k] = L;
+    if (a.causal && head_ok[k]) {
+      const int p1 = int(L) - int(a.q_len) + int(qi) + 1;
+      c_hi[k] = p1 > 0 ? uint32_t(p1) : 0u;
+      c_lo[k] = (a.q_window > 0 && c_hi[k] > a.q_window) ? c_hi[k] - a.q_window : 0u;
+    }
+  }
+  const int32_t* bt = a.block_tables + uint64_t(b) * a.max_blocks;
+  u32x4 qf[NC][D / 32];
+#pragma unroll
+  for (int k = 0; k < NC; ++k)
+#pragma unroll
+    for (int c = 0; c < D / 32; ++c) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (head_ok[k]) v = *reinterpret_cast<const u32x4*>(a.q + qoff[k] + qk_dim<kBf16, D>(c, g));
+      qf[k][c] = v;
+    }
+
+  lds_u8* const ring3 = (lds_u8*)(sh.ring);
+  const int ld_row = lane / T::CPR;
+  const int ld_pos = lane % T::CPR;
+  f32x4 acc[NC][D / 16];
+  float m_run[NC], l_run[NC];
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) acc[k][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[k] = kMaxFloor;
+    l_run[k] = 0.0f;
+  }
+
+  for (uint32_t cp = pa; cp < pb;) {
+    const uint32_t cpe = min(cp + 64, pb);
+    const int32_t bt_reg = (cp + lane < cpe) ? bt[cp + lane] : 0;
+    const uint32_t ct0 = max(cp * tpp, t0);
+    const uint32_t ct1 = min(cpe * tpp, t1);
+
+    // this wave's share of tile t (K and V) into ring slot s; a tile past the
+    // segment gets zero-length descriptors
+    auto issue = [&](int s, uint32_t t) {
+      const bool live = t < ct1;
+      const uint32_t page = min(t / tpp, cpe - 1);
+      const uint32_t phys = uint32_t(__builtin_amdgcn_readlane(bt_reg, int(page - cp)));
+      const uint32_t off0 = (t % tpp) * 16;
+#pragma unroll
+      for (int m = 0; m < LPW; ++m) {
+        const int mi = w + m * WQ;                 // load instruction of the tile pair
+        const int kv = mi / T::NI, i = mi % T::NI;
+        const uint8_t* pool = kv ? a.v_cache : a.k_cache;
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint8_t*>(pool + uint64_t(phys) * a.page_bytes), 0,
+            live ? int(a.page_bytes) : 0, 0x00020000);
+        const int row = i * T::RPI + ld_row;
+        const int chunk = ld_pos ^ T::swz(row);
+        const bool keep = row < 16 && t * 16 + row < L;
+        const int voff = keep ? int(((off0 + row) * a.num_kv_heads + kvh) * T::RB + chunk * 16)
+                              : 0x7FFFFFF0;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (lds_void*)(ring3 + s * T::SLOT + kv * T::KV + i * 1024), 16, voff, 0, 0, 2);
+      }
+    };
+
+#pragma unroll
+    for (int s = 0; s < NB - 1; ++s) issue(s, ct0 + s);
+    int s = 0;                                     // slot of tile t
+    for (uint32_t t = ct0; t < ct1; ++t) {
+      const uint32_t tok0 = t * 16;
+      // tile t is in LDS once every wave's share has landed
+      wait_vmcnt<(NB - 2) * LPW>();
+      asm volatile("s_barrier" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      issue(s == 0 ? NB - 1 : s - 1, t + NB - 1);  // the slot of tile t - 1 is free now
+      lds_u8* const kt = ring3 + s * T::SLOT;
+      lds_u8* const vt = kt + T::KV;
+
+      f32x4 sc[NC];
+#pragma unroll
+      for (int k = 0; k < NC; ++k) sc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < D / 32; ++c) {
+        const u32x4 kv = *(lds_u32x4*)(kt + n * T::RB + ((4 * c + g) ^ T::swz(n)) * 16);
+#pragma unroll
+        for (int k = 0; k < NC; ++k) sc[k] = mfma_qk<kBf16>(kv, qf[k][c], sc[k]);
+      }
+
+      bool rescale[NC];
+      float alpha[NC];
+      u32x2 pf[NC];
+#pragma unroll
+      for (int k = 0; k < NC; ++k) {
+        float sv[4];
+        float mx = -__builtin_inff();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t tok = tok0 + 4 * g + j;
+          sv[j] = (tok >= c_lo[k] && tok < c_hi[k]) ? sc[k][j] * a.logit_scale : -__builtin_inff();
+          mx = fmaxf(mx, sv[j]);
+        }
+        mx = max_over_rows(mx);
+        rescale[k] = __builtin_amdgcn_ballot_w64(mx > m_run[k] + kLazyMax) != 0;
+        alpha[k] = 1.0f;
+        if (rescale[k]) {
+          const float m_new = fmaxf(m_run[k], mx);
+          alpha[k] = __builtin_amdgcn_exp2f(m_run[k] - m_new);
+          m_run[k] = m_new;
+        }
+        uint32_t pbits[4];
+        float psum = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const float p = __builtin_amdgcn_exp2f(sv[j] - m_run[k]);
+          pbits[j] = p_bits<kBf16>(p);
+          psum += p_value<kBf16>(pbits[j]);
+        }
+        l_run[k] = l_run[k] * alpha[k] + psum;
+        pf[k] = u32x2{pbits[0] | (pbits[1] << 16), pbits[2] | (pbits[3] << 16)};
+      }
+#pragma unroll
+      for (int k = 0; k < NC; ++k)
+        if (rescale[k]) {
+#pragma unroll
+          for (int mt = 0; mt < D / 16; ++mt) acc[k][mt] *= alpha[k];
+        }
+      {
+        const int vtok = 4 * g + (n >> 2);
+        const uint32_t vrow = uint32_t(uintptr_t(vt)) + vtok * T::BRB + (n & 1) * 8;
+#pragma unroll
+        for (int q4 = 0; q4 < D / 64; ++q4) {
+          uint32_t ad[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const int mt = 4 * q4 + u;
+            ad[u] = vrow + (((2 * mt + ((n & 3) >> 1)) ^ T::bswz(vtok)) * 16);
+          }
+          u32x2 vv[4];
+          asm volatile(
+              "ds_read_b64_tr_b16 %0, %4\n\t"
+              "ds_read_b64_tr_b16 %1, %5\n\t"
+              "ds_read_b64_tr_b16 %2, %6\n\t"
+              "ds_read_b64_tr_b16 %3, %7\n\t"
+              "s_waitcnt lgkmcnt(0)"
+              : "=&v"(vv[0]), "=&v"(vv[1]), "=&v"(vv[2]), "=&v"(vv[3])
+              : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+              : "memory");
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int k = 0; k < NC; ++k)
+              acc[k][4 * q4 + u] = mfma_pv<kBf16>(vv[u], pf[k], acc[k][4 * q4 + u]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      s = s == NB - 1 ? 0 : s + 1;
+    }
+    // the ring restarts with the next segment once every wave is done with it
+    wait_vmcnt<0>();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    cp = cpe;
+  }
+
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    const float l_tot = sum_over_rows(l_run[k]);
+    const float inv = l_tot > 0.0f ? a.out_scale / l_tot : 0.0f;
+    if (!head_ok[k]) continue;
+    uint32_t qi, qh;
+    column_of(a, kvh, (chunk0 + k) * 16 + n, qi, qh);
+    if (a.out) {
+      uint16_t* orow = a.out + uint64_t(b) * a.o_seq + uint64_t(qi) * a.o_tok +
+                       uint64_t(qh) * a.o_head;
+#pragma unroll
+      for (int mt = 0; mt < D / 16; ++mt)
+        *reinterpret_cast<u32x2*>(orow + 16 * mt + 4 * g) =
+            u32x2{pack_bf16x2(acc[k][mt][0] * inv, acc[k][mt][1] * inv),
+                  pack_bf16x2(acc[k][mt][2] * inv, acc[k][mt][3] * inv)};
+      continue;
+    }
+    const uint64_t qrow = (uint64_t(b) * a.q_len + qi) * a.num_q_heads + qh;
+    float* const wbase = a.ws + qrow * a.num_splits * (D + 2);
+    float* wrow = wbase + uint64_t(slot) * (D + 2);
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) {
+      *reinterpret_cast<f32x2*>(wrow + mt * 16 + 4 * g) = f32x2{acc[k][mt][0] * inv, acc[k][mt][1] * inv};
+      *reinterpret_cast<f32x2*>(wrow + mt * 16 + 4 * g + 2) = f32x2{acc[k][mt][2] * inv, acc[k][mt][3] * inv};
+    }
+    if (g == 0) {
+      wrow[D] = m_run[k] * kLn2;
+      wrow[D + 1] = l_tot;
+    }
+    if (last && g == 0 && slot + 1 < a.num_splits) {
+      float* e = wbase + uint64_t(slot + 1) * (D + 2);
+      e[D] = -__builtin_inff();
+      e[D + 1] = -1.0f;
+    }
+  }
+}
+
 // Zeros for the query columns of row (b, kh) of a sequence without keys.
-template <int D, int NC>
+// With WQ waves sharing a row, wave w zeros its own chunks.
+template <int D, int NC, int WQ>
 __device__ __forceinline__ void zero_row(const DecodeArgs& a, uint32_t b, uint32_t kh) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, n = lane & 15;
+  const uint32_t w = WQ > 1 ? threadIdx.x >> 6 : 0u;
   const uint32_t kvh = kh / a.head_chunks, hc = kh % a.head_chunks;
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
     uint32_t qi, qh;
-    if (!column_of(a, kvh, (hc * NC + k) * 16 + n, qi, qh)) continue;
+    if (!column_of(a, kvh, ((hc * WQ + w) * NC + k) * 16 + n, qi, qh)) continue;
     uint16_t* orow = a.out + uint64_t(b) * a.o_seq + uint64_t(qi) * a.o_tok + uint64_t(qh) * a.o_head;
 #pragma unroll
     for (int mt = 0; mt < D / 16; ++mt)
@@ -910,15 +1165,12 @@ constexpr int kWavesPerSimd =
 template <int FMT, int D>
 constexpr int kMaxChunks = (FMT == kBf16 && D <= 128) ? 2 : 1;
 
-template <int FMT, int D, int NC, bool CONTIG>
-__global__ __launch_bounds__((64 * kDSplit<FMT, D>), (kWavesPerSimd<FMT, D>)) void splitk_stream(
-    DecodeArgs a) {
-  constexpr int DS = kDSplit<FMT, D>;
-  __shared__ StreamLds<FMT, D / DS, DS> sh[DS];
-  __shared__ __attribute__((aligned(16))) uint8_t xg[DS > 1 ? 2 * DS * 64 * 16 : 16];
-  StreamLds<FMT, D / DS, DS>& mine = sh[DS > 1 ? threadIdx.x >> 6 : 0];
-  lds_u8* const xg3 = (lds_u8*)xg;
-  uint32_t xturn = 0;
+// The pieces of one workgroup under the stream partition (rows of R per
+// sequence), in order: piece(b, kh, tau0, tau1, slot, last, L) for each; with
+// num_splits 1 the workgroup takes row blockIdx.x whole (and writes zeros
+// for a sequence without keys).
+template <int D, int NC, int WQ, typename Piece>
+__device__ __forceinline__ void for_each_piece(const DecodeArgs& a, Piece&& piece) {
   const uint32_t R = a.num_kv_heads * a.head_chunks;          // rows per sequence
   const uint32_t P = gridDim.x;
   const bool whole = a.num_splits == 1;                       // one wave per row
@@ -951,7 +1203,7 @@ __global__ __launch_bounds__((64 * kDSplit<FMT, D>), (kWavesPerSimd<FMT, D>)) vo
       n = row_tiles(L, a.window);
       start = pos;
       if (n == 0) {
-        if (a.out && threadIdx.x < 64) zero_row<D, NC>(a, b, kh);
+        if (a.out && (WQ > 1 || threadIdx.x < 64)) zero_row<D, NC, WQ>(a, b, kh);
         break;
       }
     } else if (cached) {
@@ -974,11 +1226,35 @@ __global__ __launch_bounds__((64 * kDSplit<FMT, D>), (kWavesPerSimd<FMT, D>)) vo
     const uint32_t tau0 = whole ? 0u : pos - start;
     const uint32_t tau1 = whole ? n : min(n, end - start);
     const uint32_t slot = whole ? 0u : pos / c - start / c;
-    run_piece<FMT, D, DS, NC, CONTIG>(a, mine, xg3, xturn, b, kh, tau0, tau1, slot,
-                          whole || start + n <= end, L);
+    piece(b, kh, tau0, tau1, slot, whole || start + n <= end, L);
     if (whole) break;
     pos = start + tau1;
   }
+}
+
+template <int FMT, int D, int NC, bool CONTIG>
+__global__ __launch_bounds__((64 * kDSplit<FMT, D>), (kWavesPerSimd<FMT, D>)) void splitk_stream(
+    DecodeArgs a) {
+  constexpr int DS = kDSplit<FMT, D>;
+  __shared__ StreamLds<FMT, D / DS, DS> sh[DS];
+  __shared__ __attribute__((aligned(16))) uint8_t xg[DS > 1 ? 2 * DS * 64 * 16 : 16];
+  StreamLds<FMT, D / DS, DS>& mine = sh[DS > 1 ? threadIdx.x >> 6 : 0];
+  lds_u8* const xg3 = (lds_u8*)xg;
+  uint32_t xturn = 0;
+  for_each_piece<D, NC, 1>(a, [&](uint32_t b, uint32_t kh, uint32_t tau0, uint32_t tau1,
+                                  uint32_t slot, bool last, uint32_t L) {
+    run_piece<FMT, D, DS, NC, CONTIG>(a, mine, xg3, xturn, b, kh, tau0, tau1, slot, last, L);
+  });
+}
+
+// WQ waves sharing the K/V tiles of each piece (BF16 query blocks).
+template <int D, int NC, int WQ>
+__global__ __launch_bounds__(64 * WQ, 1) void splitk_shared(DecodeArgs a) {
+  __shared__ SharedLds<D> sh;
+  for_each_piece<D, NC, WQ>(a, [&](uint32_t b, uint32_t kh, uint32_t tau0, uint32_t tau1,
+                                   uint32_t slot, bool last, uint32_t L) {
+    run_piece_shared<D, NC, WQ>(a, sh, b, kh, tau0, tau1, slot, last, L);
+  });
 }
 
 // Where the combine writes query row bh (sequence-major: per_seq rows per
@@ -1242,9 +1518,53 @@ static int launch_stream(DecodeArgs a, hipStream_t stream) {
   return launch_status();
 }
 
-// Two chunks per wave when the row has them and the registers allow it.
+
+// One launch of the shared-tile kernel: rows of WQ * NC column chunks.
+template <int D, int NC, int WQ>
+static int launch_shared(DecodeArgs a, hipStream_t stream) {
+  static uint64_t cache[64];
+  a.head_chunks = (a.col_chunks + NC * WQ - 1) / (NC * WQ);
+  const uint64_t rows = uint64_t(a.num_seqs) * a.num_kv_heads * a.head_chunks;
+  uint32_t tile_bound = a.max_blocks * (a.block_size / 16);
+  if (a.window > 0) tile_bound = min(tile_bound, (a.window + 14) / 16 + 1);
+  a.chunk_min = a.num_splits > 1 ? (tile_bound + a.num_splits - 2) / (a.num_splits - 1) : 1;
+  uint64_t groups = rows;
+  if (a.num_splits > 1) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kLaunch;
+    if (!cache[dev]) {
+      int cus = 0, per_cu = 0;
+      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+          hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, splitk_shared<D, NC, WQ>,
+                                                       64 * WQ, 0) != hipSuccess)
+        return kLaunch;
+#ifndef PKD_SHARED_WAVES_PER_CU
+#define PKD_SHARED_WAVES_PER_CU 8
+#endif
+      if (per_cu > PKD_SHARED_WAVES_PER_CU / WQ) per_cu = PKD_SHARED_WAVES_PER_CU / WQ;
+      cache[dev] = uint64_t(per_cu > 0 ? per_cu : 1) * uint64_t(cus > 0 ? cus : 1);
+    }
+    groups = rows * a.num_splits;
+    if (groups > cache[dev]) groups = cache[dev];
+  }
+  if (groups > 0x7FFFFFFFull) return kUnsupported;
+  hipLaunchKernelGGL((splitk_shared<D, NC, WQ>), dim3(uint32_t(groups)), dim3(64 * WQ), 0,
+                     stream, a);
+  return launch_status();
+}
+
+// Two chunks per wave when the row has them and the registers allow it; a
+// BF16 block wider than one wave's chunks (and no append) shares each tile
+// among two waves, or four when it fills more than two.
 template <int FMT, int D, bool CONTIG>
 static int launch_stream_nc(const DecodeArgs& a, hipStream_t stream) {
+  if constexpr (FMT == kBf16 && !CONTIG && D <= 256) {
+    constexpr uint32_t nc = kMaxChunks<FMT, D>;
+    if (a.col_chunks > nc && a.new_k == nullptr) {
+      if (a.col_chunks <= 2 * nc) return launch_shared<D, nc, 2>(a, stream);
+      return launch_shared<D, nc, 4>(a, stream);
+    }
+  }
   if constexpr (kMaxChunks<FMT, D> >= 2) {
     if (a.col_chunks >= 2) return launch_stream<FMT, D, 2, CONTIG>(a, stream);
   }
@@ -1707,9 +2027,9 @@ extern "C" PKD_API uint32_t paged_prefill_num_splits(uint32_t num_seqs, uint32_t
                                                      uint32_t sliding_window, uint32_t num_cus) {
   if (q_len == 0 || q_len > kMaxQueryLen || uint64_t(num_q_heads) * q_len > 0x7FFFFFFFull)
     return 1;
-  return num_splits_heuristic(num_seqs, num_q_heads * q_len, num_kv_heads, max_blocks_per_seq,
-                              block_size, prefill_row_window(q_len, causal, sliding_window),
-                              num_cus);
+  return prefill_num_splits(num_seqs, q_len, num_q_heads, num_kv_heads, max_blocks_per_seq,
+                            block_size, prefill_row_window(q_len, causal, sliding_window),
+                            num_cus);
 }
 
 extern "C" PKD_API int paged_decode_attn_reduce(const float* workspace, uint16_t* output,

@@ -180,14 +180,11 @@ inline size_t workspace_bytes(uint32_t num_seqs, uint32_t num_q_heads, uint32_t 
 // pieces one (sequence, kv head) row may be cut into. It is chosen so that this
 // bound does not force pieces longer than an even share, with room for batches
 // whose sequences are shorter than the block-table width (4x).
-inline uint32_t num_splits_heuristic(uint32_t num_seqs, uint32_t num_q_heads,
-                                     uint32_t num_kv_heads, uint32_t max_blocks_per_seq,
-                                     uint32_t block_size, uint32_t sliding_window,
-                                     uint32_t num_cus) {
-  if (num_seqs == 0 || num_kv_heads == 0 || num_q_heads < num_kv_heads || block_size == 0)
-    return 1;
-  const uint64_t rows =
-      uint64_t(num_seqs) * num_kv_heads * head_chunks(num_q_heads / num_kv_heads);
+// rows: (sequence, kv head, column group) rows the split pass will stream.
+inline uint32_t num_splits_for_rows(uint64_t rows, uint32_t max_blocks_per_seq,
+                                    uint32_t block_size, uint32_t sliding_window,
+                                    uint32_t num_cus) {
+  if (rows == 0 || block_size == 0) return 1;
   const uint64_t waves = uint64_t(num_cus ? num_cus : 256) * 4;
   const uint32_t bound = split_page_bound(max_blocks_per_seq, block_size, sliding_window);
   const uint64_t tiles = uint64_t(bound) * (block_size / 16);
@@ -196,6 +193,31 @@ inline uint32_t num_splits_heuristic(uint32_t num_seqs, uint32_t num_q_heads,
   if (s < 2) s = tiles >= 2 ? 2 : 1;
   if (s > kMaxSplits) s = kMaxSplits;
   return uint32_t(s);
+}
+
+inline uint32_t num_splits_heuristic(uint32_t num_seqs, uint32_t num_q_heads,
+                                     uint32_t num_kv_heads, uint32_t max_blocks_per_seq,
+                                     uint32_t block_size, uint32_t sliding_window,
+                                     uint32_t num_cus) {
+  if (num_seqs == 0 || num_kv_heads == 0 || num_q_heads < num_kv_heads || block_size == 0)
+    return 1;
+  const uint64_t rows =
+      uint64_t(num_seqs) * num_kv_heads * head_chunks(num_q_heads / num_kv_heads);
+  return num_splits_for_rows(rows, max_blocks_per_seq, block_size, sliding_window, num_cus);
+}
+
+// Query blocks: rows hold up to 128 query columns (group x tokens) when a
+// block is wider than 32 (a workgroup of waves shares each tile), else 16.
+// Fewer, wider rows need more pieces per row to fill the chip.
+inline uint32_t prefill_num_splits(uint32_t num_seqs, uint32_t q_len, uint32_t num_q_heads,
+                                   uint32_t num_kv_heads, uint32_t max_blocks_per_seq,
+                                   uint32_t block_size, uint32_t row_window, uint32_t num_cus) {
+  if (num_seqs == 0 || num_kv_heads == 0 || num_q_heads < num_kv_heads || q_len == 0)
+    return 1;
+  const uint64_t cols = uint64_t(num_q_heads / num_kv_heads) * q_len;
+  const uint64_t per_row = cols > 32 ? 128 : 16;
+  const uint64_t rows = uint64_t(num_seqs) * num_kv_heads * ((cols + per_row - 1) / per_row);
+  return num_splits_for_rows(rows, max_blocks_per_seq, block_size, row_window, num_cus);
 }
 
 }  // namespace pkd

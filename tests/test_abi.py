@@ -231,6 +231,10 @@ def test_prefill_num_splits(lib):
     assert ns(1, 8, 32, 8, 2048, 16, 1, 64, 256) == dec(1, 256, 8, 2048, 16, 71, 256)
     assert ns(1, 8, 32, 8, 2048, 16, 0, 64, 256) == dec(1, 256, 8, 2048, 16, 64, 256)
     assert ns(1, 0, 32, 8, 2048, 16, 1, 0, 256) == 1
+    # wider than 32 columns: rows of 128 columns (waves sharing each tile), so
+    # 32 sequences x 8 kv heads x 1 row want 1 + 4096 / 256 = 17 pieces a row
+    assert ns(32, 16, 32, 8, 256, 16, 1, 0, 256) == 17
+    assert ns(32, 64, 32, 8, 256, 16, 1, 0, 256) == 1 + -(-4096 // 512)
 
 
 def test_contig_validation(lib):

@@ -54,6 +54,11 @@ CASES = [
     ("bf16", (0, 5, 40), 8, 8, 2, 64, 16, 1, 0, 1),                     # two chunks per wave
     ("bf16", (0, 5, 40, 300), 12, 8, 2, 128, 16, 1, 0, 4),              # three chunks: 2 + 1
     ("bf16", (100, 700), 16, 32, 8, 128, 16, 1, 100, 3),                # four chunks, window
+    ("bf16", (0, 5, 40), 12, 8, 2, 64, 16, 1, 0, 1),                    # waves sharing tiles
+    ("bf16", (1, 33, 530), 24, 16, 2, 128, 32, 1, 0, 1),                # 192 columns, one piece
+    ("bf16", (1, 33, 530), 24, 16, 2, 128, 32, 1, 70, 6),
+    ("bf16", (64, 200), 9, 16, 1, 256, 16, 0, 0, 1),                    # head_dim 256, shared
+    ("bf16", (0, 64, 200), 2, 16, 1, 256, 16, 1, 0, 3),                 # two waves share, D 256
     ("fp8", (1, 17, 300, 1000), 2, 16, 8, 256, 16, 1, 0, 3),
     ("fp8", (1, 17, 300, 1000), 3, 16, 8, 256, 16, 1, 129, 5),
     ("fp8", (40, 333), 4, 8, 1, 128, 16, 1, 60, 2),
