@@ -149,7 +149,9 @@ PKD_API int bf16_absmax(const uint16_t* data, float* out_max, uint64_t n_elems,
  *                 q_stride >= num_q_heads*head_dim.
  *   block_tables: int32 [num_seqs][max_blocks_per_seq]; the entries of the
  *                 first ceil(L/bs) columns of row b must be valid pages.
- *   seq_lens:     int32 [num_seqs], 0 <= L <= max_blocks_per_seq*block_size.
+ *   seq_lens:     int32 [num_seqs], 0 <= L <= max_blocks_per_seq*block_size
+ *                 (a longer L is read as max_blocks_per_seq*block_size, so
+ *                 no read passes the sequence's block-table row).
  *   scale:        softmax scale (1/sqrt(head_dim) typically), used as given.
  *   sliding_window: 0 = attend to every key.
  * Follow with paged_decode_attn_reduce() on the same stream. */

@@ -65,6 +65,8 @@ struct DecodeArgs {
   uint32_t window;         // keys of a row: the last `window` (0: all)
   uint32_t num_seqs;
   uint32_t chunk_min;      // least tiles per wave (at most S pieces per row)
+  uint32_t max_len;        // keys a sequence can hold (block-table width x block, or the
+                           // contiguous tensors' length): longer seq_lens are clamped
   uint16_t* out;           // non-split decode (num_splits 1): BF16 output, else null
   // append: each sequence's new token, written to position L - 1 by the
   // piece that ends the row, before that piece loads its last tile
@@ -243,6 +245,13 @@ __device__ __forceinline__ uint32_t row_tiles(uint32_t L, uint32_t window) {
   return (L + 15) / 16 - lo / 16;
 }
 
+// Keys of a sequence: its length, never past what its block-table row (or
+// contiguous tensor) holds, so a length beyond the table cannot send a read
+// past the row.
+__device__ __forceinline__ uint32_t seq_len(const DecodeArgs& a, int32_t Ls) {
+  return Ls > 0 ? min(uint32_t(Ls), a.max_len) : 0u;
+}
+
 // inclusive prefix sum over the 64 lanes
 __device__ __forceinline__ uint32_t wave_scan(uint32_t x) {
   const int lane = threadIdx.x & 63;
@@ -264,7 +273,7 @@ __device__ __forceinline__ uint32_t total_tiles(const DecodeArgs& a, uint32_t ro
   for (uint32_t b0 = 0; b0 < a.num_seqs; b0 += 64) {
     const uint32_t bb = b0 + (threadIdx.x & 63);
     const int32_t Ls = bb < a.num_seqs ? a.seq_lens[bb] : 0;
-    const uint32_t t = row_tiles(Ls > 0 ? uint32_t(Ls) : 0u, a.window) * rows_per_seq;
+    const uint32_t t = row_tiles(seq_len(a, Ls), a.window) * rows_per_seq;
     tot += __shfl(wave_scan(t), 63, 64);
   }
   return tot;
@@ -277,7 +286,7 @@ __device__ __forceinline__ RowLoc find_row(const DecodeArgs& a, uint32_t pos,
   for (uint32_t b0 = 0; b0 < a.num_seqs; b0 += 64) {
     const uint32_t bb = b0 + (threadIdx.x & 63);
     const int32_t Ls = bb < a.num_seqs ? a.seq_lens[bb] : 0;
-    const uint32_t n = row_tiles(Ls > 0 ? uint32_t(Ls) : 0u, a.window);
+    const uint32_t n = row_tiles(seq_len(a, Ls), a.window);
     const uint32_t incl = wave_scan(n * rows_per_seq);
     const uint64_t hit = __builtin_amdgcn_ballot_w64(base + incl > pos);
     if (hit) {
@@ -1181,7 +1190,7 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, Piece&& piec
   if (cached && !whole) {
     const uint32_t lane = threadIdx.x & 63;
     const int32_t Ls = lane < a.num_seqs ? a.seq_lens[lane] : 0;
-    L_l = Ls > 0 ? uint32_t(Ls) : 0u;
+    L_l = seq_len(a, Ls);
     n_l = row_tiles(L_l, a.window);
     incl = wave_scan(n_l * R);
   }
@@ -1199,7 +1208,7 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, Piece&& piec
       b = blockIdx.x / R;
       kh = blockIdx.x % R;
       const int32_t Ls = a.seq_lens[b];
-      L = Ls > 0 ? uint32_t(Ls) : 0u;
+      L = seq_len(a, Ls);
       n = row_tiles(L, a.window);
       start = pos;
       if (n == 0) {
@@ -1221,7 +1230,7 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, Piece&& piec
       n = r.n;
       start = r.start;
       const int32_t Ls = a.seq_lens[b];
-      L = Ls > 0 ? uint32_t(Ls) : 0u;
+      L = seq_len(a, Ls);
     }
     const uint32_t tau0 = whole ? 0u : pos - start;
     const uint32_t tau1 = whole ? n : min(n, end - start);
@@ -1614,6 +1623,7 @@ static DecodeArgs make_args(const uint16_t* q, const void* kc, const void* vc, f
   a.window = window;
   a.num_seqs = 0;
   a.chunk_min = 1;
+  a.max_len = uint32_t(min(uint64_t(max_blocks) * bs, uint64_t(0x7FFFFFFF)));
   a.out = nullptr;
   a.new_k = nullptr;
   a.new_v = nullptr;
@@ -1987,6 +1997,7 @@ static int contig_attn(const uint16_t* q, const void* k, const void* v, uint16_t
                            num_q_heads, num_kv_heads, 16, logit_scale, out_scale, num_splits,
                            uint32_t(strides[0]), 0, 0, sliding_window, head_dim);
   set_query_block(a, q_len, uint32_t(strides[1]), causal, sliding_window);
+  a.max_len = max_seq_len;
   a.q_head_stride = uint32_t(strides[2]);
   for (int i = 0; i < 3; ++i) {
     a.k_strides[i] = strides[3 + i] * esize;

@@ -595,3 +595,20 @@ def test_cache_write_from_strided_rows(fmt):
     torch.cuda.synchronize()
     kc, vc = oracle_pools(w, geom, ks, vs)
     assert np.array_equal(pool_to_np(kd, fmt), kc) and np.array_equal(pool_to_np(vd, fmt), vc)
+
+
+def test_lengths_past_the_block_table_are_clamped():
+    """A seq_len beyond what the sequence's block-table row holds reads no
+    further than the row: the sequence attends the keys its pages hold."""
+    w = workloads.make_workload("tiny", lens=(17, 64), num_q_heads=4, num_kv_heads=2,
+                                head_dim=64, seed=21)
+    assert w.max_blocks_per_seq * w.block_size == 64
+    geom = geometry(w)
+    d = DeviceKV(w, geom)
+    kc, vc = oracle_pools(w, geom)
+    ref = oracle_decode(w, geom, kc, vc)
+    too_long = np.array([17, 5000], np.int32)
+    for S in (1, 3):
+        got = d.decode(S, seq_lens=too_long)
+        assert_close(got, ref, f"clamped S={S}")
+        assert_close(d.decode_single(S), ref, f"whole S={S}")
