@@ -1266,6 +1266,19 @@ __global__ __launch_bounds__(64 * WQ, 1) void splitk_shared(DecodeArgs a) {
   });
 }
 
+// Slots whose values each combine lane requests before the weights are known
+// (a multiple of 8; clamped to the slot count at run time).
+#ifndef PKD_COMBINE_U
+#define PKD_COMBINE_U 8
+#endif
+#ifndef PKD_COMBINE_WAVE_R
+#define PKD_COMBINE_WAVE_R 8
+#endif
+// Most workgroups a combine launch splits rows' columns up to.
+#ifndef PKD_COMBINE_MAX_WG
+#define PKD_COMBINE_MAX_WG 256
+#endif
+
 // Where the combine writes query row bh (sequence-major: per_seq rows per
 // sequence, heads rows per token): element strides of sequence, token, head.
 struct OutMap {
@@ -1279,45 +1292,65 @@ __device__ __forceinline__ uint16_t* out_row(uint16_t* out, const OutMap& om, ui
   return out + uint64_t(b) * om.seq + uint64_t(i) * om.tok + uint64_t(h) * om.head;
 }
 
-// Combine: one workgroup of NT lanes per (sequence, q head); NT = 1024 when
-// there are many slots. The (m, l) of all slots are read once into LDS (with
-// the sequence length alongside) and turned into weights; then lane t
-// accumulates the float2 column t % (D/2) over the slots i = t / (D/2)
-// (mod KS), eight loads in flight, slots without keys not read, and the KS
-// partial sums are added in a fixed order (deterministic).
-template <int D, int NT>
+// Combine: CW workgroups of NT lanes per (sequence, q head), workgroup c
+// taking CC = D / (2 CW) of the float2 columns. Lane t owns column t % CC of
+// its share and the slots i = t / CC (mod KS). It requests its first U slots'
+// values at the start, in the same round trip as the first NT slots' (m, l);
+// further (m, l) are read in chunks of NT only while no end marker has shown
+// up. The (m, l) go to LDS and become weights. A value enters the sum only
+// where its slot's weight is nonzero, so slots past the end marker, whose
+// contents are stale, never reach it. Further slots follow in rounds of eight
+// loads, and the KS partial sums are added in a fixed order (deterministic).
+template <int D, int NT, int CW>
 __global__ __launch_bounds__(NT) void reduce_kernel(const float* ws, uint16_t* out,
                                                     const int32_t* seq_lens, OutMap om,
                                                     uint32_t num_splits) {
-  constexpr int COLS = D / 2;                 // float2 columns of one split row
-  constexpr int KS = NT / COLS;               // split lanes
+  constexpr int CC = D / 2 / CW;              // float2 columns of one workgroup
+  constexpr int KS = NT / CC;                 // split lanes
   constexpr int NW = NT / 64;                 // waves
+  constexpr int U = PKD_COMBINE_U;            // slots per lane requested up front
+  static_assert(CC * CW == D / 2 && CC * KS == NT, "combine lane split");
   extern __shared__ float wsh[];              // l (then weights) and m of every slot
   __shared__ float red[NW];
   __shared__ uint32_t stops[NW];
-  __shared__ f32x2 part[KS][COLS];
+  __shared__ f32x2 part[KS][CC];
   const int tid = threadIdx.x;
-  const uint32_t bh = blockIdx.x;
+  const uint32_t bh = blockIdx.x / CW;
+  const int col = int(blockIdx.x % CW) * CC + tid % CC, ks = tid / CC;
   const uint32_t b = bh / om.per_seq;
   uint16_t* o = out_row(out, om, bh);
   const float* base = ws + uint64_t(bh) * num_splits * (D + 2);
 
+  // unconditional loads (the slot index clamped into the workspace), so that
+  // no branch sits between them and all are in flight at once
+  f32x2 v0[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t i = min(uint32_t(ks + u * KS), num_splits - 1);
+    v0[u] = *reinterpret_cast<const f32x2*>(base + uint64_t(i) * (D + 2) + 2 * col);
+  }
   // slot i counts if l_i > 0 and no earlier slot holds an end marker (l < 0)
   const int32_t L = seq_lens[b];
   uint32_t stop = num_splits;
-  for (uint32_t i = tid; i < num_splits; i += NT) {
-    const f32x2 ml = *reinterpret_cast<const f32x2*>(base + uint64_t(i) * (D + 2) + D);
-    wsh[i] = ml[1];
-    wsh[num_splits + i] = ml[0];
-    if (ml[1] < 0.0f) stop = min(stop, i);
+  for (uint32_t c0 = 0; c0 < num_splits; c0 += NT) {
+    const uint32_t i = c0 + tid;
+    uint32_t mark = num_splits;
+    if (i < num_splits) {
+      const f32x2 ml = *reinterpret_cast<const f32x2*>(base + uint64_t(i) * (D + 2) + D);
+      wsh[i] = ml[1];
+      wsh[num_splits + i] = ml[0];
+      if (ml[1] < 0.0f) mark = i;
+    }
+#pragma unroll
+    for (int of = 32; of >= 1; of >>= 1) mark = min(mark, uint32_t(__shfl_xor(int(mark), of, 64)));
+    if ((tid & 63) == 0) stops[tid >> 6] = mark;
+    __syncthreads();
+#pragma unroll
+    for (int k = 0; k < NW; ++k) stop = min(stop, stops[k]);
+    __syncthreads();
+    if (stop < num_splits) break;             // the same for every lane
   }
   if (L <= 0) stop = 0;                       // empty sequence: zeros
-#pragma unroll
-  for (int of = 32; of >= 1; of >>= 1) stop = min(stop, uint32_t(__shfl_xor(int(stop), of, 64)));
-  if ((tid & 63) == 0) stops[tid >> 6] = stop;
-  __syncthreads();
-#pragma unroll
-  for (int k = 0; k < NW; ++k) stop = min(stop, stops[k]);
   float M = -__builtin_inff();
   for (uint32_t i = tid; i < stop; i += NT)
     if (wsh[i] > 0.0f) M = fmaxf(M, wsh[num_splits + i]);
@@ -1329,14 +1362,14 @@ __global__ __launch_bounds__(NT) void reduce_kernel(const float* ws, uint16_t* o
   for (int k = 1; k < NW; ++k) M = fmaxf(M, red[k]);
   __syncthreads();
   if (M == -__builtin_inff()) {               // no slot holds a key
-    for (int d = tid; d < D; d += NT) o[d] = 0;
+    if (tid < CC) reinterpret_cast<uint32_t*>(o)[col] = 0u;
     return;
   }
   float wsum = 0.0f;
-  for (uint32_t i = tid; i < num_splits; i += NT) {
+  for (uint32_t i = tid; i < stop; i += NT) {
     const float l = wsh[i];
-    const float w = (i < stop && l > 0.0f)
-                        ? l * __builtin_amdgcn_exp2f((wsh[num_splits + i] - M) * kLog2e) : 0.0f;
+    const float w = l > 0.0f ? l * __builtin_amdgcn_exp2f((wsh[num_splits + i] - M) * kLog2e)
+                             : 0.0f;
     wsh[i] = w;
     wsum += w;
   }
@@ -1347,11 +1380,18 @@ __global__ __launch_bounds__(NT) void reduce_kernel(const float* ws, uint16_t* o
 #pragma unroll
   for (int k = 0; k < NW; ++k) wsum += red[k];
 
-  const int col = tid % COLS, ks = tid / COLS;
   f32x2 acc = {0.0f, 0.0f};
-  for (uint32_t i0 = ks; i0 < stop; i0 += 8 * KS) {
-    // eight slots per round; a slot without keys is not read (the weight is
-    // the same for every lane of a wave when D >= 128)
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const uint32_t i = ks + u * KS;
+    const float w = i < stop ? wsh[i] : 0.0f;
+    if (w != 0.0f) {
+      acc[0] = fmaf(w, v0[u][0], acc[0]);
+      acc[1] = fmaf(w, v0[u][1], acc[1]);
+    }
+  }
+  for (uint32_t i0 = ks + U * KS; i0 < stop; i0 += 8 * KS) {
+    // eight slots per round; a slot without keys is not read
     float w[8];
     f32x2 v[8];
 #pragma unroll
@@ -1368,30 +1408,30 @@ __global__ __launch_bounds__(NT) void reduce_kernel(const float* ws, uint16_t* o
       acc[1] = fmaf(w[u], v[u][1], acc[1]);
     }
   }
-  part[ks][col] = acc;
+  part[ks][tid % CC] = acc;
   __syncthreads();
-  if (tid < COLS) {
+  if (tid < CC) {
     f32x2 sum = part[0][tid];
 #pragma unroll
     for (int k = 1; k < KS; ++k) sum += part[k][tid];
     const float inv = 1.0f / fmaxf(wsum, 1e-20f);
-    const uint32_t packed = pack_bf16x2(sum[0] * inv, sum[1] * inv);
-    *reinterpret_cast<uint32_t*>(o + 2 * tid) = packed;
+    reinterpret_cast<uint32_t*>(o)[col] = pack_bf16x2(sum[0] * inv, sum[1] * inv);
   }
 }
 
-// Combine with at most 64 slots: one wave per (sequence, q head), every
-// reduction in registers. Lane i reads slot i's (m, l); the end marker and the
-// largest m come from a ballot and a cross-lane max, the sum of the weights is
-// taken in slot order. Lane c then sums float2 column c (and c + 64, ...) over
-// the slots in slot order, eight loads in flight: the same arithmetic, in the
-// same order, as the merged combine of the single-launch decode.
+// Combine with at most 64 slots and many rows: one wave per (sequence, q
+// head), every reduction in registers. Lane i reads slot i's (m, l); the end
+// marker and the largest m come from a ballot and a cross-lane max, the sum of
+// the weights is taken in slot order. Lane c then sums float2 column c (and
+// c + 64, ...) over the slots in slot order, R loads in flight; a slot whose
+// weight is 0 is not read, so no bytes beyond the live slots leave memory.
 template <int D>
 __global__ __launch_bounds__(64) void reduce_wave_kernel(const float* ws, uint16_t* out,
                                                          const int32_t* seq_lens, OutMap om,
                                                          uint32_t num_splits) {
   constexpr int COLS = D / 2;                      // float2 columns of a slot
   constexpr int NC = COLS >= 64 ? COLS / 64 : 1;   // columns per lane
+  constexpr int R = NC >= 4 ? 8 : PKD_COMBINE_WAVE_R;   // loads in flight per column
   const int lane = threadIdx.x;
   const uint32_t bh = blockIdx.x;
   const float* base = ws + uint64_t(bh) * num_splits * (D + 2);
@@ -1415,11 +1455,11 @@ __global__ __launch_bounds__(64) void reduce_wave_kernel(const float* ws, uint16
   f32x2 acc[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) acc[c] = f32x2{0.0f, 0.0f};
-  for (uint32_t i0 = 0; i0 < stop; i0 += 8) {
-    f32x2 v[8][NC];
-    float wi[8];
+  for (uint32_t i0 = 0; i0 < stop; i0 += R) {
+    f32x2 v[R][NC];
+    float wi[R];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < R; ++u) {
       const uint32_t i = i0 + u;
       // the slot's weight from its lane (a slot holding no keys weighs 0)
       wi[u] = i < stop ? __builtin_bit_cast(float, __builtin_amdgcn_readlane(
@@ -1433,7 +1473,7 @@ __global__ __launch_bounds__(64) void reduce_wave_kernel(const float* ws, uint16
       }
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u)
+    for (int u = 0; u < R; ++u)
 #pragma unroll
       for (int c = 0; c < NC; ++c) {
         acc[c][0] = fmaf(wi[u], v[u][c][0], acc[c][0]);
@@ -1643,37 +1683,53 @@ static DecodeArgs make_args(const uint16_t* q, const void* kc, const void* vc, f
   return a;
 }
 
+template <int D, int CW>
+static void launch_reduce_cols(uint64_t rows, size_t lds, const float* workspace,
+                               uint16_t* output, const int32_t* seq_lens, const OutMap& om,
+                               uint32_t num_splits, hipStream_t stream) {
+  constexpr int NT = CW == 1 ? 1024 : 256;
+  hipLaunchKernelGGL((reduce_kernel<D, NT, CW>), dim3(uint32_t(rows * CW)), dim3(NT), lds, stream,
+                     workspace, output, seq_lens, om, num_splits);
+}
+
+template <int D>
+static void launch_reduce_d(uint64_t rows, uint32_t cw, const float* workspace, uint16_t* output,
+                            const int32_t* seq_lens, const OutMap& om, uint32_t num_splits,
+                            hipStream_t stream) {
+  if (cw == 1 && num_splits <= 64) {           // one wave per (b, h), registers only
+    hipLaunchKernelGGL((reduce_wave_kernel<D>), dim3(uint32_t(rows)), dim3(64), 0, stream,
+                       workspace, output, seq_lens, om, num_splits);
+    return;
+  }
+  const size_t lds = 2 * size_t(num_splits) * sizeof(float);
+  switch (cw) {
+    case 1: launch_reduce_cols<D, 1>(rows, lds, workspace, output, seq_lens, om, num_splits, stream); break;
+    case 2: if constexpr (D >= 64) launch_reduce_cols<D, 2>(rows, lds, workspace, output, seq_lens, om, num_splits, stream); break;
+    case 4: if constexpr (D >= 128) launch_reduce_cols<D, 4>(rows, lds, workspace, output, seq_lens, om, num_splits, stream); break;
+    case 8: if constexpr (D >= 256) launch_reduce_cols<D, 8>(rows, lds, workspace, output, seq_lens, om, num_splits, stream); break;
+    case 16: if constexpr (D >= 512) launch_reduce_cols<D, 16>(rows, lds, workspace, output, seq_lens, om, num_splits, stream); break;
+  }
+}
+
+// Rows of the combine are (sequence, q head) pairs. Few rows (a small batch)
+// leave most CUs idle, so each row's columns are split over CW workgroups:
+// the largest power of two up to D / 32 with rows * CW <= 256 (by default).
+// Each of them reads every slot's (m, l), which is why CW stays 1 for many
+// rows.
 static int launch_reduce(const float* workspace, uint16_t* output, const int32_t* seq_lens,
                          const OutMap& om, uint32_t head_dim, uint32_t num_splits,
                          uint32_t num_seqs, hipStream_t stream) {
-  const uint64_t grid = uint64_t(num_seqs) * om.per_seq;
-  if (grid > 0x7FFFFFFFull) return kUnsupported;
-  const dim3 gd = dim3(uint32_t(grid));
-  if (num_splits <= 64) {                      // one wave per (b, h), registers only
-    const dim3 bw = dim3(64);
-    switch (head_dim) {
-      case 64: hipLaunchKernelGGL((reduce_wave_kernel<64>), gd, bw, 0, stream, workspace, output, seq_lens, om, num_splits); break;
-      case 128: hipLaunchKernelGGL((reduce_wave_kernel<128>), gd, bw, 0, stream, workspace, output, seq_lens, om, num_splits); break;
-      case 256: hipLaunchKernelGGL((reduce_wave_kernel<256>), gd, bw, 0, stream, workspace, output, seq_lens, om, num_splits); break;
-      case 512: hipLaunchKernelGGL((reduce_wave_kernel<512>), gd, bw, 0, stream, workspace, output, seq_lens, om, num_splits); break;
-      default: return kUnsupported;
-    }
-    return launch_status();
-  }
-  const size_t lds = 2 * size_t(num_splits) * sizeof(float);
-  const bool wide = num_splits >= 64;          // many slots: more lanes per (b, h)
-  const dim3 bd = dim3(wide ? 1024 : 256);
-#define PKD_REDUCE(DD) \
-  if (wide) hipLaunchKernelGGL((reduce_kernel<DD, 1024>), gd, bd, lds, stream, workspace, output, seq_lens, om, num_splits); \
-  else hipLaunchKernelGGL((reduce_kernel<DD, 256>), gd, bd, lds, stream, workspace, output, seq_lens, om, num_splits);
+  const uint64_t rows = uint64_t(num_seqs) * om.per_seq;
+  if (rows > 0x7FFFFFFFull / 16) return kUnsupported;
+  uint32_t cw = 1;
+  while (cw * 2 <= head_dim / 32 && rows * cw * 2 <= PKD_COMBINE_MAX_WG) cw *= 2;
   switch (head_dim) {
-    case 64: PKD_REDUCE(64) break;
-    case 128: PKD_REDUCE(128) break;
-    case 256: PKD_REDUCE(256) break;
-    case 512: PKD_REDUCE(512) break;
+    case 64: launch_reduce_d<64>(rows, cw, workspace, output, seq_lens, om, num_splits, stream); break;
+    case 128: launch_reduce_d<128>(rows, cw, workspace, output, seq_lens, om, num_splits, stream); break;
+    case 256: launch_reduce_d<256>(rows, cw, workspace, output, seq_lens, om, num_splits, stream); break;
+    case 512: launch_reduce_d<512>(rows, cw, workspace, output, seq_lens, om, num_splits, stream); break;
     default: return kUnsupported;
   }
-#undef PKD_REDUCE
   return launch_status();
 }
 
