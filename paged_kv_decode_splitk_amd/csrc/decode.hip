@@ -65,6 +65,7 @@ struct DecodeArgs {
   uint32_t window;         // keys of a row: the last `window` (0: all)
   uint32_t num_seqs;
   uint32_t chunk_min;      // least tiles per wave (at most S pieces per row)
+  uint32_t row_lead;       // most start-up tiles counted ahead of each row (split-K only)
   uint32_t max_len;        // keys a sequence can hold (block-table width x block, or the
                            // contiguous tensors' length): longer seq_lens are clamped
   uint16_t* out;           // non-split decode (num_splits 1): BF16 output, else null
@@ -252,14 +253,17 @@ __device__ __forceinline__ uint32_t seq_len(const DecodeArgs& a, int32_t Ls) {
   return Ls > 0 ? min(uint32_t(Ls), a.max_len) : 0u;
 }
 
-// inclusive prefix sum over the 64 lanes
+// Inclusive prefix sum over the 64 lanes, in DPP moves: shifts by 1, 2, 4
+// and 8 within each row of 16 lanes (lanes shifted in from outside the row
+// add 0), then lane 15 of rows 0 and 2 is added to rows 1 and 3, and lane 31
+// (the sum of rows 0 and 1) to rows 2 and 3.
 __device__ __forceinline__ uint32_t wave_scan(uint32_t x) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(x, o, 64);
-    if (lane >= o) x += y;
-  }
+  x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x111, 0xF, 0xF, false));   // row_shr:1
+  x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x112, 0xF, 0xF, false));   // row_shr:2
+  x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x114, 0xF, 0xF, false));   // row_shr:4
+  x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x118, 0xF, 0xF, false));   // row_shr:8
+  x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x142, 0xA, 0xF, false));   // row_bcast:15
+  x += uint32_t(__builtin_amdgcn_update_dpp(0, int(x), 0x143, 0xC, 0xF, false));   // row_bcast:31
   return x;
 }
 
@@ -267,36 +271,42 @@ struct RowLoc {
   uint32_t b, kh, n, start;     // sequence, kv-head/chunk index, tiles, flat start of the row
 };
 
-// Total tiles T of the launch (all rows of all sequences).
-__device__ __forceinline__ uint32_t total_tiles(const DecodeArgs& a, uint32_t rows_per_seq) {
+// Total tiles T of the launch (all rows of all sequences), and the rows
+// that have any.
+__device__ __forceinline__ uint32_t total_tiles(const DecodeArgs& a, uint32_t rows_per_seq,
+                                                uint32_t& live_rows) {
   uint32_t tot = 0;
-  for (uint32_t b0 = 0; b0 < a.num_seqs; b0 += 64) {
-    const uint32_t bb = b0 + (threadIdx.x & 63);
-    const int32_t Ls = bb < a.num_seqs ? a.seq_lens[bb] : 0;
-    const uint32_t t = row_tiles(seq_len(a, Ls), a.window) * rows_per_seq;
-    tot += __shfl(wave_scan(t), 63, 64);
-  }
-  return tot;
-}
-
-// The row holding flat tile `pos` (pos < T).
-__device__ __forceinline__ RowLoc find_row(const DecodeArgs& a, uint32_t pos,
-                                           uint32_t rows_per_seq) {
-  uint32_t base = 0;
+  live_rows = 0;
   for (uint32_t b0 = 0; b0 < a.num_seqs; b0 += 64) {
     const uint32_t bb = b0 + (threadIdx.x & 63);
     const int32_t Ls = bb < a.num_seqs ? a.seq_lens[bb] : 0;
     const uint32_t n = row_tiles(seq_len(a, Ls), a.window);
+    tot += uint32_t(__builtin_amdgcn_readlane(int(wave_scan(n * rows_per_seq)), 63));
+    live_rows += uint32_t(__builtin_popcountll(__builtin_amdgcn_ballot_w64(n > 0))) * rows_per_seq;
+  }
+  return tot;
+}
+
+// The row holding flat position `pos` (pos < T + lead * live rows), each row
+// taking its `lead` start-up positions and then its tiles.
+__device__ __forceinline__ RowLoc find_row(const DecodeArgs& a, uint32_t pos,
+                                           uint32_t rows_per_seq, uint32_t lead) {
+  uint32_t base = 0;
+  for (uint32_t b0 = 0; b0 < a.num_seqs; b0 += 64) {
+    const uint32_t bb = b0 + (threadIdx.x & 63);
+    const int32_t Ls = bb < a.num_seqs ? a.seq_lens[bb] : 0;
+    const uint32_t nt = row_tiles(seq_len(a, Ls), a.window);
+    const uint32_t n = nt > 0 ? nt + lead : 0u;
     const uint32_t incl = wave_scan(n * rows_per_seq);
     const uint64_t hit = __builtin_amdgcn_ballot_w64(base + incl > pos);
     if (hit) {
       const int l = __builtin_ctzll(hit);
-      const uint32_t nl = __shfl(n, l, 64);
-      const uint32_t excl = __shfl(incl - n * rows_per_seq, l, 64);
+      const uint32_t nl = uint32_t(__builtin_amdgcn_readlane(int(n), l));
+      const uint32_t excl = uint32_t(__builtin_amdgcn_readlane(int(incl), l)) - nl * rows_per_seq;
       const uint32_t kh = (pos - base - excl) / nl;
       return RowLoc{b0 + l, kh, nl, base + excl + kh * nl};
     }
-    base += __shfl(incl, 63, 64);
+    base += uint32_t(__builtin_amdgcn_readlane(int(incl), 63));
   }
   return RowLoc{a.num_seqs, 0, 0, base};
 }
@@ -1186,58 +1196,87 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, Piece&& piec
   // With at most 64 sequences, one length per lane, loaded once: the tile
   // counts, their prefix sums and every row lookup come from these registers.
   const bool cached = a.num_seqs <= 64;
-  uint32_t L_l = 0, n_l = 0, incl = 0;
+  uint32_t L_l = 0, n_l = 0, T = 0, live = 0, incl = 0, live_le = 0;
   if (cached && !whole) {
     const uint32_t lane = threadIdx.x & 63;
     const int32_t Ls = lane < a.num_seqs ? a.seq_lens[lane] : 0;
     L_l = seq_len(a, Ls);
     n_l = row_tiles(L_l, a.window);
     incl = wave_scan(n_l * R);
+    T = uint32_t(__builtin_amdgcn_readlane(int(incl), 63));
+    // sequences with keys: in the wave, and up to this lane
+    const uint64_t has = __builtin_amdgcn_ballot_w64(n_l > 0);
+    live = uint32_t(__builtin_popcountll(has)) * R;
+    live_le = __builtin_amdgcn_mbcnt_hi(uint32_t(has >> 32),
+                                        __builtin_amdgcn_mbcnt_lo(uint32_t(has), 0u)) +
+              (n_l > 0 ? 1u : 0u);
+  } else if (!whole) {
+    T = total_tiles(a, R, live);
   }
-  uint32_t c = 1, pos = blockIdx.x, end = blockIdx.x + 1;
+  // Start-up positions: each row with keys is laid out behind `lead` empty
+  // positions, paid by the wave that starts the row for that row's first
+  // round trips (length, block table and q, first tile, with its ring
+  // empty). They fill only the slack that rounding c up left (P*c >= T +
+  // lead*live), so no wave gets more positions than c. When c is the
+  // least chunk instead, waves are idle anyway and the rows stay aligned.
+  uint32_t c = 1, lead = 0, pos = blockIdx.x, end = blockIdx.x + 1;
   if (!whole) {
-    const uint32_t T = cached ? __shfl(incl, 63, 64) : total_tiles(a, R);
-    c = max((T + P - 1) / P, a.chunk_min);
-    pos = blockIdx.x * c;
-    end = min(pos + c, T);
+    const uint32_t c0 = (T + P - 1) / P;
+    c = max(c0, a.chunk_min);
+    if (live > 0 && c == c0) {
+      const uint32_t slack = P * c - T;            // < P: c rounds T / P up
+      lead = live * a.row_lead <= slack ? a.row_lead : slack / live;
+    }
+    incl += lead * R * live_le;                  // inclusive prefix of the laid-out spans
+    const uint32_t flat = T + lead * live;
+    pos = uint32_t(min(uint64_t(blockIdx.x) * c, uint64_t(flat)));
+    end = uint32_t(min(uint64_t(pos) + c, uint64_t(flat)));
   }
   while (pos < end) {
-    // the row holding flat tile pos: sequence b, row kh, n tiles from `start`
-    uint32_t b, kh, n, start, L;
+    // the row holding flat position pos: sequence b, row kh, its n tiles
+    // from flat position rs (behind `lead` start-up positions)
+    uint32_t b, kh, n, rs, L;
     if (whole) {
       b = blockIdx.x / R;
       kh = blockIdx.x % R;
       const int32_t Ls = a.seq_lens[b];
       L = seq_len(a, Ls);
       n = row_tiles(L, a.window);
-      start = pos;
+      rs = pos;
       if (n == 0) {
         if (a.out && (WQ > 1 || threadIdx.x < 64)) zero_row<D, NC, WQ>(a, b, kh);
         break;
       }
     } else if (cached) {
-      const int l = __builtin_ctzll(__builtin_amdgcn_ballot_w64(incl > pos));
-      n = __shfl(n_l, l, 64);
-      const uint32_t excl = __shfl(incl, l, 64) - n * R;
-      L = __shfl(L_l, l, 64);
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(incl > pos);
+      const int l = hit ? __builtin_ctzll(hit) : 64;
+      if (uint32_t(l) >= a.num_seqs) break;        // pos < T + lead * live: never taken
+      n = uint32_t(__builtin_amdgcn_readlane(int(n_l), l));
+      const uint32_t span = n + lead;
+      const uint32_t excl = uint32_t(__builtin_amdgcn_readlane(int(incl), l)) - span * R;
+      L = uint32_t(__builtin_amdgcn_readlane(int(L_l), l));
       b = uint32_t(l);
-      kh = (pos - excl) / n;
-      start = excl + kh * n;
+      kh = (pos - excl) / span;
+      rs = excl + kh * span + lead;
     } else {
-      const RowLoc r = find_row(a, pos, R);
+      const RowLoc r = find_row(a, pos, R, lead);
+      if (r.b >= a.num_seqs) break;                // as above: never taken
       b = r.b;
       kh = r.kh;
-      n = r.n;
-      start = r.start;
+      n = r.n - lead;
+      rs = r.start + lead;
       const int32_t Ls = a.seq_lens[b];
       L = seq_len(a, Ls);
     }
-    const uint32_t tau0 = whole ? 0u : pos - start;
-    const uint32_t tau1 = whole ? n : min(n, end - start);
-    const uint32_t slot = whole ? 0u : pos / c - start / c;
-    piece(b, kh, tau0, tau1, slot, whole || start + n <= end, L);
+    if (n == 0 || kh >= R) break;                  // as above: never taken
+    const uint32_t f0 = max(pos, rs);
+    const uint32_t f1 = whole ? rs + n : min(rs + n, end);
+    if (f1 > f0) {
+      // slot: waves from the one holding the row's first tile
+      piece(b, kh, f0 - rs, f1 - rs, whole ? 0u : f0 / c - rs / c, whole || rs + n <= end, L);
+    }
     if (whole) break;
-    pos = start + tau1;
+    pos = max(f1, min(rs, end));
   }
 }
 
@@ -1544,6 +1583,13 @@ static uint64_t stream_capacity() {
   return cache[dev];
 }
 
+// Start-up positions counted ahead of each row by the stream partition: a
+// row's first round trips and its ring fill cost about three tiles' time.
+#ifndef PKD_ROW_LEAD
+#define PKD_ROW_LEAD 3
+#endif
+constexpr uint32_t kRowLead = PKD_ROW_LEAD;
+
 // One launch of the stream kernel with NC column chunks per wave.
 template <int FMT, int D, int NC, bool CONTIG>
 static int launch_stream(DecodeArgs a, hipStream_t stream) {
@@ -1553,6 +1599,7 @@ static int launch_stream(DecodeArgs a, hipStream_t stream) {
   uint32_t tile_bound = a.max_blocks * (a.block_size / 16);
   if (a.window > 0) tile_bound = min(tile_bound, (a.window + 14) / 16 + 1);
   a.chunk_min = a.num_splits > 1 ? (tile_bound + a.num_splits - 2) / (a.num_splits - 1) : 1;
+  a.row_lead = kRowLead;
   // one workgroup per piece (at most num_splits per row), or as many as stay
   // resident; a workgroup is one wave, or two sharing a head_dim of 512
   uint64_t groups = rows;
@@ -1577,6 +1624,7 @@ static int launch_shared(DecodeArgs a, hipStream_t stream) {
   uint32_t tile_bound = a.max_blocks * (a.block_size / 16);
   if (a.window > 0) tile_bound = min(tile_bound, (a.window + 14) / 16 + 1);
   a.chunk_min = a.num_splits > 1 ? (tile_bound + a.num_splits - 2) / (a.num_splits - 1) : 1;
+  a.row_lead = kRowLead;
   uint64_t groups = rows;
   if (a.num_splits > 1) {
     int dev = 0;
@@ -1663,6 +1711,7 @@ static DecodeArgs make_args(const uint16_t* q, const void* kc, const void* vc, f
   a.window = window;
   a.num_seqs = 0;
   a.chunk_min = 1;
+  a.row_lead = 0;
   a.max_len = uint32_t(min(uint64_t(max_blocks) * bs, uint64_t(0x7FFFFFFF)));
   a.out = nullptr;
   a.new_k = nullptr;
