@@ -1373,15 +1373,17 @@ __global__ __launch_bounds__(NT) void reduce_kernel(const float* ws, uint16_t* o
   uint32_t stop = num_splits;
   for (uint32_t c0 = 0; c0 < num_splits; c0 += NT) {
     const uint32_t i = c0 + tid;
-    uint32_t mark = num_splits;
+    bool is_mark = false;
     if (i < num_splits) {
       const f32x2 ml = *reinterpret_cast<const f32x2*>(base + uint64_t(i) * (D + 2) + D);
       wsh[i] = ml[1];
       wsh[num_splits + i] = ml[0];
-      if (ml[1] < 0.0f) mark = i;
+      is_mark = ml[1] < 0.0f;
     }
-#pragma unroll
-    for (int of = 32; of >= 1; of >>= 1) mark = min(mark, uint32_t(__shfl_xor(int(mark), of, 64)));
+    // the wave's first end marker, if any
+    const uint64_t marks = __builtin_amdgcn_ballot_w64(is_mark);
+    const uint32_t mark = marks ? c0 + uint32_t(tid & ~63) + uint32_t(__builtin_ctzll(marks))
+                                : num_splits;
     if ((tid & 63) == 0) stops[tid >> 6] = mark;
     __syncthreads();
 #pragma unroll

@@ -145,16 +145,29 @@ __device__ __forceinline__ float sum_over_rows(float x) {
   return __uint_as_float(r2[0]) + __uint_as_float(r2[1]);
 }
 
-// wave64 reductions (full wave).
+// x from lane l ^ 1, l ^ 2 (quad permutes), 7 - l and 15 - l within the row
+// (half-row and row mirrors): four DPP moves bring every lane of a row of 16
+// into each lane's reduction.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// wave64 reductions (full wave), every lane gets the result: within rows of
+// 16 by DPP, then across the four rows by the row swaps.
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
+  v = fmaxf(v, dpp_f32<0xB1>(v));      // quad_perm [1, 0, 3, 2]
+  v = fmaxf(v, dpp_f32<0x4E>(v));      // quad_perm [2, 3, 0, 1]
+  v = fmaxf(v, dpp_f32<0x141>(v));     // row_half_mirror
+  v = fmaxf(v, dpp_f32<0x140>(v));     // row_mirror
+  return max_over_rows(v);
 }
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  return sum_over_rows(v);
 }
 
 }  // namespace pkd
