@@ -1350,7 +1350,7 @@ __global__ __launch_bounds__(NT) void reduce_kernel(const float* ws, uint16_t* o
   constexpr int U = PKD_COMBINE_U;            // slots per lane requested up front
   static_assert(CC * CW == D / 2 && CC * KS == NT, "combine lane split");
   extern __shared__ float wsh[];              // l (then weights) and m of every slot
-  __shared__ float red[NW];
+  __shared__ float red[NW], red2[NW];
   __shared__ uint32_t stops[NW];
   __shared__ f32x2 part[KS][CC];
   const int tid = threadIdx.x;
@@ -1368,44 +1368,48 @@ __global__ __launch_bounds__(NT) void reduce_kernel(const float* ws, uint16_t* o
     const uint32_t i = min(uint32_t(ks + u * KS), num_splits - 1);
     v0[u] = *reinterpret_cast<const f32x2*>(base + uint64_t(i) * (D + 2) + 2 * col);
   }
-  // slot i counts if l_i > 0 and no earlier slot holds an end marker (l < 0)
+  // slot i counts if l_i > 0 and no earlier slot holds an end marker (l < 0).
+  // One pass per NT slots finds each wave's first marker and the largest m
+  // of the wave's live slots before it; the block then takes the first
+  // marker (stop) and the largest m of the waves that start before it.
   const int32_t L = seq_lens[b];
+  const int wv = tid >> 6;
   uint32_t stop = num_splits;
+  float M = -__builtin_inff();
   for (uint32_t c0 = 0; c0 < num_splits; c0 += NT) {
     const uint32_t i = c0 + tid;
-    bool is_mark = false;
+    f32x2 ml = {-__builtin_inff(), 0.0f};
     if (i < num_splits) {
-      const f32x2 ml = *reinterpret_cast<const f32x2*>(base + uint64_t(i) * (D + 2) + D);
+      ml = *reinterpret_cast<const f32x2*>(base + uint64_t(i) * (D + 2) + D);
       wsh[i] = ml[1];
       wsh[num_splits + i] = ml[0];
-      is_mark = ml[1] < 0.0f;
     }
-    // the wave's first end marker, if any
-    const uint64_t marks = __builtin_amdgcn_ballot_w64(is_mark);
+    const uint64_t marks = __builtin_amdgcn_ballot_w64(i < num_splits && ml[1] < 0.0f);
     const uint32_t mark = marks ? c0 + uint32_t(tid & ~63) + uint32_t(__builtin_ctzll(marks))
                                 : num_splits;
-    if ((tid & 63) == 0) stops[tid >> 6] = mark;
+    const float mw = wave_max(ml[1] > 0.0f && i < mark ? ml[0] : -__builtin_inff());
+    if ((tid & 63) == 0) {
+      stops[wv] = mark;
+      red[wv] = mw;
+    }
     __syncthreads();
 #pragma unroll
     for (int k = 0; k < NW; ++k) stop = min(stop, stops[k]);
-    __syncthreads();
-    if (stop < num_splits) break;             // the same for every lane
-  }
-  if (L <= 0) stop = 0;                       // empty sequence: zeros
-  float M = -__builtin_inff();
-  for (uint32_t i = tid; i < stop; i += NT)
-    if (wsh[i] > 0.0f) M = fmaxf(M, wsh[num_splits + i]);
-  M = wave_max(M);
-  if ((tid & 63) == 0) red[tid >> 6] = M;
-  __syncthreads();
-  M = red[0];
 #pragma unroll
-  for (int k = 1; k < NW; ++k) M = fmaxf(M, red[k]);
-  __syncthreads();
+    for (int k = 0; k < NW; ++k)
+      if (c0 + 64u * k < stop) M = fmaxf(M, red[k]);
+    if (stop < num_splits || c0 + NT >= num_splits) break;   // the same for every lane
+    __syncthreads();                            // stops and red are written again
+  }
+  if (L <= 0) {                               // empty sequence: zeros
+    stop = 0;
+    M = -__builtin_inff();
+  }
   if (M == -__builtin_inff()) {               // no slot holds a key
     if (tid < CC) reinterpret_cast<uint32_t*>(o)[col] = 0u;
     return;
   }
+  // weights, each lane for the slots it read above (no barrier needed)
   float wsum = 0.0f;
   for (uint32_t i = tid; i < stop; i += NT) {
     const float l = wsh[i];
@@ -1415,11 +1419,11 @@ __global__ __launch_bounds__(NT) void reduce_kernel(const float* ws, uint16_t* o
     wsum += w;
   }
   wsum = wave_sum(wsum);
-  if ((tid & 63) == 0) red[tid >> 6] = wsum;
+  if ((tid & 63) == 0) red2[wv] = wsum;
   __syncthreads();
   wsum = 0.0f;
 #pragma unroll
-  for (int k = 0; k < NW; ++k) wsum += red[k];
+  for (int k = 0; k < NW; ++k) wsum += red2[k];
 
   f32x2 acc = {0.0f, 0.0f};
 #pragma unroll
