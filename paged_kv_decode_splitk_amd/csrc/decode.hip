@@ -1217,14 +1217,21 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, Piece&& piec
   // positions, paid by the wave that starts the row for that row's first
   // round trips (length, block table and q, first tile, with its ring
   // empty). They fill only the slack that rounding c up left (P*c >= T +
-  // lead*live), so no wave gets more positions than c. When c is the
-  // least chunk instead, waves are idle anyway and the rows stay aligned.
+  // lead*live), so no wave gets more positions than c, unless c is long
+  // enough that one more tile costs little. When c is the least chunk
+  // instead, waves are idle anyway and the rows stay aligned.
   uint32_t c = 1, lead = 0, pos = blockIdx.x, end = blockIdx.x + 1;
   if (!whole) {
     const uint32_t c0 = (T + P - 1) / P;
     c = max(c0, a.chunk_min);
     if (live > 0 && c == c0) {
-      const uint32_t slack = P * c - T;            // < P: c rounds T / P up
+      uint32_t slack = P * c - T;                  // < P: c rounds T / P up
+      // Chunks of 32 tiles or more: one more tile per wave (at most 3%) when
+      // that buys every row its whole lead.
+      if (c >= 32 && live * a.row_lead > slack && live * a.row_lead <= slack + P) {
+        ++c;
+        slack += P;
+      }
       lead = live * a.row_lead <= slack ? a.row_lead : slack / live;
     }
     incl += lead * R * live_le;                  // inclusive prefix of the laid-out spans
