@@ -58,7 +58,9 @@ extern "C" {
 
 #define PKD_OK 0
 #define PKD_ERR_INVALID_ARG (-1) /* null buffer with work to do, bad count, stride or alignment */
-#define PKD_ERR_UNSUPPORTED (-2) /* head_dim / block_size / num_splits outside the supported set */
+#define PKD_ERR_UNSUPPORTED (-2) /* head_dim / block_size / num_splits outside the supported set,
+                                  or a split-K launch of more than 2^30 16-key tiles (sequences x
+                                  kv heads x the tiles a block-table row or window can hold) */
 #define PKD_ERR_LAUNCH (-3)      /* the HIP runtime reported an error after the launch */
 
 #define PKD_MAX_SPLITS 4096u

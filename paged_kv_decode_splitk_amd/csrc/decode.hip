@@ -1603,15 +1603,22 @@ static uint64_t stream_capacity() {
 #endif
 constexpr uint32_t kRowLead = PKD_ROW_LEAD;
 
+// The partition counts tiles, start-up positions and wave ranges in 32 bits:
+// T + 3 * rows + 2 * waves stays below 2^32 for T up to 2^30 tiles.
+constexpr uint64_t kMaxLaunchTiles = 1ull << 30;
+
 // One launch of the stream kernel with NC column chunks per wave.
 template <int FMT, int D, int NC, bool CONTIG>
 static int launch_stream(DecodeArgs a, hipStream_t stream) {
   constexpr uint64_t ds = kDSplit<FMT, D>;
   a.head_chunks = (a.col_chunks + NC - 1) / NC;
   const uint64_t rows = uint64_t(a.num_seqs) * a.num_kv_heads * a.head_chunks;
-  uint32_t tile_bound = a.max_blocks * (a.block_size / 16);
-  if (a.window > 0) tile_bound = min(tile_bound, (a.window + 14) / 16 + 1);
-  a.chunk_min = a.num_splits > 1 ? (tile_bound + a.num_splits - 2) / (a.num_splits - 1) : 1;
+  uint64_t tile_bound = uint64_t(a.max_blocks) * (a.block_size / 16);
+  if (a.window > 0) tile_bound = min(tile_bound, uint64_t((a.window + 14) / 16 + 1));
+  if (rows * tile_bound > kMaxLaunchTiles) return kUnsupported;
+  a.chunk_min = a.num_splits > 1
+                    ? uint32_t((tile_bound + a.num_splits - 2) / (a.num_splits - 1))
+                    : 1u;
   a.row_lead = kRowLead;
   // one workgroup per piece (at most num_splits per row), or as many as stay
   // resident; a workgroup is one wave, or two sharing a head_dim of 512
@@ -1634,9 +1641,12 @@ static int launch_shared(DecodeArgs a, hipStream_t stream) {
   static uint64_t cache[64];
   a.head_chunks = (a.col_chunks + NC * WQ - 1) / (NC * WQ);
   const uint64_t rows = uint64_t(a.num_seqs) * a.num_kv_heads * a.head_chunks;
-  uint32_t tile_bound = a.max_blocks * (a.block_size / 16);
-  if (a.window > 0) tile_bound = min(tile_bound, (a.window + 14) / 16 + 1);
-  a.chunk_min = a.num_splits > 1 ? (tile_bound + a.num_splits - 2) / (a.num_splits - 1) : 1;
+  uint64_t tile_bound = uint64_t(a.max_blocks) * (a.block_size / 16);
+  if (a.window > 0) tile_bound = min(tile_bound, uint64_t((a.window + 14) / 16 + 1));
+  if (rows * tile_bound > kMaxLaunchTiles) return kUnsupported;
+  a.chunk_min = a.num_splits > 1
+                    ? uint32_t((tile_bound + a.num_splits - 2) / (a.num_splits - 1))
+                    : 1u;
   a.row_lead = kRowLead;
   uint64_t groups = rows;
   if (a.num_splits > 1) {

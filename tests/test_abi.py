@@ -98,6 +98,9 @@ def _decode(lib, **kw):
     (dict(bs=48), -2),
     (dict(S=0), -2),
     (dict(S=4097), -2),
+    # more than 2^30 16-key tiles in one launch: 2^16 sequences x 4 kv heads x
+    # 2^13 pages (rejected before anything is launched or read)
+    (dict(B=1 << 16, Hq=4, Hkv=4, maxb=1 << 13, q_stride=256, S=2), -2),
 ])
 def test_decode_validation(lib, kw, status):
     assert _decode(lib, **kw) == status
