@@ -258,6 +258,31 @@ def _graph_time(fn, calls, reps):
 STEPS_PER_GRAPH = 32
 
 
+def _steps_spread(fn, NL, steps):
+    """p10 / p50 / p90 of the per-step time over graph replays: the same
+    graphs of whole layer cycles as _steps_time, replayed `steps` steps' worth
+    once more with an event pair around each replay (a pass of its own, so the
+    timed run above carries no extra events)."""
+    import torch
+    per_graph = NL * max(1, -(-STEPS_PER_GRAPH // NL))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(per_graph):
+            fn(i % NL)
+    g.replay()
+    torch.cuda.synchronize()
+    reps = max(8, steps // per_graph)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    ev[0].record()
+    for r in range(reps):
+        g.replay()
+        ev[r + 1].record()
+    torch.cuda.synchronize()
+    per_step = np.array([ev[r].elapsed_time(ev[r + 1]) / per_graph for r in range(reps)])
+    del g
+    return {f"p{q}": float(np.percentile(per_step, q)) * 1e3 for q in (10, 50, 90)}
+
+
 def _steps_time(fn, NL, steps):
     """ms per step of exactly `steps` steps fn(layer), cycling over the NL
     layers. The steps are captured as a model's layers are, many to a graph
@@ -313,6 +338,7 @@ def time_workload(name, steps, warmup, kernel_reps=100, single=True):
     t0 = time.perf_counter()
     ms_step = _steps_time(lay.step, NL, steps)
     wall = time.perf_counter() - t0
+    spread = _steps_spread(lay.step, NL, steps)
     ms_sep = _steps_time(lay.step_separate, NL, steps)
     nan = float("nan")
     ms_single = _steps_time(lay.step_single, NL, steps) if single else nan
@@ -329,6 +355,7 @@ def time_workload(name, steps, warmup, kernel_reps=100, single=True):
         kv_pool_bytes_per_layer=lay.pool_bytes, attended_tokens=attended_tokens(w),
         kv_bytes_per_step=kv_bytes, steps=steps_run, ms_per_step=ms_step,
         us_per_step=ms_step * 1e3, kv_gbs=gbs(ms_step), wall_s=wall,
+        us_per_step_spread=spread,
         separate_write_us_per_step=ms_sep * 1e3, separate_write_kv_gbs=gbs(ms_sep),
         splitk_plain_us=plain_ms * 1e3, splitk_plain_gbs=gbs(plain_ms),
         non_split_us_per_step=ms_single * 1e3, non_split_kv_gbs=gbs(ms_single),
@@ -654,7 +681,8 @@ def main():
     extras = {}
     for name in args.extra:
         r, _ = time_workload(name, args.steps, args.warmup, single=not args.no_single)
-        extras[name] = {k: r[k] for k in ("us_per_step", "kv_gbs", "pct_of_peak",
+        extras[name] = {k: r[k] for k in ("us_per_step", "us_per_step_spread", "kv_gbs",
+                                          "pct_of_peak",
                                           "separate_write_us_per_step",
                                           "separate_write_kv_gbs",
                                           "splitk_plain_us", "splitk_plain_gbs",
@@ -729,6 +757,7 @@ def main():
             "step": "split-KV pass that first appends the new token's K/V (the cache write) "
                     "+ combine pass, HIP-graph replay",
         },
+        "us_per_step_spread": main_res["us_per_step_spread"],
         "separate_write_step": {k: main_res[k] for k in ("separate_write_us_per_step",
                                                           "separate_write_kv_gbs")},
         "non_split_step": {k: main_res[k] for k in ("non_split_us_per_step",
