@@ -690,7 +690,7 @@ def main():
                                           "non_split_kv_gbs",
                                           "non_split_kernel_us", "non_split_kernel_gbs",
                                           "splitk_us", "splitk_gbs", "num_splits",
-                                          "kv_bytes_per_step", "layers_rotated")}
+                                          "kv_bytes_per_step", "layers_rotated", "kv_dtype")}
         print(f"bench: {name} {r['us_per_step']:.2f} us/step {r['kv_gbs']:.0f} GB/s",
               file=sys.stderr, flush=True)
 
@@ -770,6 +770,13 @@ def main():
     }
     for name, r in extras.items():
         line[name] = r
+        # the same roofline record for the extra workload's split-K pass (with the append)
+        ach = r["kv_bytes_per_step"] / (r["splitk_us"] * 1e-6) / 1e9
+        line[name]["roofline"] = dict(
+            bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s", frac=ach / PEAK_HBM_GBS,
+            traffic=traffic_record(name, "splitk"),
+            kernel=f"paged_decode_attn_splitk_append_{r['kv_dtype']}",
+            algorithmic_bytes_per_launch=r["kv_bytes_per_step"], avg_launch_us=r["splitk_us"])
     if sweep:
         line["b1_sweep"] = sweep
     if verify:

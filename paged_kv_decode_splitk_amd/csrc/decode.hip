@@ -231,14 +231,17 @@ __device__ __forceinline__ void wait_vmcnt() {
 // Balanced ("stream") partition of one launch's work. A row is a (sequence,
 // kv head, chunk of up to 16 q heads) triple; row (b, k) has n_b tiles, the
 // 16-key tiles overlapping the sequence's attended keys. The rows are laid end
-// to end, sequence-major, into one index space of T tiles; wave w of the P
-// launched waves takes tiles [w*c, (w+1)*c) with c = max(ceil(T/P), c_min) and
-// c_min = ceil(n_bound / (S - 1)) for the host's bound n_bound on n_b. A wave
-// thus covers one or more row pieces, each a contiguous key range; the piece
-// of row r starting at flat tile f goes to workspace slot
-// floor(f/c) - floor(start(r)/c) <= S - 1. The wave that ends a row marks the
-// row's later slots empty. With S == 1, wave w takes row w whole. Every wave
-// gets the same number of tiles whatever the length mix of the batch.
+// to end, sequence-major, into one index space, each row with keys behind
+// `lead` empty start-up positions (see for_each_piece); wave w of the P
+// launched waves takes positions [w*c, (w+1)*c) with c = max(ceil(T/P), c_min)
+// (or one more when that buys the whole lead) and c_min = ceil(n_bound / (S -
+// 1)) for the host's bound n_bound on n_b. A wave thus covers one or more row
+// pieces, each a contiguous key range; the piece of row r starting at flat
+// position f goes to workspace slot floor(f/c) - floor(first(r)/c) <= S - 1,
+// first(r) being the position of the row's first tile. The wave that ends a
+// row marks the row's later slots empty. With S == 1, wave w takes row w
+// whole. Every wave gets the same number of positions whatever the length mix
+// of the batch.
 
 __device__ __forceinline__ uint32_t row_tiles(uint32_t L, uint32_t window) {
   if (L == 0) return 0;
