@@ -541,6 +541,74 @@ def time_contig(name, layout, steps, warmup, kernel_reps=100):
     return res
 
 
+def time_aux(reps=10):
+    """The two steps off the decode loop's timed path, each against HBM:
+    bf16_absmax over the FP8 workload's whole K tensor (the calibration read),
+    and reshape_and_cache_{bf16,fp8,nvfp4} writing every token of the llama8b
+    batch into a fresh pool through its slot mapping. Seeded synthetic BF16
+    values on the device; `reps` back-to-back launches between two events."""
+    import torch
+    import paged_kv_decode_splitk_amd as pkd
+    import workloads
+    dev = torch.device("cuda:0")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(5)
+    res = {}
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps * 1e3          # us per launch
+
+    wf = workloads.make_workload("fp8", with_kv=False)
+    n = int(wf.seq_lens.astype(np.int64).sum()) * wf.num_kv_heads * wf.head_dim
+    x = torch.randn(n, generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    amax = torch.zeros(1, dtype=torch.float32, device=dev)
+    us = timed(lambda: pkd.bf16_absmax(x.view(torch.int16), amax))
+    res["bf16_absmax"] = dict(elements=n, us=us, gbs=2 * n / (us * 1e-6) / 1e9,
+                              pct_of_peak=100.0 * 2 * n / (us * 1e-6) / 1e9 / PEAK_HBM_GBS)
+    del x
+
+    w = workloads.make_workload("llama8b", with_kv=False)
+    T, Hkv, D, bs = w.num_tokens, w.num_kv_heads, w.head_dim, w.block_size
+    key = torch.randn((T, Hkv * D), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
+    val = torch.randn((T, Hkv * D), generator=gen, device=dev).to(torch.bfloat16).view(torch.int16)
+    slots = torch.from_numpy(w.slot_mapping).to(dev)
+    args = (key, val)
+    for fmt in ("bf16", "fp8", "nvfp4"):
+        if fmt == "bf16":
+            page, dt, out_b = bs * Hkv * D, torch.int16, 2.0
+        elif fmt == "fp8":
+            page, dt, out_b = bs * Hkv * D, torch.uint8, 1.0
+        else:
+            stride, data = pkd.nvfp4_default_sections(Hkv, D, bs)
+            page, dt, out_b = stride, torch.uint8, 0.5 + 1.0 / 16
+        kp = torch.zeros(w.num_pages * page, dtype=dt, device=dev)
+        vp = torch.zeros_like(kp)
+        tail = (slots, Hkv, D, bs)
+        if fmt == "bf16":
+            fn = lambda: pkd.reshape_and_cache_bf16(*args, kp, vp, *tail)
+        elif fmt == "fp8":
+            fn = lambda: pkd.reshape_and_cache_fp8(*args, kp, vp, *tail, 0.01, 0.01)
+        else:
+            fn = lambda: pkd.reshape_and_cache_nvfp4(*args, kp, vp, *tail, stride, data)
+        us = timed(fn)
+        nbytes = 2 * T * Hkv * D * (2 + out_b)         # K and V: BF16 in, encoded out
+        res[f"reshape_and_cache_{fmt}"] = dict(tokens=T, us=us, gbs=nbytes / (us * 1e-6) / 1e9,
+                                               pct_of_peak=100.0 * nbytes / (us * 1e-6) / 1e9
+                                               / PEAK_HBM_GBS)
+        del kp, vp
+    del key, val
+    torch.cuda.empty_cache()
+    return res
+
+
 def counter_run(name, calls=20):
     """Only the split-K pass with the append, `calls` times over the layers
     (for rocprofv3 counter passes, which profile every dispatch)."""
@@ -722,6 +790,10 @@ def main():
               f"{r['kv_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
         contig[f"{nm}_{lay}"] = r
 
+    aux = time_aux()
+    print("bench: aux " + ", ".join(f"{k} {v['us']:.1f} us {v['gbs']:.0f} GB/s"
+                                    for k, v in aux.items()), file=sys.stderr, flush=True)
+
     # the step's dominant kernel: the split-K pass (with the append)
     fmt = main_res["kv_dtype"]
     kernel, us, tag = f"paged_decode_attn_splitk_append_{fmt}", main_res["splitk_us"], "splitk"
@@ -783,6 +855,7 @@ def main():
         line["verify"] = verify
     if contig:
         line["contiguous_kv"] = contig
+    line["aux_kernels"] = aux
     print(json.dumps(line))
 
 

@@ -87,16 +87,28 @@ __device__ __forceinline__ uint32_t e2m1_from_f32(float y) {
   return sign | c;
 }
 
+// Two already divided values -> two E4M3FN codes (low byte: a), the same
+// codes as e4m3_from_f32: NaN is 0x7F, magnitudes at or past 448 are clamped
+// to 448 first, and the gfx950 convert rounds the rest to nearest, ties to
+// even, sign kept (its subnormal codes are multiples of 2^-9).
+__device__ __forceinline__ uint32_t e4m3x2_from_f32(float a, float b) {
+  const float ca = fminf(fmaxf(a, -448.0f), 448.0f);
+  const float cb = fminf(fmaxf(b, -448.0f), 448.0f);
+  uint32_t r = uint32_t(__builtin_amdgcn_cvt_pk_fp8_f32(ca, cb, 0, false)) & 0xFFFFu;
+  if (a != a) r = (r & 0xFF00u) | 0x7Fu;
+  if (b != b) r = (r & 0x00FFu) | 0x7F00u;
+  return r;
+}
+
 // Eight BF16 values (one 16-byte load) -> eight E4M3FN codes of x / scale
 // (IEEE float32 division; scale 0 gives code 0), little-endian in 8 bytes.
 __device__ __forceinline__ u32x2 fp8_encode8(u32x4 v, float scale) {
+  if (scale == 0.0f) return u32x2{0u, 0u};
   uint32_t lo = 0, hi = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const uint32_t w = v[i];
-    const uint32_t c0 = scale == 0.0f ? 0u : e4m3_from_f32(bf16_lo(w) / scale);
-    const uint32_t c1 = scale == 0.0f ? 0u : e4m3_from_f32(bf16_hi(w) / scale);
-    const uint32_t pair = c0 | (c1 << 8);
+    const uint32_t pair = e4m3x2_from_f32(bf16_lo(w) / scale, bf16_hi(w) / scale);
     if (i < 2) lo |= pair << (16 * i);
     else hi |= pair << (16 * (i - 2));
   }
@@ -118,14 +130,27 @@ __device__ __forceinline__ u32x2 nvfp4_encode16(u32x4 v0, u32x4 v1, uint32_t& sc
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) amax = fmaxf(amax, __builtin_fabsf(x[i]));
-  scale_code = e4m3_from_f32(amax / 6.0f);
+  scale_code = e4m3x2_from_f32(amax / 6.0f, 0.0f) & 0xFFu;
   const float S = e4m3_to_f32(scale_code);
   uint32_t w0 = 0, w1 = 0;
   if (S != 0.0f) {
+    // E2M1(x / S) without the division: every threshold t of e2m1_from_f32
+    // times S is exact (t has at most 3 significant bits, S at most 4), and a
+    // BF16 x (8 significant bits) that differs from t * S differs by far more
+    // than half an fp32 ulp of the quotient, so x / S rounds to t exactly when
+    // x == t * S: comparing |x| with t * S takes the same decision.
+    const float t0 = 0.25f * S, t1 = 0.75f * S, t2 = 1.25f * S, t3 = 1.75f * S;
+    const float t4 = 2.5f * S, t5 = 3.5f * S, t6 = 5.0f * S;
+    auto code = [&](float v) -> uint32_t {
+      const float a = __builtin_fabsf(v);
+      const uint32_t c = (a <= t0) ? 0u : (a < t1) ? 1u : (a <= t2) ? 2u : (a < t3) ? 3u
+                       : (a <= t4) ? 4u : (a < t5) ? 5u : (a <= t6) ? 6u : 7u;
+      return ((__float_as_uint(v) >> 28) & 0x8u) | c;
+    };
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w0 |= e2m1_from_f32(x[i] / S) << (4 * i);
+    for (int i = 0; i < 8; ++i) w0 |= code(x[i]) << (4 * i);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w1 |= e2m1_from_f32(x[8 + i] / S) << (4 * i);
+    for (int i = 0; i < 8; ++i) w1 |= code(x[8 + i]) << (4 * i);
   }
   return u32x2{w0, w1};
 }

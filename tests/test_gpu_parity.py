@@ -75,6 +75,34 @@ def test_fp8_encoder_exhaustive_over_bf16(scale):
     assert np.array_equal(vd.cpu().numpy(), vc)
 
 
+def test_nvfp4_encoder_over_all_bf16():
+    """Every BF16 pattern but NaN (infinities and subnormals included),
+    shuffled into groups of 16, through the NVFP4 cache write, K and V in
+    different groupings. A NaN in a group is outside the format's contract
+    (the oracle's group maximum becomes NaN)."""
+    rng = np.random.default_rng(11)
+    allbits = np.arange(65536, dtype=np.uint32)
+    nan = ((allbits & 0x7F80) == 0x7F80) & ((allbits & 0x7F) != 0)
+    keep = allbits[~nan]
+    pad = rng.choice(keep, 65536 - keep.size)            # back to whole 256-value rows
+    bits = rng.permutation(np.concatenate([keep, pad])).astype(np.uint16)
+    D, Hkv, bs = 256, 1, 16
+    T = bits.size // D
+    key = bits.reshape(T, Hkv, D)
+    val = rng.permutation(bits).reshape(T, Hkv, D)
+    slots = rng.permutation(T).astype(np.int32)
+    geom = oracle.CacheGeometry("nvfp4", (T + bs - 1) // bs, bs, Hkv, D)
+    kc, vc = oracle.new_cache(geom, 0xAB), oracle.new_cache(geom, 0xAB)
+    oracle.reshape_and_cache(geom, key, val, kc, vc, slots)
+    kd = torch.full((kc.size,), 0xAB, dtype=torch.uint8, device=dev())
+    vd = kd.clone()
+    pkd.reshape_and_cache_nvfp4(u16_to_dev(key), u16_to_dev(val), kd, vd, i32_to_dev(slots), Hkv, D,
+                                bs)
+    torch.cuda.synchronize()
+    assert np.array_equal(kd.cpu().numpy(), kc)
+    assert np.array_equal(vd.cpu().numpy(), vc)
+
+
 def test_nvfp4_encoder_ties_and_ranges():
     """Groups at exact E2M1 ties, saturating scales and a wide magnitude range."""
     rng = np.random.default_rng(5)
