@@ -6,7 +6,8 @@
 // its slot names; E2M1 values with one E4M3 scale per 16; one workgroup per
 // token) and bf16_absmax (max |x| folded into an f32 with an atomic max).
 //
-// One workgroup of 256 lanes per token. A lane moves 16 bytes of BF16 source
+// One workgroup per token (256 lanes, or the whole waves a short row needs).
+// A lane moves 16 bytes of BF16 source
 // (8 elements) per step; the FP8 path writes 8 code bytes per step and the
 // NVFP4 path handles a whole 16-element group (two 16-byte source loads, 8
 // code bytes and one scale byte) per step.
@@ -70,24 +71,49 @@ template <int FMT>
 __global__ __launch_bounds__(256) void reshape_and_cache_kernel(WriteArgs a) {
   const uint32_t t = blockIdx.x;
   const int32_t slot = a.slots[t];
-  if constexpr (FMT == kBf16) {
-    // rows of up to 256 x 16 bytes: the source loads go out together with the
-    // slot load instead of waiting for it
-    const uint32_t row = a.num_kv_heads * a.head_dim;
-    if (row <= 256 * 8) {
-      const uint32_t c = threadIdx.x;
-      u32x4 kv = {0u, 0u, 0u, 0u}, vv = {0u, 0u, 0u, 0u};
-      if (c < row / 8) {
-        kv = *reinterpret_cast<const u32x4*>(a.key + uint64_t(t) * a.key_stride + c * 8);
-        vv = *reinterpret_cast<const u32x4*>(a.value + uint64_t(t) * a.value_stride + c * 8);
+  // Rows that one pass of the workgroup covers (8 elements a lane, 16 for an
+  // NVFP4 group): the K and V source loads go out together with the slot load,
+  // instead of the slot, then K, then V (the compiler cannot move V's loads
+  // above K's stores: the pointers may alias).
+  constexpr uint32_t PER = FMT == kNvfp4 ? 16 : 8;
+  const uint32_t row = a.num_kv_heads * a.head_dim;
+  if (row <= 256 * PER) {
+    const uint32_t c = threadIdx.x;
+    const bool act = c < row / PER;
+    u32x4 k0 = {0u, 0u, 0u, 0u}, v0 = k0, k1 = k0, v1 = k0;
+    if (act) {
+      const uint16_t* ks = a.key + uint64_t(t) * a.key_stride + c * PER;
+      const uint16_t* vs = a.value + uint64_t(t) * a.value_stride + c * PER;
+      k0 = *reinterpret_cast<const u32x4*>(ks);
+      v0 = *reinterpret_cast<const u32x4*>(vs);
+      if constexpr (FMT == kNvfp4) {
+        k1 = *reinterpret_cast<const u32x4*>(ks + 8);
+        v1 = *reinterpret_cast<const u32x4*>(vs + 8);
       }
-      if (slot < 0 || c >= row / 8) return;
-      const uint64_t dst = (uint64_t(uint32_t(slot) / a.block_size) * a.block_size +
-                            uint32_t(slot) % a.block_size) * row + c * 8;
-      *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.k_cache) + dst) = kv;
-      *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(a.v_cache) + dst) = vv;
-      return;
     }
+    if (slot < 0 || !act) return;
+    const uint32_t off = uint32_t(slot) % a.block_size;
+    const uint64_t page_base = uint64_t(uint32_t(slot) / a.block_size) * a.page_bytes;
+    if constexpr (FMT == kBf16) {
+      const uint64_t at = page_base + (uint64_t(off) * row + c * 8) * 2;
+      *reinterpret_cast<u32x4*>(a.k_cache + at) = k0;
+      *reinterpret_cast<u32x4*>(a.v_cache + at) = v0;
+    } else if constexpr (FMT == kFp8) {
+      const uint64_t at = page_base + uint64_t(off) * row + c * 8;
+      *reinterpret_cast<u32x2*>(a.k_cache + at) = fp8_encode8(k0, a.k_scale);
+      *reinterpret_cast<u32x2*>(a.v_cache + at) = fp8_encode8(v0, a.v_scale);
+    } else {
+      const uint64_t at = page_base + uint64_t(off) * (row / 2) + c * 8;
+      const uint64_t sat = page_base + a.data_section + uint64_t(off) * (row / 16) + c;
+      uint32_t ks_code, vs_code;
+      const u32x2 kc = nvfp4_encode16(k0, k1, ks_code);
+      const u32x2 vc = nvfp4_encode16(v0, v1, vs_code);
+      *reinterpret_cast<u32x2*>(a.k_cache + at) = kc;
+      *reinterpret_cast<u32x2*>(a.v_cache + at) = vc;
+      a.k_cache[sat] = uint8_t(ks_code);
+      a.v_cache[sat] = uint8_t(vs_code);
+    }
+    return;
   }
   if (slot < 0) return;
   const uint32_t page = uint32_t(slot) / a.block_size;
@@ -136,9 +162,15 @@ static int launch_status() {
   return e == hipSuccess ? kOk : kLaunch;
 }
 
+// One workgroup per token: 256 lanes, or for a row that one pass covers,
+// just the whole waves that row needs (an NVFP4 row of 1024 values is 64
+// groups: one wave), so no lane idles and more tokens are resident per CU.
 template <int FMT>
 static int launch_write(const WriteArgs& a, uint32_t num_tokens, hipStream_t stream) {
-  hipLaunchKernelGGL(reshape_and_cache_kernel<FMT>, dim3(num_tokens), dim3(256), 0, stream, a);
+  constexpr uint32_t per = FMT == kNvfp4 ? 16 : 8;
+  const uint32_t units = a.num_kv_heads * a.head_dim / per;
+  const uint32_t nt = units <= 256 ? (units + 63) / 64 * 64 : 256;
+  hipLaunchKernelGGL(reshape_and_cache_kernel<FMT>, dim3(num_tokens), dim3(nt), 0, stream, a);
   return launch_status();
 }
 
