@@ -624,6 +624,33 @@ def counter_run(name, calls=20):
                       "kv_bytes_per_call": attended_tokens(w) * kv_bytes_per_token(w)}))
 
 
+def trace_run(name, replays=6):
+    """Only the graph-replayed decode step (split-K with append + combine),
+    one graph of whole layer cycles replayed `replays` times after one
+    untimed replay (for a rocprofv3 kernel trace: start, end and the gap
+    between the two launches of each step)."""
+    import torch
+    import workloads
+    w = workloads.make_workload(name)
+    lay = Layers(w)
+    NL = lay.num_layers
+    per_graph = NL * max(1, -(-STEPS_PER_GRAPH // NL))
+    for i in range(NL):
+        lay.step(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(per_graph):
+            lay.step(i % NL)
+    g.replay()
+    torch.cuda.synchronize()
+    for _ in range(replays):
+        g.replay()
+    torch.cuda.synchronize()
+    print(json.dumps({"trace_run": name, "steps_per_graph": per_graph, "replays": replays,
+                      "num_splits": lay.num_splits}))
+
+
 def traffic_record(name, tag):
     """HBM bytes per launch of the dominant kernel from the committed
     rocprofv3 counter summary (profiles/traffic_<tag>_<workload>.txt), used
@@ -717,6 +744,8 @@ def main():
                     help="only the --verify timings (for kernel statistics of that call)")
     ap.add_argument("--counter-run", action="store_true",
                     help="only run the split-K pass of --workload 20 times")
+    ap.add_argument("--trace-run", action="store_true",
+                    help="only replay graphs of the decode step of --workload (kernel trace)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -730,6 +759,9 @@ def main():
         return
     if args.counter_run:
         counter_run(args.workload)
+        return
+    if args.trace_run:
+        trace_run(args.workload)
         return
     if args.verify_only:
         out = {}

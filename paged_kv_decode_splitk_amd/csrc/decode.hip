@@ -27,6 +27,8 @@
 //  * O^T[dim][head] += V^T . P on v_mfma_f32_16x16x16_bf16, V^T read from
 //    LDS with transposed reads, P rounded to BF16 in registers. A quantized V
 //    tile is first dequantized into a BF16 copy in LDS.
+#include <atomic>
+
 #include "../../include/pkd.h"
 #include "device_common.hpp"
 #include "validate.hpp"
@@ -68,6 +70,8 @@ struct DecodeArgs {
   uint32_t row_lead;       // most start-up tiles counted ahead of each row (split-K only)
   uint32_t max_len;        // keys a sequence can hold (block-table width x block, or the
                            // contiguous tensors' length): longer seq_lens are clamped
+  uint32_t static_q;       // one sequence: Q units per row, unit u streams row u % R, tiles
+                           // u / R + Q k (0: the stream partition)
   uint16_t* out;           // non-split decode (num_splits 1): BF16 output, else null
   // append: each sequence's new token, written to position L - 1 by the
   // piece that ends the row, before that piece loads its last tile
@@ -228,6 +232,127 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
+// Accesses to the LDS the tile DMA writes (the ring, and the stage of a
+// quantized V tile beside it), as inline asm. With several waves' rings in
+// one workgroup the compiler cannot tell which LDS bytes a DMA load in flight
+// writes, and would wait for every one of them (the V tile's included) before
+// each such access; the waits on the DMA are explicit instead. Reads wait for
+// their own results in the same statement, so no consumer is scheduled before
+// the data is there; writes need no wait (a wave's LDS operations execute in
+// issue order).
+template <int N>
+__device__ __forceinline__ void lds_read_b128(u32x4 (&v)[N], const uint32_t (&ad)[N]) {
+  static_assert(N == 1 || N == 2 || N == 4 || N == 8, "read count");
+  if constexpr (N == 1) {
+    asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=&v"(v[0]) : "v"(ad[0]) : "memory");
+  } else if constexpr (N == 2) {
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_b128 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]) : "v"(ad[0]), "v"(ad[1]) : "memory");
+  } else if constexpr (N == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\tds_read_b128 %1, %9\n\tds_read_b128 %2, %10\n\t"
+        "ds_read_b128 %3, %11\n\tds_read_b128 %4, %12\n\tds_read_b128 %5, %13\n\t"
+        "ds_read_b128 %6, %14\n\tds_read_b128 %7, %15\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+          "=&v"(v[6]), "=&v"(v[7])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]),
+          "v"(ad[7])
+        : "memory");
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void lds_read_b64(u32x2 (&v)[N], const uint32_t (&ad)[N]) {
+  static_assert(N == 2 || N == 4 || N == 8, "read count");
+  if constexpr (N == 2) {
+    asm volatile("ds_read_b64 %0, %2\n\tds_read_b64 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(v[1]) : "v"(ad[0]), "v"(ad[1]) : "memory");
+  } else if constexpr (N == 4) {
+    asm volatile(
+        "ds_read_b64 %0, %4\n\tds_read_b64 %1, %5\n\tds_read_b64 %2, %6\n\t"
+        "ds_read_b64 %3, %7\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b64 %0, %8\n\tds_read_b64 %1, %9\n\tds_read_b64 %2, %10\n\t"
+        "ds_read_b64 %3, %11\n\tds_read_b64 %4, %12\n\tds_read_b64 %5, %13\n\t"
+        "ds_read_b64 %6, %14\n\tds_read_b64 %7, %15\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]),
+          "=&v"(v[6]), "=&v"(v[7])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(ad[4]), "v"(ad[5]), "v"(ad[6]),
+          "v"(ad[7])
+        : "memory");
+  }
+}
+
+// NVFP4 K: N chunks of 32 codes (16 bytes) and their two scale bytes (a
+// 16-bit read each).
+template <int N>
+__device__ __forceinline__ void lds_read_fp4_chunks(u32x4 (&v)[N], uint32_t (&sc)[N],
+                                                    const uint32_t (&ad)[N],
+                                                    const uint32_t (&sad)[N]) {
+  static_assert(N == 1 || N == 2, "read count");
+  if constexpr (N == 1) {
+    asm volatile("ds_read_b128 %0, %2\n\tds_read_u16 %1, %3\n\ts_waitcnt lgkmcnt(0)"
+                 : "=&v"(v[0]), "=&v"(sc[0]) : "v"(ad[0]), "v"(sad[0]) : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\tds_read_b128 %1, %5\n\tds_read_u16 %2, %6\n\t"
+        "ds_read_u16 %3, %7\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(sc[0]), "=&v"(sc[1])
+        : "v"(ad[0]), "v"(ad[1]), "v"(sad[0]), "v"(sad[1])
+        : "memory");
+  }
+}
+
+// NVFP4 V staging: N words of 8 codes and the scale byte of each.
+template <int N>
+__device__ __forceinline__ void lds_read_fp4_words(uint32_t (&w)[N], uint32_t (&sc)[N],
+                                                   const uint32_t (&ad)[N],
+                                                   const uint32_t (&sad)[N]) {
+  static_assert(N == 2 || N == 4 || N == 8, "read count");
+  if constexpr (N == 2) {
+    asm volatile(
+        "ds_read_b32 %0, %4\n\tds_read_b32 %1, %5\n\tds_read_u8 %2, %6\n\t"
+        "ds_read_u8 %3, %7\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(w[0]), "=&v"(w[1]), "=&v"(sc[0]), "=&v"(sc[1])
+        : "v"(ad[0]), "v"(ad[1]), "v"(sad[0]), "v"(sad[1])
+        : "memory");
+  } else if constexpr (N == 4) {
+    asm volatile(
+        "ds_read_b32 %0, %8\n\tds_read_b32 %1, %9\n\tds_read_b32 %2, %10\n\t"
+        "ds_read_b32 %3, %11\n\tds_read_u8 %4, %12\n\tds_read_u8 %5, %13\n\t"
+        "ds_read_u8 %6, %14\n\tds_read_u8 %7, %15\n\ts_waitcnt lgkmcnt(0)"
+        : "=&v"(w[0]), "=&v"(w[1]), "=&v"(w[2]), "=&v"(w[3]), "=&v"(sc[0]), "=&v"(sc[1]),
+          "=&v"(sc[2]), "=&v"(sc[3])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "v"(sad[0]), "v"(sad[1]),
+          "v"(sad[2]), "v"(sad[3])
+        : "memory");
+  } else {
+    lds_read_fp4_words<4>(*reinterpret_cast<uint32_t(*)[4]>(&w[0]),
+                          *reinterpret_cast<uint32_t(*)[4]>(&sc[0]),
+                          *reinterpret_cast<const uint32_t(*)[4]>(&ad[0]),
+                          *reinterpret_cast<const uint32_t(*)[4]>(&sad[0]));
+    lds_read_fp4_words<4>(*reinterpret_cast<uint32_t(*)[4]>(&w[4]),
+                          *reinterpret_cast<uint32_t(*)[4]>(&sc[4]),
+                          *reinterpret_cast<const uint32_t(*)[4]>(&ad[4]),
+                          *reinterpret_cast<const uint32_t(*)[4]>(&sad[4]));
+  }
+}
+
+__device__ __forceinline__ void lds_write_b128(uint32_t ad, u32x4 v) {
+  asm volatile("ds_write_b128 %0, %1" : : "v"(ad), "v"(v) : "memory");
+}
+
 // Balanced ("stream") partition of one launch's work. A row is a (sequence,
 // kv head, chunk of up to 16 q heads) triple; row (b, k) has n_b tiles, the
 // 16-key tiles overlapping the sequence's attended keys. The rows are laid end
@@ -342,31 +467,54 @@ __device__ __forceinline__ void stage_v(lds_u8* vt, lds_u8* stage, int lane, uin
                                         uint32_t lo, uint32_t khi) {
   using T = LdsTraits<FMT, D>;
   constexpr int NQ = 16 * T::BCPR / 64;          // BF16 chunks per lane
+  const uint32_t vta = uint32_t(uintptr_t(vt)), sta = uint32_t(uintptr_t(stage));
+  u32x4 h[NQ];
+  if constexpr (FMT == kFp8) {
+    // codes 8c .. 8c+7: half of raw chunk c/2
+    u32x2 w[NQ];
+    uint32_t ad[NQ];
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) {
+      const int q = k * 64 + lane;
+      const int row = q / T::BCPR, c = q % T::BCPR;
+      ad[k] = vta + row * T::RB + ((c >> 1) ^ T::swz(row)) * 16 + 8 * (c & 1);
+    }
+    lds_read_b64<NQ>(w, ad);
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) {
+      const uint32_t tok = tok0 + (k * 64 + lane) / T::BCPR;
+      h[k] = fp8x8_to_bf16x8(w[k][0], w[k][1]);
+      if (MASK && !(tok >= lo && tok < khi)) h[k] = u32x4{0u, 0u, 0u, 0u};
+    }
+  } else {
+    // codes 8c .. 8c+7: a quarter of raw chunk c/4; scale group c/2. E2M1
+    // codes are always finite, so only the scale can poison a row past the
+    // keys: a NaN scale code (0x7F / 0xFF) becomes 0, every row decodes to
+    // finite values, and the zero weight of a masked key removes it. No
+    // per-row test, so the LDS reads of all chunks issue together.
+    (void)tok0;
+    (void)lo;
+    (void)khi;
+    uint32_t w[NQ], sraw[NQ], ad[NQ], sad[NQ];
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) {
+      const int q = k * 64 + lane;
+      const int row = q / T::BCPR, c = q % T::BCPR;
+      ad[k] = vta + row * T::RB + ((c >> 2) ^ T::swz(row)) * 16 + 4 * (c & 3);
+      sad[k] = vta + T::TILE + row * T::SC_ROW + (c >> 1);
+    }
+    lds_read_fp4_words<NQ>(w, sraw, ad, sad);
+#pragma unroll
+    for (int k = 0; k < NQ; ++k) {
+      const uint32_t sb = (sraw[k] & 0x7Fu) == 0x7Fu ? 0u : sraw[k];
+      h[k] = fp4x8_to_f16x8(w[k], _Float16(__builtin_amdgcn_cvt_f32_fp8(sb, 0)));
+    }
+  }
 #pragma unroll
   for (int k = 0; k < NQ; ++k) {
     const int q = k * 64 + lane;
     const int row = q / T::BCPR, c = q % T::BCPR;
-    const uint32_t tok = tok0 + row;
-    const bool ok = tok >= lo && tok < khi;
-    u32x4 h;
-    if constexpr (FMT == kFp8) {
-      // codes 8c .. 8c+7: half of raw chunk c/2
-      const u32x2 w = *(lds_u32x2*)(vt + row * T::RB + ((c >> 1) ^ T::swz(row)) * 16 + 8 * (c & 1));
-      h = fp8x8_to_bf16x8(w[0], w[1]);
-      if (MASK && !ok) h = u32x4{0u, 0u, 0u, 0u};
-    } else {
-      // codes 8c .. 8c+7: a quarter of raw chunk c/4; scale group c/2. E2M1
-      // codes are always finite, so only the scale can poison a row past the
-      // keys: a NaN scale code (0x7F / 0xFF) becomes 0, every row decodes to
-      // finite values, and the zero weight of a masked key removes it. No
-      // per-row test, so the LDS reads of all chunks issue together.
-      (void)ok;
-      const uint32_t w = *(lds_u32*)(vt + row * T::RB + ((c >> 2) ^ T::swz(row)) * 16 + 4 * (c & 3));
-      const uint32_t sraw = *(lds_u8*)(vt + T::TILE + row * T::SC_ROW + (c >> 1));
-      const uint32_t sb = (sraw & 0x7Fu) == 0x7Fu ? 0u : sraw;
-      h = fp4x8_to_f16x8(w, _Float16(__builtin_amdgcn_cvt_f32_fp8(sb, 0)));
-    }
-    *(lds_u32x4*)(stage + row * T::BRB + (c ^ T::bswz(row)) * 16) = h;
+    lds_write_b128(sta + row * T::BRB + (c ^ T::bswz(row)) * 16, h[k]);
   }
 }
 
@@ -428,86 +576,116 @@ __device__ __forceinline__ constexpr int qk_dim(int c, int g) {
   return 32 * c + 8 * g;
 }
 
-// One row piece: tiles [tau0, tau1) of row (b, kh), partial state to `slot`.
-// The row's NC chunks of 16 query columns share every K/V tile: each K or V
-// read from LDS feeds NC MFMAs.
+// The state a wave leaves after streaming its tiles: O^T (unnormalized,
+// lane (g, n) holding dims 16 mt + 4 g .. +4 of column n), the reference max
+// m_run (log2 units, at most kLazyMax below the largest logit seen) and the
+// lane's part of the weight sum l_run.
+template <int FMT, int D, int DS, int NC>
+struct WaveState {
+  f32x4 acc[NC][D / DS / 16];
+  float m_run[NC], l_run[NC];
+};
+
+// One wave streams the key tiles first + k * step, k < count, of row (b, kh)
+// (tile t holds keys 16t .. 16t + 15; keys outside [lo, L) are masked), with
+// count the tiles below `tend`. The row's NC chunks of 16 query columns share
+// every K/V tile: each K or V read from LDS feeds NC MFMAs.
 // With DS = 2 the workgroup's two waves split the head dim: wave w loads and
 // accumulates dims [w D/2, (w+1) D/2) of K, V, q and o, and the two halves of
 // every tile's logits are added through LDS (`xg`, two buffers used in turn,
 // `xturn` counting the exchanges of the launch).
+// q and the first 64 block-table entries are requested before anything that
+// depends on the length, so that when `first` and `step` do not depend on it
+// (a single sequence, see splitk_stream) those loads share its round trip.
+// can_append: the length is within the block table, so the new token (if
+// any) is written to position L - 1 by the wave holding that tile, which
+// waits for its stores only right before it requests the tile.
 template <int FMT, int D, int DS, int NC, bool CONTIG>
-__device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D / DS, DS>& sh,
-                                          lds_u8* xg, uint32_t& xturn, uint32_t b, uint32_t kh,
-                                          uint32_t tau0, uint32_t tau1, uint32_t slot, bool last,
-                                          uint32_t L) {
+__device__ __forceinline__ void stream_tiles(const DecodeArgs& a, StreamLds<FMT, D / DS, DS>& sh,
+                                             lds_u8* xg, uint32_t& xturn, uint32_t b,
+                                             uint32_t kh, uint32_t first, uint32_t step,
+                                             uint32_t tend, uint32_t L, bool can_append,
+                                             WaveState<FMT, D, DS, NC>& st) {
   static_assert(DS == 1 || NC == 1, "a split head dim carries one column chunk");
   static_assert(!CONTIG || FMT != kNvfp4, "contiguous K/V: BF16 and FP8 rows only");
-  // The piece is the same for every lane; saying so keeps the tile loop, the
-  // block-table walk and the load descriptors in scalar registers (a
-  // descriptor the compiler cannot prove uniform costs a loop per load).
+  // The tile sequence is the same for every lane; saying so keeps the tile
+  // loop, the block-table walk and the load descriptors in scalar registers
+  // (a descriptor the compiler cannot prove uniform costs a loop per load).
   b = __builtin_amdgcn_readfirstlane(b);
   kh = __builtin_amdgcn_readfirstlane(kh);
-  tau0 = __builtin_amdgcn_readfirstlane(tau0);
-  tau1 = __builtin_amdgcn_readfirstlane(tau1);
-  slot = __builtin_amdgcn_readfirstlane(slot);
-  L = __builtin_amdgcn_readfirstlane(L);
+  first = __builtin_amdgcn_readfirstlane(first);
+  step = __builtin_amdgcn_readfirstlane(step);
   constexpr int DW = D / DS;                     // head dims of this wave
   using T = LdsTraits<FMT, DW, DS>;              // tile geometry of this wave's half rows
   using TF = LdsTraits<FMT, D>;                  // full rows (strides in the pools)
   constexpr int NBUF = T::NBUF;
-  if (slot >= a.num_splits) return;      // only if a sequence outgrows its block table
   const int lane = threadIdx.x & 63;
   const int w = DS > 1 ? int(threadIdx.x >> 6) : 0;
   const int g = lane >> 4;
   const int n = lane & 15;
   const uint32_t kvh = kh / a.head_chunks, hc = kh % a.head_chunks;
-
-  const uint32_t lo = (a.window > 0 && L > a.window) ? L - a.window : 0u;
   const uint32_t tpp = a.block_size / 16;
-  const uint32_t t0 = lo / 16 + tau0, t1 = lo / 16 + tau1;   // tiles of the sequence
-  const uint32_t pa = t0 / tpp, pb = (t1 + tpp - 1) / tpp;
+  const int32_t* bt = a.block_tables + uint64_t(b) * a.max_blocks;
 
-  // column n of chunk k: query token qi, q head qh (column_of), read from
-  // q + qoff; the keys [c_lo, c_hi) it attends: the row's range, or with
-  // causal the keys up to the token's position (the last q_window of them)
+  // block-table entries of the first 64 tiles (entry per tile; any entry of
+  // the row may be read, those past the length are never used)
+  int32_t bt_first = 0;
+  if constexpr (!CONTIG) {
+    const uint64_t t = uint64_t(first) + uint64_t(lane) * step;
+    if (t < uint64_t(a.max_blocks) * tpp) bt_first = bt[t / tpp];
+  }
+
+  // q as the B operand of the QK MFMAs: column n, dims qk_dim(c, g) .. +8
   bool head_ok[NC];
-  uint64_t qoff[NC];
-  uint32_t c_lo[NC], c_hi[NC];
+  uint32_t qi_of[NC];
+  u32x4 qf[NC][DW / 32];
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
     uint32_t qi, qh;
     head_ok[k] = column_of(a, kvh, (hc * NC + k) * 16 + n, qi, qh);
-    qoff[k] = uint64_t(b) * a.q_stride + uint64_t(qi) * a.q_tok_stride +
-              uint64_t(qh) * a.q_head_stride + w * DW;
-    c_lo[k] = lo;
-    c_hi[k] = L;
-    if (a.causal && head_ok[k]) {
-      const int p1 = int(L) - int(a.q_len) + int(qi) + 1;     // position + 1
-      c_hi[k] = p1 > 0 ? uint32_t(p1) : 0u;
-      c_lo[k] = (a.q_window > 0 && c_hi[k] > a.q_window) ? c_hi[k] - a.q_window : 0u;
-    }
-  }
-  const int32_t* bt = a.block_tables + uint64_t(b) * a.max_blocks;
-  // append: written now, waited for only when the row's last tile is requested
-  bool pend = !CONTIG && a.new_k != nullptr && last;
-  if constexpr (!CONTIG) {
-    if (pend) append_token<FMT, D, DS>(a, b, kvh, L, w, lane);
-  }
-
-  // q as the B operand of the QK MFMAs: column n, dims 32c + 8g .. +8;
-  // issued ahead of the tile loads, which only ever wait for later loads.
-  u32x4 qf[NC][DW / 32];
-  float qup[NC];               // NVFP4: logits of this column's dims are scaled by qup
-#pragma unroll
-  for (int k = 0; k < NC; ++k) {
-    qup[k] = 1.0f;
-    const uint16_t* qsrc = a.q + qoff[k];
+    qi_of[k] = qi;
+    const uint16_t* qsrc = a.q + uint64_t(b) * a.q_stride + uint64_t(qi) * a.q_tok_stride +
+                           uint64_t(qh) * a.q_head_stride + w * DW;
 #pragma unroll
     for (int c = 0; c < DW / 32; ++c) {
       u32x4 v = {0u, 0u, 0u, 0u};
       if (head_ok[k]) v = *reinterpret_cast<const u32x4*>(qsrc + qk_dim<FMT, DW>(c, g));
       qf[k][c] = v;
     }
+  }
+
+  L = __builtin_amdgcn_readfirstlane(L);
+  tend = __builtin_amdgcn_readfirstlane(tend);
+  const uint32_t count = tend > first ? (tend - first + step - 1) / step : 0u;
+  const uint32_t lo = (a.window > 0 && L > a.window) ? L - a.window : 0u;
+
+  // the keys [c_lo, c_hi) column n of chunk k attends: the row's range, or
+  // with causal the keys up to its token's position (the last q_window)
+  uint32_t c_lo[NC], c_hi[NC];
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    c_lo[k] = lo;
+    c_hi[k] = L;
+    if (a.causal && head_ok[k]) {
+      const int p1 = int(L) - int(a.q_len) + int(qi_of[k]) + 1;     // position + 1
+      c_hi[k] = p1 > 0 ? uint32_t(p1) : 0u;
+      c_lo[k] = (a.q_window > 0 && c_hi[k] > a.q_window) ? c_hi[k] - a.q_window : 0u;
+    }
+  }
+
+  // append: the wave whose tiles include the one holding position L - 1
+  const uint32_t t_last = L > 0 ? (L - 1) / 16 : 0u;
+  const uint32_t k_last = t_last >= first ? (t_last - first) / step : 0xFFFFFFFFu;
+  bool pend = !CONTIG && a.new_k != nullptr && can_append && L > 0 && t_last >= first &&
+              (t_last - first) % step == 0 && k_last < count;
+  if constexpr (!CONTIG) {
+    if (pend) append_token<FMT, D, DS>(a, b, kvh, L, w, lane);
+  }
+
+  float qup[NC];               // NVFP4: logits of this column's dims are scaled by qup
+#pragma unroll
+  for (int k = 0; k < NC; ++k) {
+    qup[k] = 1.0f;
     if constexpr (FMT == kNvfp4) {
       // q in FP16 for the FP16 MFMA: shifted down by 2^e so that the
       // column's largest |q| stays below 2^15 (exact for every BF16 value in range)
@@ -543,38 +721,40 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
   const int ld_row = lane / T::CPR;                  // + i * RPI
   const int ld_pos = lane % T::CPR;
 
-  f32x4 acc[NC][DW / 16];
 #pragma unroll
   for (int k = 0; k < NC; ++k)
 #pragma unroll
-    for (int mt = 0; mt < DW / 16; ++mt) acc[k][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int mt = 0; mt < DW / 16; ++mt) st.acc[k][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   // The reference max starts at a finite floor rather than -inf, so that a
   // column whose keys in this piece are all masked keeps weights exp2(-inf -
   // floor) = 0 and rescale factors 1 (never exp2(-inf + inf)).
-  float m_run[NC], l_run[NC];
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
-    m_run[k] = kMaxFloor;
-    l_run[k] = 0.0f;
+    st.m_run[k] = kMaxFloor;
+    st.l_run[k] = 0.0f;
   }
 
-  // Segments of up to 64 pages: the block-table entries of a segment sit in
-  // one VGPR (entry per lane); the DMA ring restarts at every segment.
-  // Contiguous K/V: one segment of 16-key tiles.
-  for (uint32_t cp = pa; cp < pb;) {
-    const uint32_t cpe = CONTIG ? pb : min(cp + 64, pb);
+  // Segments of up to 64 tiles: the block-table entries of a segment's tiles
+  // sit in one VGPR (entry per lane); the DMA ring restarts at every segment.
+  for (uint32_t k0 = 0; k0 < count; k0 += 64) {
+    const uint32_t kend = min(k0 + 64, count);
     int32_t bt_reg = 0;
-    if constexpr (!CONTIG) bt_reg = (cp + lane < cpe) ? bt[cp + lane] : 0;
-    const uint32_t ct0 = max(cp * tpp, t0);
-    const uint32_t ct1 = min(cpe * tpp, t1);
+    if constexpr (!CONTIG) {
+      if (k0 == 0) {
+        bt_reg = bt_first;
+      } else {
+        const uint64_t t = uint64_t(first) + uint64_t(k0 + lane) * step;
+        bt_reg = (k0 + lane < kend) ? bt[t / tpp] : 0;
+      }
+    }
 
-    // Tile t of kind kv (0 = K, 1 = V) into ring slot s. A tile past the
-    // segment's end gets a zero-length descriptor: zeros land in LDS and no
-    // memory is read. Lanes without a row to fetch use an offset past any
-    // page, which reads nothing either.
-    auto issue = [&](int s, int kv, uint32_t t) {
-      const bool live = t < ct1;
-      if (pend && live && t + 1 == t1) {
+    // Tile k of the sequence, kind kv (0 = K, 1 = V), into ring slot s. A
+    // tile past the segment's end gets a zero-length descriptor: zeros land
+    // in LDS and no memory is read. Lanes without a row to fetch use an
+    // offset past any page, which reads nothing either.
+    auto issue = [&](int s, int kv, uint32_t k) {
+      const bool live = k < kend;
+      if (pend && live && k == k_last) {
         // the tile with the appended token: its stores must have landed
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
         wait_vmcnt<0>();
@@ -586,21 +766,21 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
       if constexpr (CONTIG) {
         // keys 16t .. 16t + 15 of sequence b, kv head kvh: the descriptor
         // spans the tile's rows below L only
-        const uint64_t* st = kv ? a.v_strides : a.k_strides;
-        const uint32_t tok0 = t * 16;
+        const uint64_t* stv = kv ? a.v_strides : a.k_strides;
+        const uint32_t tok0 = (first + k * step) * 16;
         const uint32_t nv = live ? min(16u, L - tok0) : 0u;
-        rstride = uint32_t(st[1]);
+        rstride = uint32_t(stv[1]);
         rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            const_cast<uint8_t*>(pool + uint64_t(b) * st[0] + uint64_t(tok0) * st[1] +
-                                 uint64_t(kvh) * st[2]),
+            const_cast<uint8_t*>(pool + uint64_t(b) * stv[0] + uint64_t(live ? tok0 : 0u) * stv[1] +
+                                 uint64_t(kvh) * stv[2]),
             0, nv ? int((nv - 1) * rstride + TF::RB) : 0, 0x00020000);
       } else {
-        const uint32_t page = min(t / tpp, cpe - 1);
-        const uint32_t phys = uint32_t(__builtin_amdgcn_readlane(bt_reg, int(page - cp)));
+        const uint32_t kk = min(k, kend - 1);
+        const uint32_t phys = uint32_t(__builtin_amdgcn_readlane(bt_reg, int(kk - k0)));
         rsrc = __builtin_amdgcn_make_buffer_rsrc(
             const_cast<uint8_t*>(pool + uint64_t(phys) * a.page_bytes), 0,
             live ? int(a.page_bytes) : 0, 0x00020000);
-        off0 = (t % tpp) * 16;
+        off0 = ((first + kk * step) % tpp) * 16;
       }
       lds_u8* const dst = ring3 + s * T::SLOT + kv * T::KV;
 #pragma unroll
@@ -628,16 +808,16 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
 
 #pragma unroll
     for (int s = 0; s < NBUF; ++s) {
-      issue(s, 0, ct0 + s);
-      issue(s, 1, ct0 + s);
+      issue(s, 0, k0 + s);
+      issue(s, 1, k0 + s);
     }
 
-    for (uint32_t tb = ct0; tb < ct1; tb += NBUF) {
+    for (uint32_t kb = k0; kb < kend; kb += NBUF) {
 #pragma unroll
       for (int s = 0; s < NBUF; ++s) {
-        const uint32_t t = tb + s;               // t >= ct1: phantom tile, all keys masked
-        const uint32_t tok0 = t * 16;
-        const uint32_t khi = t < ct1 ? L : 0u;
+        const uint32_t k = kb + s;               // k >= kend: phantom tile, all keys masked
+        const uint32_t tok0 = (first + k * step) * 16;
+        const uint32_t khi = k < kend ? L : 0u;
         lds_u8* const kt = ring3 + s * T::SLOT;
         lds_u8* const vt = kt + T::KV;
 
@@ -647,26 +827,33 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
         __builtin_amdgcn_sched_barrier(0);
         f32x4 sc[NC];
 #pragma unroll
-        for (int k = 0; k < NC; ++k) sc[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < NC; ++j) sc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint32_t kta = uint32_t(uintptr_t(kt));
         if constexpr (FMT == kBf16) {
+          u32x4 kv[DW / 32];
+          uint32_t ka[DW / 32];
 #pragma unroll
-          for (int c = 0; c < DW / 32; ++c) {
-            const int chunk = (4 * c + g) ^ T::swz(n);
-            const u32x4 kv = *(lds_u32x4*)(kt + n * T::RB + chunk * 16);
+          for (int c = 0; c < DW / 32; ++c) ka[c] = kta + n * T::RB + (((4 * c + g) ^ T::swz(n)) * 16);
+          lds_read_b128<DW / 32>(kv, ka);
 #pragma unroll
-            for (int k = 0; k < NC; ++k) sc[k] = mfma_qk<FMT>(kv, qf[k][c], sc[k]);
-          }
+          for (int c = 0; c < DW / 32; ++c)
+#pragma unroll
+            for (int j = 0; j < NC; ++j) sc[j] = mfma_qk<FMT>(kv[c], qf[j][c], sc[j]);
         } else if constexpr (FMT == kFp8) {
           // lane group g takes whole 16-byte chunks 4h + g (16 codes): MFMA
           // 2h + u uses its half u (q is loaded in the same dim order, qk_dim)
+          u32x4 cw[DW / 64];
+          uint32_t ka[DW / 64];
+#pragma unroll
+          for (int h = 0; h < DW / 64; ++h) ka[h] = kta + n * T::RB + (((4 * h + g) ^ T::swz(n)) * 16);
+          lds_read_b128<DW / 64>(cw, ka);
 #pragma unroll
           for (int h = 0; h < DW / 64; ++h) {
-            const u32x4 cw = *(lds_u32x4*)(kt + n * T::RB + ((4 * h + g) ^ T::swz(n)) * 16);
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
-              const u32x4 kv = fp8x8_to_bf16x8(cw[2 * u], cw[2 * u + 1]);
+              const u32x4 kv = fp8x8_to_bf16x8(cw[h][2 * u], cw[h][2 * u + 1]);
 #pragma unroll
-              for (int k = 0; k < NC; ++k) sc[k] = mfma_qk<FMT>(kv, qf[k][2 * h + u], sc[k]);
+              for (int j = 0; j < NC; ++j) sc[j] = mfma_qk<FMT>(kv, qf[j][2 * h + u], sc[j]);
             }
           }
         } else {
@@ -675,18 +862,24 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
             // dims of two scale groups): MFMA 4h + u uses its word u, so a
             // lane makes one 16-byte and one 2-byte read per chunk (q is
             // loaded in the same dim order, qk_dim)
+            u32x4 cw[DW / 128];
+            uint32_t s2[DW / 128], ka[DW / 128], sa[DW / 128];
 #pragma unroll
             for (int h = 0; h < DW / 128; ++h) {
               const int j = 4 * h + g;
-              const u32x4 cw = *(lds_u32x4*)(kt + n * T::RB + (j ^ T::swz(n)) * 16);
-              const uint32_t s2 = *(lds_u16*)(kt + T::TILE + n * T::SC_ROW + 2 * j);
-              const _Float16 S0 = _Float16(__builtin_amdgcn_cvt_f32_fp8(s2, 0));
-              const _Float16 S1 = _Float16(__builtin_amdgcn_cvt_f32_fp8(s2, 1));
+              ka[h] = kta + n * T::RB + ((j ^ T::swz(n)) * 16);
+              sa[h] = kta + T::TILE + n * T::SC_ROW + 2 * j;
+            }
+            lds_read_fp4_chunks<DW / 128>(cw, s2, ka, sa);
+#pragma unroll
+            for (int h = 0; h < DW / 128; ++h) {
+              const _Float16 S0 = _Float16(__builtin_amdgcn_cvt_f32_fp8(s2[h], 0));
+              const _Float16 S1 = _Float16(__builtin_amdgcn_cvt_f32_fp8(s2[h], 1));
 #pragma unroll
               for (int u = 0; u < 4; ++u) {
-                const u32x4 kv = fp4x8_to_f16x8(cw[u], u < 2 ? S0 : S1);
+                const u32x4 kv = fp4x8_to_f16x8(cw[h][u], u < 2 ? S0 : S1);
 #pragma unroll
-                for (int k = 0; k < NC; ++k) sc[k] = mfma_qk<FMT>(kv, qf[k][4 * h + u], sc[k]);
+                for (int q = 0; q < NC; ++q) sc[q] = mfma_qk<FMT>(kv, qf[q][4 * h + u], sc[q]);
               }
             }
           } else {
@@ -699,16 +892,16 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
 #pragma unroll
             for (int c = 0; c < DW / 32; ++c) {
               const int chunk = c ^ T::swz(n);
-              const uint32_t w = *(lds_u32*)(kt + n * T::RB + chunk * 16 + 4 * g);
+              const uint32_t wd = *(lds_u32*)(kt + n * T::RB + chunk * 16 + 4 * g);
               const float S = (c & 1) ? __builtin_amdgcn_cvt_f32_fp8(sw[c / 2], 2)
                                       : __builtin_amdgcn_cvt_f32_fp8(sw[c / 2], 0);
-              const u32x4 kv = fp4x8_to_f16x8(w, _Float16(S));
+              const u32x4 kv = fp4x8_to_f16x8(wd, _Float16(S));
 #pragma unroll
-              for (int k = 0; k < NC; ++k) sc[k] = mfma_qk<FMT>(kv, qf[k][c], sc[k]);
+              for (int q = 0; q < NC; ++q) sc[q] = mfma_qk<FMT>(kv, qf[q][c], sc[q]);
             }
           }
 #pragma unroll
-          for (int k = 0; k < NC; ++k) sc[k] *= qup[k];
+          for (int j = 0; j < NC; ++j) sc[j] *= qup[j];
         }
         if constexpr (DS > 1) {
           // the other parts of the head dim: partial logits through LDS,
@@ -726,7 +919,7 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
           sc[0] = sum;
         }
         __builtin_amdgcn_sched_barrier(0);
-        issue(s, 0, t + NBUF);
+        issue(s, 0, k + NBUF);
 
         // ---- online softmax (lane: column n, tokens tok0 + 4g + j)
         // The reference m_run follows the running max lazily: it moves only
@@ -738,34 +931,34 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
         float alpha[NC];
         u32x2 pf[NC];
 #pragma unroll
-        for (int k = 0; k < NC; ++k) {
-          const uint32_t c_khi = t < ct1 ? c_hi[k] : 0u;
+        for (int j = 0; j < NC; ++j) {
+          const uint32_t c_khi = k < kend ? c_hi[j] : 0u;
           float sv[4];
           float mx = -__builtin_inff();
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t tok = tok0 + 4 * g + j;
-            sv[j] = (tok >= c_lo[k] && tok < c_khi) ? sc[k][j] * a.logit_scale : -__builtin_inff();
-            mx = fmaxf(mx, sv[j]);
+          for (int r = 0; r < 4; ++r) {
+            const uint32_t tok = tok0 + 4 * g + r;
+            sv[r] = (tok >= c_lo[j] && tok < c_khi) ? sc[j][r] * a.logit_scale : -__builtin_inff();
+            mx = fmaxf(mx, sv[r]);
           }
           mx = max_over_rows(mx);
-          rescale[k] = __builtin_amdgcn_ballot_w64(mx > m_run[k] + kLazyMax) != 0;
-          alpha[k] = 1.0f;
-          if (rescale[k]) {
-            const float m_new = fmaxf(m_run[k], mx);
-            alpha[k] = __builtin_amdgcn_exp2f(m_run[k] - m_new);
-            m_run[k] = m_new;
+          rescale[j] = __builtin_amdgcn_ballot_w64(mx > st.m_run[j] + kLazyMax) != 0;
+          alpha[j] = 1.0f;
+          if (rescale[j]) {
+            const float m_new = fmaxf(st.m_run[j], mx);
+            alpha[j] = __builtin_amdgcn_exp2f(st.m_run[j] - m_new);
+            st.m_run[j] = m_new;
           }
           uint32_t pbits[4];
           float psum = 0.0f;
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const float p = __builtin_amdgcn_exp2f(sv[j] - m_run[k]);
-            pbits[j] = p_bits<FMT>(p);
-            psum += p_value<FMT>(pbits[j]);
+          for (int r = 0; r < 4; ++r) {
+            const float p = __builtin_amdgcn_exp2f(sv[r] - st.m_run[j]);
+            pbits[r] = p_bits<FMT>(p);
+            psum += p_value<FMT>(pbits[r]);
           }
-          l_run[k] = l_run[k] * alpha[k] + psum;
-          pf[k] = u32x2{pbits[0] | (pbits[1] << 16), pbits[2] | (pbits[3] << 16)};
+          st.l_run[j] = st.l_run[j] * alpha[j] + psum;
+          pf[j] = u32x2{pbits[0] | (pbits[1] << 16), pbits[2] | (pbits[3] << 16)};
         }
 
         // ---- V tile as BF16 rows with masked tokens zeroed: in place for a
@@ -796,17 +989,17 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
             stage_v<FMT, DW, false>(vt, stage3, lane, tok0, lo, khi);
           wave_lds_fence();
           __builtin_amdgcn_sched_barrier(0);
-          issue(s, 1, t + NBUF);                   // the raw V tile is consumed
+          issue(s, 1, k + NBUF);                   // the raw V tile is consumed
         }
         // ---- O^T += V^T P: lane supplies V[4g + n/4][16mt + 4(n%4) .. +4]. The
         // transposed reads are issued as inline asm: the compiler would otherwise
         // wait for every pending LDS-DMA load before each of them. Four reads,
         // then their MFMAs, which run while the next reads are in flight.
 #pragma unroll
-        for (int k = 0; k < NC; ++k)
-          if (rescale[k]) {
+        for (int j = 0; j < NC; ++j)
+          if (rescale[j]) {
 #pragma unroll
-            for (int mt = 0; mt < DW / 16; ++mt) acc[k][mt] *= alpha[k];
+            for (int mt = 0; mt < DW / 16; ++mt) st.acc[j][mt] *= alpha[j];
           }
         {
           const int vtok = 4 * g + (n >> 2);
@@ -834,37 +1027,128 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
 #pragma unroll
             for (int u = 0; u < 4; ++u)
 #pragma unroll
-              for (int k = 0; k < NC; ++k)
-                acc[k][4 * q4 + u] = mfma_pv<FMT>(vv[u], pf[k], acc[k][4 * q4 + u]);
+              for (int j = 0; j < NC; ++j)
+                st.acc[j][4 * q4 + u] = mfma_pv<FMT>(vv[u], pf[j], st.acc[j][4 * q4 + u]);
           }
         }
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (FMT == kBf16) issue(s, 1, t + NBUF);
+        if constexpr (FMT == kBf16) issue(s, 1, k + NBUF);
       }
     }
     wait_vmcnt<0>();                               // the ring restarts with the next segment
     wave_lds_fence();
-    cp = cpe;
+  }
+}
+
+// No marker slot.
+constexpr uint32_t kNoSlot = 0xFFFFFFFFu;
+
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) f32x2 lds_f32x2;
+
+// The end of a piece. With WI > 1 the workgroup's WI waves streamed
+// interleaved tiles of the same piece; their states merge through LDS: each
+// wave puts its O^T into its own (drained) ring and its (m, l) per column
+// into `mlx`; then every wave takes M = max m_i and the weights exp2(m_i -
+// M) in wave order, and sums the O^T blocks 16 mt .. of its share of the
+// head dims in wave order (deterministic). The piece then writes o = O / l
+// (times the FP8 v scale), m = M ln 2 and l to workspace slot `slot` of its
+// query columns, or BF16 output when the call has no split (a.out), and an end
+// marker (l = -1) in slot `marker` when that is not kNoSlot.
+template <int FMT, int D, int DS, int NC, int WI>
+__device__ __forceinline__ void finish_piece(const DecodeArgs& a, StreamLds<FMT, D / DS, DS>* shs,
+                                             lds_f32x2* mlx, WaveState<FMT, D, DS, NC>& st,
+                                             uint32_t b, uint32_t kh, uint32_t slot,
+                                             uint32_t marker) {
+  constexpr int DW = D / DS;
+  constexpr int MT = DW / 16;                    // 16-dim blocks of a wave's share
+  static_assert(WI == 1 || DS == 1, "waves interleave tiles of whole rows only");
+  static_assert(MT % WI == 0, "the merged blocks split evenly over the waves");
+  constexpr int MW = MT / WI;                    // blocks each wave merges and writes
+  const int lane = threadIdx.x & 63;
+  const int wv = int(threadIdx.x >> 6);
+  const int w = DS > 1 ? wv : 0;                 // head-dim part
+  const int wi = WI > 1 ? wv : 0;                // interleaved wave
+  // the wave that writes the piece's (m, l) and end marker: the first of the
+  // waves sharing the piece (every wave when the waves stream independently)
+  const bool lead = (DS > 1 ? w : wi) == 0;
+  const int g = lane >> 4, n = lane & 15;
+  const uint32_t kvh = kh / a.head_chunks, hc = kh % a.head_chunks;
+
+  float M[NC], lsum[NC];
+  f32x4 o[NC][MW];
+  if constexpr (WI > 1) {
+    static_assert(sizeof(StreamLds<FMT, DW, DS>) >= size_t(NC) * MT * 64 * 16,
+                  "a wave's ring holds its O^T for the merge");
+    lds_f32x4* const mine = (lds_f32x4*)(lds_u8*)(shs[wi].ring);
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) mine[(k * MT + mt) * 64 + lane] = st.acc[k][mt];
+      const float lw = sum_over_rows(st.l_run[k]);
+      if (g == 0) mlx[(wi * NC + k) * 16 + n] = f32x2{st.m_run[k], lw};
+    }
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      f32x2 ml[WI];
+      M[k] = kMaxFloor;
+#pragma unroll
+      for (int i = 0; i < WI; ++i) {
+        ml[i] = mlx[(i * NC + k) * 16 + n];
+        M[k] = fmaxf(M[k], ml[i][0]);
+      }
+      float wgt[WI];
+      lsum[k] = 0.0f;
+#pragma unroll
+      for (int i = 0; i < WI; ++i) {
+        wgt[i] = __builtin_amdgcn_exp2f(ml[i][0] - M[k]);
+        lsum[k] += wgt[i] * ml[i][1];
+      }
+      // every wave's blocks come back from LDS, its own included: indexing
+      // the register array by the wave number would move it to scratch
+#pragma unroll
+      for (int u = 0; u < MW; ++u) {
+        const int mt = wi * MW + u;
+        f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < WI; ++i)
+          s += wgt[i] * ((lds_f32x4*)(lds_u8*)(shs[i].ring))[(k * MT + mt) * 64 + lane];
+        o[k][u] = s;
+      }
+    }
+    // the rings are refilled by the next piece only once every wave has read them
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  } else {
+    (void)shs;
+    (void)mlx;
+#pragma unroll
+    for (int k = 0; k < NC; ++k) {
+      M[k] = st.m_run[k];
+      lsum[k] = sum_over_rows(st.l_run[k]);
+#pragma unroll
+      for (int u = 0; u < MW; ++u) o[k][u] = st.acc[k][u];
+    }
   }
 
 #pragma unroll
   for (int k = 0; k < NC; ++k) {
-    const float l_tot = sum_over_rows(l_run[k]);
     // a column without keys (l = 0) writes zeros
-    const float inv = l_tot > 0.0f ? a.out_scale / l_tot : 0.0f;
-    if (!head_ok[k]) continue;
+    const float inv = lsum[k] > 0.0f ? a.out_scale / lsum[k] : 0.0f;
     uint32_t qi, qh;
-    column_of(a, kvh, (hc * NC + k) * 16 + n, qi, qh);
+    if (!column_of(a, kvh, (hc * NC + k) * 16 + n, qi, qh)) continue;
     if (a.out) {
       // non-split: the whole row in one piece, the normalized output
       // straight to BF16
       uint16_t* orow = a.out + uint64_t(b) * a.o_seq + uint64_t(qi) * a.o_tok +
                        uint64_t(qh) * a.o_head + w * DW;
 #pragma unroll
-      for (int mt = 0; mt < DW / 16; ++mt)
+      for (int u = 0; u < MW; ++u) {
+        const int mt = wi * MW + u;
         *reinterpret_cast<u32x2*>(orow + 16 * mt + 4 * g) =
-            u32x2{pack_bf16x2(acc[k][mt][0] * inv, acc[k][mt][1] * inv),
-                  pack_bf16x2(acc[k][mt][2] * inv, acc[k][mt][3] * inv)};
+            u32x2{pack_bf16x2(o[k][u][0] * inv, o[k][u][1] * inv),
+                  pack_bf16x2(o[k][u][2] * inv, o[k][u][3] * inv)};
+      }
       continue;
     }
     // workspace row of the column: [B][q_len][Hq] order
@@ -872,22 +1156,23 @@ __device__ __forceinline__ void run_piece(const DecodeArgs& a, StreamLds<FMT, D 
     float* const wbase = a.ws + qrow * a.num_splits * (D + 2);
     float* wrow = wbase + uint64_t(slot) * (D + 2);
 #pragma unroll
-    for (int mt = 0; mt < DW / 16; ++mt) {
-      f32x2 lo2 = {acc[k][mt][0] * inv, acc[k][mt][1] * inv};
-      f32x2 hi2 = {acc[k][mt][2] * inv, acc[k][mt][3] * inv};
+    for (int u = 0; u < MW; ++u) {
+      const int mt = wi * MW + u;
+      f32x2 lo2 = {o[k][u][0] * inv, o[k][u][1] * inv};
+      f32x2 hi2 = {o[k][u][2] * inv, o[k][u][3] * inv};
       *reinterpret_cast<f32x2*>(wrow + w * DW + mt * 16 + 4 * g) = lo2;
       *reinterpret_cast<f32x2*>(wrow + w * DW + mt * 16 + 4 * g + 2) = hi2;
     }
-    if (g == 0 && w == 0) {
-      wrow[D] = m_run[k] * kLn2;
-      wrow[D + 1] = l_tot;
-    }
-    // the row ends in this piece: an end marker (l = -1) in the next slot
-    // tells the combine to ignore that slot and all later ones
-    if (last && g == 0 && w == 0 && slot + 1 < a.num_splits) {
-      float* e = wbase + uint64_t(slot + 1) * (D + 2);
-      e[D] = -__builtin_inff();
-      e[D + 1] = -1.0f;
+    if (g == 0 && lead) {
+      wrow[D] = M[k] * kLn2;
+      wrow[D + 1] = lsum[k];
+      // the row ends in this piece: an end marker (l = -1) tells the combine
+      // to ignore that slot and all later ones
+      if (marker != kNoSlot) {
+        float* e = wbase + uint64_t(marker) * (D + 2);
+        e[D] = -__builtin_inff();
+        e[D + 1] = -1.0f;
+      }
     }
   }
 }
@@ -1187,22 +1472,27 @@ constexpr int kWavesPerSimd =
 template <int FMT, int D>
 constexpr int kMaxChunks = (FMT == kBf16 && D <= 128) ? 2 : 1;
 
-// The pieces of one workgroup under the stream partition (rows of R per
-// sequence), in order: piece(b, kh, tau0, tau1, slot, last, L) for each; with
-// num_splits 1 the workgroup takes row blockIdx.x whole (and writes zeros
-// for a sequence without keys).
+// The pieces of partition unit `unit` of the P units of a launch (a
+// workgroup, or one of its waves when they stream independently) under the
+// stream partition (rows of R per sequence), in order: piece(b, kh, tau0,
+// tau1, slot, last, L, can_append) for each (can_append: the sequence's length
+// is within its block-table row, so its new token has a position to go to);
+// with num_splits 1 the unit takes row `unit` whole, and for a sequence
+// without keys writes zeros if `zero_lead` (the unit's lead wave).
 template <int D, int NC, int WQ, typename Piece>
-__device__ __forceinline__ void for_each_piece(const DecodeArgs& a, Piece&& piece) {
+__device__ __forceinline__ void for_each_piece(const DecodeArgs& a, uint32_t unit, uint32_t P,
+                                               bool zero_lead, Piece&& piece) {
   const uint32_t R = a.num_kv_heads * a.head_chunks;          // rows per sequence
-  const uint32_t P = gridDim.x;
   const bool whole = a.num_splits == 1;                       // one wave per row
   // With at most 64 sequences, one length per lane, loaded once: the tile
   // counts, their prefix sums and every row lookup come from these registers.
   const bool cached = a.num_seqs <= 64;
   uint32_t L_l = 0, n_l = 0, T = 0, live = 0, incl = 0, live_le = 0;
+  uint64_t over = 0;                        // sequences longer than their block-table row
   if (cached && !whole) {
     const uint32_t lane = threadIdx.x & 63;
     const int32_t Ls = lane < a.num_seqs ? a.seq_lens[lane] : 0;
+    over = __builtin_amdgcn_ballot_w64(Ls > 0 && uint32_t(Ls) > a.max_len);
     L_l = seq_len(a, Ls);
     n_l = row_tiles(L_l, a.window);
     incl = wave_scan(n_l * R);
@@ -1223,7 +1513,7 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, Piece&& piec
   // lead*live), so no wave gets more positions than c, unless c is long
   // enough that one more tile costs little. When c is the least chunk
   // instead, waves are idle anyway and the rows stay aligned.
-  uint32_t c = 1, lead = 0, pos = blockIdx.x, end = blockIdx.x + 1;
+  uint32_t c = 1, lead = 0, pos = unit, end = unit + 1;
   if (!whole) {
     const uint32_t c0 = (T + P - 1) / P;
     c = max(c0, a.chunk_min);
@@ -1239,22 +1529,25 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, Piece&& piec
     }
     incl += lead * R * live_le;                  // inclusive prefix of the laid-out spans
     const uint32_t flat = T + lead * live;
-    pos = uint32_t(min(uint64_t(blockIdx.x) * c, uint64_t(flat)));
+    pos = uint32_t(min(uint64_t(unit) * c, uint64_t(flat)));
     end = uint32_t(min(uint64_t(pos) + c, uint64_t(flat)));
   }
   while (pos < end) {
     // the row holding flat position pos: sequence b, row kh, its n tiles
     // from flat position rs (behind `lead` start-up positions)
     uint32_t b, kh, n, rs, L;
+    bool fits = true;
     if (whole) {
-      b = blockIdx.x / R;
-      kh = blockIdx.x % R;
+      b = unit / R;
+      kh = unit % R;
+      if (b >= a.num_seqs) break;                  // a unit past the rows of the launch
       const int32_t Ls = a.seq_lens[b];
+      fits = !(Ls > 0 && uint32_t(Ls) > a.max_len);
       L = seq_len(a, Ls);
       n = row_tiles(L, a.window);
       rs = pos;
       if (n == 0) {
-        if (a.out && (WQ > 1 || threadIdx.x < 64)) zero_row<D, NC, WQ>(a, b, kh);
+        if (a.out && zero_lead) zero_row<D, NC, WQ>(a, b, kh);
         break;
       }
     } else if (cached) {
@@ -1265,6 +1558,7 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, Piece&& piec
       const uint32_t span = n + lead;
       const uint32_t excl = uint32_t(__builtin_amdgcn_readlane(int(incl), l)) - span * R;
       L = uint32_t(__builtin_amdgcn_readlane(int(L_l), l));
+      fits = ((over >> l) & 1) == 0;
       b = uint32_t(l);
       kh = (pos - excl) / span;
       rs = excl + kh * span + lead;
@@ -1276,6 +1570,7 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, Piece&& piec
       n = r.n - lead;
       rs = r.start + lead;
       const int32_t Ls = a.seq_lens[b];
+      fits = !(Ls > 0 && uint32_t(Ls) > a.max_len);
       L = seq_len(a, Ls);
     }
     if (n == 0 || kh >= R) break;                  // as above: never taken
@@ -1283,25 +1578,84 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, Piece&& piec
     const uint32_t f1 = whole ? rs + n : min(rs + n, end);
     if (f1 > f0) {
       // slot: waves from the one holding the row's first tile
-      piece(b, kh, f0 - rs, f1 - rs, whole ? 0u : f0 / c - rs / c, whole || rs + n <= end, L);
+      piece(b, kh, f0 - rs, f1 - rs, whole ? 0u : f0 / c - rs / c, whole || rs + n <= end, L,
+            fits);
     }
     if (whole) break;
     pos = max(f1, min(rs, end));
   }
 }
 
-template <int FMT, int D, int NC, bool CONTIG>
-__global__ __launch_bounds__((64 * kDSplit<FMT, D>), (kWavesPerSimd<FMT, D>)) void splitk_stream(
+// Waves of a workgroup that share a piece by interleaving its tiles (wave i
+// takes tiles i, i + WI, ...) and merge their states in LDS before one
+// workspace write: four for BF16 and FP8 rows of one column chunk up to
+// head_dim 256 (one wave per SIMD of a CU), so a launch writes a quarter of the
+// partials and the combine reads a quarter of the slots.
+// Waves that interleave the tiles of one piece where the rows allow it: one
+// per SIMD of a CU for BF16 and FP8 rows up to head_dim 256 of one column
+// chunk (a wave's ring then holds its O^T for the merge).
+template <int FMT, int D, int NC>
+constexpr int kMergeWaves = (kDSplit<FMT, D> == 1 && FMT != kNvfp4 && NC == 1) ? 4 : 1;
+
+// Waves of a stream workgroup: WI interleaving waves, or the DS waves of a
+// split head dim, or one.
+template <int FMT, int D, int WI>
+constexpr int kGroupWaves = kDSplit<FMT, D> > 1 ? kDSplit<FMT, D> : WI;
+
+// The stream kernel, one partition unit per workgroup. WI = 1: a unit is one
+// wave (two sharing a split head dim), which may cross rows (split-K passes
+// over a batch). WI > 1: the WI waves of a workgroup take the tiles of one
+// piece in turn (wave i tiles i, i + WI, ...) and merge their states in LDS
+// before one write (a single sequence, one piece per workgroup; or a whole
+// row per workgroup with no split), so the launch writes a WI-th of the
+// partials.
+template <int FMT, int D, int NC, bool CONTIG, int WI>
+__global__ __launch_bounds__((64 * kGroupWaves<FMT, D, WI>), (kWavesPerSimd<FMT, D>)) void splitk_stream(
     DecodeArgs a) {
   constexpr int DS = kDSplit<FMT, D>;
-  __shared__ StreamLds<FMT, D / DS, DS> sh[DS];
+  constexpr int GW = kGroupWaves<FMT, D, WI>;
+  static_assert(WI == 1 || WI == kMergeWaves<FMT, D, NC>, "interleaved waves merge in LDS");
+  __shared__ StreamLds<FMT, D / DS, DS> sh[GW];
   __shared__ __attribute__((aligned(16))) uint8_t xg[DS > 1 ? 2 * DS * 64 * 16 : 16];
-  StreamLds<FMT, D / DS, DS>& mine = sh[DS > 1 ? threadIdx.x >> 6 : 0];
+  __shared__ f32x2 mlx[WI > 1 ? WI * NC * 16 : 1];
+  const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  StreamLds<FMT, D / DS, DS>& mine = sh[GW > 1 ? wv : 0];
+  const uint32_t wi = WI > 1 ? wv : 0;
+  const uint32_t unit = blockIdx.x, P = gridDim.x;
   lds_u8* const xg3 = (lds_u8*)xg;
+  lds_f32x2* const mlx3 = (lds_f32x2*)mlx;
   uint32_t xturn = 0;
-  for_each_piece<D, NC, 1>(a, [&](uint32_t b, uint32_t kh, uint32_t tau0, uint32_t tau1,
-                                  uint32_t slot, bool last, uint32_t L) {
-    run_piece<FMT, D, DS, NC, CONTIG>(a, mine, xg3, xturn, b, kh, tau0, tau1, slot, last, L);
+  if (a.static_q) {
+    // One sequence, no window: unit u takes row u % R and, as j = u / R of
+    // the row's Q units, its tiles j + Q m (wave i of an interleaving group
+    // the m = i mod WI). Which tiles a wave streams does not depend on the
+    // length, so its q and block-table entries are requested in the same
+    // round trip as the length.
+    const uint32_t R = a.num_kv_heads * a.head_chunks;
+    const uint32_t Q = a.static_q;                 // <= num_splits
+    const uint32_t kh = unit % R, j = unit / R;
+    if (j >= Q) return;                            // a unit past the R * Q of the launch
+    const int32_t Ls = a.seq_lens[0];
+    const uint32_t L = seq_len(a, Ls);
+    WaveState<FMT, D, DS, NC> st;
+    stream_tiles<FMT, D, DS, NC, CONTIG>(a, mine, xg3, xturn, 0, kh, j + Q * wi, Q * WI,
+                                         (L + 15) / 16, L, !(Ls > 0 && uint32_t(Ls) > a.max_len),
+                                         st);
+    finish_piece<FMT, D, DS, NC, WI>(a, sh, mlx3, st, 0, kh, j,
+                                     (j == 0 && Q < a.num_splits) ? Q : kNoSlot);
+    return;
+  }
+  for_each_piece<D, NC, 1>(a, unit, P, wv == 0,
+                           [&](uint32_t b, uint32_t kh, uint32_t tau0, uint32_t tau1,
+                               uint32_t slot, bool last, uint32_t L, bool fits) {
+    if (slot >= a.num_splits) return;      // only if a sequence outgrows its block table
+    const uint32_t lo = (a.window > 0 && L > a.window) ? L - a.window : 0u;
+    const uint32_t t0 = lo / 16 + tau0, t1 = lo / 16 + tau1;   // tiles of the sequence
+    WaveState<FMT, D, DS, NC> st;
+    stream_tiles<FMT, D, DS, NC, CONTIG>(a, mine, xg3, xturn, b, kh, t0 + wi, WI, t1, L, fits,
+                                         st);
+    finish_piece<FMT, D, DS, NC, WI>(a, sh, mlx3, st, b, kh, slot,
+                                     (last && slot + 1 < a.num_splits) ? slot + 1 : kNoSlot);
   });
 }
 
@@ -1309,8 +1663,9 @@ __global__ __launch_bounds__((64 * kDSplit<FMT, D>), (kWavesPerSimd<FMT, D>)) vo
 template <int D, int NC, int WQ>
 __global__ __launch_bounds__(64 * WQ, 1) void splitk_shared(DecodeArgs a) {
   __shared__ SharedLds<D> sh;
-  for_each_piece<D, NC, WQ>(a, [&](uint32_t b, uint32_t kh, uint32_t tau0, uint32_t tau1,
-                                   uint32_t slot, bool last, uint32_t L) {
+  for_each_piece<D, NC, WQ>(a, blockIdx.x, gridDim.x, true,
+                            [&](uint32_t b, uint32_t kh, uint32_t tau0, uint32_t tau1,
+                                uint32_t slot, bool last, uint32_t L, bool) {
     run_piece_shared<D, NC, WQ>(a, sh, b, kh, tau0, tau1, slot, last, L);
   });
 }
@@ -1547,28 +1902,31 @@ static int launch_status() {
   return e == hipSuccess ? kOk : kLaunch;
 }
 
-// Resident waves per CU of the stream kernel (workgroups x waves per workgroup).
-template <int FMT, int D, int NC, bool CONTIG>
+// Resident waves per CU of a stream kernel (workgroups x waves per workgroup).
+template <int FMT, int D, int NC, bool CONTIG, int WI>
 static int stream_occupancy() {
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, splitk_stream<FMT, D, NC, CONTIG>,
-                                                   64 * kDSplit<FMT, D>, 0) != hipSuccess)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, splitk_stream<FMT, D, NC, CONTIG, WI>,
+                                                   64 * kGroupWaves<FMT, D, WI>, 0) != hipSuccess)
     return 0;
-  return per_cu * kDSplit<FMT, D>;
+  return per_cu * kGroupWaves<FMT, D, WI>;
 }
 
-// Waves the stream kernel launches on the current device: all resident at
-// once (at most the occupancy), cached per device and kernel instance.
-template <int FMT, int D, int NC, bool CONTIG>
+// Waves a stream kernel launches on the current device: all resident at
+// once (at most the occupancy), cached per device and kernel instance. The
+// cache entries are atomics: host threads that launch at the same time may
+// both compute an entry, and store the same value.
+template <int FMT, int D, int NC, bool CONTIG, int WI>
 static uint64_t stream_capacity() {
-  static uint64_t cache[64];
+  static std::atomic<uint64_t> cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  if (cache[dev]) return cache[dev];
+  const uint64_t known = cache[dev].load(std::memory_order_relaxed);
+  if (known) return known;
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     return 0;
-  int per_cu = stream_occupancy<FMT, D, NC, CONTIG>();
+  int per_cu = stream_occupancy<FMT, D, NC, CONTIG, WI>();
   if (per_cu <= 0 || cus <= 0) return 0;
 #ifndef PKD_STREAM_WAVES_PER_CU
 #define PKD_STREAM_WAVES_PER_CU 4
@@ -1595,8 +1953,9 @@ static uint64_t stream_capacity() {
                          : kDSplit<FMT, D> > 2  ? PKD_STREAM_WAVES_PER_CU_Q4
                                                 : PKD_STREAM_WAVES_PER_CU_Q);
   if (per_cu > cap) per_cu = cap;
-  cache[dev] = uint64_t(per_cu) * uint64_t(cus);
-  return cache[dev];
+  const uint64_t waves = uint64_t(per_cu) * uint64_t(cus);
+  cache[dev].store(waves, std::memory_order_relaxed);
+  return waves;
 }
 
 // Start-up positions counted ahead of each row by the stream partition: a
@@ -1610,10 +1969,39 @@ constexpr uint32_t kRowLead = PKD_ROW_LEAD;
 // T + 3 * rows + 2 * waves stays below 2^32 for T up to 2^30 tiles.
 constexpr uint64_t kMaxLaunchTiles = 1ull << 30;
 
-// One launch of the stream kernel with NC column chunks per wave.
+// One launch of the stream kernel with NC column chunks per wave, WI
+// interleaving waves per piece (or 1: independent waves).
+template <int FMT, int D, int NC, bool CONTIG, int WI>
+static int launch_stream_wi(DecodeArgs a, uint64_t rows, hipStream_t stream) {
+  constexpr uint32_t gw = kGroupWaves<FMT, D, WI>;    // waves of a workgroup, one unit
+  // a unit of WI interleaving waves takes WI positions in one tile's time
+  a.row_lead = kRowLead * WI;
+  uint64_t units = rows;
+  if (a.num_splits > 1) {
+    const uint64_t cap = stream_capacity<FMT, D, NC, CONTIG, WI>() / gw;
+    units = rows * a.num_splits;
+    if (cap && units > cap) units = cap;
+    // One sequence without a window: Q units per row, each taking every Q-th
+    // tile, fill the same resident capacity and start without waiting for the
+    // length (at most num_splits slots per row).
+    if (a.static_q) {
+      a.static_q = uint32_t(max(uint64_t(1), min(cap / rows, uint64_t(a.num_splits))));
+      units = rows * a.static_q;
+    }
+  }
+  const uint64_t groups = units;
+  if (groups > 0x7FFFFFFFull) return kUnsupported;
+  hipLaunchKernelGGL((splitk_stream<FMT, D, NC, CONTIG, WI>), dim3(uint32_t(groups)),
+                     dim3(uint32_t(64 * gw)), 0, stream, a);
+  return launch_status();
+}
+
+// One launch of the stream kernel with NC column chunks per wave: a batch's
+// split-K pass on independent waves; one sequence without a window, and the
+// non-split call, on waves that interleave each piece's tiles where the rows
+// allow it.
 template <int FMT, int D, int NC, bool CONTIG>
 static int launch_stream(DecodeArgs a, hipStream_t stream) {
-  constexpr uint64_t ds = kDSplit<FMT, D>;
   a.head_chunks = (a.col_chunks + NC - 1) / NC;
   const uint64_t rows = uint64_t(a.num_seqs) * a.num_kv_heads * a.head_chunks;
   uint64_t tile_bound = uint64_t(a.max_blocks) * (a.block_size / 16);
@@ -1622,26 +2010,21 @@ static int launch_stream(DecodeArgs a, hipStream_t stream) {
   a.chunk_min = a.num_splits > 1
                     ? uint32_t((tile_bound + a.num_splits - 2) / (a.num_splits - 1))
                     : 1u;
-  a.row_lead = kRowLead;
-  // one workgroup per piece (at most num_splits per row), or as many as stay
-  // resident; a workgroup is one wave, or two sharing a head_dim of 512
-  uint64_t groups = rows;
-  if (a.num_splits > 1) {
-    groups = rows * a.num_splits;
-    const uint64_t cap = stream_capacity<FMT, D, NC, CONTIG>() / ds;
-    if (cap && groups > cap) groups = cap;
-  }
-  if (groups > 0x7FFFFFFFull) return kUnsupported;
-  hipLaunchKernelGGL((splitk_stream<FMT, D, NC, CONTIG>), dim3(uint32_t(groups)),
-                     dim3(uint32_t(64 * ds)), 0, stream, a);
-  return launch_status();
+  constexpr int wis = kMergeWaves<FMT, D, NC>;            // the single-piece form
+  constexpr uint32_t unit_waves = kGroupWaves<FMT, D, wis>;
+  a.static_q = 0;                               // set to Q by launch_stream_wi
+  if (a.num_splits > 1 && a.num_seqs == 1 && a.window == 0)
+    a.static_q = stream_capacity<FMT, D, NC, CONTIG, wis>() / unit_waves >= rows ? 1u : 0u;
+  if (a.num_splits == 1 || a.static_q)
+    return launch_stream_wi<FMT, D, NC, CONTIG, wis>(a, rows, stream);
+  return launch_stream_wi<FMT, D, NC, CONTIG, 1>(a, rows, stream);
 }
 
 
 // One launch of the shared-tile kernel: rows of WQ * NC column chunks.
 template <int D, int NC, int WQ>
 static int launch_shared(DecodeArgs a, hipStream_t stream) {
-  static uint64_t cache[64];
+  static std::atomic<uint64_t> cache[64];
   a.head_chunks = (a.col_chunks + NC * WQ - 1) / (NC * WQ);
   const uint64_t rows = uint64_t(a.num_seqs) * a.num_kv_heads * a.head_chunks;
   uint64_t tile_bound = uint64_t(a.max_blocks) * (a.block_size / 16);
@@ -1655,7 +2038,8 @@ static int launch_shared(DecodeArgs a, hipStream_t stream) {
   if (a.num_splits > 1) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kLaunch;
-    if (!cache[dev]) {
+    uint64_t cap = cache[dev].load(std::memory_order_relaxed);
+    if (!cap) {
       int cus = 0, per_cu = 0;
       if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
           hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, splitk_shared<D, NC, WQ>,
@@ -1665,10 +2049,11 @@ static int launch_shared(DecodeArgs a, hipStream_t stream) {
 #define PKD_SHARED_WAVES_PER_CU 8
 #endif
       if (per_cu > PKD_SHARED_WAVES_PER_CU / WQ) per_cu = PKD_SHARED_WAVES_PER_CU / WQ;
-      cache[dev] = uint64_t(per_cu > 0 ? per_cu : 1) * uint64_t(cus > 0 ? cus : 1);
+      cap = uint64_t(per_cu > 0 ? per_cu : 1) * uint64_t(cus > 0 ? cus : 1);
+      cache[dev].store(cap, std::memory_order_relaxed);
     }
     groups = rows * a.num_splits;
-    if (groups > cache[dev]) groups = cache[dev];
+    if (groups > cap) groups = cap;
   }
   if (groups > 0x7FFFFFFFull) return kUnsupported;
   hipLaunchKernelGGL((splitk_shared<D, NC, WQ>), dim3(uint32_t(groups)), dim3(64 * WQ), 0,
@@ -1739,6 +2124,7 @@ static DecodeArgs make_args(const uint16_t* q, const void* kc, const void* vc, f
   a.chunk_min = 1;
   a.row_lead = 0;
   a.max_len = uint32_t(min(uint64_t(max_blocks) * bs, uint64_t(0x7FFFFFFF)));
+  a.static_q = 0;
   a.out = nullptr;
   a.new_k = nullptr;
   a.new_v = nullptr;
