@@ -245,7 +245,10 @@ def _graph_time(fn, calls, reps):
             fn(i)
     g.replay()
     torch.cuda.synchronize()
+    # one more untimed replay, then the timed ones queue behind it: the GPU
+    # never waits for the host's graph launch inside the timed window
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    g.replay()
     a.record()
     for _ in range(reps):
         g.replay()
@@ -273,6 +276,7 @@ def _steps_spread(fn, NL, steps):
     torch.cuda.synchronize()
     reps = max(8, steps // per_graph)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    g.replay()                                   # untimed; the timed replays queue behind it
     ev[0].record()
     for r in range(reps):
         g.replay()
@@ -305,11 +309,14 @@ def _steps_time(fn, NL, steps):
         graphs.append((g, count))
     # the same K steps once untimed first: the GPU reaches the clocks it holds
     # under a steady decode load (the first graph replays after the host-side
-    # capture run measurably slower)
+    # capture run measurably slower). No host synchronization between them
+    # and the timed run: its first graph is already queued when the untimed
+    # steps end, as in a serving loop, so the host's launch latency stays
+    # outside the timed window.
+    torch.cuda.synchronize()
     for g, count in graphs:
         for _ in range(count):
             g.replay()
-    torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for g, count in graphs:
@@ -361,6 +368,7 @@ def time_workload(name, steps, warmup, kernel_reps=100, single=True):
         non_split_us_per_step=ms_single * 1e3, non_split_kv_gbs=gbs(ms_single),
         non_split_kernel_us=single_ms * 1e3, non_split_kernel_gbs=gbs(single_ms),
         splitk_us=k_ms * 1e3, splitk_gbs=gbs(k_ms),
+        k_scale=lay.k_scale, v_scale=lay.v_scale,
     )
     res["pct_of_peak"] = 100.0 * res["kv_gbs"] / PEAK_HBM_GBS
     del lay
@@ -671,26 +679,33 @@ def traffic_record(name, tag):
         return None
 
 
-def cpu_baseline(w, budget_s=12.0, max_reps=50):
-    """The float64 oracle on the host: repeated decode steps of the same
-    workload (gather + dequantize + attention of every sequence) until the
-    time budget is spent; the caches are written once before timing."""
+def cpu_baseline(w, budget_s=12.0, max_seqs=None, k_scale=1.0, v_scale=1.0, max_reps=50):
+    """The float64 oracle on the host: decode steps of a sample of the
+    workload's sequences (the first `max_seqs`, or all), repeated until the
+    time budget is spent, each sequence's page gather, dequantization and
+    softmax attention timed; the sample's caches are written once before
+    timing (in token chunks, untimed). Scaled to GB/s of attended KV."""
     import oracle
     from threadpoolctl import threadpool_info
     geom = oracle.CacheGeometry(w.kv_dtype, w.num_pages, w.block_size, w.num_kv_heads,
                                 w.head_dim)
     kc, vc = oracle.new_cache(geom, 0), oracle.new_cache(geom, 0)
-    oracle.reshape_and_cache(geom, w.k_bits, w.v_bits, kc, vc, w.slot_mapping)
+    nseq = w.num_seqs if max_seqs is None else min(int(max_seqs), w.num_seqs)
+    seqs = list(range(nseq))
+    tok = np.nonzero(np.isin(w.token_seq, seqs))[0]
+    for i in range(0, tok.size, 4096):
+        part = tok[i:i + 4096]
+        oracle.reshape_and_cache(geom, w.k_bits[part], w.v_bits[part], kc, vc,
+                                 w.slot_mapping[part], k_scale=k_scale, v_scale=v_scale)
     kv_bytes = attended_tokens(w) * kv_bytes_per_token(w)
-    per_seq = []
     total_t, total_bytes, reps = 0.0, 0, 0
     lens = w.seq_lens.astype(np.int64)
     while total_t < budget_s and reps < max_reps:
-        for b in range(w.num_seqs):
+        for b in seqs:
             t0 = time.perf_counter()
             oracle.paged_decode_attention(geom, w.q_bits, kc, vc, w.block_tables, w.seq_lens,
                                           w.num_q_heads, w.scale, sliding_window=w.sliding_window,
-                                          seqs=[b])
+                                          k_scale=k_scale, v_scale=v_scale, seqs=[b])
             dt = time.perf_counter() - t0
             total_t += dt
             L = lens[b] if w.sliding_window <= 0 else min(lens[b], w.sliding_window)
@@ -700,14 +715,19 @@ def cpu_baseline(w, budget_s=12.0, max_reps=50):
         reps += 1
     blas = [p.get("num_threads", 1) for p in threadpool_info()]
     threads = max(blas) if blas else 1
+    sample = (f"{w.name}: float64 NumPy oracle decode (page gather, dequant, softmax attention) "
+              f"of {'all ' + str(nseq) if nseq == w.num_seqs else 'the first ' + str(nseq) + ' of ' + str(w.num_seqs)} "
+              f"sequences, {total_bytes / kv_bytes:.2f} steps' worth of KV in {total_t:.1f} s; "
+              f"cache write untimed; {len(os.sched_getaffinity(0))} host cores visible, BLAS "
+              f"threads {threads}")
     return dict(value=total_bytes / total_t / 1e9, unit="GB/s", cores=int(threads),
-                kind="oracle",
-                sample=(f"{w.name}: float64 NumPy oracle decode (page gather, dequant, softmax "
-                        f"attention) of the workload's sequences, {total_bytes / kv_bytes:.2f} "
-                        f"steps' worth of KV in {total_t:.1f} s; cache write untimed; "
-                        f"{len(os.sched_getaffinity(0))} host cores visible, BLAS threads "
-                        f"{threads}"),
-                s_per_step=total_t * kv_bytes / total_bytes)
+                kind="oracle", sample=sample, s_per_step=total_t * kv_bytes / total_bytes)
+
+
+# Bounded oracle samples beside each extra workload: (seconds, sequences).
+CPU_SAMPLES = {"b1_32k": (6.0, None), "fp8": (6.0, 8), "nvfp4": (6.0, 4),
+               "b1_1k": (1.5, None), "b1_4k": (1.5, None), "b1_8k": (1.5, None),
+               "b1_16k": (2.0, None)}
 
 
 def copy_calibration(nbytes=1 << 30, reps=5):
@@ -727,7 +747,7 @@ def main():
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="llama8b")
-    ap.add_argument("--extra", nargs="*", default=["b1_32k"])
+    ap.add_argument("--extra", nargs="*", default=["b1_32k", "fp8", "nvfp4"])
     ap.add_argument("--sweep", nargs="*", default=["b1_1k", "b1_4k", "b1_8k", "b1_16k"],
                     help="B=1 context sweep: step and split-K kernel per context")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -779,8 +799,18 @@ def main():
     print(f"bench: {args.workload} {main_res['us_per_step']:.2f} us/step "
           f"{main_res['kv_gbs']:.0f} GB/s", file=sys.stderr, flush=True)
     extras = {}
+    def side_baseline(name, r, wl):
+        if args.no_cpu_baseline:
+            return None
+        budget, nseq = CPU_SAMPLES.get(name, (6.0, 8))
+        cb = cpu_baseline(wl, budget_s=budget, max_seqs=nseq, k_scale=r["k_scale"],
+                          v_scale=r["v_scale"])
+        print(f"bench: {name} oracle {cb['value']:.3f} GB/s ({cb['s_per_step']:.3f} s/step)",
+              file=sys.stderr, flush=True)
+        return cb
+
     for name in args.extra:
-        r, _ = time_workload(name, args.steps, args.warmup, single=not args.no_single)
+        r, wx = time_workload(name, args.steps, args.warmup, single=not args.no_single)
         extras[name] = {k: r[k] for k in ("us_per_step", "us_per_step_spread", "kv_gbs",
                                           "pct_of_peak",
                                           "separate_write_us_per_step",
@@ -793,16 +823,20 @@ def main():
                                           "kv_bytes_per_step", "layers_rotated", "kv_dtype")}
         print(f"bench: {name} {r['us_per_step']:.2f} us/step {r['kv_gbs']:.0f} GB/s",
               file=sys.stderr, flush=True)
+        extras[name]["cpu_baseline"] = side_baseline(name, r, wx)
+        del wx
 
     sweep = {}
     for name in args.sweep:
-        r, _ = time_workload(name, args.steps, args.warmup, single=False)
+        r, wx = time_workload(name, args.steps, args.warmup, single=False)
         sweep[name] = {k: r[k] for k in ("us_per_step", "kv_gbs", "pct_of_peak", "splitk_us",
                                          "splitk_gbs", "splitk_plain_us", "splitk_plain_gbs",
                                          "num_splits", "kv_bytes_per_step")}
         print(f"bench: sweep {name} {r['us_per_step']:.2f} us/step, split-K "
               f"{r['splitk_plain_us']:.2f} us {r['splitk_plain_gbs']:.0f} GB/s",
               file=sys.stderr, flush=True)
+        sweep[name]["cpu_baseline"] = side_baseline(name, r, wx)
+        del wx
     verify = {}
     by_name = {}
     for spec in args.verify:

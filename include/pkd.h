@@ -136,9 +136,10 @@ PKD_API int bf16_absmax(const uint16_t* data, float* out_max, uint64_t n_elems,
  *   offset j % bs; logit s_j = (q . k_j) * scale (the scale applied after the
  *   dot); output = softmax(s) . V.
  * Splits: the keys of every (b, h) are divided into at most num_splits
- *   pieces, each a contiguous key range; how the launch's work is divided
- *   among waves is internal (equal key counts across the waves it launches,
- *   whatever the batch's length mix).
+ *   pieces, each a set of 16-key tiles (a contiguous range over a batch; for
+ *   one sequence without a window, every Q-th tile); how the launch's work is
+ *   divided among waves is internal (equal key counts across the waves it
+ *   launches, whatever the batch's length mix).
  * Workspace: float32 [num_seqs][num_q_heads][num_splits][head_dim + 2]; slot i
  *   of (b, h) holds a piece's o (head_dim values, its softmax-normalized
  *   output), m and l = sum of exp(s_j - m), where m is a reference logit at
@@ -249,12 +250,17 @@ PKD_API int paged_decode_attn_reduce(const float* workspace, uint16_t* output,
  * block_tables, seq_lens, max_blocks_per_seq, num_seqs, head counts,
  * head_dim, block_size, scale, q_stride, cache layout); sliding_window,
  * workspace and num_splits are extensions.
- *   num_splits == 1: one wave per (sequence, kv head, 16 q heads) row writes
- *     the output, as the non-split launcher does; workspace is not used
- *     (may be null).
+ *   num_splits == 1: one workgroup per (sequence, kv head, 16 q heads) row
+ *     writes the output, as the non-split launcher does (BF16 and FP8 rows
+ *     up to head_dim 256: four waves that take the row's tiles in turn and
+ *     merge in LDS); workspace is not used (may be null). Only
+ *     num_seqs x num_kv_heads workgroups then read the whole cache: slow
+ *     for few, long sequences (one sequence of 32K keys, 8 kv heads: some
+ *     50x the split path).
  *   num_splits > 1: the split-K pass and the combine, as two launches on
  *     `stream`; workspace as for the split-K calls
- *     (paged_decode_workspace_bytes).
+ *     (paged_decode_workspace_bytes). paged_decode_num_splits() gives the
+ *     split count to use.
  * Sequences with seq_lens[b] == 0 get zeros. Other arguments and errors as
  * for the split-K calls; output must be 16-byte aligned. */
 PKD_API int paged_decode_attn_bf16(const uint16_t* q, const uint16_t* k_cache,
@@ -307,7 +313,9 @@ PKD_API int paged_decode_attn_nvfp4(const uint16_t* q, const uint8_t* k_cache,
  *   q_len > 1), heads head_dim apart, 16-byte aligned.
  * output: BF16 [num_seqs][q_len][num_q_heads][head_dim], contiguous.
  * num_splits == 1: one pass writes the output (workspace unused, may be
- *   null). num_splits > 1: the split-K pass and the combine, two launches;
+ *   null; one workgroup per row, slow for long contexts, see
+ *   paged_prefill_num_splits). num_splits > 1: the split-K pass and the
+ *   combine, two launches;
  *   workspace of paged_decode_workspace_bytes(num_seqs, num_q_heads * q_len,
  *   head_dim, num_splits) bytes, laid out [num_seqs][q_len][num_q_heads]
  *   [num_splits][head_dim + 2] (the combine is paged_decode_attn_reduce with

@@ -130,6 +130,23 @@ def _stream(t: torch.Tensor, stream) -> Optional[int]:
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+def _num_cus(t: torch.Tensor) -> int:
+    return torch.cuda.get_device_properties(t.device).multi_processor_count
+
+
+def _splits_and_workspace(name, num_splits, workspace, heuristic, rows, head_dim, q):
+    """num_splits None: the library's split heuristic for the device; a
+    workspace must then be given whenever it picks more than one split."""
+    if num_splits is None:
+        num_splits = heuristic()
+    if num_splits > 1 and workspace is None:
+        need = paged_decode_workspace_bytes(rows[0], rows[1], head_dim, num_splits)
+        raise PkdError(f"{name}: num_splits={num_splits} needs a float32 workspace of {need} "
+                       "bytes (paged_decode_workspace_bytes); pass workspace=, or num_splits=1 "
+                       "for the non-split path")
+    return num_splits
+
+
 def _need_gpu(*ts):
     for t in ts:
         if t is not None and not t.is_cuda:
@@ -250,11 +267,28 @@ def paged_decode_num_splits(num_seqs, num_q_heads, num_kv_heads, max_blocks_per_
 
 # ---------------------------------------------------------------- whole decode
 
+def _decode_splits(name, num_splits, workspace, q, num_seqs, num_q_heads, num_kv_heads,
+                   max_blocks_per_seq, block_size, sliding_window, head_dim):
+    return _splits_and_workspace(
+        name, num_splits, workspace,
+        lambda: paged_decode_num_splits(num_seqs, num_q_heads, num_kv_heads, max_blocks_per_seq,
+                                        block_size, sliding_window, _num_cus(q)),
+        (num_seqs, num_q_heads), head_dim, q)
+
+
+# num_splits None (the default) takes the library's split heuristic for the
+# device, with the split-K pass and the combine (a workspace is then needed);
+# num_splits 1 is the non-split path: one workgroup per (sequence, kv head)
+# row, slow for long contexts (few rows, long serial scans).
+
 def paged_decode_attn_bf16(q, k_cache, v_cache, output, block_tables, seq_lens,
                            max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads, head_dim,
                            block_size, scale, q_stride, sliding_window=0, workspace=None,
-                           num_splits=1, stream=None):
+                           num_splits=None, stream=None):
     _need_gpu(q, k_cache, v_cache, output, block_tables, seq_lens, workspace)
+    num_splits = _decode_splits("paged_decode_attn_bf16", num_splits, workspace, q, num_seqs,
+                                num_q_heads, num_kv_heads, max_blocks_per_seq, block_size,
+                                sliding_window, head_dim)
     _check(lib().paged_decode_attn_bf16(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(output), _ptr(block_tables), _ptr(seq_lens),
         max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
@@ -265,8 +299,11 @@ def paged_decode_attn_bf16(q, k_cache, v_cache, output, block_tables, seq_lens,
 def paged_decode_attn_fp8(q, k_cache, v_cache, output, block_tables, seq_lens,
                           max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads, head_dim,
                           block_size, scale, k_scale, v_scale, q_stride, cache_stride,
-                          sliding_window=0, workspace=None, num_splits=1, stream=None):
+                          sliding_window=0, workspace=None, num_splits=None, stream=None):
     _need_gpu(q, k_cache, v_cache, output, block_tables, seq_lens, workspace)
+    num_splits = _decode_splits("paged_decode_attn_fp8", num_splits, workspace, q, num_seqs,
+                                num_q_heads, num_kv_heads, max_blocks_per_seq, block_size,
+                                sliding_window, head_dim)
     _check(lib().paged_decode_attn_fp8(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(output), _ptr(block_tables), _ptr(seq_lens),
         max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
@@ -277,8 +314,11 @@ def paged_decode_attn_fp8(q, k_cache, v_cache, output, block_tables, seq_lens,
 def paged_decode_attn_nvfp4(q, k_cache, v_cache, output, block_tables, seq_lens,
                             max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads, head_dim,
                             block_size, scale, q_stride, block_stride_bytes, data_section_bytes,
-                            sliding_window=0, workspace=None, num_splits=1, stream=None):
+                            sliding_window=0, workspace=None, num_splits=None, stream=None):
     _need_gpu(q, k_cache, v_cache, output, block_tables, seq_lens, workspace)
+    num_splits = _decode_splits("paged_decode_attn_nvfp4", num_splits, workspace, q, num_seqs,
+                                num_q_heads, num_kv_heads, max_blocks_per_seq, block_size,
+                                sliding_window, head_dim)
     _check(lib().paged_decode_attn_nvfp4(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(output), _ptr(block_tables), _ptr(seq_lens),
         max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
@@ -339,6 +379,16 @@ def paged_decode_attn_splitk_append_nvfp4(q, key, value, k_cache, v_cache, works
 
 # ---------------------------------------------------------------- query blocks
 
+def _prefill_splits(name, num_splits, workspace, q, num_seqs, q_len, num_q_heads, num_kv_heads,
+                    max_blocks_per_seq, block_size, causal, sliding_window, head_dim):
+    return _splits_and_workspace(
+        name, num_splits, workspace,
+        lambda: paged_prefill_num_splits(num_seqs, q_len, num_q_heads, num_kv_heads,
+                                         max_blocks_per_seq, block_size, causal, sliding_window,
+                                         _num_cus(q)),
+        (num_seqs, num_q_heads * q_len), head_dim, q)
+
+
 def _q_strides(num_q_heads, head_dim, q_len, q_stride, q_token_stride):
     ts = num_q_heads * head_dim if q_token_stride is None else q_token_stride
     qs = q_len * ts if q_stride is None else q_stride
@@ -348,10 +398,13 @@ def _q_strides(num_q_heads, head_dim, q_len, q_stride, q_token_stride):
 def paged_prefill_attn_bf16(q, k_cache, v_cache, output, block_tables, seq_lens,
                             max_blocks_per_seq, num_seqs, q_len, num_q_heads, num_kv_heads,
                             head_dim, block_size, scale, causal=True, sliding_window=0,
-                            q_stride=None, q_token_stride=None, workspace=None, num_splits=1,
+                            q_stride=None, q_token_stride=None, workspace=None, num_splits=None,
                             stream=None):
     _need_gpu(q, k_cache, v_cache, output, block_tables, seq_lens, workspace)
     qs, ts = _q_strides(num_q_heads, head_dim, q_len, q_stride, q_token_stride)
+    num_splits = _prefill_splits("paged_prefill_attn_bf16", num_splits, workspace, q, num_seqs,
+                                 q_len, num_q_heads, num_kv_heads, max_blocks_per_seq,
+                                 block_size, causal, sliding_window, head_dim)
     _check(lib().paged_prefill_attn_bf16(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(output), _ptr(block_tables), _ptr(seq_lens),
         max_blocks_per_seq, num_seqs, q_len, num_q_heads, num_kv_heads, head_dim, block_size,
@@ -363,9 +416,12 @@ def paged_prefill_attn_fp8(q, k_cache, v_cache, output, block_tables, seq_lens,
                            max_blocks_per_seq, num_seqs, q_len, num_q_heads, num_kv_heads,
                            head_dim, block_size, scale, k_scale, v_scale, cache_stride,
                            causal=True, sliding_window=0, q_stride=None, q_token_stride=None,
-                           workspace=None, num_splits=1, stream=None):
+                           workspace=None, num_splits=None, stream=None):
     _need_gpu(q, k_cache, v_cache, output, block_tables, seq_lens, workspace)
     qs, ts = _q_strides(num_q_heads, head_dim, q_len, q_stride, q_token_stride)
+    num_splits = _prefill_splits("paged_prefill_attn_fp8", num_splits, workspace, q, num_seqs,
+                                 q_len, num_q_heads, num_kv_heads, max_blocks_per_seq,
+                                 block_size, causal, sliding_window, head_dim)
     _check(lib().paged_prefill_attn_fp8(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(output), _ptr(block_tables), _ptr(seq_lens),
         max_blocks_per_seq, num_seqs, q_len, num_q_heads, num_kv_heads, head_dim, block_size,
@@ -378,9 +434,12 @@ def paged_prefill_attn_nvfp4(q, k_cache, v_cache, output, block_tables, seq_lens
                              max_blocks_per_seq, num_seqs, q_len, num_q_heads, num_kv_heads,
                              head_dim, block_size, scale, block_stride_bytes, data_section_bytes,
                              causal=True, sliding_window=0, q_stride=None, q_token_stride=None,
-                             workspace=None, num_splits=1, stream=None):
+                             workspace=None, num_splits=None, stream=None):
     _need_gpu(q, k_cache, v_cache, output, block_tables, seq_lens, workspace)
     qs, ts = _q_strides(num_q_heads, head_dim, q_len, q_stride, q_token_stride)
+    num_splits = _prefill_splits("paged_prefill_attn_nvfp4", num_splits, workspace, q, num_seqs,
+                                 q_len, num_q_heads, num_kv_heads, max_blocks_per_seq,
+                                 block_size, causal, sliding_window, head_dim)
     _check(lib().paged_prefill_attn_nvfp4(
         _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(output), _ptr(block_tables), _ptr(seq_lens),
         max_blocks_per_seq, num_seqs, q_len, num_q_heads, num_kv_heads, head_dim, block_size,
@@ -417,10 +476,16 @@ def _strides_arg(q_strides, k_strides, v_strides, o_strides):
 
 def contig_kv_attn_bf16(q, k, v, output, seq_lens, num_seqs, q_len, max_seq_len, num_q_heads,
                         num_kv_heads, head_dim, scale, q_strides, k_strides, v_strides,
-                        o_strides, causal=True, sliding_window=0, workspace=None, num_splits=1,
+                        o_strides, causal=True, sliding_window=0, workspace=None, num_splits=None,
                         stream=None):
     _need_gpu(q, k, v, output, seq_lens, workspace)
     st = _strides_arg(q_strides, k_strides, v_strides, o_strides)
+    num_splits = _splits_and_workspace(
+        "contig_kv_attn_bf16", num_splits, workspace,
+        lambda: paged_prefill_num_splits(num_seqs, q_len, num_q_heads, num_kv_heads,
+                                         (max_seq_len + 15) // 16, 16, causal, sliding_window,
+                                         _num_cus(q)),
+        (num_seqs, num_q_heads * q_len), head_dim, q)
     _check(lib().contig_kv_attn_bf16(
         _ptr(q), _ptr(k), _ptr(v), _ptr(output), _ptr(seq_lens), num_seqs, q_len, max_seq_len,
         num_q_heads, num_kv_heads, head_dim, float(scale), st, int(bool(causal)),
@@ -430,9 +495,15 @@ def contig_kv_attn_bf16(q, k, v, output, seq_lens, num_seqs, q_len, max_seq_len,
 def contig_kv_attn_fp8(q, k, v, output, seq_lens, num_seqs, q_len, max_seq_len, num_q_heads,
                        num_kv_heads, head_dim, scale, k_scale, v_scale, q_strides, k_strides,
                        v_strides, o_strides, causal=True, sliding_window=0, workspace=None,
-                       num_splits=1, stream=None):
+                       num_splits=None, stream=None):
     _need_gpu(q, k, v, output, seq_lens, workspace)
     st = _strides_arg(q_strides, k_strides, v_strides, o_strides)
+    num_splits = _splits_and_workspace(
+        "contig_kv_attn_fp8", num_splits, workspace,
+        lambda: paged_prefill_num_splits(num_seqs, q_len, num_q_heads, num_kv_heads,
+                                         (max_seq_len + 15) // 16, 16, causal, sliding_window,
+                                         _num_cus(q)),
+        (num_seqs, num_q_heads * q_len), head_dim, q)
     _check(lib().contig_kv_attn_fp8(
         _ptr(q), _ptr(k), _ptr(v), _ptr(output), _ptr(seq_lens), num_seqs, q_len, max_seq_len,
         num_q_heads, num_kv_heads, head_dim, float(scale), float(k_scale), float(v_scale), st,

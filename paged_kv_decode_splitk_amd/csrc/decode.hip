@@ -1483,7 +1483,7 @@ template <int D, int NC, int WQ, typename Piece>
 __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, uint32_t unit, uint32_t P,
                                                bool zero_lead, Piece&& piece) {
   const uint32_t R = a.num_kv_heads * a.head_chunks;          // rows per sequence
-  const bool whole = a.num_splits == 1;                       // one wave per row
+  const bool whole = a.num_splits == 1;                       // one unit per row
   // With at most 64 sequences, one length per lane, loaded once: the tile
   // counts, their prefix sums and every row lookup come from these registers.
   const bool cached = a.num_seqs <= 64;
@@ -2194,7 +2194,7 @@ static int launch_reduce(const float* workspace, uint16_t* output, const int32_t
   return launch_status();
 }
 
-// Non-split decode (num_splits 1): one wave per row writes the output. More
+// Non-split decode (num_splits 1): one workgroup per row writes the output. More
 // splits: the split-K pass and the combine, as two launches.
 template <int FMT, bool CONTIG = false>
 static int launch_decode(DecodeArgs a, uint16_t* output, uint32_t num_seqs, uint32_t head_dim,

@@ -3,6 +3,9 @@ library, oracle pools written by the oracle from the same seeded inputs, and
 the comparison rule. Nothing here computes attention or encodes values."""
 from __future__ import annotations
 
+import concurrent.futures
+import os
+
 import numpy as np
 import torch
 
@@ -174,17 +177,34 @@ class DeviceKV:
         return res
 
 
+ORACLE_CHUNK = 4096          # tokens per oracle cache-write call
+ORACLE_THREADS = min(16, len(os.sched_getaffinity(0)))
+
+
 def oracle_pools(w, geom, k_scale=1.0, v_scale=1.0, seqs=None, fill=None):
     """Oracle pools written by the oracle's cache write (all tokens, or only
-    the tokens of the sequences in ``seqs``)."""
+    the tokens of the sequences in ``seqs``). The tokens go through the
+    oracle in chunks on a few host threads: slots are unique, so the chunks
+    write disjoint bytes, and small chunks keep the encoders' float64
+    temporaries small."""
     fill = POISON[geom.fmt] if fill is None else fill
     kc, vc = oracle.new_cache(geom, fill), oracle.new_cache(geom, fill)
     if seqs is None:
         tok = np.arange(w.num_tokens)
     else:
         tok = np.nonzero(np.isin(w.token_seq, np.asarray(seqs)))[0]
-    oracle.reshape_and_cache(geom, w.k_bits[tok], w.v_bits[tok], kc, vc, w.slot_mapping[tok],
-                             k_scale=k_scale, v_scale=v_scale)
+
+    def write(part):
+        oracle.reshape_and_cache(geom, w.k_bits[part], w.v_bits[part], kc, vc,
+                                 w.slot_mapping[part], k_scale=k_scale, v_scale=v_scale)
+
+    parts = [tok[i:i + ORACLE_CHUNK] for i in range(0, tok.size, ORACLE_CHUNK)]
+    if len(parts) <= 1:
+        for part in parts:
+            write(part)
+    else:
+        with concurrent.futures.ThreadPoolExecutor(ORACLE_THREADS) as ex:
+            list(ex.map(write, parts))
     return kc, vc
 
 
@@ -205,6 +225,25 @@ def assert_close(got, ref, what=""):
         raise AssertionError(f"{what}: {bad.sum()} of {bad.size} outside atol=rtol=1e-2; "
                              f"max err {np.nanmax(err):.3e}; first {idx.tolist()}")
     return float(err.max()) if err.size else 0.0
+
+
+_FULL = {}
+
+
+def full_size_reference(name):
+    """(workload, geometry, k_scale, v_scale, oracle K pool, oracle V pool,
+    oracle decode of every sequence) of a full-size workload, built once per
+    test session: every token goes through the oracle's cache write and
+    every sequence through its decode."""
+    if name not in _FULL:
+        import workloads
+        w = workloads.make_workload(name)
+        geom = geometry(w)
+        ks, vs = fp8_scales(w) if w.kv_dtype == "fp8" else (1.0, 1.0)
+        kc, vc = oracle_pools(w, geom, ks, vs)
+        ref = oracle_decode(w, geom, kc, vc, ks, vs)
+        _FULL[name] = (w, geom, ks, vs, kc, vc, ref)
+    return _FULL[name]
 
 
 def fp8_scales(w):

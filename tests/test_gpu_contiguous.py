@@ -81,20 +81,18 @@ def test_paged_twin_is_bit_identical(n, S):
 
 
 def test_full_size_llama8b_contiguous():
-    """B=32, lengths U[512, 4096], (b, h, l, d) K/V: sampled sequences
-    against the oracle at the heuristic split count, and the whole batch bit
-    for bit against the paged decode of the same rows."""
+    """B=32, lengths U[512, 4096], (b, h, l, d) K/V: every sequence against
+    the oracle at the heuristic split count, and the whole batch bit for bit
+    against the paged decode of the same rows."""
     w = workloads.make_workload("llama8b")
     S = pkd.paged_decode_num_splits(w.num_seqs, w.num_q_heads, w.num_kv_heads,
                                     w.max_blocks_per_seq, w.block_size, 0,
                                     torch.cuda.get_device_properties(0).multi_processor_count)
     c = Contig(w, "bhld", Lmax=w.max_blocks_per_seq * w.block_size)
     got = c.run(w.q_bits.reshape(w.num_seqs, 1, w.num_q_heads, w.head_dim), 1, S)
-    order = np.argsort(w.seq_lens)
-    seqs = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2])})
-    ref = c.oracle(w.q_bits.reshape(w.num_seqs, 1, w.num_q_heads, w.head_dim), 1, seqs=seqs)
-    err = assert_close(got[seqs], ref, "llama8b contiguous")
+    ref = c.oracle(w.q_bits.reshape(w.num_seqs, 1, w.num_q_heads, w.head_dim), 1)
+    err = assert_close(got, ref, "llama8b contiguous")
     d = DeviceKV(w, geometry(w))
     paged = d.prefill(w.q_bits.reshape(w.num_seqs, 1, w.num_q_heads, w.head_dim), 1, S)
     assert np.array_equal(paged, got)
-    print(f"[llama8b contiguous] S={S} seqs={seqs} max_abs_err={err:.3e}", flush=True)
+    print(f"[llama8b contiguous] S={S} all {w.num_seqs} seqs max_abs_err={err:.3e}", flush=True)

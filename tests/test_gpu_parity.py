@@ -12,9 +12,9 @@ import torch
 import oracle
 import paged_kv_decode_splitk_amd as pkd
 import workloads
-from gpu_cases import (DeviceKV, POISON, alloc_pool, assert_close, dev, fp8_scales, geometry,
-                       gpu_absmax, i32_to_dev, oracle_decode, oracle_pools, pool_to_np,
-                       u16_to_dev)
+from gpu_cases import (DeviceKV, POISON, alloc_pool, assert_close, dev, fp8_scales,
+                       full_size_reference, geometry, gpu_absmax, i32_to_dev, oracle_decode,
+                       oracle_pools, pool_to_np, u16_to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -319,55 +319,34 @@ def test_deterministic():
 
 # ------------------------------------------------------------------ full-size workloads
 
-def _full_size(name, sample):
-    w = workloads.make_workload(name)
+def _full_size(name):
+    """The full-size workload in the launch configuration the bench times
+    (the library's split count): the pools written by the library equal the
+    oracle's byte for byte (every page, the unwritten bytes of partial last
+    pages included), and every sequence's output matches the oracle."""
+    w, geom, ks, vs, kc, vc, ref = full_size_reference(name)
     fmt = w.kv_dtype
     print(f"[{name}] B={w.num_seqs} T={w.num_tokens} fmt={fmt}", flush=True)
-    geom = geometry(w)
-    if fmt == "fp8":
-        ks, vs = fp8_scales(w)
-    else:
-        ks = vs = 1.0
     d = DeviceKV(w, geom, ks, vs)
+    assert np.array_equal(pool_to_np(d.k, fmt), kc) and np.array_equal(pool_to_np(d.v, fmt), vc)
     S = pkd.paged_decode_num_splits(w.num_seqs, w.num_q_heads, w.num_kv_heads,
                                     w.max_blocks_per_seq, w.block_size, w.sliding_window,
                                     _num_cus())
     got = d.decode(S)
-    seqs = sample(w)
-    kc, vc = oracle_pools(w, geom, ks, vs, seqs=seqs)
-    # the pages of the sampled sequences hold the same bytes on both sides
-    units = geom.page_units()
-    kd = pool_to_np(d.k, fmt).reshape(w.num_pages, units)
-    ko = kc.reshape(w.num_pages, units)
-    vd = pool_to_np(d.v, fmt).reshape(w.num_pages, units)
-    vo = vc.reshape(w.num_pages, units)
-    for b in seqs:
-        n = (int(w.seq_lens[b]) + w.block_size - 1) // w.block_size
-        pages = w.block_tables[b, :n]
-        full = pages[: int(w.seq_lens[b]) // w.block_size]      # completely written pages
-        assert np.array_equal(kd[full], ko[full]) and np.array_equal(vd[full], vo[full])
-    ref = oracle_decode(w, geom, kc, vc, ks, vs, seqs=seqs)
-    err = assert_close(got[seqs], ref, name)
-    print(f"[{name}] num_splits={S} sampled seqs={list(seqs)} max_abs_err={err:.3e}", flush=True)
+    err = assert_close(got, ref, name)
+    print(f"[{name}] num_splits={S} all {w.num_seqs} seqs max_abs_err={err:.3e}", flush=True)
     del d
     torch.cuda.empty_cache()
 
 
-def _spread(w, k=4):
-    order = np.argsort(w.seq_lens)
-    pick = {int(order[0]), int(order[-1])}
-    pick.update(int(i) for i in np.linspace(0, w.num_seqs - 1, k).astype(int))
-    return sorted(pick)
-
-
 @pytest.mark.parametrize("name", ["llama8b", "fp8", "nvfp4"])
 def test_full_size_batched(name):
-    _full_size(name, _spread)
+    _full_size(name)
 
 
 @pytest.mark.parametrize("name", ["b1_1k", "b1_4k", "b1_8k", "b1_16k", "b1_32k"])
 def test_full_size_b1_long_context(name):
-    _full_size(name, lambda w: [0])
+    _full_size(name)
 
 
 # ------------------------------------------------------------------ whole-decode call
@@ -440,21 +419,18 @@ def test_whole_decode_graph_replay():
         del graph
 
 
-@pytest.mark.parametrize("name", ["llama8b", "b1_32k"])
+@pytest.mark.parametrize("name", ["llama8b", "b1_32k", "fp8", "nvfp4"])
 def test_whole_decode_full_size(name):
-    w = workloads.make_workload(name)
-    geom = geometry(w)
-    d = DeviceKV(w, geom)
+    w, geom, ks, vs, kc, vc, ref = full_size_reference(name)
+    d = DeviceKV(w, geom, ks, vs)
     S = pkd.paged_decode_num_splits(w.num_seqs, w.num_q_heads, w.num_kv_heads,
                                     w.max_blocks_per_seq, w.block_size, w.sliding_window,
                                     _num_cus())
-    seqs = _spread(w) if w.num_seqs > 1 else [0]
-    kc, vc = oracle_pools(w, geom, seqs=seqs)
-    ref = oracle_decode(w, geom, kc, vc, seqs=seqs)
     for n_splits in (1, S):
         got = d.decode_single(n_splits)
-        err = assert_close(got[seqs], ref, f"{name} S={n_splits}")
-        print(f"[{name}] whole decode num_splits={n_splits} max_abs_err={err:.3e}", flush=True)
+        err = assert_close(got, ref, f"{name} S={n_splits}")
+        print(f"[{name}] whole decode num_splits={n_splits} all {w.num_seqs} seqs "
+              f"max_abs_err={err:.3e}", flush=True)
     del d
     torch.cuda.empty_cache()
 
@@ -552,18 +528,21 @@ def test_split_k_append(case):
     assert np.array_equal(got, full.decode(S))
 
 
-def test_split_k_append_full_size():
-    w = workloads.make_workload("llama8b")
-    geom = geometry(w)
+@pytest.mark.parametrize("name", ["llama8b", "b1_32k", "fp8", "nvfp4"])
+def test_split_k_append_full_size(name):
+    """The decode step the bench times: pools holding every token but each
+    sequence's last, the append call writing those and attending. Pools and
+    outputs of every sequence against the oracle's."""
+    w, geom, ks, vs, kc, vc, ref = full_size_reference(name)
     S = pkd.paged_decode_num_splits(w.num_seqs, w.num_q_heads, w.num_kv_heads,
                                     w.max_blocks_per_seq, w.block_size, w.sliding_window,
                                     _num_cus())
-    got, d = _append_decode(w, geom, 1.0, 1.0, S)
-    seqs = _spread(w)
-    kc, vc = oracle_pools(w, geom, seqs=seqs)
-    ref = oracle_decode(w, geom, kc, vc, seqs=seqs)
-    err = assert_close(got[seqs], ref, "llama8b append")
-    print(f"[llama8b] append num_splits={S} max_abs_err={err:.3e}", flush=True)
+    got, d = _append_decode(w, geom, ks, vs, S)
+    fmt = w.kv_dtype
+    assert np.array_equal(pool_to_np(d.k, fmt), kc) and np.array_equal(pool_to_np(d.v, fmt), vc)
+    err = assert_close(got, ref, f"{name} append")
+    print(f"[{name}] append num_splits={S} all {w.num_seqs} seqs max_abs_err={err:.3e}",
+          flush=True)
     del d
     torch.cuda.empty_cache()
 
@@ -640,3 +619,38 @@ def test_lengths_past_the_block_table_are_clamped():
         got = d.decode(S, seq_lens=too_long)
         assert_close(got, ref, f"clamped S={S}")
         assert_close(d.decode_single(S), ref, f"whole S={S}")
+
+
+def test_append_skips_lengths_past_the_block_table():
+    """The split-K append with a length beyond the sequence's block-table row
+    writes nothing for that sequence (its stored keys stay), while a sequence
+    within its row appends as usual. The appended rows of the long sequence
+    are NaN patterns, so a write anywhere in its pages would show."""
+    w = workloads.make_workload("tiny", lens=(17, 64), num_q_heads=4, num_kv_heads=2,
+                                head_dim=64, seed=21)
+    geom = geometry(w)
+    d = DeviceKV(w, geom)
+    kc, vc = oracle_pools(w, geom)
+    ref = oracle_decode(w, geom, kc, vc)
+    B, Hq, Hkv, D, bs = w.num_seqs, w.num_q_heads, w.num_kv_heads, w.head_dim, w.block_size
+    last = w.last_token_index()
+    rows_k = np.full((B, Hkv * D), POISON["bf16"], np.uint16)
+    rows_v = np.full((B, Hkv * D), POISON["bf16"], np.uint16)
+    rows_k[0] = w.k_bits[last[0]].reshape(-1)            # sequence 0 re-appends its last key
+    rows_v[0] = w.v_bits[last[0]].reshape(-1)
+    key, val = u16_to_dev(rows_k.reshape(-1)), u16_to_dev(rows_v.reshape(-1))
+    q = u16_to_dev(w.q_bits.reshape(-1))
+    bt = i32_to_dev(w.block_tables)
+    lens = i32_to_dev(np.array([17, 5000], np.int32))
+    for S in (1, 3):
+        ws = torch.full((pkd.paged_decode_workspace_bytes(B, Hq, D, S) // 4,), float("nan"),
+                        dtype=torch.float32, device=dev())
+        out = torch.empty((B, Hq, D), dtype=torch.bfloat16, device=dev())
+        pkd.paged_decode_attn_splitk_append_bf16(q, key, val, d.k, d.v, ws, bt, lens,
+                                                 w.max_blocks_per_seq, Hq, Hkv, D, bs,
+                                                 float(w.scale), S, Hq * D, B)
+        pkd.paged_decode_attn_reduce(ws, out, lens, Hq, D, S, B)
+        torch.cuda.synchronize()
+        assert np.array_equal(pool_to_np(d.k, "bf16"), kc), f"K pool changed, S={S}"
+        assert np.array_equal(pool_to_np(d.v, "bf16"), vc), f"V pool changed, S={S}"
+        assert_close(out.float().cpu().numpy().astype(np.float64), ref, f"append clamped S={S}")

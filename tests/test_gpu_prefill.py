@@ -8,7 +8,8 @@ import torch
 import oracle
 import paged_kv_decode_splitk_amd as pkd
 import workloads
-from gpu_cases import (DeviceKV, assert_close, fp8_scales, geometry, oracle_pools,
+from gpu_cases import (DeviceKV, assert_close, fp8_scales, full_size_reference, geometry,
+                       oracle_pools,
                        oracle_prefill, pool_to_np)
 
 pytestmark = pytest.mark.gpu
@@ -176,23 +177,18 @@ def test_deterministic_and_split_invariant():
                                         ("nvfp4", 2)])
 def test_full_size_speculative_verify(name, q_len):
     """Full-size workloads with a q_len-token verify block per sequence, at
-    the split count the heuristic picks; sampled sequences against the
-    oracle."""
-    w = workloads.make_workload(name)
+    the split count the heuristic picks; every sequence against the oracle."""
+    w, geom, ks, vs, kc, vc, _ = full_size_reference(name)
     print(f"[{name} q_len={q_len}] B={w.num_seqs} T={w.num_tokens}", flush=True)
-    geom = geometry(w)
-    ks, vs = fp8_scales(w) if w.kv_dtype == "fp8" else (1.0, 1.0)
     d = DeviceKV(w, geom, ks, vs)
     S = pkd.paged_prefill_num_splits(w.num_seqs, q_len, w.num_q_heads, w.num_kv_heads,
                                      w.max_blocks_per_seq, w.block_size, True,
                                      w.sliding_window, _num_cus())
     q = workloads.query_block(w, q_len, seed=1)
     got = d.prefill(q, q_len, S)
-    order = np.argsort(w.seq_lens)
-    seqs = sorted({int(order[0]), int(order[-1]), int(order[len(order) // 2])})
-    kc, vc = oracle_pools(w, geom, ks, vs, seqs=seqs)
-    ref = oracle_prefill(w, geom, kc, vc, q, q_len, k_scale=ks, v_scale=vs, seqs=seqs)
-    err = assert_close(got[seqs], ref, name)
-    print(f"[{name} q_len={q_len}] num_splits={S} seqs={seqs} max_abs_err={err:.3e}", flush=True)
+    ref = oracle_prefill(w, geom, kc, vc, q, q_len, k_scale=ks, v_scale=vs)
+    err = assert_close(got, ref, name)
+    print(f"[{name} q_len={q_len}] num_splits={S} all {w.num_seqs} seqs max_abs_err={err:.3e}",
+          flush=True)
     del d
     torch.cuda.empty_cache()

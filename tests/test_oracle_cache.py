@@ -112,6 +112,44 @@ def test_nvfp4_write_layout(pad):
         assert np.all(dview[s // bs, s % bs] == 0xEE) and np.all(sview[s // bs, s % bs] == 0xEE)
 
 
+@pytest.mark.parametrize("pad", [(0, 0), (64, 32)])
+def test_read_rows_nvfp4_exact_through_reshape_view(pad):
+    """The NVFP4 branch of read_kv_rows equals, bit for bit, the rows
+    gathered through a reshape view of the page bytes (codes unpacked low
+    nibble first, scales from their own section view) and decoded by
+    nvfp4_decode_groups: no index formula of read_kv_rows is reused."""
+    bs, Hkv, D = 16, 2, 128
+    data = bs * Hkv * D // 2 + pad[0]
+    stride = data + bs * Hkv * D // 16 + pad[1]
+    geom, slots, kb, vb = _setup("nvfp4", bs=bs, Hkv=Hkv, D=D, pages=7, ntok=80, seed=9,
+                                 block_stride_bytes=stride, data_section_bytes=data)
+    kc, vc = new_cache(geom, 0xEE), new_cache(geom, 0xEE)
+    reshape_and_cache(geom, kb, vb, kc, vc, slots)
+    got = oracle.read_kv_rows(geom, kc, slots // bs, slots % bs)
+    pages = kc.reshape(geom.num_pages, stride)
+    dview = pages[:, :bs * Hkv * D // 2].reshape(geom.num_pages, bs, Hkv, D // 2)
+    sview = pages[:, data:data + bs * Hkv * D // 16].reshape(geom.num_pages, bs, Hkv, D // 16)
+    byte = dview[slots // bs, slots % bs]                      # [n, Hkv, D/2]
+    codes = np.stack([byte & 0xF, byte >> 4], axis=-1).reshape(len(slots), Hkv, D // 16, 16)
+    want = F.nvfp4_decode_groups(codes, sview[slots // bs, slots % bs]).reshape(len(slots), Hkv, D)
+    assert np.array_equal(got, want)
+    # and each row is what the group encoder gives for its BF16 source
+    for t in range(len(slots)):
+        src = F.bf16_to_f64(kb[t]).astype(np.float32).reshape(Hkv, D // 16, 16)
+        c, sc = F.nvfp4_encode_groups(src)
+        assert np.array_equal(got[t], F.nvfp4_decode_groups(c, sc).reshape(Hkv, D))
+
+
+def test_read_rows_bf16_exact_through_reshape_view():
+    geom, slots, kb, vb = _setup("bf16", Hkv=4, D=128, pages=5, ntok=60, seed=4)
+    kc, vc = new_cache(geom, 0x7FC0), new_cache(geom, 0x7FC0)
+    reshape_and_cache(geom, kb, vb, kc, vc, slots)
+    got = oracle.read_kv_rows(geom, vc, slots // 16, slots % 16)
+    view = vc.reshape(geom.num_pages, 16, 4, 128)
+    assert np.array_equal(got, F.bf16_to_f64(view[slots // 16, slots % 16]))
+    assert np.array_equal(got, F.bf16_to_f64(vb))
+
+
 def test_read_rows_decodes_fp8_as_code_times_scale():
     geom = CacheGeometry("fp8", 1, 16, 1, 16)
     kc = np.arange(256, dtype=np.uint8)
