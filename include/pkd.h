@@ -62,6 +62,8 @@ extern "C" {
                                   or a split-K launch of more than 2^30 16-key tiles (sequences x
                                   kv heads x the tiles a block-table row or window can hold) */
 #define PKD_ERR_LAUNCH (-3)      /* the HIP runtime reported an error after the launch */
+#define PKD_ERR_SCRATCH (-4)     /* paged_decode_attn_bf16_noalloc: the call needs more than
+                                    PKD_SCRATCH_BYTES of split-K workspace */
 
 #define PKD_MAX_SPLITS 4096u
 
@@ -293,6 +295,27 @@ PKD_API int paged_decode_attn_nvfp4(const uint16_t* q, const uint8_t* k_cache,
                                     uint32_t q_stride, uint64_t block_stride_bytes,
                                     uint64_t data_section_bytes, uint32_t sliding_window,
                                     float* workspace, uint32_t num_splits, hipStream_t stream);
+
+/* For callers that cannot allocate (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): paged_decode_attn_bf16
+ * without the workspace argument. Its split-K partials go to a static device
+ * array of PKD_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends; the call allocates and frees nothing. num_splits
+ * > 1 needs paged_decode_workspace_bytes(num_seqs, num_q_heads, head_dim,
+ * num_splits) <= PKD_SCRATCH_BYTES, else PKD_ERR_SCRATCH (nothing enqueued);
+ * num_splits == 1 uses no scratch. Calls on one GPU share the array: calls
+ * that overlap on one GPU (different streams, not ordered) race, calls in
+ * one stream do not. Other arguments, results and errors as for
+ * paged_decode_attn_bf16. */
+#define PKD_SCRATCH_BYTES (16u << 20)
+PKD_API int paged_decode_attn_bf16_noalloc(const uint16_t* q, const uint16_t* k_cache,
+                                           const uint16_t* v_cache, uint16_t* output,
+                                           const int32_t* block_tables, const int32_t* seq_lens,
+                                           uint32_t max_blocks_per_seq, uint32_t num_seqs,
+                                           uint32_t num_q_heads, uint32_t num_kv_heads,
+                                           uint32_t head_dim, uint32_t block_size, float scale,
+                                           uint32_t q_stride, uint32_t sliding_window,
+                                           uint32_t num_splits, hipStream_t stream);
 
 /* ---------------------------------------------------------------- query blocks
  * Multi-token paged attention over the same block table: q_len query tokens

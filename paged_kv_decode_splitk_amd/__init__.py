@@ -23,7 +23,7 @@ __all__ = [
     "paged_decode_attn_splitk_fp8", "paged_decode_attn_splitk_nvfp4",
     "paged_decode_attn_reduce", "paged_decode_attn_splitk_append_bf16",
     "paged_decode_attn_splitk_append_fp8", "paged_decode_attn_splitk_append_nvfp4",
-    "paged_decode_attn_bf16", "paged_decode_attn_fp8",
+    "paged_decode_attn_bf16", "paged_decode_attn_fp8", "paged_decode_attn_bf16_noalloc",
     "paged_decode_attn_nvfp4", "paged_prefill_attn_bf16", "paged_prefill_attn_fp8",
     "paged_prefill_attn_nvfp4", "paged_prefill_num_splits", "contig_kv_attn_bf16",
     "contig_kv_attn_fp8", "layout_strides",
@@ -69,6 +69,8 @@ _SIGNATURES = {
                                      _F32, _F32, _F32, _U32, _U64, _U32, _P, _U32, _P]),
     "paged_decode_attn_nvfp4": (_INT, [_P, _P, _P, _P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32,
                                        _F32, _U32, _U64, _U64, _U32, _P, _U32, _P]),
+    "paged_decode_attn_bf16_noalloc": (_INT, [_P, _P, _P, _P, _P, _P, _U32, _U32, _U32, _U32, _U32,
+                                              _U32, _F32, _U32, _U32, _U32, _P]),
     "paged_prefill_attn_bf16": (_INT, [_P, _P, _P, _P, _P, _P, _U32, _U32, _U32, _U32, _U32,
                                        _U32, _U32, _F32, _U32, _U32, _U32, _U32, _P, _U32, _P]),
     "paged_prefill_attn_fp8": (_INT, [_P, _P, _P, _P, _P, _P, _U32, _U32, _U32, _U32, _U32, _U32,
@@ -325,6 +327,27 @@ def paged_decode_attn_nvfp4(q, k_cache, v_cache, output, block_tables, seq_lens,
         float(scale), q_stride, block_stride_bytes, data_section_bytes, sliding_window,
         _ptr(workspace), num_splits, _stream(q, stream)),
         "paged_decode_attn_nvfp4")
+
+
+SCRATCH_BYTES = 16 << 20        # PKD_SCRATCH_BYTES
+
+
+def paged_decode_attn_bf16_noalloc(q, k_cache, v_cache, output, block_tables, seq_lens,
+                                   max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads,
+                                   head_dim, block_size, scale, q_stride, sliding_window=0,
+                                   num_splits=None, stream=None):
+    """paged_decode_attn_bf16 with the library's static device scratch as
+    the workspace (no allocation by the caller or the library)."""
+    _need_gpu(q, k_cache, v_cache, output, block_tables, seq_lens)
+    if num_splits is None:
+        num_splits = paged_decode_num_splits(num_seqs, num_q_heads, num_kv_heads,
+                                             max_blocks_per_seq, block_size, sliding_window,
+                                             _num_cus(q))
+    _check(lib().paged_decode_attn_bf16_noalloc(
+        _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(output), _ptr(block_tables), _ptr(seq_lens),
+        max_blocks_per_seq, num_seqs, num_q_heads, num_kv_heads, head_dim, block_size,
+        float(scale), q_stride, sliding_window, num_splits, _stream(q, stream)),
+        "paged_decode_attn_bf16_noalloc")
 
 
 # ---------------------------------------------------------------- split-K with append

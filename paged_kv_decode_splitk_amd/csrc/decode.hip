@@ -28,6 +28,7 @@
 //    LDS with transposed reads, P rounded to BF16 in registers. A quantized V
 //    tile is first dequantized into a BF16 copy in LDS.
 #include <atomic>
+#include <mutex>
 
 #include "../../include/pkd.h"
 #include "device_common.hpp"
@@ -2408,6 +2409,70 @@ extern "C" PKD_API int paged_decode_attn_nvfp4(
   return launch_decode<kNvfp4>(a, output, num_seqs, head_dim, stream);
 }
 
+// ---------------------------------------------------------------------------
+// The BF16 whole decode without a caller workspace. The split-K partials go
+// to `scratch`, a file-scope device array of kScratchBytes that every GPU the
+// library runs on holds until the process ends. In host code the array's
+// name stands for a host-side shadow, not device memory: its device address
+// comes from hipGetSymbolAddress, taken once per device (with that device
+// current) on the first call there, and only that address reaches the
+// kernels. Calls on one GPU share the array; calls that overlap on one GPU
+// (different streams) race. The split-K pass leaves no requirement on the
+// array's contents (the combine reads only slots written in the same call),
+// so nothing is cleared.
+constexpr size_t kScratchBytes = PKD_SCRATCH_BYTES;
+static __device__ __align__(256) float scratch[kScratchBytes / sizeof(float)];
+
+static float* scratch_on_device(int& status) {
+  static std::once_flag once[64];
+  static float* ptr[64];
+  static hipError_t err[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+    status = kLaunch;
+    return nullptr;
+  }
+  std::call_once(once[dev], [dev] {
+    void* p = nullptr;
+    err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    ptr[dev] = static_cast<float*>(p);
+  });
+  if (err[dev] != hipSuccess || ptr[dev] == nullptr) {
+    status = kLaunch;
+    return nullptr;
+  }
+  return ptr[dev];
+}
+
+extern "C" PKD_API int paged_decode_attn_bf16_noalloc(
+    const uint16_t* q, const uint16_t* k_cache, const uint16_t* v_cache, uint16_t* output,
+    const int32_t* block_tables, const int32_t* seq_lens, uint32_t max_blocks_per_seq,
+    uint32_t num_seqs, uint32_t num_q_heads, uint32_t num_kv_heads, uint32_t head_dim,
+    uint32_t block_size, float scale, uint32_t q_stride, uint32_t sliding_window,
+    uint32_t num_splits, hipStream_t stream) {
+  if (num_seqs == 0) return kOk;
+  // the checks of the whole decode, the scratch standing in for the workspace
+  static const uint64_t kAligned = 16;
+  int st = check_single(q, k_cache, v_cache, output, reinterpret_cast<const void*>(kAligned),
+                        block_tables, seq_lens, max_blocks_per_seq, num_q_heads, num_kv_heads,
+                        head_dim, block_size, num_splits, q_stride);
+  if (st) return st;
+  float* ws = nullptr;
+  if (num_splits > 1) {
+    const uint64_t rows = uint64_t(num_seqs) * num_q_heads;     // both factors < 2^32
+    if (rows > kScratchBytes ||
+        rows * num_splits * (uint64_t(head_dim) + 2) * sizeof(float) > kScratchBytes)
+      return kScratch;
+    ws = scratch_on_device(st);
+    if (!ws) return st;
+  }
+  const uint64_t page_bytes = uint64_t(block_size) * num_kv_heads * head_dim * 2;
+  DecodeArgs a = make_args(q, k_cache, v_cache, ws, block_tables, seq_lens, max_blocks_per_seq,
+                           num_q_heads, num_kv_heads, block_size, scale * kLog2e, 1.0f,
+                           num_splits, q_stride, page_bytes, 0, sliding_window, head_dim);
+  return launch_decode<kBf16>(a, output, num_seqs, head_dim, stream);
+}
+
 // Query-block arguments on top of the decode arguments: column chunks over
 // the group's q_len x group columns, the row window widened for a causal
 // window (the first token's keys through the last token's).
@@ -2591,6 +2656,7 @@ extern "C" PKD_API const char* pkd_status_string(int status) {
     case kInvalid: return "invalid argument";
     case kUnsupported: return "unsupported shape";
     case kLaunch: return "kernel launch failed";
+    case kScratch: return "workspace larger than the static scratch";
     default: return "unknown status";
   }
 }

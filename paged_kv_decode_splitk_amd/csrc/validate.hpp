@@ -11,6 +11,7 @@ constexpr int kOk = 0;
 constexpr int kInvalid = -1;
 constexpr int kUnsupported = -2;
 constexpr int kLaunch = -3;
+constexpr int kScratch = -4;       // the call needs more workspace than the static scratch
 constexpr uint32_t kMaxSplits = 4096;
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }

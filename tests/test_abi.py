@@ -66,6 +66,7 @@ def test_status_strings(lib):
     assert pkd.pkd_status_string(-1) == "invalid argument"
     assert pkd.pkd_status_string(-2) == "unsupported shape"
     assert pkd.pkd_status_string(-3) == "kernel launch failed"
+    assert pkd.pkd_status_string(-4) == "workspace larger than the static scratch"
     assert pkd.pkd_status_string(7) == "unknown status"
 
 
@@ -275,3 +276,29 @@ def test_contig_validation(lib):
     odd[4] = 72                               # 72 one-byte codes: not a multiple of 16 bytes
     assert f8(A16, A16, A16, A16, A16, 2, 4, 48, 4, 2, 64, 0.125, 1.0, 1.0, arr(odd), 1, 0, A16,
               2, None) == -1
+
+
+def test_noalloc_validation(lib):
+    """The static-scratch decode validates like the whole decode and rejects
+    a split-K workspace larger than the scratch, before touching the GPU."""
+    f = lib.paged_decode_attn_bf16_noalloc
+    # q, k, v, out, bt, lens, maxb, B, Hq, Hkv, D, bs, scale, q_stride, W, S
+    base = [A16, A16, A16, A16, A16, A16, 64, 2, 32, 8, 128, 16, 0.125, 4096, 0, 8, None]
+
+    def call(**kw):
+        a = list(base)
+        for k, v in kw.items():
+            a[{"out": 3, "S": 15, "Hq": 8, "D": 10, "q": 0, "B": 7}[k]] = v
+        return f(*a)
+
+    assert call(out=None) == -1
+    assert call(Hq=5) == -1
+    assert call(D=96) == -2
+    assert call(S=0) == -2
+    assert call(q=None) == -1
+    # 2 x 32 rows x 1024 slots x 130 floats: 34 MB > 16 MiB
+    assert call(S=1024) == -4
+    # 4096 sequences x 32 rows at 8 slots: 545 MB
+    assert call(B=4096) == -4
+    assert f(None, None, None, None, None, None, 4, 0, 4, 2, 64, 16, 0.125, 256, 0, 2,
+             None) == 0                         # no sequences: a no-op
