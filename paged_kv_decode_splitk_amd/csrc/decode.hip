@@ -199,6 +199,12 @@ struct LdsTraits {
 #ifndef PKD_LDS_NBUF128
 #define PKD_LDS_NBUF128 1
 #endif
+#ifndef PKD_EARLY_K
+#define PKD_EARLY_K 1
+#endif
+#ifndef PKD_EARLY_V
+#define PKD_EARLY_V 0
+#endif
 #ifndef PKD_LDS_NBUF_Q
 #define PKD_LDS_NBUF_Q 1
 #endif
@@ -463,9 +469,9 @@ typedef __attribute__((address_space(3))) uint16_t lds_u16;
 // consecutive chunks of one row: no bank conflicts. Rows of keys outside
 // [lo, khi) become zeros for FP8 (selected when MASK: its codes may be NaN);
 // NVFP4 rows only have NaN scales cleared (their weight is zero).
-template <int FMT, int D, bool MASK>
+template <int FMT, int D, bool MASK, typename AfterRead>
 __device__ __forceinline__ void stage_v(lds_u8* vt, lds_u8* stage, int lane, uint32_t tok0,
-                                        uint32_t lo, uint32_t khi) {
+                                        uint32_t lo, uint32_t khi, AfterRead&& after_read) {
   using T = LdsTraits<FMT, D>;
   constexpr int NQ = 16 * T::BCPR / 64;          // BF16 chunks per lane
   const uint32_t vta = uint32_t(uintptr_t(vt)), sta = uint32_t(uintptr_t(stage));
@@ -481,6 +487,7 @@ __device__ __forceinline__ void stage_v(lds_u8* vt, lds_u8* stage, int lane, uin
       ad[k] = vta + row * T::RB + ((c >> 1) ^ T::swz(row)) * 16 + 8 * (c & 1);
     }
     lds_read_b64<NQ>(w, ad);
+    after_read();
 #pragma unroll
     for (int k = 0; k < NQ; ++k) {
       const uint32_t tok = tok0 + (k * 64 + lane) / T::BCPR;
@@ -490,9 +497,11 @@ __device__ __forceinline__ void stage_v(lds_u8* vt, lds_u8* stage, int lane, uin
   } else {
     // codes 8c .. 8c+7: a quarter of raw chunk c/4; scale group c/2. E2M1
     // codes are always finite, so only the scale can poison a row past the
-    // keys: a NaN scale code (0x7F / 0xFF) becomes 0, every row decodes to
-    // finite values, and the zero weight of a masked key removes it. No
-    // per-row test, so the LDS reads of all chunks issue together.
+    // keys: in a partial tile (MASK) a NaN scale code (0x7F / 0xFF) becomes
+    // 0, every row decodes to finite values, and the zero weight of a masked
+    // key removes it (a key's own scale, as the cache write encodes it, is
+    // never NaN). No per-row test, so the LDS reads of all chunks issue
+    // together.
     (void)tok0;
     (void)lo;
     (void)khi;
@@ -505,9 +514,10 @@ __device__ __forceinline__ void stage_v(lds_u8* vt, lds_u8* stage, int lane, uin
       sad[k] = vta + T::TILE + row * T::SC_ROW + (c >> 1);
     }
     lds_read_fp4_words<NQ>(w, sraw, ad, sad);
+    after_read();
 #pragma unroll
     for (int k = 0; k < NQ; ++k) {
-      const uint32_t sb = (sraw[k] & 0x7Fu) == 0x7Fu ? 0u : sraw[k];
+      const uint32_t sb = (MASK && (sraw[k] & 0x7Fu) == 0x7Fu) ? 0u : sraw[k];
       h[k] = fp4x8_to_f16x8(w[k], _Float16(__builtin_amdgcn_cvt_f32_fp8(sb, 0)));
     }
   }
@@ -716,6 +726,11 @@ __device__ __forceinline__ void stream_tiles(const DecodeArgs& a, StreamLds<FMT,
       }
     }
   }
+  // logit scale of each column: the call's (times log2 e) and, for NVFP4, the
+  // power of two the column's q was shifted down by (exact either way)
+  float lscale[NC];
+#pragma unroll
+  for (int k = 0; k < NC; ++k) lscale[k] = a.logit_scale * qup[k];
 
   lds_u8* const ring3 = (lds_u8*)(sh.ring);
   lds_u8* const stage3 = (lds_u8*)(sh.stage);
@@ -830,12 +845,26 @@ __device__ __forceinline__ void stream_tiles(const DecodeArgs& a, StreamLds<FMT,
 #pragma unroll
         for (int j = 0; j < NC; ++j) sc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
         const uint32_t kta = uint32_t(uintptr_t(kt));
+        // The K slot is free once its rows are in registers (the reads wait
+        // for themselves): for NVFP4 tiles, whose K decode is long, the next K
+        // tile is requested before the decode and the MFMAs (measured: 3% on
+        // the NVFP4 batch, within noise for BF16 and FP8).
+        bool k_issued = false;
+        auto issue_k_early = [&]() {
+          if constexpr (PKD_EARLY_K && FMT == kNvfp4) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue(s, 0, k + NBUF);
+            __builtin_amdgcn_sched_barrier(0);
+            k_issued = true;
+          }
+        };
         if constexpr (FMT == kBf16) {
           u32x4 kv[DW / 32];
           uint32_t ka[DW / 32];
 #pragma unroll
           for (int c = 0; c < DW / 32; ++c) ka[c] = kta + n * T::RB + (((4 * c + g) ^ T::swz(n)) * 16);
           lds_read_b128<DW / 32>(kv, ka);
+          issue_k_early();
 #pragma unroll
           for (int c = 0; c < DW / 32; ++c)
 #pragma unroll
@@ -848,6 +877,7 @@ __device__ __forceinline__ void stream_tiles(const DecodeArgs& a, StreamLds<FMT,
 #pragma unroll
           for (int h = 0; h < DW / 64; ++h) ka[h] = kta + n * T::RB + (((4 * h + g) ^ T::swz(n)) * 16);
           lds_read_b128<DW / 64>(cw, ka);
+          issue_k_early();
 #pragma unroll
           for (int h = 0; h < DW / 64; ++h) {
 #pragma unroll
@@ -872,6 +902,7 @@ __device__ __forceinline__ void stream_tiles(const DecodeArgs& a, StreamLds<FMT,
               sa[h] = kta + T::TILE + n * T::SC_ROW + 2 * j;
             }
             lds_read_fp4_chunks<DW / 128>(cw, s2, ka, sa);
+            issue_k_early();
 #pragma unroll
             for (int h = 0; h < DW / 128; ++h) {
               const _Float16 S0 = _Float16(__builtin_amdgcn_cvt_f32_fp8(s2[h], 0));
@@ -901,8 +932,6 @@ __device__ __forceinline__ void stream_tiles(const DecodeArgs& a, StreamLds<FMT,
               for (int q = 0; q < NC; ++q) sc[q] = mfma_qk<FMT>(kv, qf[q][c], sc[q]);
             }
           }
-#pragma unroll
-          for (int j = 0; j < NC; ++j) sc[j] *= qup[j];
         }
         if constexpr (DS > 1) {
           // the other parts of the head dim: partial logits through LDS,
@@ -920,7 +949,7 @@ __device__ __forceinline__ void stream_tiles(const DecodeArgs& a, StreamLds<FMT,
           sc[0] = sum;
         }
         __builtin_amdgcn_sched_barrier(0);
-        issue(s, 0, k + NBUF);
+        if (!k_issued) issue(s, 0, k + NBUF);
 
         // ---- online softmax (lane: column n, tokens tok0 + 4g + j)
         // The reference m_run follows the running max lazily: it moves only
@@ -939,7 +968,7 @@ __device__ __forceinline__ void stream_tiles(const DecodeArgs& a, StreamLds<FMT,
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const uint32_t tok = tok0 + 4 * g + r;
-            sv[r] = (tok >= c_lo[j] && tok < c_khi) ? sc[j][r] * a.logit_scale : -__builtin_inff();
+            sv[r] = (tok >= c_lo[j] && tok < c_khi) ? sc[j][r] * lscale[j] : -__builtin_inff();
             mx = fmaxf(mx, sv[r]);
           }
           mx = max_over_rows(mx);
@@ -983,14 +1012,20 @@ __device__ __forceinline__ void stream_tiles(const DecodeArgs& a, StreamLds<FMT,
           vsrc = stage3;
           // FP8 codes of masked tokens may be anything (NaN included), so
           // partial tiles select zeros; E2M1 codes are always finite, so a
-          // masked NVFP4 row just takes a zero scale
-          if (FMT == kFp8 && (tok0 < lo || tok0 + 16 > khi))
-            stage_v<FMT, DW, true>(vt, stage3, lane, tok0, lo, khi);
+          // masked NVFP4 row just takes a zero scale. The raw V slot is free
+          // once its codes are in registers: the next V tile is requested
+          // then, before the dequant and the stage writes.
+          auto next_v = [&]() {
+            __builtin_amdgcn_sched_barrier(0);
+            issue(s, 1, k + NBUF);
+            __builtin_amdgcn_sched_barrier(0);
+          };
+          if (tok0 < lo || tok0 + 16 > khi)
+            stage_v<FMT, DW, true>(vt, stage3, lane, tok0, lo, khi, next_v);
           else
-            stage_v<FMT, DW, false>(vt, stage3, lane, tok0, lo, khi);
+            stage_v<FMT, DW, false>(vt, stage3, lane, tok0, lo, khi, next_v);
           wave_lds_fence();
           __builtin_amdgcn_sched_barrier(0);
-          issue(s, 1, k + NBUF);                   // the raw V tile is consumed
         }
         // ---- O^T += V^T P: lane supplies V[4g + n/4][16mt + 4(n%4) .. +4]. The
         // transposed reads are issued as inline asm: the compiler would otherwise
@@ -1002,7 +1037,40 @@ __device__ __forceinline__ void stream_tiles(const DecodeArgs& a, StreamLds<FMT,
 #pragma unroll
             for (int mt = 0; mt < DW / 16; ++mt) st.acc[j][mt] *= alpha[j];
           }
-        {
+        // BF16 rows up to head_dim 128: every transposed read first, then the
+        // next V tile is requested (its slot is free), then the MFMAs.
+        constexpr bool early_v = FMT == kBf16 && PKD_EARLY_V && DW <= 128;
+        if constexpr (early_v) {
+          const int vtok = 4 * g + (n >> 2);
+          const uint32_t vrow = uint32_t(uintptr_t(vsrc)) + vtok * T::BRB + (n & 1) * 8;
+          u32x2 vv[DW / 16];
+#pragma unroll
+          for (int q4 = 0; q4 < DW / 64; ++q4) {
+            uint32_t ad[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              const int mt = 4 * q4 + u;
+              ad[u] = vrow + (((2 * mt + ((n & 3) >> 1)) ^ T::bswz(vtok)) * 16);
+            }
+            asm volatile(
+                "ds_read_b64_tr_b16 %0, %4\n\t"
+                "ds_read_b64_tr_b16 %1, %5\n\t"
+                "ds_read_b64_tr_b16 %2, %6\n\t"
+                "ds_read_b64_tr_b16 %3, %7\n\t"
+                "s_waitcnt lgkmcnt(0)"
+                : "=&v"(vv[4 * q4]), "=&v"(vv[4 * q4 + 1]), "=&v"(vv[4 * q4 + 2]),
+                  "=&v"(vv[4 * q4 + 3])
+                : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+                : "memory");
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          issue(s, 1, k + NBUF);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int mt = 0; mt < DW / 16; ++mt)
+#pragma unroll
+            for (int j = 0; j < NC; ++j) st.acc[j][mt] = mfma_pv<FMT>(vv[mt], pf[j], st.acc[j][mt]);
+        } else {
           const int vtok = 4 * g + (n >> 2);
           const uint32_t vrow = uint32_t(uintptr_t(vsrc)) + vtok * T::BRB + (n & 1) * 8;
 #pragma unroll
@@ -1033,7 +1101,7 @@ __device__ __forceinline__ void stream_tiles(const DecodeArgs& a, StreamLds<FMT,
           }
         }
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (FMT == kBf16) issue(s, 1, k + NBUF);
+        if constexpr (FMT == kBf16 && !early_v) issue(s, 1, k + NBUF);
       }
     }
     wait_vmcnt<0>();                               // the ring restarts with the next segment
