@@ -262,7 +262,13 @@ PKD_API int paged_decode_attn_reduce(const float* workspace, uint16_t* output,
  *   num_splits > 1: the split-K pass and the combine, as two launches on
  *     `stream`; workspace as for the split-K calls
  *     (paged_decode_workspace_bytes). paged_decode_num_splits() gives the
- *     split count to use.
+ *     split count to use. Short rows are the exception: when every
+ *     sequence's keys fit 12 tiles of 16 (by max_blocks_per_seq x
+ *     block_size, or by the window) and all num_seqs x num_kv_heads rows
+ *     are resident at once (BF16 and FP8 rows up to head_dim 256, G <= 16),
+ *     the call runs the num_splits == 1 form in one launch, which is faster
+ *     there (one sequence of 128 keys, 8 kv heads: 6.2 against 7.6 us), and
+ *     leaves the workspace untouched.
  * Sequences with seq_lens[b] == 0 get zeros. Other arguments and errors as
  * for the split-K calls; output must be 16-byte aligned. */
 PKD_API int paged_decode_attn_bf16(const uint16_t* q, const uint16_t* k_cache,

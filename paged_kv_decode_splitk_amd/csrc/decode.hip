@@ -73,6 +73,8 @@ struct DecodeArgs {
                            // contiguous tensors' length): longer seq_lens are clamped
   uint32_t static_q;       // one sequence: Q units per row, unit u streams row u % R, tiles
                            // u / R + Q k (0: the stream partition)
+  uint32_t head_group;     // split-K over a batch: kv heads that share each partition unit's
+                           // tiles, one workgroup each, placed on one XCD (1: none)
   uint16_t* out;           // non-split decode (num_splits 1): BF16 output, else null
   // append: each sequence's new token, written to position L - 1 by the
   // piece that ends the row, before that piece loads its last tile
@@ -1551,7 +1553,9 @@ constexpr int kMaxChunks = (FMT == kBf16 && D <= 128) ? 2 : 1;
 template <int D, int NC, int WQ, typename Piece>
 __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, uint32_t unit, uint32_t P,
                                                bool zero_lead, Piece&& piece) {
-  const uint32_t R = a.num_kv_heads * a.head_chunks;          // rows per sequence
+  // rows per sequence; kv heads in groups of head_group share one row's
+  // pieces, each head its own workgroup
+  const uint32_t R = a.num_kv_heads / a.head_group * a.head_chunks;
   const bool whole = a.num_splits == 1;                       // one unit per row
   // With at most 64 sequences, one length per lane, loaded once: the tile
   // counts, their prefix sums and every row lookup come from these registers.
@@ -1690,7 +1694,7 @@ __global__ __launch_bounds__((64 * kGroupWaves<FMT, D, WI>), (kWavesPerSimd<FMT,
   const uint32_t wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   StreamLds<FMT, D / DS, DS>& mine = sh[GW > 1 ? wv : 0];
   const uint32_t wi = WI > 1 ? wv : 0;
-  const uint32_t unit = blockIdx.x, P = gridDim.x;
+  uint32_t unit = blockIdx.x, P = gridDim.x;
   lds_u8* const xg3 = (lds_u8*)xg;
   lds_f32x2* const mlx3 = (lds_f32x2*)mlx;
   uint32_t xturn = 0;
@@ -1714,10 +1718,25 @@ __global__ __launch_bounds__((64 * kGroupWaves<FMT, D, WI>), (kWavesPerSimd<FMT,
                                      (j == 0 && Q < a.num_splits) ? Q : kNoSlot);
     return;
   }
+  // Kv heads grouped by head_group: the group's workgroups of one unit are 8
+  // apart in the grid (units in runs of 8), so the dispatcher, which deals
+  // workgroups to the 8 XCDs in turn, puts them on one XCD, where the cache
+  // lines their rows share (NVFP4 scale rows, rows shorter than a line) are
+  // fetched from HBM once. The grid is a multiple of 8 * head_group.
+  const uint32_t hg = a.head_group;
+  uint32_t member = 0;
+  if (hg > 1) {
+    member = (unit / 8) % hg;
+    unit = unit / (8 * hg) * 8 + unit % 8;
+    P /= hg;
+  }
   for_each_piece<D, NC, 1>(a, unit, P, wv == 0,
-                           [&](uint32_t b, uint32_t kh, uint32_t tau0, uint32_t tau1,
+                           [&](uint32_t b, uint32_t kg, uint32_t tau0, uint32_t tau1,
                                uint32_t slot, bool last, uint32_t L, bool fits) {
     if (slot >= a.num_splits) return;      // only if a sequence outgrows its block table
+    // the row of kv head (head group, member), column chunk kg % head_chunks
+    const uint32_t kh =
+        hg > 1 ? ((kg / a.head_chunks) * hg + member) * a.head_chunks + kg % a.head_chunks : kg;
     const uint32_t lo = (a.window > 0 && L > a.window) ? L - a.window : 0u;
     const uint32_t t0 = lo / 16 + tau0, t1 = lo / 16 + tau1;   // tiles of the sequence
     WaveState<FMT, D, DS, NC> st;
@@ -2038,6 +2057,21 @@ constexpr uint32_t kRowLead = PKD_ROW_LEAD;
 // T + 3 * rows + 2 * waves stays below 2^32 for T up to 2^30 tiles.
 constexpr uint64_t kMaxLaunchTiles = 1ull << 30;
 
+// Kv heads per head group of a batch's split-K pass: the adjacent heads
+// whose rows share a 128-byte line in their shortest section (the NVFP4
+// scale rows of D/16 bytes; any row shorter than a line), at most 8 and a
+// divisor of the kv heads.
+#ifndef PKD_HEAD_GROUP
+#define PKD_HEAD_GROUP 0
+#endif
+template <int FMT, int D>
+static uint32_t head_group_of(uint32_t num_kv_heads) {
+  constexpr uint32_t row = FMT == kNvfp4 ? D / 16 : (FMT == kFp8 ? D : 2 * D);
+  uint32_t hg = PKD_HEAD_GROUP > 0 ? PKD_HEAD_GROUP : (row >= 128 ? 1u : min(128u / row, 8u));
+  while (hg > 1 && num_kv_heads % hg != 0) hg /= 2;
+  return hg;
+}
+
 // One launch of the stream kernel with NC column chunks per wave, WI
 // interleaving waves per piece (or 1: independent waves).
 template <int FMT, int D, int NC, bool CONTIG, int WI>
@@ -2056,6 +2090,10 @@ static int launch_stream_wi(DecodeArgs a, uint64_t rows, hipStream_t stream) {
     if (a.static_q) {
       a.static_q = uint32_t(max(uint64_t(1), min(cap / rows, uint64_t(a.num_splits))));
       units = rows * a.static_q;
+    } else if (a.head_group > 1) {
+      // partition units in whole runs of 8, head_group workgroups each
+      const uint64_t hg = a.head_group;
+      units = max(uint64_t(8), units / hg / 8 * 8) * hg;
     }
   }
   const uint64_t groups = units;
@@ -2086,6 +2124,7 @@ static int launch_stream(DecodeArgs a, hipStream_t stream) {
     a.static_q = stream_capacity<FMT, D, NC, CONTIG, wis>() / unit_waves >= rows ? 1u : 0u;
   if (a.num_splits == 1 || a.static_q)
     return launch_stream_wi<FMT, D, NC, CONTIG, wis>(a, rows, stream);
+  a.head_group = head_group_of<FMT, D>(a.num_kv_heads);
   return launch_stream_wi<FMT, D, NC, CONTIG, 1>(a, rows, stream);
 }
 
@@ -2194,6 +2233,7 @@ static DecodeArgs make_args(const uint16_t* q, const void* kc, const void* vc, f
   a.row_lead = 0;
   a.max_len = uint32_t(min(uint64_t(max_blocks) * bs, uint64_t(0x7FFFFFFF)));
   a.static_q = 0;
+  a.head_group = 1;
   a.out = nullptr;
   a.new_k = nullptr;
   a.new_v = nullptr;
@@ -2263,18 +2303,56 @@ static int launch_reduce(const float* workspace, uint16_t* output, const int32_t
   return launch_status();
 }
 
-// Non-split decode (num_splits 1): one workgroup per row writes the output. More
-// splits: the split-K pass and the combine, as two launches.
+// Rows of at most this many 16-key tiles (by the block-table width, or the
+// window) are decoded in one launch whatever the split count.
+#ifndef PKD_ONE_LAUNCH_TILES
+#define PKD_ONE_LAUNCH_TILES 12
+#endif
+
+// Whether a decode (one query token) runs faster as the one-launch form:
+// one workgroup of interleaving waves per row, merging in LDS, where the
+// rows are short and all of them are resident at once. The split pass and
+// the combine are two launches of a few dependent round trips each; at one
+// sequence of 8 kv heads they take 7.6 us at 128 keys, the one-launch form
+// 6.2 us, and the two are even at 256 keys (0.8 us per further tile of a
+// wave).
+template <int FMT, int D, bool CONTIG>
+static bool one_launch_fits(const DecodeArgs& a, uint32_t num_seqs) {
+  if constexpr (kMergeWaves<FMT, D, 1> > 1) {
+    constexpr int wi = kMergeWaves<FMT, D, 1>;
+    if (a.q_len != 1 || a.col_chunks != 1) return false;
+    uint64_t tile_bound = uint64_t(a.max_blocks) * (a.block_size / 16);
+    if (a.window > 0) tile_bound = min(tile_bound, uint64_t((a.window + 14) / 16 + 1));
+    const uint64_t rows = uint64_t(num_seqs) * a.num_kv_heads;
+    const uint64_t resident = stream_capacity<FMT, D, 1, CONTIG, wi>() / kGroupWaves<FMT, D, wi>;
+    return tile_bound <= PKD_ONE_LAUNCH_TILES && rows <= resident;
+  }
+  return false;
+}
+
+// Non-split decode (num_splits 1), or a decode of short rows: one workgroup
+// per row writes the output. Otherwise the split-K pass and the combine, as
+// two launches.
 template <int FMT, bool CONTIG = false>
 static int launch_decode(DecodeArgs a, uint16_t* output, uint32_t num_seqs, uint32_t head_dim,
                          hipStream_t stream) {
-  if (a.num_splits > 1) {
+  bool one = a.num_splits == 1;
+  if (!one) {
+    switch (head_dim) {
+      case 64: one = one_launch_fits<FMT, 64, CONTIG>(a, num_seqs); break;
+      case 128: one = one_launch_fits<FMT, 128, CONTIG>(a, num_seqs); break;
+      case 256: one = one_launch_fits<FMT, 256, CONTIG>(a, num_seqs); break;
+      default: break;
+    }
+  }
+  if (!one) {
     const int st = launch_splitk<FMT, CONTIG>(a, num_seqs, head_dim, stream);
     if (st) return st;
     const OutMap om = {a.o_seq, a.o_tok, a.o_head, a.num_q_heads * a.q_len, a.num_q_heads};
     return launch_reduce(a.ws, output, a.seq_lens, om, head_dim, a.num_splits, num_seqs, stream);
   }
   a.out = output;
+  a.num_splits = 1;
   return launch_splitk<FMT, CONTIG>(a, num_seqs, head_dim, stream);
 }
 

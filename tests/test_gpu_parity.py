@@ -419,6 +419,44 @@ def test_whole_decode_graph_replay():
         del graph
 
 
+SHORT_CASES = [
+    # fmt, lens, Hq, Hkv, D, bs, window, one launch expected
+    ("bf16", (128,), 32, 8, 128, 16, 0, True),              # one sequence, 8 tiles per row
+    ("bf16", (0, 5, 190, 64, 17, 100), 32, 8, 128, 16, 0, True),
+    ("fp8", (30, 150, 1), 16, 8, 256, 16, 0, True),
+    ("bf16", (1, 500, 333), 8, 2, 64, 16, 100, True),       # the window bounds the rows
+    ("bf16", (0, 5, 190, 64, 17, 100) * 8, 32, 8, 128, 16, 0, False),   # 384 rows: two launches
+    ("bf16", (40, 250), 32, 8, 128, 16, 0, False),          # 16 tiles per row: two launches
+]
+
+
+@pytest.mark.parametrize("case", SHORT_CASES,
+                         ids=[f"{c[0]}-B{len(c[1])}-D{c[4]}-W{c[6]}" for c in SHORT_CASES])
+def test_whole_decode_short_rows(case):
+    """Short rows (at most 12 tiles by the block-table width or the window),
+    all resident at once: the whole-decode call runs the one-launch form
+    whatever num_splits says, so its output is that of num_splits 1, bit for
+    bit; otherwise the split pass and the combine. Both against the oracle."""
+    fmt, lens, Hq, Hkv, D, bs, window, one = case
+    w = workloads.make_workload("tiny", lens=lens, num_q_heads=Hq, num_kv_heads=Hkv, head_dim=D,
+                                block_size=bs, sliding_window=window, kv_dtype=fmt, seed=len(lens))
+    geom = geometry(w)
+    ks, vs = _fp8_small_scales(w) if fmt == "fp8" else (1.0, 1.0)
+    d = DeviceKV(w, geom, ks, vs)
+    kc, vc = oracle_pools(w, geom, ks, vs)
+    ref = oracle_decode(w, geom, kc, vc, ks, vs)
+    single = d.decode_single(1)
+    assert_close(single, ref, f"{case} S=1")
+    S = pkd.paged_decode_num_splits(w.num_seqs, Hq, Hkv, w.max_blocks_per_seq, bs, window,
+                                    _num_cus())
+    for n_splits in sorted({2, S}):
+        got = d.decode_single(n_splits)
+        assert_close(got, ref, f"{case} S={n_splits}")
+        if one:
+            assert np.array_equal(got, single), f"S={n_splits}: not the one-launch form"
+        assert np.all(got[w.seq_lens == 0] == 0)
+
+
 @pytest.mark.parametrize("name", ["llama8b", "b1_32k", "fp8", "nvfp4"])
 def test_whole_decode_full_size(name):
     w, geom, ks, vs, kc, vc, ref = full_size_reference(name)

@@ -49,3 +49,37 @@ def test_partition_start_up_positions(B, Hq, Hkv, lo, hi, seed, q_len):
         assert_close(d.prefill(q, q_len, S, causal=True), ref, f"query block B={B}")
     del d
     torch.cuda.empty_cache()
+
+
+# NVFP4 batches whose kv heads share cache lines (scale rows of head_dim/16
+# bytes, code rows under 128 bytes): the split-K pass runs the heads of a
+# group as workgroups of one partition unit, 8 apart in the grid. Every head
+# of every sequence is compared, in lengths-in-registers and from-memory
+# batches, with and without a window.
+GROUP_CASES = [
+    # B, Hq, Hkv, D, lo, hi, window, seed
+    (24, 16, 8, 128, 100, 2500, 0, 5),      # groups of 8 heads
+    (70, 8, 4, 64, 50, 1200, 0, 6),         # groups of 4, lengths from memory
+    (12, 16, 2, 512, 300, 4000, 700, 7),    # groups of 2, sliding window
+    (16, 12, 6, 256, 1, 900, 0, 8),         # 6 heads: groups of 2
+]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,D,lo,hi,window,seed", GROUP_CASES)
+def test_nvfp4_head_groups(B, Hq, Hkv, D, lo, hi, window, seed):
+    lens = tuple(int(x) for x in np.random.default_rng(seed).integers(lo, hi, B, endpoint=True))
+    print(f"[head groups] nvfp4 B={B} Hq={Hq} Hkv={Hkv} D={D} lens U[{lo},{hi}] W={window} "
+          f"seed={seed}", flush=True)
+    w = workloads.make_workload("nvfp4", lens=lens, num_q_heads=Hq, num_kv_heads=Hkv,
+                                head_dim=D, sliding_window=window, seed=200 + seed)
+    geom = geometry(w)
+    d = DeviceKV(w, geom)
+    kc, vc = oracle_pools(w, geom)
+    ref = oracle_decode(w, geom, kc, vc)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    import paged_kv_decode_splitk_amd as pkd
+    S = pkd.paged_decode_num_splits(B, Hq, Hkv, w.max_blocks_per_seq, w.block_size, window, cus)
+    for n_splits in (S, 5):
+        assert_close(d.decode(n_splits), ref, f"nvfp4 head groups S={n_splits}")
+    del d
+    torch.cuda.empty_cache()
