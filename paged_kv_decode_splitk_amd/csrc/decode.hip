@@ -190,10 +190,14 @@ struct LdsTraits {
   static constexpr int RPI = 64 / CPR;           // rows per load instruction
   static constexpr int NI = RPI >= 16 ? 1 : 16 / RPI;   // load instructions per tile
   static constexpr int TILE = NI * 1024;         // LDS bytes of the codes of a tile
-  // NVFP4 group scales: 16 rows of D/16 bytes, one load of 16-byte or 4-byte pieces
+  // NVFP4 group scales: 16 rows of D/16 bytes in one load, of 4-byte pieces
+  // for rows up to 16 bytes (the wave's 64 lanes then write no more LDS than
+  // the 256 bytes of scales: 2.4% off the NVFP4 batch's split pass against
+  // 16-byte pieces, 48 of whose lanes wrote zeros), else 16-byte pieces
   static constexpr int SC_ROW = D / 16;
-  static constexpr int SC_SIZE = SC_ROW >= 16 ? 16 : 4;
+  static constexpr int SC_SIZE = SC_ROW > 16 ? 16 : 4;
   static constexpr int SC_LPR = SC_ROW / SC_SIZE;       // lanes per scale row
+  static_assert(FMT != kNvfp4 || 16 * SC_LPR <= 64, "one load covers the 16 scale rows");
   static constexpr int SC_TILE = FMT == kNvfp4 ? 64 * SC_SIZE : 0;
   static constexpr int KV = TILE + SC_TILE;      // LDS bytes of one K or V tile
   static constexpr int NDMA = NI + (FMT == kNvfp4 ? 1 : 0);   // load instructions per tile
