@@ -49,6 +49,7 @@ DESCRIPTIONS = {
     "b1_8k": "B=1 BF16 decode at 8K context: 32 q / 8 kv heads, head_dim 128, block 16",
     "b1_4k": "B=1 BF16 decode at 4K context: 32 q / 8 kv heads, head_dim 128, block 16",
     "b1_1k": "B=1 BF16 decode at 1K context: 32 q / 8 kv heads, head_dim 128, block 16",
+    "b1_128": "B=1 BF16 decode at 128 keys: 32 q / 8 kv heads, head_dim 128, block 16",
     "fp8": "FP8-E4M3 KV decode: B=64, 16 q / 8 kv heads, head_dim 256, block 16, "
            "seq_lens U[1K, 8K], sliding window 4096",
     "nvfp4": "NVFP4 KV decode: B=16, 16 q / 2 kv heads, head_dim 512, block 16, "
@@ -229,6 +230,20 @@ class Layers:
         pkd.paged_decode_attn_reduce(self.ws, self.out, self.lens, w.num_q_heads, w.head_dim,
                                      self.num_splits, w.num_seqs)
 
+    def whole(self, layer, num_splits):
+        """The whole-decode call without the cache write: num_splits 1 is the
+        one-launch form; with the split heuristic's count the library runs the
+        split pass and the combine, or the one-launch form for short rows."""
+        import paged_kv_decode_splitk_amd as pkd
+        w = self.w
+        assert w.kv_dtype == "bf16"
+        pkd.paged_decode_attn_bf16(self.q, self.k[layer], self.v[layer], self.out, self.bt,
+                                   self.lens, w.max_blocks_per_seq, w.num_seqs, w.num_q_heads,
+                                   w.num_kv_heads, w.head_dim, w.block_size, float(w.scale),
+                                   w.num_q_heads * w.head_dim, sliding_window=w.sliding_window,
+                                   workspace=self.ws if num_splits > 1 else None,
+                                   num_splits=num_splits)
+
     def step_single(self, layer):
         """Write the new token's K/V, then the non-split decode (one launch)."""
         self._write(self.new_key, self.new_val, self.k[layer], self.v[layer], self.new_slots)
@@ -328,7 +343,7 @@ def _steps_time(fn, NL, steps):
     return a.elapsed_time(b) / steps
 
 
-def time_workload(name, steps, warmup, kernel_reps=100, single=True):
+def time_workload(name, steps, warmup, kernel_reps=100, single=True, whole=False):
     import torch
     import workloads
     w = workloads.make_workload(name)
@@ -353,6 +368,14 @@ def time_workload(name, steps, warmup, kernel_reps=100, single=True):
     single_ms = _graph_time(lambda i: lay.decode(i % NL), kernel_reps, 3) if single else nan
     k_ms = _graph_time(lambda i: lay.splitk_append(i % NL), kernel_reps, 3)
     plain_ms = _graph_time(lambda i: lay.splitk(i % NL), kernel_reps, 3)
+    whole_one_ms = whole_ms = nan
+    if whole:
+        # the whole-decode call (no cache write), back to back over the layers
+        for i in range(NL):
+            lay.whole(i, 1)
+            lay.whole(i, lay.num_splits)
+        whole_one_ms = _graph_time(lambda i: lay.whole(i % NL, 1), kernel_reps, 3)
+        whole_ms = _graph_time(lambda i: lay.whole(i % NL, lay.num_splits), kernel_reps, 3)
 
     kv_bytes = attended_tokens(w) * kv_bytes_per_token(w)
     gbs = lambda ms: kv_bytes / (ms * 1e-3) / 1e9
@@ -368,6 +391,7 @@ def time_workload(name, steps, warmup, kernel_reps=100, single=True):
         non_split_us_per_step=ms_single * 1e3, non_split_kv_gbs=gbs(ms_single),
         non_split_kernel_us=single_ms * 1e3, non_split_kernel_gbs=gbs(single_ms),
         splitk_us=k_ms * 1e3, splitk_gbs=gbs(k_ms),
+        whole_decode_us=whole_ms * 1e3, whole_decode_one_launch_us=whole_one_ms * 1e3,
         k_scale=lay.k_scale, v_scale=lay.v_scale,
     )
     res["pct_of_peak"] = 100.0 * res["kv_gbs"] / PEAK_HBM_GBS
@@ -726,7 +750,7 @@ def cpu_baseline(w, budget_s=12.0, max_seqs=None, k_scale=1.0, v_scale=1.0, max_
 
 # Bounded oracle samples beside each extra workload: (seconds, sequences).
 CPU_SAMPLES = {"b1_32k": (6.0, None), "fp8": (6.0, 8), "nvfp4": (6.0, 4),
-               "b1_1k": (1.5, None), "b1_4k": (1.5, None), "b1_8k": (1.5, None),
+               "b1_128": (0.5, None), "b1_1k": (1.5, None), "b1_4k": (1.5, None), "b1_8k": (1.5, None),
                "b1_16k": (2.0, None)}
 
 
@@ -748,8 +772,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=40)
     ap.add_argument("--workload", default="llama8b")
     ap.add_argument("--extra", nargs="*", default=["b1_32k", "fp8", "nvfp4"])
-    ap.add_argument("--sweep", nargs="*", default=["b1_1k", "b1_4k", "b1_8k", "b1_16k"],
-                    help="B=1 context sweep: step and split-K kernel per context")
+    ap.add_argument("--sweep", nargs="*", default=["b1_128", "b1_1k", "b1_4k", "b1_8k", "b1_16k"],
+                    help="B=1 context sweep: step, split-K kernel and whole-decode call per "
+                         "context")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--copy-calibration", action="store_true")
@@ -828,12 +853,14 @@ def main():
 
     sweep = {}
     for name in args.sweep:
-        r, wx = time_workload(name, args.steps, args.warmup, single=False)
+        r, wx = time_workload(name, args.steps, args.warmup, single=False, whole=True)
         sweep[name] = {k: r[k] for k in ("us_per_step", "kv_gbs", "pct_of_peak", "splitk_us",
                                          "splitk_gbs", "splitk_plain_us", "splitk_plain_gbs",
+                                         "whole_decode_us", "whole_decode_one_launch_us",
                                          "num_splits", "kv_bytes_per_step")}
         print(f"bench: sweep {name} {r['us_per_step']:.2f} us/step, split-K "
-              f"{r['splitk_plain_us']:.2f} us {r['splitk_plain_gbs']:.0f} GB/s",
+              f"{r['splitk_plain_us']:.2f} us {r['splitk_plain_gbs']:.0f} GB/s, whole decode "
+              f"{r['whole_decode_us']:.2f} us (one launch {r['whole_decode_one_launch_us']:.2f})",
               file=sys.stderr, flush=True)
         sweep[name]["cpu_baseline"] = side_baseline(name, r, wx)
         del wx

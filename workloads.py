@@ -14,7 +14,7 @@ log; values are i.i.d. normal draws, because no dataset is involved):
                block table = a random permutation of 8 pages laid out 2 x 4.
 * ``llama8b``  32 seqs, lens uniform in [512, 4096], 32 q / 8 kv heads,
                head_dim 128, block 16, shuffled page pool.
-* ``b1_<ctx>`` 1 seq of ctx tokens (1K..32K), 32 q / 8 kv heads, head_dim 128.
+* ``b1_<ctx>`` 1 seq of ctx tokens (128, 1K..32K), 32 q / 8 kv heads, head_dim 128.
 * ``fp8``      64 seqs, lens uniform in [1K, 8K], 16 q / 8 kv heads,
                head_dim 256, sliding window 4096, K/V ~ N(0, 2^2).
 * ``nvfp4``    16 seqs, lens uniform in [2K, 16K], 16 q / 2 kv heads,
@@ -96,6 +96,7 @@ _SPECS = {
 }
 for _ctx in (1024, 4096, 8192, 16384, 32768):
     _SPECS[f"b1_{_ctx // 1024}k"] = ("bf16", 1, 32, 8, 128, 16, ("fixed", (_ctx,)), 0, 1.0, 2, ())
+_SPECS["b1_128"] = ("bf16", 1, 32, 8, 128, 16, ("fixed", (128,)), 0, 1.0, 2, ())
 
 WORKLOADS = dict(_SPECS)
 
