@@ -703,6 +703,31 @@ def traffic_record(name, tag):
         return None
 
 
+def counters_record(name):
+    """SQ-counter utilization of the split-K pass from the committed rocprofv3
+    summary (profiles/counters_splitk_<workload>.txt), used only while the
+    kernel sources still hash to what was profiled; None otherwise."""
+    path = os.path.join(ROOT, "profiles", f"counters_splitk_{name}.txt")
+    if not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip().split()[0]
+    if rec.get("source_hash") != source_hash():
+        return None
+    keys = ("valu_busy_pct_of_simd_cycles", "mfma_busy_pct_of_simd_cycles",
+            "valu_insts_per_wave_tile", "wave_cycles_issuing_pct", "wave_cycles_waiting_any_pct",
+            "lds_bank_conflict_cycles_pct_of_cu_cycles")
+    try:
+        out = {k: float(rec[k]) for k in keys}
+    except (KeyError, ValueError):
+        return None
+    out["source"] = f"profiles/counters_splitk_{name}.txt"
+    return out
+
+
 def cpu_baseline(w, budget_s=12.0, max_seqs=None, k_scale=1.0, v_scale=1.0, max_reps=50):
     """The float64 oracle on the host: decode steps of a sample of the
     workload's sequences (the first `max_seqs`, or all), repeated until the
@@ -895,7 +920,7 @@ def main():
     roofline = dict(bound="hbm", achieved=achieved, peak=PEAK_HBM_GBS, unit="GB/s",
                     frac=achieved / PEAK_HBM_GBS, traffic=traffic, kernel=kernel,
                     algorithmic_bytes_per_launch=main_res["kv_bytes_per_step"],
-                    avg_launch_us=us)
+                    avg_launch_us=us, sq_counters=counters_record(args.workload))
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, budget_s=args.cpu_budget)
@@ -941,7 +966,8 @@ def main():
             bound="hbm", achieved=ach, peak=PEAK_HBM_GBS, unit="GB/s", frac=ach / PEAK_HBM_GBS,
             traffic=traffic_record(name, "splitk"),
             kernel=f"paged_decode_attn_splitk_append_{r['kv_dtype']}",
-            algorithmic_bytes_per_launch=r["kv_bytes_per_step"], avg_launch_us=r["splitk_us"])
+            algorithmic_bytes_per_launch=r["kv_bytes_per_step"], avg_launch_us=r["splitk_us"],
+            sq_counters=counters_record(name))
     if sweep:
         line["b1_sweep"] = sweep
     if verify:
