@@ -29,6 +29,9 @@ CASES = [
     ("fp8", "bhld", (1, 17, 300, 1000), 1, 16, 8, 256, 1, 129, 5),
     ("fp8", "bhld", (40, 333), 4, 8, 1, 128, 1, 60, 1),
     ("fp8", "blhd", (40, 100), 2, 16, 2, 512, 1, 0, 2),
+    # FP8 rows of 64 bytes: the split pass runs kv heads in groups of two
+    ("fp8", "bhld", (5, 300, 0, 777, 64), 1, 16, 4, 64, 0, 0, 5),
+    ("fp8", "blhd", (5, 300, 0, 777, 64), 1, 8, 8, 64, 0, 200, 9),
 ]
 
 

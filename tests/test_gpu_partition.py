@@ -83,3 +83,27 @@ def test_nvfp4_head_groups(B, Hq, Hkv, D, lo, hi, window, seed):
         assert_close(d.decode(n_splits), ref, f"nvfp4 head groups S={n_splits}")
     del d
     torch.cuda.empty_cache()
+
+
+def test_fp8_head_groups():
+    """FP8 rows of head_dim 64 are 64 bytes: two kv heads share each line, and
+    the split pass groups them in pairs (lengths in registers and from memory)."""
+    import oracle
+    import paged_kv_decode_splitk_amd as pkd
+    for B, seed in ((24, 11), (80, 12)):
+        lens = tuple(int(x) for x in np.random.default_rng(seed).integers(0, 1500, B))
+        print(f"[head groups] fp8 B={B} Hkv=4 D=64 seed={seed}", flush=True)
+        w = workloads.make_workload("fp8", lens=lens, num_q_heads=16, num_kv_heads=4,
+                                    head_dim=64, sliding_window=0, seed=300 + seed)
+        ks = np.float32(oracle.bf16_absmax(w.k_bits) / np.float32(448.0))
+        vs = np.float32(oracle.bf16_absmax(w.v_bits) / np.float32(448.0))
+        geom = geometry(w)
+        d = DeviceKV(w, geom, ks, vs)
+        kc, vc = oracle_pools(w, geom, ks, vs)
+        ref = oracle_decode(w, geom, kc, vc, ks, vs)
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        S = pkd.paged_decode_num_splits(B, 16, 4, w.max_blocks_per_seq, w.block_size, 0, cus)
+        for n_splits in (S, 3):
+            assert_close(d.decode(n_splits), ref, f"fp8 head groups B={B} S={n_splits}")
+        del d
+        torch.cuda.empty_cache()
