@@ -379,7 +379,12 @@ __device__ __forceinline__ void lds_write_b128(uint32_t ad, u32x4 v) {
 // first(r) being the position of the row's first tile. The wave that ends a
 // row marks the row's later slots empty. With S == 1, wave w takes row w
 // whole. Every wave gets the same number of positions whatever the length mix
-// of the batch.
+// of the batch. ("Wave" here is the partition unit: one workgroup, whose
+// waves may split the head dim or interleave a piece's tiles.) Adjacent kv
+// heads whose rows share cache lines may be partitioned as one row group,
+// each member streaming the same tiles of its own row (head_group). One
+// sequence without a window skips this partition for a fixed one that does
+// not depend on the length (static_q).
 
 __device__ __forceinline__ uint32_t row_tiles(uint32_t L, uint32_t window) {
   if (L == 0) return 0;
@@ -1547,13 +1552,14 @@ constexpr int kWavesPerSimd =
 template <int FMT, int D>
 constexpr int kMaxChunks = (FMT == kBf16 && D <= 128) ? 2 : 1;
 
-// The pieces of partition unit `unit` of the P units of a launch (a
-// workgroup, or one of its waves when they stream independently) under the
-// stream partition (rows of R per sequence), in order: piece(b, kh, tau0,
-// tau1, slot, last, L, can_append) for each (can_append: the sequence's length
-// is within its block-table row, so its new token has a position to go to);
-// with num_splits 1 the unit takes row `unit` whole, and for a sequence
-// without keys writes zeros if `zero_lead` (the unit's lead wave).
+// The pieces of partition unit `unit` of the P units of a launch (one
+// workgroup) under the stream partition (rows of R per sequence; with kv-head
+// groups, a row stands for the group's head_group rows and kh is the group's
+// row index), in order: piece(b, kh, tau0, tau1, slot, last, L, can_append)
+// for each (can_append: the sequence's length is within its block-table row,
+// so its new token has a position to go to); with num_splits 1 the unit takes
+// row `unit` whole, and for a sequence without keys writes zeros if
+// `zero_lead` (the unit's lead wave).
 template <int D, int NC, int WQ, typename Piece>
 __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, uint32_t unit, uint32_t P,
                                                bool zero_lead, Piece&& piece) {
@@ -1665,12 +1671,10 @@ __device__ __forceinline__ void for_each_piece(const DecodeArgs& a, uint32_t uni
 
 // Waves of a workgroup that share a piece by interleaving its tiles (wave i
 // takes tiles i, i + WI, ...) and merge their states in LDS before one
-// workspace write: four for BF16 and FP8 rows of one column chunk up to
-// head_dim 256 (one wave per SIMD of a CU), so a launch writes a quarter of the
-// partials and the combine reads a quarter of the slots.
-// Waves that interleave the tiles of one piece where the rows allow it: one
-// per SIMD of a CU for BF16 and FP8 rows up to head_dim 256 of one column
-// chunk (a wave's ring then holds its O^T for the merge).
+// workspace write: four, one per SIMD of a CU, for BF16 and FP8 rows of one
+// column chunk up to head_dim 256 (a wave's ring then holds its O^T for the
+// merge). A launch then writes a quarter of the partials and the combine
+// reads a quarter of the slots.
 template <int FMT, int D, int NC>
 constexpr int kMergeWaves = (kDSplit<FMT, D> == 1 && FMT != kNvfp4 && NC == 1) ? 4 : 1;
 
