@@ -8,8 +8,11 @@
 // softmax state (m, l) to a float32 workspace [head_dim values, m, l]; one
 // combine merges them into BF16 with a 1e-20 guard on the denominator.
 //
-// Work unit: one wavefront per piece of a (sequence, kv head, chunk of up to
-// 16 query columns) row. A kv head's columns are its group's q heads, times
+// Work unit: a piece of a (sequence, kv head, chunk of up to 16 query
+// columns) row, streamed by one wavefront (by two that split a head_dim of
+// 512, or by four that take its tiles in turn and merge in LDS for one
+// sequence and for the one-launch decode). A kv head's columns are its
+// group's q heads, times
 // the q_len tokens of a query block (pegainfer issue #1008, the paged prefill
 // launch; AstrAI log, the unified causal offset): all of them are served by
 // the one pass over its pages, so each K/V byte leaves HBM once per step
@@ -19,14 +22,16 @@
 //  * K and V tiles stream from HBM into an LDS ring with direct-to-LDS buffer
 //    loads, one block-table lookup per tile.
 //  * S = K . Q^T on v_mfma_f32_16x16x32_bf16 (M = keys, N = query columns,
-//    K = head_dim; columns beyond the group's are zero). FP8 / NVFP4 K codes
-//    are dequantized to BF16 in registers on their way from LDS to the MFMA
-//    (exact: every E4M3 value and every E2M1 x E4M3 product is a BF16 value).
+//    K = head_dim; columns beyond the group's are zero). FP8 K codes are
+//    dequantized to BF16 and NVFP4 codes to FP16 (whose MFMAs that format
+//    uses) in registers on their way from LDS to the MFMA (exact: every E4M3
+//    value is a BF16 value, every E2M1 x E4M3 product an FP16 value).
 //  * Online softmax in fp32 on the MFMA output layout (lane l: head l%16,
 //    tokens 4g..4g+3), exp2 with log2(e) folded into the logit scale.
 //  * O^T[dim][head] += V^T . P on v_mfma_f32_16x16x16_bf16, V^T read from
-//    LDS with transposed reads, P rounded to BF16 in registers. A quantized V
-//    tile is first dequantized into a BF16 copy in LDS.
+//    LDS with transposed reads, P rounded to BF16 in registers (FP16 for
+//    NVFP4). A quantized V tile is first dequantized into a 16-bit copy in
+//    LDS.
 #include <atomic>
 #include <mutex>
 
@@ -207,9 +212,6 @@ struct LdsTraits {
 #endif
 #ifndef PKD_EARLY_K
 #define PKD_EARLY_K 1
-#endif
-#ifndef PKD_EARLY_V
-#define PKD_EARLY_V 0
 #endif
 #ifndef PKD_LDS_NBUF_Q
 #define PKD_LDS_NBUF_Q 1
@@ -1048,71 +1050,36 @@ __device__ __forceinline__ void stream_tiles(const DecodeArgs& a, StreamLds<FMT,
 #pragma unroll
             for (int mt = 0; mt < DW / 16; ++mt) st.acc[j][mt] *= alpha[j];
           }
-        // BF16 rows up to head_dim 128: every transposed read first, then the
-        // next V tile is requested (its slot is free), then the MFMAs.
-        constexpr bool early_v = FMT == kBf16 && PKD_EARLY_V && DW <= 128;
-        if constexpr (early_v) {
-          const int vtok = 4 * g + (n >> 2);
-          const uint32_t vrow = uint32_t(uintptr_t(vsrc)) + vtok * T::BRB + (n & 1) * 8;
-          u32x2 vv[DW / 16];
+        const int vtok = 4 * g + (n >> 2);
+        const uint32_t vrow = uint32_t(uintptr_t(vsrc)) + vtok * T::BRB + (n & 1) * 8;
 #pragma unroll
-          for (int q4 = 0; q4 < DW / 64; ++q4) {
-            uint32_t ad[4];
+        for (int q4 = 0; q4 < DW / 64; ++q4) {
+          uint32_t ad[4];
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const int mt = 4 * q4 + u;
-              ad[u] = vrow + (((2 * mt + ((n & 3) >> 1)) ^ T::bswz(vtok)) * 16);
-            }
-            asm volatile(
-                "ds_read_b64_tr_b16 %0, %4\n\t"
-                "ds_read_b64_tr_b16 %1, %5\n\t"
-                "ds_read_b64_tr_b16 %2, %6\n\t"
-                "ds_read_b64_tr_b16 %3, %7\n\t"
-                "s_waitcnt lgkmcnt(0)"
-                : "=&v"(vv[4 * q4]), "=&v"(vv[4 * q4 + 1]), "=&v"(vv[4 * q4 + 2]),
-                  "=&v"(vv[4 * q4 + 3])
-                : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
-                : "memory");
+          for (int u = 0; u < 4; ++u) {
+            const int mt = 4 * q4 + u;
+            ad[u] = vrow + (((2 * mt + ((n & 3) >> 1)) ^ T::bswz(vtok)) * 16);
           }
-          __builtin_amdgcn_sched_barrier(0);
-          issue(s, 1, k + NBUF);
-          __builtin_amdgcn_sched_barrier(0);
+          // four transposed reads and their wait in one statement: the outputs
+          // exist only after the wait, so no consumer can be scheduled earlier
+          u32x2 vv[4];
+          asm volatile(
+              "ds_read_b64_tr_b16 %0, %4\n\t"
+              "ds_read_b64_tr_b16 %1, %5\n\t"
+              "ds_read_b64_tr_b16 %2, %6\n\t"
+              "ds_read_b64_tr_b16 %3, %7\n\t"
+              "s_waitcnt lgkmcnt(0)"
+              : "=&v"(vv[0]), "=&v"(vv[1]), "=&v"(vv[2]), "=&v"(vv[3])
+              : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+              : "memory");
 #pragma unroll
-          for (int mt = 0; mt < DW / 16; ++mt)
+          for (int u = 0; u < 4; ++u)
 #pragma unroll
-            for (int j = 0; j < NC; ++j) st.acc[j][mt] = mfma_pv<FMT>(vv[mt], pf[j], st.acc[j][mt]);
-        } else {
-          const int vtok = 4 * g + (n >> 2);
-          const uint32_t vrow = uint32_t(uintptr_t(vsrc)) + vtok * T::BRB + (n & 1) * 8;
-#pragma unroll
-          for (int q4 = 0; q4 < DW / 64; ++q4) {
-            uint32_t ad[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const int mt = 4 * q4 + u;
-              ad[u] = vrow + (((2 * mt + ((n & 3) >> 1)) ^ T::bswz(vtok)) * 16);
-            }
-            // four transposed reads and their wait in one statement: the outputs
-            // exist only after the wait, so no consumer can be scheduled earlier
-            u32x2 vv[4];
-            asm volatile(
-                "ds_read_b64_tr_b16 %0, %4\n\t"
-                "ds_read_b64_tr_b16 %1, %5\n\t"
-                "ds_read_b64_tr_b16 %2, %6\n\t"
-                "ds_read_b64_tr_b16 %3, %7\n\t"
-                "s_waitcnt lgkmcnt(0)"
-                : "=&v"(vv[0]), "=&v"(vv[1]), "=&v"(vv[2]), "=&v"(vv[3])
-                : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
-                : "memory");
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-#pragma unroll
-              for (int j = 0; j < NC; ++j)
-                st.acc[j][4 * q4 + u] = mfma_pv<FMT>(vv[u], pf[j], st.acc[j][4 * q4 + u]);
-          }
+            for (int j = 0; j < NC; ++j)
+              st.acc[j][4 * q4 + u] = mfma_pv<FMT>(vv[u], pf[j], st.acc[j][4 * q4 + u]);
         }
         __builtin_amdgcn_sched_barrier(0);
-        if constexpr (FMT == kBf16 && !early_v) issue(s, 1, k + NBUF);
+        if constexpr (FMT == kBf16) issue(s, 1, k + NBUF);
       }
     }
     wait_vmcnt<0>();                               // the ring restarts with the next segment
@@ -1150,7 +1117,7 @@ __device__ __forceinline__ void finish_piece(const DecodeArgs& a, StreamLds<FMT,
   const int w = DS > 1 ? wv : 0;                 // head-dim part
   const int wi = WI > 1 ? wv : 0;                // interleaved wave
   // the wave that writes the piece's (m, l) and end marker: the first of the
-  // waves sharing the piece (every wave when the waves stream independently)
+  // waves sharing the piece
   const bool lead = (DS > 1 ? w : wi) == 0;
   const int g = lane >> 4, n = lane & 15;
   const uint32_t kvh = kh / a.head_chunks, hc = kh % a.head_chunks;
