@@ -62,6 +62,7 @@ GROUP_CASES = [
     (70, 8, 4, 64, 50, 1200, 0, 6),         # groups of 4, lengths from memory
     (12, 16, 2, 512, 300, 4000, 700, 7),    # groups of 2, sliding window
     (16, 12, 6, 256, 1, 900, 0, 8),         # 6 heads: groups of 2
+    (5, 40, 2, 128, 10, 900, 0, 9),         # G = 20: two column chunks per kv head
 ]
 
 
