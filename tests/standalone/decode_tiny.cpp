@@ -163,6 +163,57 @@ int main(int argc, char** argv) {
   HIP_OK(hipMemcpy(got.data(), out, got.size() * 2, hipMemcpyDeviceToHost));
   ok = close(got, g.out, "whole decode, num_splits 1") && ok;
 
+  // the decode step with the cache write folded in: a cache holding every
+  // token but each sequence's last, then the split-K pass that appends it
+  {
+    std::vector<int32_t> first_slots(g.slot_mapping);
+    std::vector<uint16_t> last_k, last_v;
+    uint32_t t0 = 0;
+    for (uint32_t b = 0; b < g.B; ++b) {
+      const uint32_t L = uint32_t(g.seq_lens[b]);
+      const uint32_t last = t0 + L - 1;                // sequences of the fixture are not empty
+      first_slots[last] = -1;                           // a negative slot is skipped
+      last_k.insert(last_k.end(), &g.k[size_t(last) * row], &g.k[size_t(last + 1) * row]);
+      last_v.insert(last_v.end(), &g.v[size_t(last) * row], &g.v[size_t(last + 1) * row]);
+      t0 += L;
+    }
+    uint16_t *kc2, *vc2, *lk, *lv;
+    int32_t* slots2;
+    if (upload(&kc2, nan_pool) || upload(&vc2, nan_pool) || upload(&slots2, first_slots) ||
+        upload(&lk, last_k) || upload(&lv, last_v))
+      return 2;
+    PKD_CALL(reshape_and_cache_bf16(k, v, kc2, vc2, slots2, g.T, g.Hkv, g.D, g.bs, row, row,
+                                    nullptr));
+    const uint32_t S = 3;
+    float* ws;
+    HIP_OK(hipMalloc(reinterpret_cast<void**>(&ws), paged_decode_workspace_bytes(g.B, g.Hq, g.D, S)));
+    HIP_OK(hipMemset(out, 0xFF, got.size() * 2));
+    PKD_CALL(paged_decode_attn_splitk_append_bf16(q, lk, lv, kc2, vc2, ws, bt, lens, g.max_blocks,
+                                                g.Hq, g.Hkv, g.D, g.bs, g.scale, S, g.Hq * g.D, row,
+                                                row, g.B, 0, nullptr));
+    PKD_CALL(paged_decode_attn_reduce(ws, out, lens, g.Hq, g.D, S, g.B, nullptr));
+    HIP_OK(hipDeviceSynchronize());
+    HIP_OK(hipMemcpy(got.data(), out, got.size() * 2, hipMemcpyDeviceToHost));
+    ok = close(got, g.out, "split-K with append + combine") && ok;
+    std::vector<uint16_t> kh2(pool), vh2(pool);
+    HIP_OK(hipMemcpy(kh2.data(), kc2, pool * 2, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(vh2.data(), vc2, pool * 2, hipMemcpyDeviceToHost));
+    const bool same = kh2 == kw && vh2 == vw;
+    std::printf("%-34s %s\n", "appended cache bytes", same ? "ok" : "FAIL");
+    ok = ok && same;
+    for (void* p2 : {static_cast<void*>(kc2), static_cast<void*>(vc2), static_cast<void*>(lk),
+                     static_cast<void*>(lv), static_cast<void*>(slots2), static_cast<void*>(ws)})
+      HIP_OK(hipFree(p2));
+  }
+
+  // the whole decode on the library's static scratch (no workspace argument)
+  HIP_OK(hipMemset(out, 0xFF, got.size() * 2));
+  PKD_CALL(paged_decode_attn_bf16_noalloc(q, kc, vc, out, bt, lens, g.max_blocks, g.B, g.Hq, g.Hkv,
+                                        g.D, g.bs, g.scale, g.Hq * g.D, 0, 3, nullptr));
+  HIP_OK(hipDeviceSynchronize());
+  HIP_OK(hipMemcpy(got.data(), out, got.size() * 2, hipMemcpyDeviceToHost));
+  ok = close(got, g.out, "whole decode without workspace") && ok;
+
   // an invalid call is refused with a status, and nothing runs
   const int st = paged_decode_attn_splitk_bf16(q, kc, vc, nullptr, bt, lens, g.max_blocks, g.Hq,
                                                g.Hkv, g.D, g.bs, g.scale, 2, g.Hq * g.D, g.B, 0,

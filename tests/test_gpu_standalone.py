@@ -1,7 +1,9 @@
 """The standalone C++ test of the C ABI (tests/standalone/decode_tiny.cpp),
 run as its own process: cache write, split-K + combine at three split
-counts and the whole-decode call on the tiny workload, against the oracle's
-output stored in tests/golden/tiny_decode.txt."""
+counts, the split-K pass with the cache write folded in (output and cache
+bytes), the whole-decode call and the whole decode without a workspace, on
+the tiny workload, against the oracle's output stored in
+tests/golden/tiny_decode.txt."""
 import os
 import subprocess
 
